@@ -1,0 +1,172 @@
+"""CPU oracle for N:M bitmask sparse GEMV -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP product path never imports,
+links or executes it, and it shares no code with that path: the arithmetic
+lives in ``nm_oracle.c`` (plain C, fp64), built with gcc, and this module only
+marshals numpy arrays into it.
+
+Functions and the passages they follow (SparseDecoding, arXiv 2610.12327):
+
+* :func:`pack` / :func:`unpack` -- bitmask indexing with values in increasing
+  column order ("Method", kernel subsection, item (1) "Bitmask indexing"), one
+  bit at a time.
+* :func:`count_bad_groups` -- the N:M constraint (N kept in each group of M
+  consecutive weights; "Related work", N:M paragraph).
+* :func:`masked_gemv` -- the dense product of the masked weights with x in
+  fp64, which is what the sparse kernel computes exactly up to rounding
+  ("Method", "Decoding is dominated by SpMV operations").
+* :func:`decode16` -- binary16 / bfloat16 bit patterns to float64 from the
+  format definitions.
+
+Every function here is pinned in ``tests/test_oracle_pins.py`` against facts
+that do not come from this code (library routines, closed forms, brute force,
+exhaustive enumeration, the worked bit-count example printed on the pages).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nm_oracle.c")
+_LIB = os.path.join(_HERE, "libnm_oracle.so")
+
+OK = 0
+ERR_UNSUPPORTED = -2
+ERR_SHAPE = -3
+ERR_MASK = -5
+
+_lib = None
+
+
+def build() -> str:
+    """Compile nm_oracle.c with gcc into libnm_oracle.so (always rebuilds)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    ci = ctypes.c_int
+    lib.oracle_decode16.argtypes = [p, i64, ci, p]
+    lib.oracle_decode16.restype = None
+    lib.oracle_pattern_supported.argtypes = [ci, ci]
+    lib.oracle_pattern_supported.restype = ci
+    lib.oracle_count_bad_groups.argtypes = [p, i64, i64, ci, ci]
+    lib.oracle_count_bad_groups.restype = i64
+    lib.oracle_pack.argtypes = [p, p, i64, i64, ci, ci, p, p]
+    lib.oracle_pack.restype = ci
+    lib.oracle_unpack.argtypes = [p, p, i64, i64, ci, ci, p, p]
+    lib.oracle_unpack.restype = ci
+    lib.oracle_masked_gemv_f64.argtypes = [p, p, ci, p, ci, i64, i64, p, i64, ci, p]
+    lib.oracle_masked_gemv_f64.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _bits16(a) -> np.ndarray:
+    """View a float16 / uint16 / int16 array as contiguous uint16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype.itemsize != 2:
+        raise TypeError(f"expected a 16-bit array, got {a.dtype}")
+    return a.view(np.uint16)
+
+
+def _keep_u8(keep) -> np.ndarray:
+    return np.ascontiguousarray(keep).astype(np.uint8, copy=False)
+
+
+def decode16(bits, is_bf16: bool) -> np.ndarray:
+    """float64 values of binary16 (is_bf16=False) or bfloat16 bit patterns."""
+    b = _bits16(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_decode16(_ptr(b), b.size, int(bool(is_bf16)), _ptr(out))
+    return out
+
+
+def pattern_supported(n: int, m: int) -> bool:
+    return bool(_load().oracle_pattern_supported(n, m))
+
+
+def count_bad_groups(keep, n: int, m: int) -> int:
+    k = _keep_u8(keep)
+    rows, cols = k.shape
+    return int(_load().oracle_count_bad_groups(_ptr(k), rows, cols, n, m))
+
+
+def pack(W, keep, n: int, m: int):
+    """Return (status, values uint16[rows, cols*n/m], bits uint32[rows, cols/32])."""
+    w = _bits16(W)
+    k = _keep_u8(keep)
+    rows, cols = w.shape
+    if k.shape != w.shape:
+        raise ValueError("W and keep must have the same shape")
+    vcols = cols * n // m if m else 0
+    values = np.zeros((rows, max(vcols, 0)), dtype=np.uint16)
+    bits = np.zeros((rows, cols // 32), dtype=np.uint32)
+    st = _load().oracle_pack(_ptr(w), _ptr(k), rows, cols, n, m, _ptr(values), _ptr(bits))
+    return st, values, bits
+
+
+def unpack(values, bits, cols: int, n: int, m: int):
+    """Return (status, W uint16[rows, cols], keep uint8[rows, cols])."""
+    v = _bits16(values)
+    b = np.ascontiguousarray(bits, dtype=np.uint32)
+    rows = b.shape[0]
+    W = np.zeros((rows, cols), dtype=np.uint16)
+    keep = np.zeros((rows, cols), dtype=np.uint8)
+    st = _load().oracle_unpack(_ptr(v), _ptr(b), rows, cols, n, m, _ptr(W), _ptr(keep))
+    return st, W, keep
+
+
+def masked_gemv(W, keep, x, is_bf16: bool, rows_idx=None, threads: int = 1) -> np.ndarray:
+    """fp64 y[b, i] = sum_c keep[r, c] * W[r, c] * x[b, c] for r = rows_idx[i].
+
+    ``keep=None`` gives the dense product.  x is (batch, cols) or (cols,);
+    the result is (batch, nrows) float64 (or (nrows,) for 1-D x).
+    """
+    w = _bits16(W)
+    rows, cols = w.shape
+    xb = _bits16(x)
+    squeeze = xb.ndim == 1
+    if squeeze:
+        xb = xb.reshape(1, -1)
+    if xb.shape[1] != cols:
+        raise ValueError("x length must equal the number of columns")
+    batch = xb.shape[0]
+    if rows_idx is None:
+        idx = None
+        nrows = rows
+    else:
+        idx = np.ascontiguousarray(rows_idx, dtype=np.int64)
+        if idx.size and (idx.min() < 0 or idx.max() >= rows):
+            raise IndexError("row index out of range")
+        nrows = idx.size
+    k = None if keep is None else _keep_u8(keep)
+    if k is not None and k.shape != w.shape:
+        raise ValueError("W and keep must have the same shape")
+    y = np.zeros((batch, nrows), dtype=np.float64)
+    _load().oracle_masked_gemv_f64(
+        _ptr(w), None if k is None else _ptr(k), int(bool(is_bf16)), _ptr(xb), batch,
+        rows, cols, None if idx is None else _ptr(idx), nrows, int(threads), _ptr(y))
+    return y[0] if squeeze else y

@@ -1,0 +1,255 @@
+"""Pins for the CPU oracle: facts that do not come from the oracle itself.
+
+Each test names the passage of the pages (SparseDecoding, arXiv 2610.12327) or
+the mathematical fact it checks.  A plausible mistake in the oracle -- a wrong
+bit order, a dropped term, a transposed operand, a mis-decoded exponent --
+fails at least one of them.
+"""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_gemv_memory_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---- binary16 / bfloat16 decoding ---------------------------------------------
+
+def test_decode_f16_all_patterns_match_numpy():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode16(bits, is_bf16=False)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # sign of zero survives
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0])
+
+
+def test_decode_bf16_all_patterns_match_float32_top_half():
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    got = oracle.decode16(bits.astype(np.uint16), is_bf16=True)
+    with np.errstate(invalid="ignore"):
+        ref = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_decode_known_values():
+    # closed forms: 1.0, -2.0, smallest subnormal, largest finite
+    f16 = np.array([0x3C00, 0xC000, 0x0001, 0x7BFF], dtype=np.uint16)
+    assert list(oracle.decode16(f16, False)) == [1.0, -2.0, 2.0 ** -24, 65504.0]
+    bf = np.array([0x3F80, 0xC000, 0x0001, 0x7F7F], dtype=np.uint16)
+    assert list(oracle.decode16(bf, True)) == [1.0, -2.0, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127]
+
+
+# ---- pack / unpack ------------------------------------------------------------
+
+def _brute_pack(W, keep):
+    """Pack from the list of kept columns (a second, independent formulation)."""
+    rows, cols = W.shape
+    vals, words = [], []
+    for r in range(rows):
+        kept = [c for c in range(cols) if keep[r, c]]
+        vals.append([int(W[r, c]) for c in sorted(kept)])
+        words.append([sum(1 << (c - 32 * w) for c in kept if c // 32 == w) for w in range(cols // 32)])
+    return np.array(vals, dtype=np.uint16), np.array(words, dtype=np.uint32)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32)])
+def test_pack_matches_brute_force(n, m):
+    rows, cols = 5, 96
+    W = synth.weights(rows, cols, seed=7)
+    keep = synth.random_mask(rows, cols, n, m, seed=11)
+    st, values, bits = oracle.pack(W, keep, n, m)
+    assert st == oracle.OK
+    bv, bb = _brute_pack(W, keep)
+    assert np.array_equal(values, bv)
+    assert np.array_equal(bits, bb)
+
+
+def test_pack_exhaustive_2of4_words():
+    """Every one of the 6**8 aligned 2:4 words, as the rows of one matrix.
+
+    With W[r, c] = c the packed values of a row are its kept column indices,
+    which pins the bit <-> column mapping (bit b of word w is column 32w+b)
+    and the increasing-column value order ("Method", item (1))."""
+    nibbles = np.array([0b0011, 0b0101, 0b0110, 0b1001, 0b1010, 0b1100], dtype=np.uint32)
+    idx = np.arange(6 ** 8, dtype=np.int64)
+    word = np.zeros(idx.shape, dtype=np.uint32)
+    for g in range(8):
+        word |= nibbles[(idx // 6 ** g) % 6] << np.uint32(4 * g)
+    keep = ((word[:, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(np.uint8)
+    W = np.broadcast_to(np.arange(32, dtype=np.uint16), keep.shape).copy()
+    st, values, bits = oracle.pack(W, keep, 2, 4)
+    assert st == oracle.OK
+    assert np.array_equal(bits[:, 0], word)
+    assert len(np.unique(bits[:, 0])) == 6 ** 8
+    expect = np.nonzero(keep)[1].reshape(-1, 16).astype(np.uint16)
+    assert np.array_equal(values, expect)
+    # 16 set bits in every aligned word ("Method", item (2))
+    assert np.all(np.unpackbits(bits.view(np.uint8), axis=1).sum(axis=1) == 16)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32)])
+def test_every_word_has_16_set_bits(n, m):
+    W = synth.weights(64, 256, seed=3)
+    keep = synth.topn_mask(W, n, m)
+    st, values, bits = oracle.pack(W, keep, n, m)
+    assert st == oracle.OK
+    pop = np.unpackbits(bits.view(np.uint8).reshape(bits.shape + (4,)), axis=-1).sum(axis=-1)
+    assert np.all(pop == 16)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32)])
+def test_unpack_inverts_pack(n, m):
+    W = synth.weights(33, 160, seed=5, dtype="bf16")
+    keep = synth.random_mask(33, 160, n, m, seed=6)
+    st, values, bits = oracle.pack(W, keep, n, m)
+    assert st == oracle.OK
+    st, W2, k2 = oracle.unpack(values, bits, 160, n, m)
+    assert st == oracle.OK
+    assert np.array_equal(k2, keep)
+    assert np.array_equal(W2, np.where(keep != 0, W, 0).astype(np.uint16))
+
+
+def test_pack_moves_raw_patterns():
+    """Kept -0.0, subnormals, inf and NaN patterns survive unchanged (the mask
+    decides what is kept, not the value)."""
+    W = np.array([[0x8000, 0x0001, 0x7C00, 0x7E01] * 8], dtype=np.uint16)
+    keep = np.array([[1, 1, 0, 0, 0, 0, 1, 1] * 4], dtype=np.uint8)
+    st, values, bits = oracle.pack(W, keep, 2, 4)
+    assert st == oracle.OK
+    assert list(values[0, :4]) == [0x8000, 0x0001, 0x7C00, 0x7E01]
+    assert bits[0, 0] == 0xC3C3C3C3
+
+
+def test_pack_rejects_bad_inputs():
+    W = synth.weights(2, 64, seed=1)
+    keep = synth.random_mask(2, 64, 2, 4, seed=2)
+    bad = keep.copy()
+    bad[1, 5] ^= 1  # one group now holds 1 or 3
+    assert oracle.pack(W, bad, 2, 4)[0] == oracle.ERR_MASK
+    assert oracle.count_bad_groups(bad, 2, 4) == 1
+    assert oracle.pack(W, keep, 1, 4)[0] == oracle.ERR_UNSUPPORTED
+    assert oracle.pack(W, keep, 3, 8)[0] == oracle.ERR_UNSUPPORTED
+    assert oracle.pack(W[:, :48], keep[:, :48], 2, 4)[0] == oracle.ERR_SHAPE
+
+
+def test_sizes_match_worked_slice_on_the_pages():
+    """The explainer's 32-column fp16 slice: 256 value bits + one 32-bit word
+    = 288 bits against 512 dense; 2 metadata bits per kept weight."""
+    g = json.load(open(os.path.join(GOLDEN, "p4_bit_count.json")))
+    m2 = json.load(open(os.path.join(GOLDEN, "p2_metadata_bits.json")))
+    W = synth.weights(1, g["cols"], seed=0)
+    keep = synth.topn_mask(W, 2, 4)
+    st, values, bits = oracle.pack(W, keep, 2, 4)
+    assert st == oracle.OK
+    assert values.size == g["kept"]
+    assert values.nbytes * 8 == g["kept_value_bits"]
+    assert bits.nbytes * 8 == g["bitmask_metadata_bits"]
+    assert values.nbytes * 8 + bits.nbytes * 8 == g["bitmask_slice_bits"]
+    assert W.nbytes * 8 == g["dense_slice_bits"]
+    assert g["kept"] * 32 + values.nbytes * 8 == g["int32_index_slice_bits"]
+    per_nz = bits.nbytes * 8 / values.size
+    assert per_nz == g["bitmask_bits_per_kept_weight"] == m2["bitmask_bits_per_nonzero"]
+    assert m2["int32_index_bits_per_nonzero"] / per_nz == m2["reduction_vs_int32"]
+    assert m2["uint8_offset_bits_per_nonzero"] / per_nz == m2["reduction_vs_uint8"]
+    assert abs(g["bitmask_slice_bits"] / g["dense_slice_bits"] - g["bitmask_fraction_of_dense_approx"]) < 0.01
+
+
+def test_packed_size_is_pattern_independent():
+    """All 50% patterns keep the same bytes per row ("Experiments", Table 3
+    paragraph: identical memory traffic per row)."""
+    W = synth.weights(8, 256, seed=9)
+    sizes = set()
+    for n, m in [(2, 4), (4, 8), (8, 16), (16, 32)]:
+        st, values, bits = oracle.pack(W, synth.topn_mask(W, n, m), n, m)
+        assert st == oracle.OK
+        sizes.add((values.nbytes, bits.nbytes))
+    assert sizes == {(8 * 128 * 2, 8 * 8 * 4)}
+
+
+# ---- the product ----------------------------------------------------------------
+
+def _f64(bits, bf16):
+    if bf16:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n,m", [(2, 4), (16, 32)])
+def test_masked_gemv_matches_numpy_matmul(dtype, n, m):
+    rows, cols, batch = 37, 320, 3
+    W = synth.weights(rows, cols, seed=1, dtype=dtype)
+    keep = synth.topn_mask(W, n, m)
+    x = synth.activations(batch, cols, seed=1, dtype=dtype)
+    bf = dtype == "bf16"
+    y = oracle.masked_gemv(W, keep, x, bf)
+    ref = _f64(x, bf) @ (_f64(W, bf) * keep).T
+    assert y.shape == (batch, rows)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-15)
+    # dense product (keep=None) is the unmasked matmul
+    yd = oracle.masked_gemv(W, None, x, bf)
+    assert np.allclose(yd, _f64(x, bf) @ _f64(W, bf).T, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_masked_gemv_integer_inputs_exact(dtype):
+    rows, cols, batch = 50, 512, 4
+    W = synth.integer_weights(rows, cols, seed=2, dtype=dtype)
+    xi = np.random.default_rng(3).integers(-4, 5, size=(batch, cols))
+    x = synth.f32_to_16_bits(xi.astype(np.float32), dtype)
+    keep = synth.random_mask(rows, cols, 2, 4, seed=4)
+    Wi = np.rint(_f64(W, dtype == "bf16")).astype(np.int64)
+    exact = xi @ (Wi * keep).T
+    y = oracle.masked_gemv(W, keep, x, dtype == "bf16")
+    assert np.array_equal(y, exact.astype(np.float64))
+
+
+def test_masked_gemv_one_hot_picks_a_column():
+    rows, cols = 20, 128
+    W = synth.weights(rows, cols, seed=8)
+    keep = synth.topn_mask(W, 2, 4)
+    Wf = _f64(W, False)
+    for j in (0, 1, 31, 32, 77, 127):
+        x = np.zeros(cols, dtype=np.float16)
+        x[j] = 1.0
+        y = oracle.masked_gemv(W, keep, x.view(np.uint16), False)
+        assert np.array_equal(y, Wf[:, j] * keep[:, j])
+
+
+def test_masked_gemv_all_ones_sums_kept_values():
+    rows, cols = 16, 256
+    W = synth.weights(rows, cols, seed=12)
+    keep = synth.topn_mask(W, 4, 8)
+    st, values, bits = oracle.pack(W, keep, 4, 8)
+    x = np.ones(cols, dtype=np.float16).view(np.uint16)
+    y = oracle.masked_gemv(W, keep, x, False)
+    ref = np.array([np.sum(values[r].view(np.float16).astype(np.float64)) for r in range(rows)])
+    assert np.allclose(y, ref, rtol=1e-13, atol=0)
+
+
+def test_masked_gemv_row_sampling_matches_full():
+    W = synth.weights(64, 128, seed=13)
+    keep = synth.topn_mask(W, 2, 4)
+    x = synth.activations(2, 128, seed=13)
+    full = oracle.masked_gemv(W, keep, x, False, threads=4)
+    idx = np.array([63, 0, 17, 17, 5])
+    part = oracle.masked_gemv(W, keep, x, False, rows_idx=idx)
+    assert np.array_equal(part, full[:, idx])
+
+
+def test_masked_gemv_empty_cols_is_zero():
+    W = np.zeros((3, 0), dtype=np.uint16)
+    x = np.zeros((1, 0), dtype=np.uint16)
+    y = oracle.masked_gemv(W, np.zeros((3, 0), np.uint8), x, False)
+    assert np.array_equal(y, np.zeros((1, 3)))
