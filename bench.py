@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the N:M bitmask sparse GEMV on one MI355X.
+
+Workload: the seven linear projections of one Llama-3.1-8B-shaped decoder
+layer (q, o 4096x4096; k, v 1024x4096; gate, up 14336x4096; down 4096x14336),
+each a seeded synthetic 2:4 fp16 matrix (weights N(0, 0.02), the 2 largest
+|w| of every 4 kept), x ~ N(0, 1) with 0.1% outlier channels x20, batch 1.
+A step is one pass of the hot path over the layer: the seven nm_spmv calls.
+
+Measurement:
+* every projection has its own rotation of packed copies totalling >= 1 GiB,
+  so no call finds its weights in the 256 MiB Infinity Cache or in L2;
+* each step's seven launches are captured once in a HIP graph and replayed
+  (the kernels are a few microseconds long, shorter than a Python launch);
+* the K timed steps are bracketed by torch.cuda.synchronize() and HIP events;
+* per-kernel duration: a graph of back-to-back launches of one projection
+  over its rotation, HIP events around each replay, divided by the launches;
+* value = algorithmic bytes of the layer (packed values + mask words + x + y,
+  each moved once) / step time.
+The dense comparison runs the same protocol with nm_dense_gemv and with
+torch.nn.functional.linear on dense copies.  The CPU baseline times the oracle
+(fp64 dense-masked product) on the same layer on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_gemv_memory_amd import native, synth, workloads  # noqa: E402
+
+METRIC = "µs/call and achieved HBM GB/s (% of peak) for 2:4 sparse GEMV, batch 1"
+PEAK_GBS = 8000.0  # MI355X HBM3E, published
+ROTATE_BYTES = 1 << 30
+DEV = torch.device("cuda:0")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def t16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).to(DEV)
+
+
+def pow2_copies(nbytes):
+    return max(2, 1 << math.ceil(math.log2(max(1.0, ROTATE_BYTES / nbytes))))
+
+
+class Proj:
+    """One projection: host inputs, packed rotation copies, dense copies."""
+
+    def __init__(self, mt, batches, want_dense):
+        self.mt = mt
+        self.name = mt.name
+        t0 = time.time()
+        self.W = synth.weights(mt.rows, mt.cols, seed=mt.seed, dtype=mt.dtype)
+        self.keep = synth.topn_mask(self.W, mt.n, mt.m)
+        self.X = {b: synth.activations(b, mt.cols, seed=mt.seed, dtype=mt.dtype, outliers=mt.outliers)
+                  for b in batches}
+        Wd = t16(self.W)
+        values, bits = native.nm_pack(Wd, torch.from_numpy(self.keep).to(DEV), mt.n, mt.m)
+        self.sbytes = {b: workloads.sparse_bytes(mt.rows, mt.cols, mt.n, mt.m, b, 4) for b in batches}
+        self.dbytes = {b: workloads.dense_bytes(mt.rows, mt.cols, b, 4) for b in batches}
+        packed = values.numel() * 2 + bits.numel() * 4
+        self.nc = pow2_copies(packed)
+        self.vals = [values] + [values.clone() for _ in range(self.nc - 1)]
+        self.bits = [bits] + [bits.clone() for _ in range(self.nc - 1)]
+        self.ndc = pow2_copies(Wd.numel() * 2) if want_dense else 0
+        self.dense = ([Wd] + [Wd.clone() for _ in range(self.ndc - 1)]) if want_dense else []
+        if not want_dense:
+            del Wd
+        self.Xd = {b: t16(self.X[b]) for b in batches}
+        self.Y = {b: torch.empty((b, mt.rows), dtype=torch.float32, device=DEV) for b in batches}
+        self.args = {}
+        log(f"  {self.name:5s} {mt.rows}x{mt.cols}: {self.nc} packed copies "
+            f"({self.nc * packed / 2**30:.2f} GiB), {self.ndc} dense copies, {time.time() - t0:.1f}s")
+
+    def sparse_call(self, b, c):
+        """Launch the sparse product on copy c at batch b (raw C call)."""
+        L = native.lib()
+        mt = self.mt
+        st = L.nm_spmm_small(self.vals[c].data_ptr(), self.bits[c].data_ptr(), self.Xd[b].data_ptr(),
+                             self.Y[b].data_ptr(), b, mt.rows, mt.cols, mt.n, mt.m, native.NM_F16,
+                             native.NM_F32, torch.cuda.current_stream().cuda_stream) if b > 1 else \
+            L.nm_spmv(self.vals[c].data_ptr(), self.bits[c].data_ptr(), self.Xd[b].data_ptr(),
+                      self.Y[b].data_ptr(), mt.rows, mt.cols, mt.n, mt.m, native.NM_F16,
+                      native.NM_F32, torch.cuda.current_stream().cuda_stream)
+        if st != native.NM_OK:
+            raise native.NMError(st, f"{self.name} sparse b={b}")
+
+    def dense_call(self, b, c):
+        L = native.lib()
+        mt = self.mt
+        st = L.nm_dense_gemv(self.dense[c].data_ptr(), self.Xd[b].data_ptr(), self.Y[b].data_ptr(), b,
+                             mt.rows, mt.cols, native.NM_F16, native.NM_F32,
+                             torch.cuda.current_stream().cuda_stream)
+        if st != native.NM_OK:
+            raise native.NMError(st, f"{self.name} dense b={b}")
+
+    def torch_call(self, b, c):
+        torch.nn.functional.linear(self.Xd[b], self.dense[c])
+
+
+def capture(fn):
+    """Capture fn() (a few kernel launches) into a HIP graph."""
+    fn()  # eager run first: initialises everything outside capture
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def time_steps(graphs, steps, warmup):
+    """Replay graphs[i % len] for warmup + steps; return ms per timed step."""
+    n = len(graphs)
+    for i in range(warmup):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[(warmup + i) % n].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def chain_graphs(projs, call, b, nsteps, copies_attr):
+    graphs = []
+    for s in range(nsteps):
+        def step(s=s):
+            for p in projs:
+                call(p, b, s % getattr(p, copies_attr))
+        graphs.append(capture(step))
+    return graphs
+
+
+def per_kernel_us(p, call, b, ncopies, reps):
+    """Average duration of one launch: a graph of back-to-back launches over
+    the projection's rotation, HIP events around each replay."""
+    g = capture(lambda: [call(p, b, c) for c in range(ncopies)])
+    g.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, z in evs:
+        a.record()
+        g.replay()
+        z.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(z) for a, z in evs]
+    return 1e3 * float(np.median(ms)) / ncopies
+
+
+def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
+    """The oracle on the whole layer at batch 1, on the host cores."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = max(1, min(threads, os.cpu_count() or 1))
+    total_bytes = sum(p.sbytes[1] for p in projs)
+    reps, wall = 0, 0.0
+    errs = {}
+    while True:
+        t0 = time.perf_counter()
+        for p in projs:
+            y = oracle.masked_gemv(p.W, p.keep, p.X[1], False, threads=threads)
+            if reps == 0:
+                got = gpu_y[p.name].astype(np.float64)
+                errs[p.name] = float(np.linalg.norm(got - y[0]) / np.linalg.norm(y[0]))
+        wall += time.perf_counter() - t0
+        reps += 1
+        if wall * threads >= min_cpu_seconds or reps >= 20:
+            break
+    sec_per_layer = wall / reps
+    return {
+        "value": total_bytes / sec_per_layer / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"the whole workload: all 7 projections of the layer at batch 1, {reps} passes "
+                   f"(fp64 dense-masked product, C + OpenMP over rows); "
+                   f"{1e6 * sec_per_layer:.0f} us per layer pass"),
+        "us_per_step": 1e6 * sec_per_layer,
+        "gpu_vs_oracle_rel_l2": errs,
+        "host": platform.processor() or platform.machine(),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--reps", type=int, default=20, help="replays per per-kernel timing")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense comparison")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batch4", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the N:M SpMV path is built and timed on a single "
+              "MI355X (row or K sharding across GPUs is a design note, not implemented)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    native.lib()  # fail loudly if the HIP library is missing
+
+    batches = (1,) if args.no_batch4 else (1, 4)
+    want_dense = not args.no_dense
+    log(f"building the Llama-3.1-8B layer workload (2:4 fp16), batches {batches}")
+    projs = [Proj(mt, batches, want_dense) for mt, _ in workloads.config_matrices(2)]
+    layer_bytes = {b: sum(p.sbytes[b] for p in projs) for b in batches}
+    nsteps = min(args.steps + args.warmup, 256)
+
+    out = {}
+    timings = {}
+    for b in batches:
+        log(f"sparse chain b={b}: capturing {nsteps} step graphs")
+        g = chain_graphs(projs, Proj.sparse_call, b, nsteps, "nc")
+        torch.cuda.synchronize()
+        ms = time_steps(g, args.steps, args.warmup)
+        timings[("sparse", b)] = ms
+        del g
+        if want_dense:
+            for kind, call in (("dense", Proj.dense_call), ("torch", Proj.torch_call)):
+                g = chain_graphs(projs, call, b, nsteps, "ndc")
+                timings[(kind, b)] = time_steps(g, args.steps, args.warmup)
+                del g
+        for k, v in timings.items():
+            if k[1] == b:
+                log(f"  {k[0]:6s} b={b}: {1e3 * v:8.1f} us/step")
+
+    # per-kernel durations (batch 1) and the roofline of the dominant kernel
+    per = {}
+    for p in projs:
+        us = per_kernel_us(p, Proj.sparse_call, 1, p.nc, args.reps)
+        d = {"us": round(us, 3), "GB/s": round(p.sbytes[1] / us / 1e3, 1),
+             "frac_of_peak": round(p.sbytes[1] / us / 1e3 / PEAK_GBS, 4)}
+        if want_dense:
+            dus = per_kernel_us(p, Proj.dense_call, 1, p.ndc, args.reps)
+            tus = per_kernel_us(p, Proj.torch_call, 1, p.ndc, args.reps)
+            d.update({"dense_us": round(dus, 3), "torch_linear_us": round(tus, 3),
+                      "speedup_vs_best_dense": round(min(dus, tus) / us, 3)})
+        per[f"{p.name} {p.mt.rows}x{p.mt.cols}"] = d
+        log(f"  {p.name:5s} {p.mt.rows:5d}x{p.mt.cols:5d}: {us:7.2f} us  "
+            f"{d['GB/s']:7.1f} GB/s ({100 * d['frac_of_peak']:.1f}% of 8 TB/s)"
+            + (f"  dense {d['dense_us']:.2f} us, torch {d['torch_linear_us']:.2f} us" if want_dense else ""))
+    dom = max(projs, key=lambda p: per[f"{p.name} {p.mt.rows}x{p.mt.cols}"]["us"])
+    dk = per[f"{dom.name} {dom.mt.rows}x{dom.mt.cols}"]
+    roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(dk["GB/s"] / PEAK_GBS, 4), "traffic": None,
+                "kernel": f"nm_spmv_kernel {dom.mt.rows}x{dom.mt.cols} 2:4 fp16 b1",
+                "bytes_per_launch": dom.sbytes[1], "us_per_launch": dk["us"]}
+
+    ms = timings[("sparse", 1)]
+    res = {
+        "metric": METRIC,
+        "value": round(layer_bytes[1] / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped decoder layer, 7 projections "
+                               "(q,o 4096x4096; k,v 1024x4096; gate,up 14336x4096; down 4096x14336), "
+                               "2:4 fp16, x N(0,1) + 0.1% outlier channels x20",
+                   "batch": 1, "pattern": "2:4", "bytes_per_step": layer_bytes[1],
+                   "launches_per_step": len(projs), "timing": "HIP-graph replay per step, "
+                   ">=1 GiB rotation per projection (cache-cold)"},
+        "frac_of_peak": round(layer_bytes[1] / (ms * 1e-3) / 1e9 / PEAK_GBS, 4),
+        "us_per_call": per,
+        "roofline": roofline,
+    }
+    if want_dense:
+        res["dense_ms_per_step"] = {"nm_dense_gemv": round(timings[("dense", 1)], 5),
+                                    "torch_linear": round(timings[("torch", 1)], 5)}
+        res["speedup_vs_best_dense"] = round(min(timings[("dense", 1)], timings[("torch", 1)]) / ms, 3)
+    if 4 in batches:
+        ms4 = timings[("sparse", 4)]
+        b4 = {"ms_per_step": round(ms4, 5), "GB/s": round(layer_bytes[4] / (ms4 * 1e-3) / 1e9, 1)}
+        if want_dense:
+            b4["dense_ms_per_step"] = {"nm_dense_gemv": round(timings[("dense", 4)], 5),
+                                       "torch_linear": round(timings[("torch", 4)], 5)}
+            b4["speedup_vs_best_dense"] = round(min(timings[("dense", 4)], timings[("torch", 4)]) / ms4, 3)
+        res["batch4"] = b4
+    if not args.no_cpu_baseline:
+        gpu_y = {}
+        for p in projs:
+            p.sparse_call(1, 0)
+        torch.cuda.synchronize()
+        for p in projs:
+            gpu_y[p.name] = p.Y[1][0].cpu().numpy()
+        log("cpu baseline: timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(projs, gpu_y)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * nm_sparse.h -- C ABI of the N:M bitmask sparse GEMV library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation: at decode time every pruned linear layer computes
+ * y = W_sparse . x for one token (batch 1) or a few tokens (batch 2..8).
+ * W keeps N of every M consecutive weights of a row (N:M semi-structured
+ * sparsity) and is stored as
+ *   - values: the kept weights of each row in increasing column order, and
+ *   - bits:   one bit per column, 32 columns per 32-bit word, a set bit
+ *             meaning "this column's weight is kept".
+ * Passages that define it, in "SparseDecoding: Decoding-Aware Pruning for
+ * Accurate and Efficient LLM Inference" (paper text):
+ *   - Method, kernel subsection, opening paragraph: decoding is dominated by
+ *     N:M SpMV at batch one and small batch;
+ *   - same subsection, item (1) "Bitmask indexing": one bit per column, kept
+ *     weights stored in increasing column order so the set bits line up with
+ *     the stored values; 2 bits of metadata per kept weight at 50%;
+ *   - same subsection, item (2) "Fixed-step bitmask traversal": at 50% N:M
+ *     density with M <= 32 every aligned 32-bit word holds exactly 16 set
+ *     bits, and the least significant set bit gives the next kept column;
+ *   - Appendix C (kernel implementation): one compiled kernel per N:M pattern,
+ *     N and M fixed at compile time.
+ *
+ * Layout (shared by every entry point):
+ *   - rows R = output features (d_out), cols K = input features (d_in);
+ *     dense W is R x K row-major (leading dimension K);
+ *   - N:M groups run along a row (along K); only the 50% patterns
+ *     N = M/2, M in {4, 8, 16, 32} are supported;
+ *   - K must be a multiple of 32 (hence of M);
+ *   - values: R x (K/2) 16-bit elements, row-major, row stride K/2;
+ *     the 16 kept values of word w of a row are values[r][16w .. 16w+15];
+ *   - bits:   R x (K/32) uint32 words, row-major, row stride K/32;
+ *     bit b (LSB = 0) of word w is column 32w + b;
+ *   - x: batch x K row-major (one token per row); y: batch x R row-major,
+ *     i.e. y = x . W_sparse^T, the convention of torch.nn.functional.linear.
+ *
+ * Ownership and streams: every pointer below is a device pointer the caller
+ * allocated and owns; the library keeps no pointer after a call returns and
+ * allocates no memory, except nm_pack (see there).  `stream` is a hipStream_t
+ * passed as void* (NULL = the null stream); all device work of a call is
+ * enqueued on it.  nm_spmv, nm_spmm_small and nm_dense_gemv return as soon as
+ * the work is enqueued.
+ *
+ * Errors: every function returns an nm_status.  All argument checks run on
+ * the host before any HIP call, so a call that returns NM_ERR_INVALID_ARG,
+ * NM_ERR_UNSUPPORTED, NM_ERR_SHAPE or NM_ERR_ALIGN has done nothing on the
+ * device.  NM_ERR_HIP means a HIP runtime call or a kernel launch failed
+ * (nm_last_hip_error() gives the HIP error code).  A pointer may be NULL only
+ * when the buffer it stands for holds zero bytes.
+ */
+#ifndef NM_SPARSE_H
+#define NM_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NM_OK = 0,
+  NM_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, batch out of range */
+  NM_ERR_UNSUPPORTED = -2, /* N:M pattern or dtype combination not supported */
+  NM_ERR_SHAPE = -3,       /* K not a multiple of 32 */
+  NM_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
+  NM_ERR_MASK = -5,        /* nm_pack: some M-group does not keep exactly N */
+  NM_ERR_HIP = -6          /* HIP runtime or launch failure */
+} nm_status;
+
+typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_F32 = 2 } nm_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *nm_status_string(int status);
+
+/* HIP error code (hipError_t as int) of the last NM_ERR_HIP returned on the
+ * calling thread, 0 if none. */
+int nm_last_hip_error(void);
+
+/* Sizes in bytes of the packed buffers of an R x K matrix under pattern N:M
+ * with 16-bit elements of type dt (Method item (1): K*N/M values and K/32
+ * words per row).  Pure host arithmetic.
+ *   values_bytes = rows * cols * n / m * 2,  bits_bytes = rows * cols / 8.
+ * Errors: NM_ERR_INVALID_ARG (negative sizes, NULL outputs),
+ * NM_ERR_UNSUPPORTED (pattern, dt not 16-bit), NM_ERR_SHAPE (cols % 32). */
+int nm_packed_bytes(int64_t rows, int64_t cols, int n, int m, nm_dtype dt,
+                    size_t *values_bytes, size_t *bits_bytes);
+
+/* Pack a dense matrix and its keep-mask into values + bits (Method item (1)).
+ *   W:      device, rows x cols 16-bit elements (dt = NM_F16 or NM_BF16),
+ *           row-major, 2-byte aligned; copied as raw bit patterns, so -0.0,
+ *           subnormals, inf and NaN survive unchanged;
+ *   keep:   device, rows x cols bytes, row-major; nonzero = kept;
+ *   values: device, rows x cols*n/m 16-bit elements (output), 16-byte aligned;
+ *   bits:   device, rows x cols/32 uint32 (output), 4-byte aligned.
+ * The mask decides what is kept, never the value: a kept zero is stored.
+ * Validates that every M-group of every row keeps exactly N entries.  The
+ * call is synchronous: it waits for `stream` to read back the count of
+ * invalid groups, and allocates (and frees) 4 bytes of device memory for it.
+ * Returns NM_ERR_MASK when any group is invalid; values and bits then hold
+ * unspecified contents, but nothing outside them was written. */
+int nm_pack(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
+            int n, int m, nm_dtype dt, void *values, uint32_t *bits,
+            void *stream);
+
+/* Batch-1 sparse matrix-vector product (Method, kernel subsection; the
+ * decoding-specialised N:M SpMV):
+ *   y[r] = sum over kept columns c of row r of W[r][c] * x[c],  r < rows.
+ *   values, bits: as produced by nm_pack for pattern n:m (values 16-byte
+ *           aligned, bits 4-byte aligned); bits must hold exactly 16 set bits
+ *           per word -- a word that does not yields an unspecified result for
+ *           its row but no access outside the buffers;
+ *   x:      device, cols elements of in_dt, 16-byte aligned;
+ *   y:      device, rows elements of out_dt (overwritten), aligned to its
+ *           element size.
+ * in_dt is NM_F16 or NM_BF16 (values and x share it); out_dt is NM_F32 or
+ * in_dt (then rounded to nearest, ties to even).  Products are exact in
+ * fp32 and every sum is accumulated in fp32.  Asynchronous on `stream`. */
+int nm_spmv(const void *values, const uint32_t *bits, const void *x, void *y,
+            int64_t rows, int64_t cols, int n, int m, nm_dtype in_dt,
+            nm_dtype out_dt, void *stream);
+
+/* Small-batch product, the same operation for 1 <= batch <= 8 tokens (Method,
+ * kernel subsection: batch-one and small-batch decoding):
+ *   Y[b][r] = sum over kept c of W[r][c] * X[b][c].
+ *   X: device, batch x cols row-major, 16-byte aligned;
+ *   Y: device, batch x rows row-major (overwritten).
+ * Other arguments, precision and errors as nm_spmv; batch outside 1..8 gives
+ * NM_ERR_INVALID_ARG. */
+int nm_spmm_small(const void *values, const uint32_t *bits, const void *X,
+                  void *Y, int batch, int64_t rows, int64_t cols, int n, int m,
+                  nm_dtype in_dt, nm_dtype out_dt, void *stream);
+
+/* Dense comparison, the decode GEMV the sparse kernel replaces (Experiments,
+ * Table 3 paragraph: speedups are against the dense model's decode):
+ *   Y[b][r] = sum over all c of W[r][c] * X[b][c],  1 <= batch <= 8.
+ *   W: device, rows x cols row-major 16-bit (in_dt), 16-byte aligned;
+ *   X, Y, precision, errors: as nm_spmm_small (cols must be a multiple of
+ *   32 here too). */
+int nm_dense_gemv(const void *W, const void *X, void *Y, int batch,
+                  int64_t rows, int64_t cols, nm_dtype in_dt, nm_dtype out_dt,
+                  void *stream);
+
+/* Launch shape of the sparse and dense kernels, for tuning sweeps.  Fields
+ * set to 0 take the library's choice for the shape.
+ *   threads_per_wg: 64, 128, 256, 512 or 1024;
+ *   rows_per_wave:  1, 2 or 4 rows processed together by one wavefront;
+ *   seg_cols:       columns of x staged in LDS at a time (multiple of 32);
+ *                   K is walked in segments of this width. */
+typedef struct {
+  int threads_per_wg;
+  int rows_per_wave;
+  int seg_cols;
+} nm_launch_cfg;
+
+/* The launch shape nm_spmm_small / nm_dense_gemv would use for a call
+ * (dense != 0 selects the dense kernel).  Pure host arithmetic apart from
+ * one query of the current device's properties on first use. */
+int nm_default_launch(int64_t rows, int64_t cols, int batch, int dense,
+                      nm_launch_cfg *cfg);
+
+/* nm_spmm_small / nm_dense_gemv with an explicit launch shape (cfg may be
+ * NULL for the default).  Invalid shapes give NM_ERR_INVALID_ARG. */
+int nm_spmm_small_cfg(const void *values, const uint32_t *bits, const void *X,
+                      void *Y, int batch, int64_t rows, int64_t cols, int n,
+                      int m, nm_dtype in_dt, nm_dtype out_dt,
+                      const nm_launch_cfg *cfg, void *stream);
+int nm_dense_gemv_cfg(const void *W, const void *X, void *Y, int batch,
+                      int64_t rows, int64_t cols, nm_dtype in_dt,
+                      nm_dtype out_dt, const nm_launch_cfg *cfg, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NM_SPARSE_H */

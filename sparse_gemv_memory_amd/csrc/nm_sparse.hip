@@ -1,0 +1,766 @@
+// nm_sparse.hip -- N:M bitmask sparse GEMV for AMD Instinct MI355X (gfx950).
+//
+// Kernels and the C ABI declared in include/nm_sparse.h.  What is computed
+// follows "SparseDecoding: Decoding-Aware Pruning for Accurate and Efficient
+// LLM Inference" (paper text):
+//   - Method, kernel subsection, item (1) "Bitmask indexing": per row one bit
+//     per column, kept weights stored in increasing column order;
+//   - item (2) "Fixed-step bitmask traversal": at 50% N:M density each
+//     aligned 32-bit word has exactly 16 set bits, so the per-word loop has a
+//     fixed trip count; each step takes the least significant set bit as the
+//     next kept column and clears it;
+//   - Appendix C: one kernel per pattern with N and M fixed at compile time.
+// The Triton/A100 kernel described there is prior art only; the design here
+// is for CDNA4:
+//   - x is staged once per workgroup in LDS (the paper's kernel read x
+//     through L1 instead) in a padded layout, so the per-nonzero gathers of
+//     a wavefront spread over the LDS banks;
+//   - each lane owns one 16-byte chunk of a row's values (8 kept weights, one
+//     half of a mask word), so a wavefront reads 1 KiB of contiguous values
+//     per load instruction with 128-bit loads;
+//   - each lane walks its half-word in a fixed 8-step LSB scan (v_ffbl_b32),
+//     pairs two gathered x values into one register and accumulates with
+//     v_dot2_f32_{f16,bf16} (fp16/bf16 products are exact in fp32);
+//   - one wavefront per row (or a few rows), reduced across lanes at the end;
+//   - no MFMA: the operation is an HBM-bound matrix-vector product.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "nm_sparse.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr size_t kLdsBudget = 64 * 1024;  // bytes of LDS one workgroup may use
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + w.lo * x.lo + w.hi * x.hi with 16-bit pairs and an fp32 accumulator.
+template <bool BF>
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+  if constexpr (BF)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, w),
+                                           __builtin_bit_cast(b2_t, x), acc,
+                                           false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w),
+                                  __builtin_bit_cast(h2_t, x), acc, false);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// fp32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ void store_out(void *y, int64_t idx, float v,
+                                          int kind) {
+  if (kind == NM_F32)
+    static_cast<float *>(y)[idx] = v;
+  else if (kind == NM_F16)
+    static_cast<_Float16 *>(y)[idx] = (_Float16)v;  // v_cvt_f16_f32, RNE
+  else
+    static_cast<uint16_t *>(y)[idx] = f32_to_bf16_rne(v);
+}
+
+// LDS layout of a segment of x for the sparse kernel.  Column c of the
+// segment holds the BP batch values of that column in one slot of SB bytes;
+// the 32 slots of a mask word are followed by PB pad bytes, and PB bytes sit
+// in front of word 0.  The pad shifts consecutive words across LDS banks.  A
+// tail of 8 slots keeps the reads of a malformed mask word (fewer set bits
+// than its pattern requires, which walks into the sentinel bits) inside the
+// allocation.
+template <int BP>
+struct XLay {
+  static constexpr int SB = 2 * BP;
+  static constexpr int PB = SB < 4 ? 4 : SB;
+  static constexpr int WS = 32 * SB + PB;
+  static constexpr int FP = PB;
+  static constexpr size_t bytes(int seg_cols) {
+    return FP + (size_t)(seg_cols / 32) * WS + 8 * SB;
+  }
+};
+
+template <int BP>
+__device__ __forceinline__ void stage_x_sparse(char *lds,
+                                               const uint16_t *__restrict__ x,
+                                               int B, int K, int s0, int S) {
+  using L = XLay<BP>;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  if constexpr (BP == 1) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + s0);
+    for (int j = tid; j < S / 8; j += nthr) {
+      const uint4 q = src[j];
+      uint32_t *d =
+          reinterpret_cast<uint32_t *>(lds + L::FP + (j >> 2) * L::WS + (j & 3) * 16);
+      d[0] = q.x;
+      d[1] = q.y;
+      d[2] = q.z;
+      d[3] = q.w;
+    }
+  } else {
+    for (int c = tid; c < S; c += nthr) {
+      uint32_t d[BP / 2];
+#pragma unroll
+      for (int p = 0; p < BP / 2; ++p) {
+        const uint32_t lo = (2 * p < B) ? x[(int64_t)(2 * p) * K + s0 + c] : 0u;
+        const uint32_t hi = (2 * p + 1 < B) ? x[(int64_t)(2 * p + 1) * K + s0 + c] : 0u;
+        d[p] = lo | (hi << 16);
+      }
+      char *dst = lds + L::FP + (c >> 5) * L::WS + (c & 31) * L::SB;
+      if constexpr (BP == 2) {
+        *reinterpret_cast<uint32_t *>(dst) = d[0];
+      } else if constexpr (BP == 4) {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(d[0], d[1]);
+      } else {
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
+      }
+    }
+  }
+}
+
+// One lane's 16-byte chunk: 8 kept weights (4 packed pairs in v) whose
+// columns are the 8 lowest set bits of m.  `base` is the LDS byte address of
+// column 0 of the chunk's column range.  Two LSB-scan steps feed one dot2.
+template <bool BF, int BP>
+__device__ __forceinline__ void chunk8(const char *lds, uint32_t base,
+                                       uint32_t m, const uint4 v,
+                                       float (&acc)[BP]) {
+  using L = XLay<BP>;
+  const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  const char *wb = lds + base;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // m is never zero here (see the callers), so v_ffbl_b32 is well defined
+    const uint32_t c0 = __builtin_ctz(m);
+    m &= m - 1;
+    const uint32_t c1 = __builtin_ctz(m);
+    m &= m - 1;
+    const char *p0 = wb + c0 * L::SB;
+    const char *p1 = wb + c1 * L::SB;
+    if constexpr (BP == 1) {
+      // two 16-bit LDS reads into the low and high halves of one register
+      u16x2_t pr;
+      pr[0] = *reinterpret_cast<const uint16_t *>(p0);
+      pr[1] = *reinterpret_cast<const uint16_t *>(p1);
+      acc[0] = dot2<BF>(vv[j], __builtin_bit_cast(uint32_t, pr), acc[0]);
+    } else {
+      uint32_t X0[BP / 2], X1[BP / 2];
+      if constexpr (BP == 2) {
+        X0[0] = *reinterpret_cast<const uint32_t *>(p0);
+        X1[0] = *reinterpret_cast<const uint32_t *>(p1);
+      } else if constexpr (BP == 4) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(p0);
+        const uint2 b = *reinterpret_cast<const uint2 *>(p1);
+        X0[0] = a.x; X0[1] = a.y;
+        X1[0] = b.x; X1[1] = b.y;
+      } else {
+        const uint4 a = *reinterpret_cast<const uint4 *>(p0);
+        const uint4 b = *reinterpret_cast<const uint4 *>(p1);
+        X0[0] = a.x; X0[1] = a.y; X0[2] = a.z; X0[3] = a.w;
+        X1[0] = b.x; X1[1] = b.y; X1[2] = b.z; X1[3] = b.w;
+      }
+#pragma unroll
+      for (int d = 0; d < BP / 2; ++d) {
+        // (x0[b], x1[b]) pairs for batch rows b = 2d and 2d+1
+        const uint32_t lo = (X0[d] & 0xffffu) | (X1[d] << 16);
+        const uint32_t hi = (X0[d] >> 16) | (X1[d] & 0xffff0000u);
+        acc[2 * d] = dot2<BF>(vv[j], lo, acc[2 * d]);
+        acc[2 * d + 1] = dot2<BF>(vv[j], hi, acc[2 * d + 1]);
+      }
+    }
+  }
+}
+
+// Sparse product.  Workgroup g owns rows g*WPG*RPW + i*WPG + wave (i < RPW);
+// K is walked in segments of `seg` columns, each staged in LDS once per
+// workgroup.  Lane l of a wave handles value chunks l, l+64, ... of the
+// segment; chunk q is half (q & 1) of mask word q >> 1.
+//   M32 = false (M <= 16): a half-word's 16 columns hold exactly 8 kept
+//         weights, so the odd lane scans the upper 16 bits of the word;
+//   M32 = true (16:32): the 8 kept weights of the odd lane are set bits 8..15
+//         of the word, so it first clears the 8 lowest set bits.
+template <bool BF, int BP, bool M32, int RPW>
+__global__ __launch_bounds__(1024) void nm_spmv_kernel(
+    const uint4 *__restrict__ values, const uint32_t *__restrict__ bits,
+    const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R,
+    int K, int seg, int out_kind) {
+  using L = XLay<BP>;
+  constexpr int U = RPW >= 4 ? 2 : 4;  // chunks per lane per load batch
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int wpg = blockDim.x / kWave;
+  const int64_t row0 = (int64_t)blockIdx.x * wpg * RPW + wid;
+  const int64_t cpr = K >> 4;  // 16-byte value chunks per row
+  const int64_t wpr = K >> 5;  // mask words per row
+  const uint32_t h = lane & 1;
+
+  float acc[RPW][BP];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int b = 0; b < BP; ++b) acc[i][b] = 0.f;
+
+  for (int s0 = 0; s0 < K; s0 += seg) {
+    const int S = min(seg, K - s0);
+    if (s0) __syncthreads();  // all waves are done with the previous segment
+    stage_x_sparse<BP>(lds, x, B, K, s0, S);
+    __syncthreads();
+    const int nch = S >> 4;
+    const int64_t cbeg = s0 >> 4;
+    for (int t0 = 0; t0 < nch; t0 += kWave * U) {
+      uint4 v[RPW][U];
+      uint32_t mw[RPW][U];
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int64_t r = row0 + (int64_t)i * wpg;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = t0 + kWave * u + lane;
+          if (r < R && q < nch) {
+            v[i][u] = values[r * cpr + cbeg + q];
+            mw[i][u] = bits[r * wpr + ((cbeg + q) >> 1)];
+          } else {
+            v[i][u] = make_uint4(0, 0, 0, 0);
+            mw[i][u] = 0;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int64_t r = row0 + (int64_t)i * wpg;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = t0 + kWave * u + lane;
+          if (r < R && q < nch) {
+            uint32_t base = L::FP + (uint32_t)(q >> 1) * L::WS;
+            uint32_t m = mw[i][u];
+            if constexpr (!M32) {
+              // this lane's 16 columns in the low half; the sentinel bits
+              // above them keep every scan step on a nonzero word
+              m = (m >> (h << 4)) | 0xffff0000u;
+              base += h * (16 * L::SB);
+            } else {
+              // a word without exactly 16 set bits is replaced by one that
+              // keeps the scan in range (its row's result is then undefined)
+              if (__popc(m) != 16) m = 0xffffu;
+              if (h) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) m &= m - 1;
+              }
+            }
+            chunk8<BF, BP>(lds, base, m, v[i][u], acc[i]);
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int64_t r = row0 + (int64_t)i * wpg;
+    if (r < R) {  // uniform across the wave
+#pragma unroll
+      for (int b = 0; b < BP; ++b) {
+        const float s = wave_sum(acc[i][b]);
+        if (lane == 0 && b < B) store_out(y, (int64_t)b * R + r, s, out_kind);
+      }
+    }
+  }
+}
+
+// Dense comparison: lane l handles 16-byte chunks (8 columns) l, l+64, ...
+// of a row; x is staged in LDS as BP contiguous rows of `seg` columns.
+template <bool BF, int BP, int RPW>
+__global__ __launch_bounds__(1024) void nm_dense_kernel(
+    const uint4 *__restrict__ W, const uint16_t *__restrict__ x,
+    void *__restrict__ y, int B, int64_t R, int K, int seg, int out_kind) {
+  constexpr int U = RPW >= 4 ? 2 : 4;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int wpg = blockDim.x / kWave;
+  const int64_t row0 = (int64_t)blockIdx.x * wpg * RPW + wid;
+  const int64_t cpr = K >> 3;  // 16-byte chunks per row
+
+  float acc[RPW][BP];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int b = 0; b < BP; ++b) acc[i][b] = 0.f;
+
+  for (int s0 = 0; s0 < K; s0 += seg) {
+    const int S = min(seg, K - s0);
+    if (s0) __syncthreads();
+    for (int b = 0; b < BP; ++b) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)b * K + s0);
+      uint4 *dst = reinterpret_cast<uint4 *>(lds + (size_t)b * seg * 2);
+      for (int j = threadIdx.x; j < S / 8; j += blockDim.x)
+        dst[j] = (b < B) ? src[j] : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+    const int nch = S >> 3;
+    const int64_t cbeg = s0 >> 3;
+    for (int t0 = 0; t0 < nch; t0 += kWave * U) {
+      uint4 v[RPW][U];
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int64_t r = row0 + (int64_t)i * wpg;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = t0 + kWave * u + lane;
+          v[i][u] = (r < R && q < nch) ? W[r * cpr + cbeg + q] : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = t0 + kWave * u + lane;
+        if (q < nch) {
+#pragma unroll
+          for (int b = 0; b < BP; ++b) {
+            const uint4 xq =
+                *reinterpret_cast<const uint4 *>(lds + (size_t)b * seg * 2 + (size_t)q * 16);
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+              float a = acc[i][b];
+              a = dot2<BF>(v[i][u].x, xq.x, a);
+              a = dot2<BF>(v[i][u].y, xq.y, a);
+              a = dot2<BF>(v[i][u].z, xq.z, a);
+              a = dot2<BF>(v[i][u].w, xq.w, a);
+              acc[i][b] = a;
+            }
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int64_t r = row0 + (int64_t)i * wpg;
+    if (r < R) {
+#pragma unroll
+      for (int b = 0; b < BP; ++b) {
+        const float s = wave_sum(acc[i][b]);
+        if (lane == 0 && b < B) store_out(y, (int64_t)b * R + r, s, out_kind);
+      }
+    }
+  }
+}
+
+// Pack (Method item (1)).  One wavefront per row, 64 columns per step: lane l
+// tests column c0 + l, a ballot forms the two 32-bit words, and the count of
+// set bits below the lane (an mbcnt-style prefix) is the kept weight's slot
+// among its word's 16 values.  Lanes at the start of each M-group check that
+// the group keeps exactly M/2; the number of bad groups is added to *bad.
+template <int M>
+__global__ __launch_bounds__(256) void nm_pack_kernel(
+    const uint16_t *__restrict__ W, const uint8_t *__restrict__ keep,
+    int64_t R, int K, uint16_t *__restrict__ values,
+    uint32_t *__restrict__ bits, int *__restrict__ bad) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wpg = blockDim.x / kWave;
+  const uint32_t lb = lane & 31;
+  const uint32_t below = (1u << lb) - 1u;
+  const uint32_t gmask = (M == 32) ? 0xffffffffu : ((1u << M) - 1u);
+  int nbad = 0;
+  for (int64_t r = (int64_t)blockIdx.x * wpg + threadIdx.x / kWave; r < R;
+       r += (int64_t)gridDim.x * wpg) {
+    const uint16_t *wr = W + r * K;
+    const uint8_t *kr = keep + r * K;
+    uint16_t *vr = values + r * (K / 2);
+    uint32_t *br = bits + r * (K / 32);
+    for (int c0 = 0; c0 < K; c0 += kWave) {
+      const int c = c0 + lane;
+      const bool in = c < K;
+      const bool kept = in && kr[c] != 0;
+      const uint16_t wv = in ? wr[c] : (uint16_t)0;
+      const uint64_t bal = __ballot(kept);
+      const uint32_t word = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
+      const uint32_t slot = __popc(word & below);
+      const int64_t wg = (c0 >> 5) + (lane >> 5);
+      if (kept && slot < 16) vr[wg * 16 + slot] = wv;
+      if (in && lb == 0) br[wg] = word;
+      bool badg = false;
+      if (in && (lb % M) == 0) badg = __popc((word >> lb) & gmask) != M / 2;
+      nbad += badg ? 1 : 0;
+    }
+  }
+  // sum over the wave, one atomic per wave
+  for (int o = kWave / 2; o > 0; o >>= 1) nbad += __shfl_xor(nbad, o, kWave);
+  if (lane == 0 && nbad) atomicAdd(bad, nbad);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+thread_local int g_last_hip = 0;
+
+nm_status hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return NM_ERR_HIP;
+}
+
+struct DevInfo {
+  bool init = false;
+  int cus = 0;
+  size_t lds_per_wg = 0;
+};
+constexpr int kMaxDev = 64;
+DevInfo g_dev[kMaxDev];
+std::mutex g_dev_mu;
+
+nm_status device_info(DevInfo *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDev) return NM_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_dev_mu);
+  DevInfo &d = g_dev[dev];
+  if (!d.init) {
+    int cus = 0, lds = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    d.cus = cus;
+    d.lds_per_wg = (size_t)lds;
+    d.init = true;
+  }
+  *out = d;
+  return NM_OK;
+}
+
+bool pattern_ok(int n, int m) {
+  return (m == 4 || m == 8 || m == 16 || m == 32) && 2 * n == m;
+}
+
+bool is16(nm_dtype d) { return d == NM_F16 || d == NM_BF16; }
+
+bool out_ok(nm_dtype in, nm_dtype out) { return out == NM_F32 || out == in; }
+
+bool aligned(const void *p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Argument checks common to the products; nothing here touches HIP.
+nm_status check_dims(int64_t rows, int64_t cols, int batch) {
+  if (rows < 0 || cols < 0 || batch < 1 || batch > 8) return NM_ERR_INVALID_ARG;
+  if (rows > INT32_MAX || cols > INT32_MAX) return NM_ERR_INVALID_ARG;
+  if (cols % 32 != 0) return NM_ERR_SHAPE;
+  return NM_OK;
+}
+
+int pad_batch(int b) { return b <= 1 ? 1 : b <= 2 ? 2 : b <= 4 ? 4 : 8; }
+
+size_t sparse_lds_bytes(int bp, int seg) {
+  switch (bp) {
+    case 1: return XLay<1>::bytes(seg);
+    case 2: return XLay<2>::bytes(seg);
+    case 4: return XLay<4>::bytes(seg);
+    default: return XLay<8>::bytes(seg);
+  }
+}
+
+size_t dense_lds_bytes(int bp, int seg) { return (size_t)bp * seg * 2; }
+
+size_t lds_bytes(bool dense, int bp, int seg) {
+  return dense ? dense_lds_bytes(bp, seg) : sparse_lds_bytes(bp, seg);
+}
+
+// Widest segment (multiple of 32 columns) whose LDS image fits `budget`.
+int max_seg(bool dense, int bp, size_t budget) {
+  int lo = 32, hi = 1 << 20;
+  if (lds_bytes(dense, bp, lo) > budget) return 0;
+  while (lo < hi) {
+    int mid = ((lo + hi) / 2 + 31) / 32 * 32;
+    if (mid >= hi) mid = hi;
+    if (lds_bytes(dense, bp, mid) <= budget) lo = mid; else hi = mid - 32;
+  }
+  return lo;
+}
+
+nm_status default_cfg(int64_t rows, int64_t cols, int batch, bool dense,
+                      nm_launch_cfg *cfg) {
+  DevInfo di;
+  nm_status st = device_info(&di);
+  if (st != NM_OK) return st;
+  const int bp = pad_batch(batch);
+  const size_t budget = di.lds_per_wg < kLdsBudget ? di.lds_per_wg : kLdsBudget;
+  const int smax = max_seg(dense, bp, budget);
+  int seg;
+  if (cols <= smax) {
+    seg = cols > 0 ? (int)cols : 32;
+  } else {
+    seg = smax >= 1024 ? smax / 1024 * 1024 : smax;
+  }
+  const size_t lds = lds_bytes(dense, bp, seg);
+  cfg->seg_cols = seg;
+  cfg->threads_per_wg = lds > 32 * 1024 ? 512 : 256;
+  cfg->rows_per_wave = bp == 1 ? 1 : 2;
+  (void)rows;
+  return NM_OK;
+}
+
+nm_status check_cfg(const nm_launch_cfg &c, bool dense, int bp,
+                    const DevInfo &di) {
+  const int t = c.threads_per_wg;
+  if (!(t == 64 || t == 128 || t == 256 || t == 512 || t == 1024)) return NM_ERR_INVALID_ARG;
+  if (!(c.rows_per_wave == 1 || c.rows_per_wave == 2 || c.rows_per_wave == 4))
+    return NM_ERR_INVALID_ARG;
+  if (c.seg_cols <= 0 || c.seg_cols % 32 != 0) return NM_ERR_INVALID_ARG;
+  if (lds_bytes(dense, bp, c.seg_cols) > di.lds_per_wg) return NM_ERR_INVALID_ARG;
+  return NM_OK;
+}
+
+nm_status resolve_cfg(int64_t rows, int64_t cols, int batch, bool dense,
+                      const nm_launch_cfg *user, nm_launch_cfg *out) {
+  nm_status st = default_cfg(rows, cols, batch, dense, out);
+  if (st != NM_OK) return st;
+  if (user) {
+    if (user->threads_per_wg) out->threads_per_wg = user->threads_per_wg;
+    if (user->rows_per_wave) out->rows_per_wave = user->rows_per_wave;
+    if (user->seg_cols) out->seg_cols = user->seg_cols;
+  }
+  DevInfo di;
+  st = device_info(&di);
+  if (st != NM_OK) return st;
+  return check_cfg(*out, dense, pad_batch(batch), di);
+}
+
+typedef void (*sparse_fn)(const uint4 *, const uint32_t *, const uint16_t *,
+                          void *, int, int64_t, int, int, int);
+typedef void (*dense_fn)(const uint4 *, const uint16_t *, void *, int, int64_t,
+                         int, int, int);
+
+template <bool BF, int BP, bool M32>
+sparse_fn pick_sparse_rpw(int rpw) {
+  switch (rpw) {
+    case 1: return nm_spmv_kernel<BF, BP, M32, 1>;
+    case 2: return nm_spmv_kernel<BF, BP, M32, 2>;
+    default: return nm_spmv_kernel<BF, BP, M32, 4>;
+  }
+}
+
+template <bool BF, bool M32>
+sparse_fn pick_sparse_bp(int bp, int rpw) {
+  switch (bp) {
+    case 1: return pick_sparse_rpw<BF, 1, M32>(rpw);
+    case 2: return pick_sparse_rpw<BF, 2, M32>(rpw);
+    case 4: return pick_sparse_rpw<BF, 4, M32>(rpw);
+    default: return pick_sparse_rpw<BF, 8, M32>(rpw);
+  }
+}
+
+sparse_fn pick_sparse(bool bf, bool m32, int bp, int rpw) {
+  if (bf) return m32 ? pick_sparse_bp<true, true>(bp, rpw) : pick_sparse_bp<true, false>(bp, rpw);
+  return m32 ? pick_sparse_bp<false, true>(bp, rpw) : pick_sparse_bp<false, false>(bp, rpw);
+}
+
+template <bool BF, int BP>
+dense_fn pick_dense_rpw(int rpw) {
+  switch (rpw) {
+    case 1: return nm_dense_kernel<BF, BP, 1>;
+    case 2: return nm_dense_kernel<BF, BP, 2>;
+    default: return nm_dense_kernel<BF, BP, 4>;
+  }
+}
+
+template <bool BF>
+dense_fn pick_dense_bp(int bp, int rpw) {
+  switch (bp) {
+    case 1: return pick_dense_rpw<BF, 1>(rpw);
+    case 2: return pick_dense_rpw<BF, 2>(rpw);
+    case 4: return pick_dense_rpw<BF, 4>(rpw);
+    default: return pick_dense_rpw<BF, 8>(rpw);
+  }
+}
+
+dense_fn pick_dense(bool bf, int bp, int rpw) {
+  return bf ? pick_dense_bp<true>(bp, rpw) : pick_dense_bp<false>(bp, rpw);
+}
+
+int sparse_product(const void *values, const uint32_t *bits, const void *X,
+                   void *Y, int batch, int64_t rows, int64_t cols, int n,
+                   int m, nm_dtype in_dt, nm_dtype out_dt,
+                   const nm_launch_cfg *user, void *stream) {
+  nm_status st = check_dims(rows, cols, batch);
+  if (st != NM_OK) return st;
+  if (!pattern_ok(n, m) || !is16(in_dt) || !out_ok(in_dt, out_dt)) return NM_ERR_UNSUPPORTED;
+  const bool empty_w = rows == 0 || cols == 0;
+  if ((!values && !empty_w) || (!bits && !empty_w) || (!X && cols != 0) ||
+      (!Y && rows != 0))
+    return NM_ERR_INVALID_ARG;
+  const uintptr_t ysz = out_dt == NM_F32 ? 4 : 2;
+  if (!aligned(values, 16) || !aligned(bits, 4) || !aligned(X, 16) || !aligned(Y, ysz))
+    return NM_ERR_ALIGN;
+  if (rows == 0) return NM_OK;
+  nm_launch_cfg cfg;
+  st = resolve_cfg(rows, cols, batch, false, user, &cfg);
+  if (st != NM_OK) return st;
+  const int bp = pad_batch(batch);
+  sparse_fn fn = pick_sparse(in_dt == NM_BF16, m == 32, bp, cfg.rows_per_wave);
+  const int64_t rows_per_wg = (int64_t)(cfg.threads_per_wg / kWave) * cfg.rows_per_wave;
+  const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+  if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
+                     sparse_lds_bytes(bp, cfg.seg_cols), (hipStream_t)stream,
+                     (const uint4 *)values, bits, (const uint16_t *)X, Y, batch,
+                     rows, (int)cols, cfg.seg_cols, (int)out_dt);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NM_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nm_status_string(int status) {
+  switch (status) {
+    case NM_OK: return "NM_OK";
+    case NM_ERR_INVALID_ARG: return "NM_ERR_INVALID_ARG: invalid argument";
+    case NM_ERR_UNSUPPORTED: return "NM_ERR_UNSUPPORTED: unsupported pattern or dtype";
+    case NM_ERR_SHAPE: return "NM_ERR_SHAPE: cols must be a multiple of 32";
+    case NM_ERR_ALIGN: return "NM_ERR_ALIGN: misaligned pointer";
+    case NM_ERR_MASK: return "NM_ERR_MASK: an M-group does not keep exactly N";
+    case NM_ERR_HIP: return "NM_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown nm_status";
+  }
+}
+
+int nm_last_hip_error(void) { return g_last_hip; }
+
+int nm_packed_bytes(int64_t rows, int64_t cols, int n, int m, nm_dtype dt,
+                    size_t *values_bytes, size_t *bits_bytes) {
+  if (rows < 0 || cols < 0 || !values_bytes || !bits_bytes) return NM_ERR_INVALID_ARG;
+  if (!pattern_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
+  if (cols % 32 != 0) return NM_ERR_SHAPE;
+  if (rows > INT32_MAX || cols > INT32_MAX) return NM_ERR_INVALID_ARG;
+  const uint64_t rc = (uint64_t)rows * (uint64_t)cols;
+  *values_bytes = (size_t)(rc / (uint64_t)m * (uint64_t)n * 2u);
+  *bits_bytes = (size_t)(rc / 8u);
+  return NM_OK;
+}
+
+int nm_pack(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
+            int n, int m, nm_dtype dt, void *values, uint32_t *bits,
+            void *stream) {
+  if (rows < 0 || cols < 0) return NM_ERR_INVALID_ARG;
+  if (rows > INT32_MAX || cols > INT32_MAX) return NM_ERR_INVALID_ARG;
+  if (!pattern_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
+  if (cols % 32 != 0) return NM_ERR_SHAPE;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (!W || !keep || !values || !bits)) return NM_ERR_INVALID_ARG;
+  if (!aligned(W, 2) || !aligned(values, 16) || !aligned(bits, 4)) return NM_ERR_ALIGN;
+  if (empty) return NM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  int *dbad = nullptr;
+  hipError_t e = hipMalloc((void **)&dbad, sizeof(int));
+  if (e != hipSuccess) return hip_fail(e);
+  int hbad = 0;
+  e = hipMemsetAsync(dbad, 0, sizeof(int), s);
+  if (e == hipSuccess) {
+    const int threads = 256, wpg = threads / kWave;
+    int64_t grid = (rows + wpg - 1) / wpg;
+    if (grid > (1 << 20)) grid = 1 << 20;
+    const int K = (int)cols;
+    const uint16_t *w16 = (const uint16_t *)W;
+    uint16_t *v16 = (uint16_t *)values;
+    switch (m) {
+      case 4: hipLaunchKernelGGL(nm_pack_kernel<4>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, v16, bits, dbad); break;
+      case 8: hipLaunchKernelGGL(nm_pack_kernel<8>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, v16, bits, dbad); break;
+      case 16: hipLaunchKernelGGL(nm_pack_kernel<16>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, v16, bits, dbad); break;
+      default: hipLaunchKernelGGL(nm_pack_kernel<32>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, v16, bits, dbad); break;
+    }
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipMemcpyAsync(&hbad, dbad, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  hipError_t ef = hipFree(dbad);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ef != hipSuccess) return hip_fail(ef);
+  return hbad ? NM_ERR_MASK : NM_OK;
+}
+
+int nm_spmv(const void *values, const uint32_t *bits, const void *x, void *y,
+            int64_t rows, int64_t cols, int n, int m, nm_dtype in_dt,
+            nm_dtype out_dt, void *stream) {
+  return sparse_product(values, bits, x, y, 1, rows, cols, n, m, in_dt, out_dt,
+                        nullptr, stream);
+}
+
+int nm_spmm_small(const void *values, const uint32_t *bits, const void *X,
+                  void *Y, int batch, int64_t rows, int64_t cols, int n, int m,
+                  nm_dtype in_dt, nm_dtype out_dt, void *stream) {
+  return sparse_product(values, bits, X, Y, batch, rows, cols, n, m, in_dt,
+                        out_dt, nullptr, stream);
+}
+
+int nm_spmm_small_cfg(const void *values, const uint32_t *bits, const void *X,
+                      void *Y, int batch, int64_t rows, int64_t cols, int n,
+                      int m, nm_dtype in_dt, nm_dtype out_dt,
+                      const nm_launch_cfg *cfg, void *stream) {
+  return sparse_product(values, bits, X, Y, batch, rows, cols, n, m, in_dt,
+                        out_dt, cfg, stream);
+}
+
+int nm_default_launch(int64_t rows, int64_t cols, int batch, int dense,
+                      nm_launch_cfg *cfg) {
+  if (!cfg) return NM_ERR_INVALID_ARG;
+  nm_status st = check_dims(rows, cols, batch);
+  if (st != NM_OK) return st;
+  return default_cfg(rows, cols, batch, dense != 0, cfg);
+}
+
+int nm_dense_gemv_cfg(const void *W, const void *X, void *Y, int batch,
+                      int64_t rows, int64_t cols, nm_dtype in_dt,
+                      nm_dtype out_dt, const nm_launch_cfg *user,
+                      void *stream) {
+  nm_status st = check_dims(rows, cols, batch);
+  if (st != NM_OK) return st;
+  if (!is16(in_dt) || !out_ok(in_dt, out_dt)) return NM_ERR_UNSUPPORTED;
+  const bool empty_w = rows == 0 || cols == 0;
+  if ((!W && !empty_w) || (!X && cols != 0) || (!Y && rows != 0)) return NM_ERR_INVALID_ARG;
+  const uintptr_t ysz = out_dt == NM_F32 ? 4 : 2;
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, ysz)) return NM_ERR_ALIGN;
+  if (rows == 0) return NM_OK;
+  nm_launch_cfg cfg;
+  st = resolve_cfg(rows, cols, batch, true, user, &cfg);
+  if (st != NM_OK) return st;
+  const int bp = pad_batch(batch);
+  dense_fn fn = pick_dense(in_dt == NM_BF16, bp, cfg.rows_per_wave);
+  const int64_t rows_per_wg = (int64_t)(cfg.threads_per_wg / kWave) * cfg.rows_per_wave;
+  const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+  if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
+                     dense_lds_bytes(bp, cfg.seg_cols), (hipStream_t)stream,
+                     (const uint4 *)W, (const uint16_t *)X, Y, batch, rows,
+                     (int)cols, cfg.seg_cols, (int)out_dt);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NM_OK : hip_fail(e);
+}
+
+int nm_dense_gemv(const void *W, const void *X, void *Y, int batch,
+                  int64_t rows, int64_t cols, nm_dtype in_dt, nm_dtype out_dt,
+                  void *stream) {
+  return nm_dense_gemv_cfg(W, X, Y, batch, rows, cols, in_dt, out_dt, nullptr,
+                           stream);
+}
+
+}  // extern "C"

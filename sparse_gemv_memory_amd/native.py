@@ -1,0 +1,236 @@
+"""ctypes binding of libnm_sparse.so (the C ABI in include/nm_sparse.h).
+
+Argument marshalling only: every step of the product runs in the HIP kernels
+of the library.  PyTorch supplies device memory and the current HIP stream.
+There is no fallback: if the library is not built, or a tensor is not on the
+GPU, the call raises.
+
+The functions carry the C names:
+
+* :func:`nm_packed_bytes` -- packed buffer sizes;
+* :func:`nm_pack` -- dense W + keep-mask -> (values, bits);
+* :func:`nm_spmv` -- batch-1 sparse product;
+* :func:`nm_spmm_small` -- batch 1..8 sparse product;
+* :func:`nm_dense_gemv` -- dense comparison product;
+* :func:`nm_default_launch` -- the launch shape the library would choose.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from .build import LIB
+
+NM_OK = 0
+NM_ERR_INVALID_ARG = -1
+NM_ERR_UNSUPPORTED = -2
+NM_ERR_SHAPE = -3
+NM_ERR_ALIGN = -4
+NM_ERR_MASK = -5
+NM_ERR_HIP = -6
+
+NM_F16 = 0
+NM_BF16 = 1
+NM_F32 = 2
+
+_DT = {torch.float16: NM_F16, torch.bfloat16: NM_BF16, torch.float32: NM_F32}
+
+
+class NMError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = f"{what}: {status_string(status)}"
+        if status == NM_ERR_HIP:
+            msg += f" (hipError {lib().nm_last_hip_error()})"
+        super().__init__(msg)
+
+
+class LaunchCfg(ctypes.Structure):
+    _fields_ = [("threads_per_wg", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
+                ("seg_cols", ctypes.c_int)]
+
+    def as_tuple(self):
+        return (self.threads_per_wg, self.rows_per_wave, self.seg_cols)
+
+
+_lib = None
+
+
+def lib():
+    """Load libnm_sparse.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is not built; run `python -m sparse_gemv_memory_amd.build` "
+                           "or __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB)
+    p, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.nm_status_string.argtypes = [ci]
+    L.nm_status_string.restype = ctypes.c_char_p
+    L.nm_last_hip_error.argtypes = []
+    L.nm_last_hip_error.restype = ci
+    L.nm_packed_bytes.argtypes = [i64, i64, ci, ci, ci, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.nm_packed_bytes.restype = ci
+    L.nm_pack.argtypes = [p, p, i64, i64, ci, ci, ci, p, p, p]
+    L.nm_pack.restype = ci
+    L.nm_spmv.argtypes = [p, p, p, p, i64, i64, ci, ci, ci, ci, p]
+    L.nm_spmv.restype = ci
+    L.nm_spmm_small.argtypes = [p, p, p, p, ci, i64, i64, ci, ci, ci, ci, p]
+    L.nm_spmm_small.restype = ci
+    L.nm_spmm_small_cfg.argtypes = [p, p, p, p, ci, i64, i64, ci, ci, ci, ci,
+                                    ctypes.POINTER(LaunchCfg), p]
+    L.nm_spmm_small_cfg.restype = ci
+    L.nm_dense_gemv.argtypes = [p, p, p, ci, i64, i64, ci, ci, p]
+    L.nm_dense_gemv.restype = ci
+    L.nm_dense_gemv_cfg.argtypes = [p, p, p, ci, i64, i64, ci, ci, ctypes.POINTER(LaunchCfg), p]
+    L.nm_dense_gemv_cfg.restype = ci
+    L.nm_default_launch.argtypes = [i64, i64, ci, ci, ctypes.POINTER(LaunchCfg)]
+    L.nm_default_launch.restype = ci
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().nm_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != NM_OK:
+        raise NMError(status, what)
+
+
+def _dev(t: torch.Tensor, name: str) -> Optional[int]:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _in_dt(t: torch.Tensor) -> int:
+    if t.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _cfg_ptr(cfg):
+    if cfg is None:
+        return None
+    c = LaunchCfg(*cfg) if not isinstance(cfg, LaunchCfg) else cfg
+    return ctypes.byref(c)
+
+
+def nm_packed_bytes(rows: int, cols: int, n: int, m: int, dtype=torch.float16) -> Tuple[int, int]:
+    vb, bb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().nm_packed_bytes(rows, cols, n, m, _DT[dtype], ctypes.byref(vb), ctypes.byref(bb)),
+           "nm_packed_bytes")
+    return vb.value, bb.value
+
+
+def nm_pack(W: torch.Tensor, keep: torch.Tensor, n: int, m: int):
+    """Pack a (rows, cols) fp16/bf16 W and a same-shape keep-mask.
+
+    Returns (values, bits): values (rows, cols*n/m) of W's dtype and bits
+    (rows, cols/32) int32 holding the uint32 mask words.  Raises NMError with
+    status NM_ERR_MASK if a group does not keep exactly n of m.
+    """
+    if W.dim() != 2 or keep.shape != W.shape:
+        raise ValueError("W must be 2-D and keep must have its shape")
+    if keep.dtype not in (torch.uint8, torch.bool, torch.int8):
+        raise TypeError("keep must be uint8, int8 or bool")
+    rows, cols = W.shape
+    dt = _in_dt(W)
+    vcols = cols * n // m if m > 0 and n >= 0 else 0  # the library validates n, m
+    values = torch.empty((rows, vcols), dtype=W.dtype, device=W.device)
+    bits = torch.empty((rows, cols // 32), dtype=torch.int32, device=W.device)
+    with torch.cuda.device(W.device):
+        st = lib().nm_pack(_dev(W, "W"), _dev(keep, "keep"), rows, cols, n, m, dt,
+                           _dev(values, "values"), _dev(bits, "bits"), _stream(W.device))
+    _check(st, "nm_pack")
+    return values, bits
+
+
+def _sparse_args(values, bits, X):
+    if values.dim() != 2 or bits.dim() != 2 or values.shape[0] != bits.shape[0]:
+        raise ValueError("values and bits must be 2-D with the same number of rows")
+    if bits.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("bits must be int32 (uint32 mask words)")
+    if values.dtype != X.dtype:
+        raise TypeError("values and x must have the same dtype")
+    rows = values.shape[0]
+    cols = bits.shape[1] * 32
+    if values.shape[1] * 2 != cols:
+        raise ValueError("values must hold cols/2 elements per row (50% N:M)")
+    return rows, cols
+
+
+def nm_spmv(values, bits, x, n: int, m: int, out_dtype=torch.float32, out=None, cfg=None):
+    """y = W_sparse . x for one token; x has shape (cols,) or (1, cols)."""
+    rows, cols = _sparse_args(values, bits, x)
+    if x.numel() != cols:
+        raise ValueError("x must have cols elements")
+    y = out if out is not None else torch.empty((rows,), dtype=out_dtype, device=values.device)
+    if y.numel() != rows or y.dtype != out_dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    with torch.cuda.device(values.device):
+        if cfg is None:
+            st = lib().nm_spmv(_dev(values, "values"), _dev(bits, "bits"), _dev(x, "x"),
+                               _dev(y, "y"), rows, cols, n, m, _in_dt(x), _DT[out_dtype],
+                               _stream(values.device))
+        else:
+            st = lib().nm_spmm_small_cfg(_dev(values, "values"), _dev(bits, "bits"), _dev(x, "x"),
+                                         _dev(y, "y"), 1, rows, cols, n, m, _in_dt(x),
+                                         _DT[out_dtype], _cfg_ptr(cfg), _stream(values.device))
+    _check(st, "nm_spmv")
+    return y
+
+
+def nm_spmm_small(values, bits, X, n: int, m: int, out_dtype=torch.float32, out=None, cfg=None):
+    """Y = X . W_sparse^T for X of shape (batch, cols), 1 <= batch <= 8."""
+    rows, cols = _sparse_args(values, bits, X)
+    if X.dim() != 2 or X.shape[1] != cols:
+        raise ValueError("X must be (batch, cols)")
+    batch = X.shape[0]
+    Y = out if out is not None else torch.empty((batch, rows), dtype=out_dtype, device=values.device)
+    if tuple(Y.shape) != (batch, rows) or Y.dtype != out_dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    with torch.cuda.device(values.device):
+        st = lib().nm_spmm_small_cfg(_dev(values, "values"), _dev(bits, "bits"), _dev(X, "X"),
+                                     _dev(Y, "Y"), batch, rows, cols, n, m, _in_dt(X),
+                                     _DT[out_dtype], _cfg_ptr(cfg), _stream(values.device))
+    _check(st, "nm_spmm_small")
+    return Y
+
+
+def nm_dense_gemv(W, X, out_dtype=torch.float32, out=None, cfg=None):
+    """Y = X . W^T, dense, for X of shape (batch, cols) or (cols,)."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    rows, cols = W.shape
+    squeeze = X.dim() == 1
+    X2 = X.reshape(1, -1) if squeeze else X
+    if X2.shape[1] != cols or W.dtype != X.dtype:
+        raise ValueError("X must be (batch, cols) with W's dtype")
+    batch = X2.shape[0]
+    Y = out if out is not None else torch.empty((batch, rows), dtype=out_dtype, device=W.device)
+    with torch.cuda.device(W.device):
+        st = lib().nm_dense_gemv_cfg(_dev(W, "W"), _dev(X2, "X"), _dev(Y, "Y"), batch, rows, cols,
+                                     _in_dt(W), _DT[out_dtype], _cfg_ptr(cfg), _stream(W.device))
+    _check(st, "nm_dense_gemv")
+    return Y.reshape(-1) if squeeze else Y
+
+
+def nm_default_launch(rows: int, cols: int, batch: int, dense: bool = False) -> LaunchCfg:
+    c = LaunchCfg()
+    _check(lib().nm_default_launch(rows, cols, batch, int(bool(dense)), ctypes.byref(c)),
+           "nm_default_launch")
+    return c

@@ -1,0 +1,154 @@
+"""The C ABI without a GPU: the library loads, exports every function declared
+in include/*.h, and rejects bad arguments on the host before any HIP call.
+
+Fake device addresses are passed where a pointer is needed: a rejected call
+never dereferences or launches anything, and rows == 0 returns NM_OK without
+touching the device.
+"""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from sparse_gemv_memory_amd import build as nbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INV, UNSUP, SHAPE, ALIGN = 0, -1, -2, -3, -4
+F16, BF16, F32 = 0, 1, 2
+
+P = 0x7F0000000000  # a 256-byte aligned fake address, never dereferenced
+
+
+@pytest.fixture(scope="session")
+def L():
+    if not os.path.exists(nbuild.LIB):
+        nbuild.build()
+    from sparse_gemv_memory_amd import native
+    return native.lib()
+
+
+def _declared():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b(nm_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("nm_packed_bytes", "nm_pack", "nm_spmv", "nm_spmm_small", "nm_dense_gemv",
+              "nm_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(L):
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert missing == []
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert L.nm_status_string(s).decode().startswith("NM_")
+    assert L.nm_status_string(123).decode() == "unknown nm_status"
+    assert L.nm_last_hip_error() == 0
+
+
+def _pb(L, rows, cols, n, m, dt=F16):
+    vb, bb = ctypes.c_size_t(), ctypes.c_size_t()
+    st = L.nm_packed_bytes(rows, cols, n, m, dt, ctypes.byref(vb), ctypes.byref(bb))
+    return st, vb.value, bb.value
+
+
+def test_packed_bytes_closed_form(L):
+    # K*N/M values and K/32 words per row; the same bytes for every 50% pattern
+    for n, m in ((2, 4), (4, 8), (8, 16), (16, 32)):
+        assert _pb(L, 14336, 4096, n, m) == (OK, 14336 * 4096, 14336 * 4096 // 8)
+    assert _pb(L, 0, 4096, 2, 4) == (OK, 0, 0)
+    assert _pb(L, 3, 0, 2, 4, BF16) == (OK, 0, 0)
+    assert _pb(L, 4, 48, 2, 4)[0] == SHAPE
+    assert _pb(L, 4, 64, 1, 4)[0] == UNSUP
+    assert _pb(L, 4, 64, 3, 6)[0] == UNSUP
+    assert _pb(L, 4, 64, 2, 4, F32)[0] == UNSUP
+    assert _pb(L, -1, 64, 2, 4)[0] == INV
+    assert L.nm_packed_bytes(1, 32, 2, 4, F16, None, None) == INV
+
+
+def _spmv(L, values=P, bits=P, x=P, y=P, rows=8, cols=64, n=2, m=4, i=F16, o=F32):
+    return L.nm_spmv(values, bits, x, y, rows, cols, n, m, i, o, None)
+
+
+def test_spmv_rejects_bad_arguments(L):
+    assert _spmv(L, rows=-1) == INV
+    assert _spmv(L, cols=-32) == INV
+    assert _spmv(L, cols=48) == SHAPE
+    assert _spmv(L, cols=2 ** 31) == INV
+    assert _spmv(L, n=1, m=4) == UNSUP
+    assert _spmv(L, n=32, m=64) == UNSUP
+    assert _spmv(L, n=4, m=4) == UNSUP
+    assert _spmv(L, i=F32) == UNSUP
+    assert _spmv(L, i=F16, o=BF16) == UNSUP
+    assert _spmv(L, values=None) == INV
+    assert _spmv(L, bits=None) == INV
+    assert _spmv(L, x=None) == INV
+    assert _spmv(L, y=None) == INV
+    assert _spmv(L, values=P + 8) == ALIGN
+    assert _spmv(L, bits=P + 2) == ALIGN
+    assert _spmv(L, x=P + 4) == ALIGN
+    assert _spmv(L, y=P + 2, o=F32) == ALIGN
+    assert _spmv(L, y=P + 1, o=F16) == ALIGN
+
+
+def test_empty_calls_do_nothing(L):
+    # rows == 0: nothing to compute, no device work, NULL pointers allowed
+    assert _spmv(L, values=None, bits=None, x=P, y=None, rows=0) == OK
+    assert _spmv(L, values=None, bits=None, x=None, y=None, rows=0, cols=0) == OK
+    assert _spmv(L, values=None, bits=None, x=None, y=None, rows=0) == INV  # x has cols elements
+    assert L.nm_spmm_small(None, None, P, None, 4, 0, 64, 2, 4, F16, F32, None) == OK
+    assert L.nm_dense_gemv(None, P, None, 8, 0, 64, BF16, F32, None) == OK
+    assert L.nm_pack(None, None, 0, 64, 2, 4, F16, None, None, None) == OK
+    assert L.nm_pack(None, None, 5, 0, 2, 4, F16, None, None, None) == OK
+
+
+def test_spmm_small_batch_range(L):
+    for b in (0, 9, -1):
+        assert L.nm_spmm_small(P, P, P, P, b, 8, 64, 2, 4, F16, F32, None) == INV
+    assert L.nm_spmm_small(P, P, P, P, 2, 8, 96 + 8, 2, 4, F16, F32, None) == SHAPE
+
+
+def test_dense_rejects_bad_arguments(L):
+    assert L.nm_dense_gemv(P, P, P, 0, 8, 64, F16, F32, None) == INV
+    assert L.nm_dense_gemv(P, P, P, 9, 8, 64, F16, F32, None) == INV
+    assert L.nm_dense_gemv(P, P, P, 1, 8, 40, F16, F32, None) == SHAPE
+    assert L.nm_dense_gemv(P, P, P, 1, 8, 64, F32, F32, None) == UNSUP
+    assert L.nm_dense_gemv(None, P, P, 1, 8, 64, F16, F32, None) == INV
+    assert L.nm_dense_gemv(P + 2, P, P, 1, 8, 64, F16, F32, None) == ALIGN
+
+
+def test_pack_rejects_bad_arguments(L):
+    def pack(W=P, keep=P, rows=4, cols=64, n=2, m=4, dt=F16, v=P, b=P):
+        return L.nm_pack(W, keep, rows, cols, n, m, dt, v, b, None)
+    assert pack(rows=-1) == INV
+    assert pack(cols=96 + 16) == SHAPE
+    assert pack(n=2, m=8) == UNSUP
+    assert pack(dt=F32) == UNSUP
+    assert pack(W=None) == INV
+    assert pack(keep=None) == INV
+    assert pack(v=None) == INV
+    assert pack(b=None) == INV
+    assert pack(W=P + 1) == ALIGN
+    assert pack(v=P + 2) == ALIGN
+    assert pack(b=P + 2) == ALIGN
+
+
+def test_launch_cfg_validation_is_host_only(L):
+    from sparse_gemv_memory_amd.native import LaunchCfg
+    c = LaunchCfg()
+    assert L.nm_default_launch(8, 48, 1, 0, ctypes.byref(c)) == SHAPE
+    assert L.nm_default_launch(8, 64, 9, 0, ctypes.byref(c)) == INV
+    assert L.nm_default_launch(8, 64, 1, 0, None) == INV

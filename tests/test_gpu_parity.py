@@ -1,0 +1,320 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars:
+* nm_pack: values and bits bit-exact;
+* products with fp32 output: rel-L2 <= 1e-3 against the oracle's fp64 result
+  (per matrix and batch); with integer-valued inputs every partial sum is an
+  exact integer below 2**24, so the fp32 output must equal the oracle exactly;
+* products with 16-bit output: within 1 ulp of the fp64 result rounded to
+  nearest-even.
+Full-size workloads are checked on sampled rows that the oracle computes one by
+one, with the launch shape the benchmark uses (the library default).
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_gemv_memory_amd import native, synth, workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 1e-3
+PATTERNS = [(2, 4), (4, 8), (8, 16), (16, 32)]
+TDT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def t16(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(TDT[dtype]).to(DEV)
+
+
+def u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def u32(t):
+    return t.contiguous().cpu().numpy().view(np.uint32)
+
+
+def f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel_l2(got, want):
+    d = np.linalg.norm(want)
+    return np.linalg.norm(got - want) / d if d > 0 else np.linalg.norm(got)
+
+
+def inputs(rows, cols, n, m, dtype, batch, seed, mask="topn"):
+    W = synth.weights(rows, cols, seed=seed, dtype=dtype)
+    keep = synth.topn_mask(W, n, m) if mask == "topn" else synth.random_mask(rows, cols, n, m, seed + 1)
+    X = synth.activations(batch, cols, seed=seed, dtype=dtype)
+    return W, keep, X
+
+
+def gpu_pack(W, keep, n, m, dtype):
+    return native.nm_pack(t16(W, dtype), torch.from_numpy(keep).to(DEV), n, m)
+
+
+def round16_f64(a, dtype):
+    """fp64 -> nearest-even 16-bit pattern (binary16 via numpy; bfloat16 by
+    rounding the significand to 8 bits)."""
+    if dtype == "f16":
+        return a.astype(np.float16).view(np.uint16)
+    mant, ex = np.frexp(a)
+    q = np.rint(mant * 256.0)  # 8 significant bits, ties to even
+    r = np.ldexp(q, ex - 8).astype(np.float32)  # exact in fp32
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def ordered16(bits):
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+# ---- pack -------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n,m", PATTERNS)
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (37, 320), (130, 1056), (64, 4096)])
+@pytest.mark.parametrize("mask", ["topn", "random"])
+def test_pack_bit_exact(rows, cols, n, m, dtype, mask):
+    W, keep, _ = inputs(rows, cols, n, m, dtype, 1, seed=rows * 7 + cols, mask=mask)
+    values, bits = gpu_pack(W, keep, n, m, dtype)
+    st, ov, ob = oracle.pack(W, keep, n, m)
+    assert st == oracle.OK
+    assert np.array_equal(u16(values), ov)
+    assert np.array_equal(u32(bits), ob)
+
+
+def test_pack_exhaustive_2of4_words():
+    """All 6**8 aligned 2:4 words; with W[r, c] = c the packed values of a row
+    are its kept column numbers."""
+    nib = np.array([0b0011, 0b0101, 0b0110, 0b1001, 0b1010, 0b1100], dtype=np.uint32)
+    idx = np.arange(6 ** 8, dtype=np.int64)
+    word = np.zeros(idx.shape, dtype=np.uint32)
+    for g in range(8):
+        word |= nib[(idx // 6 ** g) % 6] << np.uint32(4 * g)
+    keep = ((word[:, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(np.uint8)
+    W = np.broadcast_to(np.arange(32, dtype=np.uint16), keep.shape).copy()
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    st, ov, ob = oracle.pack(W, keep, 2, 4)
+    assert st == oracle.OK
+    assert np.array_equal(u32(bits)[:, 0], word)
+    assert np.array_equal(u16(values), ov)
+
+
+def test_pack_keeps_raw_patterns():
+    W = np.array([[0x8000, 0x0001, 0x7C00, 0x7E01] * 8] * 3, dtype=np.uint16)
+    keep = np.array([[1, 1, 0, 0, 0, 0, 1, 1] * 4] * 3, dtype=np.uint8)
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    assert list(u16(values)[0, :4]) == [0x8000, 0x0001, 0x7C00, 0x7E01]
+    assert np.all(u32(bits) == 0xC3C3C3C3)
+
+
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_pack_rejects_invalid_mask_without_writing_outside(n, m):
+    rows, cols = 9, 160
+    W, keep, _ = inputs(rows, cols, n, m, "f16", 1, seed=3, mask="random")
+    keep[4, 37] ^= 1  # one group now keeps n-1 or n+1
+    guard = 4096
+    vbuf = torch.full((guard + rows * cols // 2 + guard,), 0x5A5A, dtype=torch.int32, device=DEV)
+    bbuf = torch.full((guard + rows * cols // 32 + guard,), 0x5A5A, dtype=torch.int32, device=DEV)
+    vptr = vbuf.data_ptr() + guard * 4
+    bptr = bbuf.data_ptr() + guard * 4
+    Wd = t16(W, "f16")
+    kd = torch.from_numpy(keep).to(DEV)
+    st = native.lib().nm_pack(Wd.data_ptr(), kd.data_ptr(), rows, cols, n, m, native.NM_F16,
+                              vptr, bptr, torch.cuda.current_stream().cuda_stream)
+    assert st == native.NM_ERR_MASK
+    v = vbuf.cpu().numpy()
+    b = bbuf.cpu().numpy()
+    nv = rows * cols // 2 * 2 // 4  # int32 slots covered by the values
+    assert np.all(v[:guard] == 0x5A5A) and np.all(v[guard + nv:] == 0x5A5A)
+    assert np.all(b[:guard] == 0x5A5A) and np.all(b[guard + rows * cols // 32:] == 0x5A5A)
+    with pytest.raises(native.NMError):
+        gpu_pack(W, keep, n, m, "f16")
+
+
+# ---- products ---------------------------------------------------------------
+
+SHAPES = [(1, 32), (5, 96), (37, 320), (129, 1056), (300, 4096), (70, 14336)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n,m", PATTERNS)
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_spmv_matches_oracle(rows, cols, n, m, dtype):
+    W, keep, X = inputs(rows, cols, n, m, dtype, 1, seed=rows + cols + m)
+    values, bits = gpu_pack(W, keep, n, m, dtype)
+    y = native.nm_spmv(values, bits, t16(X[0], dtype), n, m)
+    want = oracle.masked_gemv(W, keep, X[0], dtype == "bf16")
+    assert rel_l2(f64(y), want) <= TOL
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("n,m", [(2, 4), (16, 32)])
+def test_spmm_small_matches_oracle(batch, n, m, dtype):
+    rows, cols = 203, 2080  # 65 words: ragged against every load batch
+    W, keep, X = inputs(rows, cols, n, m, dtype, batch, seed=batch)
+    values, bits = gpu_pack(W, keep, n, m, dtype)
+    Y = native.nm_spmm_small(values, bits, t16(X, dtype), n, m)
+    want = oracle.masked_gemv(W, keep, X, dtype == "bf16")
+    for b in range(batch):
+        assert rel_l2(f64(Y[b]), want[b]) <= TOL
+
+
+CFGS = [(64, 1, 32), (64, 4, 96), (128, 2, 1024), (256, 1, 0), (256, 4, 64),
+        (512, 2, 2080), (1024, 1, 160), (1024, 4, 0)]
+
+
+@pytest.mark.parametrize("cfg", CFGS)
+@pytest.mark.parametrize("batch", [1, 3, 8])
+@pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (16, 32)])
+def test_launch_shapes_integer_exact(cfg, batch, n, m):
+    """Every launch shape (threads, rows per wave, LDS segment) gives the exact
+    result on integer inputs, including segments that split K raggedly."""
+    rows, cols = 257, 2080
+    W = synth.integer_weights(rows, cols, seed=5)
+    keep = synth.random_mask(rows, cols, n, m, seed=6)
+    xi = np.random.default_rng(7).integers(-4, 5, size=(batch, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    values, bits = gpu_pack(W, keep, n, m, "f16")
+    Y = native.nm_spmm_small(values, bits, t16(X, "f16"), n, m, cfg=cfg)
+    want = oracle.masked_gemv(W, keep, X, False)
+    assert np.array_equal(f64(Y), want)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_integer_inputs_bit_exact(n, m, dtype):
+    rows, cols = 311, 4096
+    W = synth.integer_weights(rows, cols, seed=11, dtype=dtype)
+    keep = synth.random_mask(rows, cols, n, m, seed=12)
+    xi = np.random.default_rng(13).integers(-4, 5, size=(4, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, dtype)
+    values, bits = gpu_pack(W, keep, n, m, dtype)
+    want = oracle.masked_gemv(W, keep, X, dtype == "bf16")
+    y1 = native.nm_spmv(values, bits, t16(X[0], dtype), n, m)
+    assert np.array_equal(f64(y1), want[0])
+    Y = native.nm_spmm_small(values, bits, t16(X, dtype), n, m)
+    assert np.array_equal(f64(Y), want)
+
+
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_one_hot_x_selects_a_column(n, m):
+    """x = e_j gives y[r] = W[r, j] * keep[r, j] exactly: pins the bit ->
+    column mapping end to end."""
+    rows, cols = 64, 1024
+    W, keep, _ = inputs(rows, cols, n, m, "f16", 1, seed=21)
+    values, bits = gpu_pack(W, keep, n, m, "f16")
+    Wf = W.view(np.float16).astype(np.float64)
+    for j in (0, 1, 15, 16, 17, 31, 32, 511, 1000, 1023):
+        x = np.zeros(cols, dtype=np.float16)
+        x[j] = 1.0
+        y = native.nm_spmv(values, bits, t16(x.view(np.uint16), "f16"), n, m)
+        assert np.array_equal(f64(y), Wf[:, j] * keep[:, j])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("batch", [1, 4, 8])
+def test_16bit_output_within_one_ulp(batch, dtype):
+    rows, cols, n, m = 515, 4096, 4, 8
+    W, keep, X = inputs(rows, cols, n, m, dtype, batch, seed=31)
+    values, bits = gpu_pack(W, keep, n, m, dtype)
+    Y = native.nm_spmm_small(values, bits, t16(X, dtype), n, m, out_dtype=TDT[dtype])
+    want = round16_f64(oracle.masked_gemv(W, keep, X, dtype == "bf16"), dtype)
+    diff = np.abs(ordered16(u16(Y)) - ordered16(want))
+    assert diff.max() <= 1
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("batch", [1, 2, 5, 8])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 320), (300, 4096)])
+def test_dense_gemv_matches_oracle(rows, cols, batch, dtype):
+    W = synth.weights(rows, cols, seed=41, dtype=dtype)
+    X = synth.activations(batch, cols, seed=41, dtype=dtype)
+    Y = native.nm_dense_gemv(t16(W, dtype), t16(X, dtype))
+    want = oracle.masked_gemv(W, None, X, dtype == "bf16")
+    for b in range(batch):
+        assert rel_l2(f64(Y[b]), want[b]) <= TOL
+
+
+def test_dense_integer_exact():
+    rows, cols = 129, 2080
+    W = synth.integer_weights(rows, cols, seed=51)
+    xi = np.random.default_rng(52).integers(-4, 5, size=(8, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    for cfg in (None, (64, 4, 96), (1024, 2, 1024)):
+        Y = native.nm_dense_gemv(t16(W, "f16"), t16(X, "f16"), cfg=cfg)
+        assert np.array_equal(f64(Y), oracle.masked_gemv(W, None, X, False))
+
+
+def test_zero_columns_give_zero_output():
+    values = torch.empty((7, 0), dtype=torch.float16, device=DEV)
+    bits = torch.empty((7, 0), dtype=torch.int32, device=DEV)
+    x = torch.empty((0,), dtype=torch.float16, device=DEV)
+    y = torch.full((7,), 3.0, device=DEV)
+    native.nm_spmv(values, bits, x, 2, 4, out=y)
+    assert torch.count_nonzero(y).item() == 0
+
+
+# ---- full-size workloads, sampled rows ----------------------------------------
+
+def _full_cases():
+    cases = []
+    for cfg_id in (1, 2, 3, 4):
+        for mt, batches in workloads.config_matrices(cfg_id):
+            cases.append(pytest.param(mt, batches, id=f"cfg{cfg_id}-{mt.name}-{mt.rows}x{mt.cols}"))
+    # the 32-layer sweep: the first and the last layer
+    for mt, batches in workloads.config_matrices(5):
+        if mt.seed % 1000 == 0 or mt.seed // 1000 % 1000 in (0, 31):
+            pass
+    sweep = workloads.config_matrices(5)
+    for mt, batches in sweep[:7] + sweep[-7:]:
+        cases.append(pytest.param(mt, batches, id=f"cfg5-seed{mt.seed}-{mt.name}"))
+    return cases
+
+
+SAMPLE_ROWS = 384
+
+
+@pytest.mark.parametrize("mt,batches", _full_cases())
+def test_full_size_sampled_rows(mt, batches):
+    rng = np.random.default_rng(mt.seed + 99)
+    W = synth.weights(mt.rows, mt.cols, seed=mt.seed, dtype=mt.dtype)
+    keep = synth.topn_mask(W, mt.n, mt.m)
+    Wd = t16(W, mt.dtype)
+    values, bits = native.nm_pack(Wd, torch.from_numpy(keep).to(DEV), mt.n, mt.m)
+    idx = np.sort(rng.choice(mt.rows, size=min(SAMPLE_ROWS, mt.rows), replace=False))
+    # pack: bit-exact on the sampled rows, and 16 set bits in every word
+    st, ov, ob = oracle.pack(W[idx], keep[idx], mt.n, mt.m)
+    assert st == oracle.OK
+    ti = torch.from_numpy(idx).to(DEV)
+    assert np.array_equal(u16(values.index_select(0, ti)), ov)
+    assert np.array_equal(u32(bits.index_select(0, ti)), ob)
+    allbits = u32(bits)
+    pop = np.unpackbits(allbits.view(np.uint8)).reshape(-1, 32).sum(axis=1)
+    assert np.all(pop == 16)
+    bf = mt.dtype == "bf16"
+    for batch in batches:
+        X = synth.activations(batch, mt.cols, seed=mt.seed, dtype=mt.dtype, outliers=mt.outliers)
+        Xd = t16(X, mt.dtype)
+        if batch == 1:
+            Y = native.nm_spmv(values, bits, Xd[0], mt.n, mt.m).reshape(1, -1)
+        else:
+            Y = native.nm_spmm_small(values, bits, Xd, mt.n, mt.m)
+        Ys = f64(Y.index_select(1, ti))
+        want = oracle.masked_gemv(W, keep, X, bf, rows_idx=idx, threads=8)
+        for b in range(batch):
+            assert rel_l2(Ys[b], want[b]) <= TOL, (mt, batch, b)
+        # the dense comparison kernel on the same sampled rows
+        Yd = f64(native.nm_dense_gemv(Wd, Xd).index_select(1, ti))
+        wd = oracle.masked_gemv(W, None, X, bf, rows_idx=idx, threads=8)
+        for b in range(batch):
+            assert rel_l2(Yd[b], wd[b]) <= TOL, (mt, batch, b)
