@@ -170,6 +170,17 @@ int nm_dense_gemv_cfg(const void *W, const void *X, void *Y, int batch,
                       int64_t rows, int64_t cols, nm_dtype in_dt,
                       nm_dtype out_dt, const nm_launch_cfg *cfg, void *stream);
 
+/* Calibration read (measurement only, not part of the product path): loads
+ * every byte of buf once with 128-bit loads and writes one word per wavefront
+ * of the grid to out (grid * threads_per_wg / 64 uint32, device), so the
+ * loads cannot be elided.  Gives the device's achievable HBM read rate and
+ * the per-launch fixed cost beside the sparse kernel, and is the read of
+ * known size that scales the fetch-size counters.
+ *   buf: device, bytes % 16 == 0, 16-byte aligned; grid >= 1 workgroups of
+ *   threads_per_wg (64..1024, a power of two).  Asynchronous on `stream`. */
+int nm_stream_read(const void *buf, size_t bytes, uint32_t *out, int grid,
+                   int threads_per_wg, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

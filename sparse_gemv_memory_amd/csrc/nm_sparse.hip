@@ -36,7 +36,7 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr size_t kLdsBudget = 64 * 1024;  // bytes of LDS one workgroup may use
+constexpr size_t kLdsCap = 160 * 1024;  // LDS one workgroup may use (CU total on gfx950)
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
@@ -54,9 +54,22 @@ __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
                                   __builtin_bit_cast(h2_t, x), acc, false);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+// v + (v of the DPP-selected lane); rows outside ROW_MASK add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false);
+  return v + __int_as_float(t);
+}
+
+// Sum over the 64 lanes with DPP moves only (no LDS traffic); the result is
+// valid in lane 63.
+__device__ __forceinline__ float wave_sum_to_63(float v) {
+  v = dpp_add<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]: pairs
+  v = dpp_add<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]: quads
+  v = dpp_add<0x141, 0xf>(v);  // row_half_mirror: 8 lanes
+  v = dpp_add<0x140, 0xf>(v);  // row_mirror: 16 lanes (a row)
+  v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
@@ -96,33 +109,52 @@ struct XLay {
   }
 };
 
+// Staging of x into the XLay<BP> layout, one 8-column group at a time: the
+// group's 16-byte chunk of each batch row is loaded, and for BP > 1 the
+// chunks are transposed in registers into 8 column slots of BP values.
 template <int BP>
-__device__ __forceinline__ void stage_x_sparse(char *lds,
-                                               const uint16_t *__restrict__ x,
-                                               int B, int K, int s0, int S) {
+struct XGroup {
+  uint4 r[BP];
+};
+
+// Load group g (columns s0 + 8g .. +7) of every batch row; rows b >= B read
+// row B-1 and are zeroed, so the number of loads issued never depends on B.
+template <int BP>
+__device__ __forceinline__ void xgroup_load(XGroup<BP> &xg, const uint16_t *__restrict__ x,
+                                            int B, int K, int s0, int g) {
+#pragma unroll
+  for (int b = 0; b < BP; ++b) {
+    const int bb = b < B ? b : B - 1;
+    xg.r[b] = reinterpret_cast<const uint4 *>(x + (int64_t)bb * K + s0)[g];
+  }
+#pragma unroll
+  for (int b = 1; b < BP; ++b)
+    if (b >= B) xg.r[b] = make_uint4(0, 0, 0, 0);
+}
+
+template <int BP>
+__device__ __forceinline__ void xgroup_store(char *lds, const XGroup<BP> &xg, int g) {
   using L = XLay<BP>;
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int c0 = 8 * g;  // segment column of the group's first column
+  char *wbase = lds + L::FP + (c0 >> 5) * L::WS + (c0 & 31) * L::SB;
   if constexpr (BP == 1) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + s0);
-    for (int j = tid; j < S / 8; j += nthr) {
-      const uint4 q = src[j];
-      uint32_t *d =
-          reinterpret_cast<uint32_t *>(lds + L::FP + (j >> 2) * L::WS + (j & 3) * 16);
-      d[0] = q.x;
-      d[1] = q.y;
-      d[2] = q.z;
-      d[3] = q.w;
-    }
+    uint32_t *d = reinterpret_cast<uint32_t *>(wbase);
+    d[0] = xg.r[0].x;
+    d[1] = xg.r[0].y;
+    d[2] = xg.r[0].z;
+    d[3] = xg.r[0].w;
   } else {
-    for (int c = tid; c < S; c += nthr) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
       uint32_t d[BP / 2];
 #pragma unroll
       for (int p = 0; p < BP / 2; ++p) {
-        const uint32_t lo = (2 * p < B) ? x[(int64_t)(2 * p) * K + s0 + c] : 0u;
-        const uint32_t hi = (2 * p + 1 < B) ? x[(int64_t)(2 * p + 1) * K + s0 + c] : 0u;
-        d[p] = lo | (hi << 16);
+        const uint4 &a = xg.r[2 * p], &b = xg.r[2 * p + 1];
+        const uint32_t da = (e >> 1) == 0 ? a.x : (e >> 1) == 1 ? a.y : (e >> 1) == 2 ? a.z : a.w;
+        const uint32_t db = (e >> 1) == 0 ? b.x : (e >> 1) == 1 ? b.y : (e >> 1) == 2 ? b.z : b.w;
+        d[p] = (e & 1) ? ((da >> 16) | (db & 0xffff0000u)) : ((da & 0xffffu) | (db << 16));
       }
-      char *dst = lds + L::FP + (c >> 5) * L::WS + (c & 31) * L::SB;
+      char *dst = wbase + e * L::SB;
       if constexpr (BP == 2) {
         *reinterpret_cast<uint32_t *>(dst) = d[0];
       } else if constexpr (BP == 4) {
@@ -131,6 +163,18 @@ __device__ __forceinline__ void stage_x_sparse(char *lds,
         *reinterpret_cast<uint4 *>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
       }
     }
+  }
+}
+
+// Stage groups first, first + step, ... of the segment [s0, s0 + S).
+template <int BP>
+__device__ __forceinline__ void stage_x_sparse(char *lds, const uint16_t *__restrict__ x,
+                                               int B, int K, int s0, int S, int first,
+                                               int step) {
+  for (int g = first; g < S / 8; g += step) {
+    XGroup<BP> xg;
+    xgroup_load<BP>(xg, x, B, K, s0, g);
+    xgroup_store<BP>(lds, xg, g);
   }
 }
 
@@ -187,29 +231,225 @@ __device__ __forceinline__ void chunk8(const char *lds, uint32_t base,
   }
 }
 
-// Sparse product.  Workgroup g owns rows g*WPG*RPW + i*WPG + wave (i < RPW);
-// K is walked in segments of `seg` columns, each staged in LDS once per
-// workgroup.  Lane l of a wave handles value chunks l, l+64, ... of the
+// Process value chunk q (< nch) of a row with the lane's registers: select
+// the lane's 16 columns of mask word q >> 1 and run the 8-step scan.
+//   M32 = false (M <= 16): a half-word's 16 columns hold exactly 8 kept
+//         weights, so the odd lane scans the upper 16 bits of the word;
+//   M32 = true (16:32): the 8 kept weights of the odd lane are set bits 8..15
+//         of the word, so it first clears the 8 lowest set bits.
+template <bool BF, int BP, bool M32>
+__device__ __forceinline__ void chunk(const char *lds, int q, uint32_t mw, const uint4 v,
+                                      float (&acc)[BP]) {
+  using L = XLay<BP>;
+  const uint32_t h = q & 1;
+  uint32_t base = L::FP + (uint32_t)(q >> 1) * L::WS;
+  uint32_t m = mw;
+  if constexpr (!M32) {
+    // this lane's 16 columns in the low half; the sentinel bits above them
+    // keep every scan step on a nonzero word
+    m = (m >> (h << 4)) | 0xffff0000u;
+    base += h * (16 * L::SB);
+  } else {
+    // a word without exactly 16 set bits is replaced by one that keeps the
+    // scan in range (its row's result is then undefined)
+    if (__popc(m) != 16) m = 0xffffu;
+    if (h) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m &= m - 1;
+    }
+  }
+  chunk8<BF, BP>(lds, base, m, v, acc);
+}
+
+// Registers of one load batch: U value chunks and their mask words.
+template <int U>
+struct Batch {
+  uint4 v[U];
+  uint32_t m[U];
+};
+
+// Word 3 of a raw buffer resource for the gfx9 family (gfx950): untyped
+// 32-bit data, no swizzle; with stride 0 the range check is per byte offset.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the weight loads: nt (non-temporal).  Every weight byte is
+// read exactly once per call, and streaming it with nt measured 7-9% more
+// HBM read bandwidth on gfx950 than the default policy.
+constexpr int kStreamAux = 2;
+
+// Load batch t of a row segment: lane l gets value chunks t*64U + l + 64u
+// (u < U) and their mask words.  Raw buffer loads: the resource holds the
+// segment's base and byte size, so the per-lane offsets are loop-invariant,
+// the batch offset is a scalar, and a chunk past the end reads zeros (the
+// hardware range check) without touching memory.  nch = 0 makes a dummy
+// batch that keeps the wait counts uniform and costs no memory traffic.
+template <int U>
+__device__ __forceinline__ void load_batch(Batch<U> &bt, const uint4 *vrow,
+                                           const uint32_t *brow, int nch, int t, int lane) {
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void *)vrow, 0, nch * 16, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)brow, 0, nch * 2, kRsrcWord3);
+  const int sv = t * (kWave * U * 16), sb = t * (kWave * U * 2);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    bt.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rv, lane * 16 + u * kWave * 16, sv, kStreamAux));
+    bt.m[u] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lane >> 1) * 4 + u * kWave * 2, sb,
+                                                   kStreamAux);
+  }
+}
+
+// Consume a load batch.  A chunk past the row end (zeros, see load_batch) is
+// computed like any other at the row's last column range, without a branch,
+// and its sum is dropped by a select.  Straight-line code keeps the wait
+// counts of the pipeline exact.
+template <bool BF, int BP, bool M32, int U>
+__device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, int q0, int nch,
+                                          float (&acc)[BP]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int q = q0 + kWave * u;
+    const int qc = min(q, nch - 1);
+    float part[BP];
+#pragma unroll
+    for (int b = 0; b < BP; ++b) part[b] = 0.f;
+    chunk<BF, BP, M32>(lds, qc, bt.m[u], bt.v[u], part);
+#pragma unroll
+    for (int b = 0; b < BP; ++b) acc[b] += q < nch ? part[b] : 0.f;
+  }
+}
+
+template <int BP>
+__device__ __forceinline__ void finish_row(float (&acc)[BP], void *y, int B, int64_t R,
+                                           int64_t r, int lane, int out_kind) {
+#pragma unroll
+  for (int b = 0; b < BP; ++b) {
+    const float s = wave_sum_to_63(acc[b]);
+    if (lane == kWave - 1 && b < B) store_out(y, (int64_t)b * R + r, s, out_kind);
+    acc[b] = 0.f;
+  }
+}
+
+// Reduce the row sums of the wave's row i and park them in lane i of res
+// (no store inside the item loop; the wave stores its rows once at the end).
+template <int BP>
+__device__ __forceinline__ void collect_row(float (&acc)[BP], float (&res)[BP], int i, int lane) {
+#pragma unroll
+  for (int b = 0; b < BP; ++b) {
+    const float s = wave_sum_to_63(acc[b]);
+    const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kWave - 1));
+    res[b] = lane == i ? sv : res[b];
+    acc[b] = 0.f;
+  }
+}
+
+// Sparse product when all of x fits the LDS budget (the common case).  x is
+// staged once per workgroup; wave w of the grid owns the rpw consecutive rows
+// from w * rpw.  Its work is a sequence of items (row, load batch of U chunks
+// per lane) run as a two-stage software pipeline: the loads of item k+1 are
+// in flight while item k is consumed.  The first item's loads are issued
+// before x is committed to LDS, so the x and weight latencies overlap.
+template <bool BF, int BP, bool M32>
+__global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
+    const uint4 *__restrict__ values, const uint32_t *__restrict__ bits,
+    const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int rpw,
+    int out_kind) {
+  constexpr int U = 4;
+  constexpr int XS = BP == 1 ? 4 : 1;  // x groups per thread held in registers
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wpg = blockDim.x / kWave;
+  const int nch = K >> 4;                                // value chunks per row
+  const int nb = (nch + kWave * U - 1) / (kWave * U);    // load batches per row
+  // wave index as a wave-uniform (scalar) value: the item loop below is then
+  // scalar control flow and the wait counts of the pipeline stay exact
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t r0 = ((int64_t)blockIdx.x * wpg + wid) * rpw;
+  const int64_t left = R - r0;
+  const int nrows = left <= 0 ? 0 : (left < rpw ? (int)left : rpw);
+  const int nitems = nrows * nb;
+  const int64_t cpr = nch, wpr = K >> 5;
+
+  float acc[BP];
+#pragma unroll
+  for (int b = 0; b < BP; ++b) acc[b] = 0.f;
+  if (K == 0) {  // every sum is empty
+    for (int r = 0; r < nrows; ++r) finish_row<BP>(acc, y, B, R, r0 + r, lane, out_kind);
+    return;
+  }
+
+  // x: the first XS groups per thread are loaded, then the weights of the
+  // wave's first two items, then the groups are written to LDS.  Every load
+  // here is issued unconditionally (indices clamped, dummy batches) so that
+  // the waits before the LDS writes count exactly and leave the weight loads
+  // in flight.
+  const int ngx = K >> 3;
+  XGroup<BP> xg[XS];
+#pragma unroll
+  for (int s = 0; s < XS; ++s)
+    xgroup_load<BP>(xg[s], x, B, K, 0, min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1));
+  // the wave's items k = 0, 1 are in flight before x is committed to LDS;
+  // an item past the wave's last is a dummy load (no memory traffic)
+  auto item_load = [&](Batch<U> &bt, int k) {
+    const bool real = k < nitems;
+    const int ii = real ? k / nb : 0, tt = real ? k - ii * nb : 0;
+    const int64_t r = real ? r0 + ii : 0;
+    load_batch<U>(bt, values + r * cpr, bits + r * wpr, real ? nch : 0, tt, lane);
+  };
+  Batch<U> A, Bt;
+  item_load(A, 0);
+  item_load(Bt, 1);
+  // clamped groups rewrite group ngx-1 with the same data it already holds
+#pragma unroll
+  for (int s = 0; s < XS; ++s)
+    xgroup_store<BP>(lds, xg[s], min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1));
+  stage_x_sparse<BP>(lds, x, B, K, 0, K, threadIdx.x + XS * blockDim.x, blockDim.x);
+  __syncthreads();
+
+  float res[BP];  // lane i holds the sums of the wave's row i
+#pragma unroll
+  for (int b = 0; b < BP; ++b) res[b] = 0.f;
+  // two-buffer pipeline: while one batch is consumed the other is in flight
+  for (int k = 0; k < nitems; k += 2) {
+    const int i = k / nb, t = k - i * nb;
+    run_batch<BF, BP, M32, U>(lds, A, t * kWave * U + lane, nch, acc);
+    if (t == nb - 1) collect_row<BP>(acc, res, i, lane);
+    item_load(A, k + 2);
+    if (k + 1 >= nitems) break;
+    const int i1 = (k + 1) / nb, t1 = (k + 1) - i1 * nb;
+    run_batch<BF, BP, M32, U>(lds, Bt, t1 * kWave * U + lane, nch, acc);
+    if (t1 == nb - 1) collect_row<BP>(acc, res, i1, lane);
+    item_load(Bt, k + 3);
+  }
+  if (lane < nrows) {
+#pragma unroll
+    for (int b = 0; b < BP; ++b)
+      if (b < B) store_out(y, (int64_t)b * R + r0 + lane, res[b], out_kind);
+  }
+}
+
+// Sparse product when x does not fit the LDS budget in one piece.
+// Workgroup g owns rows g*WPG*RPW + i*WPG + wave (i < RPW), processed
+// together; K is walked in segments of `seg` columns, each staged in LDS once
+// per workgroup, and the RPW x BP accumulators live in registers throughout.  Lane l of a wave handles value chunks l, l+64, ... of the
 // segment; chunk q is half (q & 1) of mask word q >> 1.
 //   M32 = false (M <= 16): a half-word's 16 columns hold exactly 8 kept
 //         weights, so the odd lane scans the upper 16 bits of the word;
 //   M32 = true (16:32): the 8 kept weights of the odd lane are set bits 8..15
 //         of the word, so it first clears the 8 lowest set bits.
 template <bool BF, int BP, bool M32, int RPW>
-__global__ __launch_bounds__(1024) void nm_spmv_kernel(
+__global__ __launch_bounds__(1024) void nm_spmv_seg_kernel(
     const uint4 *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R,
     int K, int seg, int out_kind) {
-  using L = XLay<BP>;
   constexpr int U = RPW >= 4 ? 2 : 4;  // chunks per lane per load batch
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
   const int wpg = blockDim.x / kWave;
-  const int64_t row0 = (int64_t)blockIdx.x * wpg * RPW + wid;
+  const int64_t row0 =
+      (int64_t)blockIdx.x * wpg * RPW + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t cpr = K >> 4;  // 16-byte value chunks per row
   const int64_t wpr = K >> 5;  // mask words per row
-  const uint32_t h = lane & 1;
 
   float acc[RPW][BP];
 #pragma unroll
@@ -220,68 +460,29 @@ __global__ __launch_bounds__(1024) void nm_spmv_kernel(
   for (int s0 = 0; s0 < K; s0 += seg) {
     const int S = min(seg, K - s0);
     if (s0) __syncthreads();  // all waves are done with the previous segment
-    stage_x_sparse<BP>(lds, x, B, K, s0, S);
+    stage_x_sparse<BP>(lds, x, B, K, s0, S, threadIdx.x, blockDim.x);
     __syncthreads();
     const int nch = S >> 4;
     const int64_t cbeg = s0 >> 4;
     for (int t0 = 0; t0 < nch; t0 += kWave * U) {
-      uint4 v[RPW][U];
-      uint32_t mw[RPW][U];
+      Batch<U> bt[RPW];
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
-        const int64_t r = row0 + (int64_t)i * wpg;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int q = t0 + kWave * u + lane;
-          if (r < R && q < nch) {
-            v[i][u] = values[r * cpr + cbeg + q];
-            mw[i][u] = bits[r * wpr + ((cbeg + q) >> 1)];
-          } else {
-            v[i][u] = make_uint4(0, 0, 0, 0);
-            mw[i][u] = 0;
-          }
-        }
+        // rows past R reload row R-1 (wave-uniform) and are never stored
+        const int64_t r = min(row0 + (int64_t)i * wpg, R - 1);
+        load_batch<U>(bt[i], values + r * cpr + cbeg, bits + r * wpr + (cbeg >> 1), nch,
+                      t0 / (kWave * U), lane);
       }
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int64_t r = row0 + (int64_t)i * wpg;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int q = t0 + kWave * u + lane;
-          if (r < R && q < nch) {
-            uint32_t base = L::FP + (uint32_t)(q >> 1) * L::WS;
-            uint32_t m = mw[i][u];
-            if constexpr (!M32) {
-              // this lane's 16 columns in the low half; the sentinel bits
-              // above them keep every scan step on a nonzero word
-              m = (m >> (h << 4)) | 0xffff0000u;
-              base += h * (16 * L::SB);
-            } else {
-              // a word without exactly 16 set bits is replaced by one that
-              // keeps the scan in range (its row's result is then undefined)
-              if (__popc(m) != 16) m = 0xffffu;
-              if (h) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) m &= m - 1;
-              }
-            }
-            chunk8<BF, BP>(lds, base, m, v[i][u], acc[i]);
-          }
-        }
-      }
+      for (int i = 0; i < RPW; ++i)
+        run_batch<BF, BP, M32, U>(lds, bt[i], t0 + lane, nch, acc[i]);
     }
   }
 
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int64_t r = row0 + (int64_t)i * wpg;
-    if (r < R) {  // uniform across the wave
-#pragma unroll
-      for (int b = 0; b < BP; ++b) {
-        const float s = wave_sum(acc[i][b]);
-        if (lane == 0 && b < B) store_out(y, (int64_t)b * R + r, s, out_kind);
-      }
-    }
+    if (r < R) finish_row<BP>(acc[i], y, B, R, r, lane, out_kind);  // uniform per wave
   }
 }
 
@@ -357,8 +558,8 @@ __global__ __launch_bounds__(1024) void nm_dense_kernel(
     if (r < R) {
 #pragma unroll
       for (int b = 0; b < BP; ++b) {
-        const float s = wave_sum(acc[i][b]);
-        if (lane == 0 && b < B) store_out(y, (int64_t)b * R + r, s, out_kind);
+        const float s = wave_sum_to_63(acc[i][b]);
+        if (lane == kWave - 1 && b < B) store_out(y, (int64_t)b * R + r, s, out_kind);
       }
     }
   }
@@ -405,6 +606,38 @@ __global__ __launch_bounds__(256) void nm_pack_kernel(
   // sum over the wave, one atomic per wave
   for (int o = kWave / 2; o > 0; o >>= 1) nbad += __shfl_xor(nbad, o, kWave);
   if (lane == 0 && nbad) atomicAdd(bad, nbad);
+}
+
+// Calibration read: every 16-byte chunk of buf is loaded once with the same
+// 128-bit non-temporal buffer loads as the sparse kernel's weights (wave w
+// reads chunks w*64*U + l + 64u, grid-strided), and each wave writes one
+// word so the loads cannot be dropped.  It gives the achievable HBM read rate
+// and the per-launch fixed cost, and is the plain read of known size that
+// scales the fetch-size counters.
+__global__ __launch_bounds__(1024) void nm_stream_read_kernel(const char *__restrict__ buf,
+                                                               int64_t nchunks,
+                                                               uint32_t *__restrict__ out) {
+  constexpr int U = 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  uint32_t acc = 0;
+  for (int64_t c0 = wave * kWave * U; c0 < nchunks; c0 += nwaves * kWave * U) {
+    const int64_t left = nchunks - c0;
+    const int nbytes = (int)((left < kWave * U ? left : kWave * U) * 16);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(buf + c0 * 16), 0, nbytes, kRsrcWord3);
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           r, lane * 16 + u * kWave * 16, 0, kStreamAux));
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  const int sv = __reduce_or_sync(~0ull, (int)acc);
+  if (lane == 0) out[wave] = (uint32_t)sv;
 }
 
 // ---------------------------------------------------------------------------
@@ -496,36 +729,70 @@ int max_seg(bool dense, int bp, size_t budget) {
   return lo;
 }
 
+size_t lds_budget(const DevInfo &di) {
+  return di.lds_per_wg < kLdsCap ? di.lds_per_wg : kLdsCap;
+}
+
+// Is this a launch of the single-segment row kernel (all of x in LDS)?
+bool rows_kernel(bool dense, int64_t cols, int seg) {
+  return !dense && seg >= cols;
+}
+
+int threads_for_lds(size_t lds) {
+  return lds <= 40 * 1024 ? 256 : lds <= 80 * 1024 ? 512 : 1024;
+}
+
 nm_status default_cfg(int64_t rows, int64_t cols, int batch, bool dense,
                       nm_launch_cfg *cfg) {
   DevInfo di;
   nm_status st = device_info(&di);
   if (st != NM_OK) return st;
   const int bp = pad_batch(batch);
-  const size_t budget = di.lds_per_wg < kLdsBudget ? di.lds_per_wg : kLdsBudget;
+  const size_t budget = lds_budget(di);
   const int smax = max_seg(dense, bp, budget);
+  if (!dense && sparse_lds_bytes(bp, (int)cols) <= budget) {
+    // row kernel: x staged once per workgroup.  When the rows split evenly
+    // over the CUs, every wave gets the same number of rows rpw (<= 8), with
+    // at least two workgroups per CU: x is staged rarely and no CU finishes
+    // early.  Otherwise one row per wave, and the hardware balances the
+    // workgroups.
+    cfg->seg_cols = cols > 0 ? (int)cols : 32;
+    cfg->threads_per_wg = threads_for_lds(sparse_lds_bytes(bp, cfg->seg_cols));
+    const int64_t per_cu_rows = (int64_t)di.cus * (cfg->threads_per_wg / kWave);
+    int rpw = 1;
+    if (rows % per_cu_rows == 0) {
+      const int64_t q = rows / per_cu_rows;  // rows per wave if one workgroup per CU
+      for (int d = 8; d >= 2; --d)
+        if (q % d == 0 && q / d >= 2) { rpw = d; break; }
+    }
+    cfg->rows_per_wave = rpw;
+    return NM_OK;
+  }
   int seg;
   if (cols <= smax) {
     seg = cols > 0 ? (int)cols : 32;
   } else {
     seg = smax >= 1024 ? smax / 1024 * 1024 : smax;
   }
-  const size_t lds = lds_bytes(dense, bp, seg);
   cfg->seg_cols = seg;
-  cfg->threads_per_wg = lds > 32 * 1024 ? 512 : 256;
+  cfg->threads_per_wg = threads_for_lds(lds_bytes(dense, bp, seg));
   cfg->rows_per_wave = bp == 1 ? 1 : 2;
-  (void)rows;
   return NM_OK;
 }
 
-nm_status check_cfg(const nm_launch_cfg &c, bool dense, int bp,
+nm_status check_cfg(const nm_launch_cfg &c, int64_t cols, bool dense, int bp,
                     const DevInfo &di) {
   const int t = c.threads_per_wg;
   if (!(t == 64 || t == 128 || t == 256 || t == 512 || t == 1024)) return NM_ERR_INVALID_ARG;
+  if (c.seg_cols <= 0 || c.seg_cols % 32 != 0) return NM_ERR_INVALID_ARG;
+  if (rows_kernel(dense, cols, c.seg_cols)) {
+    if (c.rows_per_wave < 1 || c.rows_per_wave > 64) return NM_ERR_INVALID_ARG;
+    if (sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32) > lds_budget(di)) return NM_ERR_INVALID_ARG;
+    return NM_OK;
+  }
   if (!(c.rows_per_wave == 1 || c.rows_per_wave == 2 || c.rows_per_wave == 4))
     return NM_ERR_INVALID_ARG;
-  if (c.seg_cols <= 0 || c.seg_cols % 32 != 0) return NM_ERR_INVALID_ARG;
-  if (lds_bytes(dense, bp, c.seg_cols) > di.lds_per_wg) return NM_ERR_INVALID_ARG;
+  if (lds_bytes(dense, bp, c.seg_cols) > lds_budget(di)) return NM_ERR_INVALID_ARG;
   return NM_OK;
 }
 
@@ -541,36 +808,53 @@ nm_status resolve_cfg(int64_t rows, int64_t cols, int batch, bool dense,
   DevInfo di;
   st = device_info(&di);
   if (st != NM_OK) return st;
-  return check_cfg(*out, dense, pad_batch(batch), di);
+  return check_cfg(*out, cols, dense, pad_batch(batch), di);
 }
 
-typedef void (*sparse_fn)(const uint4 *, const uint32_t *, const uint16_t *,
-                          void *, int, int64_t, int, int, int);
+typedef void (*seg_fn)(const uint4 *, const uint32_t *, const uint16_t *, void *, int,
+                       int64_t, int, int, int);
+typedef void (*rows_fn)(const uint4 *, const uint32_t *, const uint16_t *, void *, int,
+                        int64_t, int, int, int);
 typedef void (*dense_fn)(const uint4 *, const uint16_t *, void *, int, int64_t,
                          int, int, int);
 
 template <bool BF, int BP, bool M32>
-sparse_fn pick_sparse_rpw(int rpw) {
+seg_fn pick_seg_rpw(int rpw) {
   switch (rpw) {
-    case 1: return nm_spmv_kernel<BF, BP, M32, 1>;
-    case 2: return nm_spmv_kernel<BF, BP, M32, 2>;
-    default: return nm_spmv_kernel<BF, BP, M32, 4>;
+    case 1: return nm_spmv_seg_kernel<BF, BP, M32, 1>;
+    case 2: return nm_spmv_seg_kernel<BF, BP, M32, 2>;
+    default: return nm_spmv_seg_kernel<BF, BP, M32, 4>;
   }
 }
 
 template <bool BF, bool M32>
-sparse_fn pick_sparse_bp(int bp, int rpw) {
+seg_fn pick_seg_bp(int bp, int rpw) {
   switch (bp) {
-    case 1: return pick_sparse_rpw<BF, 1, M32>(rpw);
-    case 2: return pick_sparse_rpw<BF, 2, M32>(rpw);
-    case 4: return pick_sparse_rpw<BF, 4, M32>(rpw);
-    default: return pick_sparse_rpw<BF, 8, M32>(rpw);
+    case 1: return pick_seg_rpw<BF, 1, M32>(rpw);
+    case 2: return pick_seg_rpw<BF, 2, M32>(rpw);
+    case 4: return pick_seg_rpw<BF, 4, M32>(rpw);
+    default: return pick_seg_rpw<BF, 8, M32>(rpw);
   }
 }
 
-sparse_fn pick_sparse(bool bf, bool m32, int bp, int rpw) {
-  if (bf) return m32 ? pick_sparse_bp<true, true>(bp, rpw) : pick_sparse_bp<true, false>(bp, rpw);
-  return m32 ? pick_sparse_bp<false, true>(bp, rpw) : pick_sparse_bp<false, false>(bp, rpw);
+seg_fn pick_seg(bool bf, bool m32, int bp, int rpw) {
+  if (bf) return m32 ? pick_seg_bp<true, true>(bp, rpw) : pick_seg_bp<true, false>(bp, rpw);
+  return m32 ? pick_seg_bp<false, true>(bp, rpw) : pick_seg_bp<false, false>(bp, rpw);
+}
+
+template <bool BF, bool M32>
+rows_fn pick_rows_bp(int bp) {
+  switch (bp) {
+    case 1: return nm_spmv_rows_kernel<BF, 1, M32>;
+    case 2: return nm_spmv_rows_kernel<BF, 2, M32>;
+    case 4: return nm_spmv_rows_kernel<BF, 4, M32>;
+    default: return nm_spmv_rows_kernel<BF, 8, M32>;
+  }
+}
+
+rows_fn pick_rows(bool bf, bool m32, int bp) {
+  if (bf) return m32 ? pick_rows_bp<true, true>(bp) : pick_rows_bp<true, false>(bp);
+  return m32 ? pick_rows_bp<false, true>(bp) : pick_rows_bp<false, false>(bp);
 }
 
 template <bool BF, int BP>
@@ -615,14 +899,25 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
   st = resolve_cfg(rows, cols, batch, false, user, &cfg);
   if (st != NM_OK) return st;
   const int bp = pad_batch(batch);
-  sparse_fn fn = pick_sparse(in_dt == NM_BF16, m == 32, bp, cfg.rows_per_wave);
-  const int64_t rows_per_wg = (int64_t)(cfg.threads_per_wg / kWave) * cfg.rows_per_wave;
-  const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
-  if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
-                     sparse_lds_bytes(bp, cfg.seg_cols), (hipStream_t)stream,
-                     (const uint4 *)values, bits, (const uint16_t *)X, Y, batch,
-                     rows, (int)cols, cfg.seg_cols, (int)out_dt);
+  const bool bf = in_dt == NM_BF16, m32 = m == 32;
+  const int wpg = cfg.threads_per_wg / kWave;
+  if (rows_kernel(false, cols, cfg.seg_cols)) {
+    const int64_t rows_per_wg = (int64_t)wpg * cfg.rows_per_wave;
+    const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+    if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(pick_rows(bf, m32, bp), dim3((unsigned)grid), dim3(cfg.threads_per_wg),
+                       sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32), (hipStream_t)stream,
+                       (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
+                       (int)cols, cfg.rows_per_wave, (int)out_dt);
+  } else {
+    const int64_t rows_per_wg = (int64_t)wpg * cfg.rows_per_wave;
+    const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+    if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(pick_seg(bf, m32, bp, cfg.rows_per_wave), dim3((unsigned)grid),
+                       dim3(cfg.threads_per_wg), sparse_lds_bytes(bp, cfg.seg_cols),
+                       (hipStream_t)stream, (const uint4 *)values, bits, (const uint16_t *)X, Y,
+                       batch, rows, (int)cols, cfg.seg_cols, (int)out_dt);
+  }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? NM_OK : hip_fail(e);
 }
@@ -763,4 +1058,18 @@ int nm_dense_gemv(const void *W, const void *X, void *Y, int batch,
                            stream);
 }
 
+int nm_stream_read(const void *buf, size_t bytes, uint32_t *out, int grid, int threads_per_wg,
+                   void *stream) {
+  if (!buf || !out || bytes == 0 || grid < 1) return NM_ERR_INVALID_ARG;
+  if (bytes % 16 != 0) return NM_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return NM_ERR_ALIGN;
+  const int t = threads_per_wg;
+  if (!(t == 64 || t == 128 || t == 256 || t == 512 || t == 1024)) return NM_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(nm_stream_read_kernel, dim3((unsigned)grid), dim3(t), 0, (hipStream_t)stream,
+                     (const char *)buf, (int64_t)(bytes / 16), out);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NM_OK : hip_fail(e);
+}
+
 }  // extern "C"
+
