@@ -12,6 +12,9 @@ Measurement:
   so no call finds its weights in the 256 MiB Infinity Cache or in L2;
 * each step's seven launches are captured once in a HIP graph and replayed
   (the kernels are a few microseconds long, shorter than a Python launch);
+  the graph follows the layer's data flow: q, k, v (same input) run as
+  parallel branches, then o, then gate and up in parallel, then down; the
+  strictly serial chain of the seven launches is timed beside it;
 * the K timed steps are bracketed by torch.cuda.synchronize() and HIP events;
 * per-kernel duration: a graph of back-to-back launches of one projection
   over its rotation, HIP events around each replay, divided by the launches;
@@ -138,12 +141,37 @@ def time_steps(graphs, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def chain_graphs(projs, call, b, nsteps, copies_attr):
+# The layer's data flow: q, k, v read the same x and are independent; o
+# follows them; gate and up read the same x; down follows them.
+LAYER_STAGES = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+_side = []
+
+
+def chain_graphs(projs, call, b, nsteps, copies_attr, parallel=True):
+    """One graph per step.  parallel: the independent projections of a stage
+    run on side streams (default priority) as parallel graph branches;
+    otherwise the seven launches form one serial chain."""
+    by_name = {p.name: p for p in projs}
+    while len(_side) < 2:
+        _side.append(torch.cuda.Stream())
     graphs = []
     for s in range(nsteps):
         def step(s=s):
-            for p in projs:
-                call(p, b, s % getattr(p, copies_attr))
+            if not parallel:
+                for p in projs:
+                    call(p, b, s % getattr(p, copies_attr))
+                return
+            main = torch.cuda.current_stream()
+            for stage in LAYER_STAGES:
+                side = _side[:len(stage) - 1]
+                for st in side:
+                    st.wait_stream(main)
+                call(by_name[stage[0]], b, s % getattr(by_name[stage[0]], copies_attr))
+                for name, st in zip(stage[1:], side):
+                    with torch.cuda.stream(st):
+                        call(by_name[name], b, s % getattr(by_name[name], copies_attr))
+                for st in side:
+                    main.wait_stream(st)
         graphs.append(capture(step))
     return graphs
 
@@ -200,6 +228,50 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
     }
 
 
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of
+# `bench.py --counters`, each scaled by the same counter's reading for a plain
+# 64 MiB copy (fetch x 2.0, write x 1.0), keyed by the SHA-256 of the kernel
+# source they were taken on.  Any change to the source makes the figure stale,
+# and it is then reported as null.
+MEASURED_TRAFFIC = {
+    # (rows, cols): (source sha256, bytes per launch); see
+    # profiles/nm_spmv_14336x4096_hbm_counters.md
+    (14336, 4096): ("d6c83f5e64683961f7b002d9a7bfb52a92c0717590ba35a48a3d7536007e7b05",
+                    66283986),
+}
+
+
+def measured_traffic(rows, cols):
+    import hashlib
+    src = os.path.join(ROOT, "sparse_gemv_memory_amd", "csrc", "nm_sparse.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    entry = MEASURED_TRAFFIC.get((rows, cols))
+    if entry and entry[0] == digest:
+        return entry[1]
+    return None
+
+
+def counters_run():
+    """Eager launches with known byte counts, for hardware-counter passes."""
+    mt = [m for m, _ in workloads.config_matrices(2) if m.name == "gate"][0]
+    p = Proj(mt, (1,), False)
+    torch.cuda.synchronize()
+    for c in range(5):
+        p.sparse_call(1, c)
+    torch.cuda.synchronize()
+    n = 64 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=DEV).fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"sparse_kernel_bytes_per_launch": p.sbytes[1],
+                      "sparse_kernel_read_bytes": p.sbytes[1] - mt.rows * 4,
+                      "sparse_kernel_write_bytes": mt.rows * 4,
+                      "copy_bytes_each_way": n}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +281,10 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch4", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="short eager run for rocprofv3 --pmc: the 14336x4096 sparse kernel on "
+                         "5 cache-cold copies, then 5 plain copies of 64 MiB (the known-size "
+                         "reference for FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -222,6 +298,9 @@ def main():
         sys.exit(2)
     native.lib()  # fail loudly if the HIP library is missing
 
+    if args.counters:
+        counters_run()
+        return
     batches = (1,) if args.no_batch4 else (1, 4)
     want_dense = not args.no_dense
     log(f"building the Llama-3.1-8B layer workload (2:4 fp16), batches {batches}")
@@ -229,23 +308,21 @@ def main():
     layer_bytes = {b: sum(p.sbytes[b] for p in projs) for b in batches}
     nsteps = min(args.steps + args.warmup, 256)
 
-    out = {}
     timings = {}
+    kinds = [("sparse", Proj.sparse_call, "nc")]
+    if want_dense:
+        kinds += [("dense", Proj.dense_call, "ndc"), ("torch", Proj.torch_call, "ndc")]
     for b in batches:
-        log(f"sparse chain b={b}: capturing {nsteps} step graphs")
-        g = chain_graphs(projs, Proj.sparse_call, b, nsteps, "nc")
-        torch.cuda.synchronize()
-        ms = time_steps(g, args.steps, args.warmup)
-        timings[("sparse", b)] = ms
-        del g
-        if want_dense:
-            for kind, call in (("dense", Proj.dense_call), ("torch", Proj.torch_call)):
-                g = chain_graphs(projs, call, b, nsteps, "ndc")
-                timings[(kind, b)] = time_steps(g, args.steps, args.warmup)
+        for kind, call, attr in kinds:
+            for par in (True, False):
+                g = chain_graphs(projs, call, b, nsteps, attr, parallel=par)
+                torch.cuda.synchronize()
+                timings[(kind, b, par)] = time_steps(g, args.steps, args.warmup)
                 del g
         for k, v in timings.items():
             if k[1] == b:
-                log(f"  {k[0]:6s} b={b}: {1e3 * v:8.1f} us/step")
+                log(f"  {k[0]:6s} b={b} {'layer graph' if k[2] else 'serial chain'}: "
+                    f"{1e3 * v:8.1f} us/step")
 
     # per-kernel durations (batch 1) and the roofline of the dominant kernel
     per = {}
@@ -262,14 +339,25 @@ def main():
         log(f"  {p.name:5s} {p.mt.rows:5d}x{p.mt.cols:5d}: {us:7.2f} us  "
             f"{d['GB/s']:7.1f} GB/s ({100 * d['frac_of_peak']:.1f}% of 8 TB/s)"
             + (f"  dense {d['dense_us']:.2f} us, torch {d['torch_linear_us']:.2f} us" if want_dense else ""))
-    dom = max(projs, key=lambda p: per[f"{p.name} {p.mt.rows}x{p.mt.cols}"]["us"])
-    dk = per[f"{dom.name} {dom.mt.rows}x{dom.mt.cols}"]
-    roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": PEAK_GBS, "unit": "GB/s",
-                "frac": round(dk["GB/s"] / PEAK_GBS, 4), "traffic": None,
-                "kernel": f"nm_spmv_kernel {dom.mt.rows}x{dom.mt.cols} 2:4 fp16 b1",
-                "bytes_per_launch": dom.sbytes[1], "us_per_launch": dk["us"]}
+    # the dominant kernel: the launch shape with the most time per step (the
+    # 14336x4096 shape runs twice per layer, as gate and up)
+    shape_time = {}
+    for p in projs:
+        key = (p.mt.rows, p.mt.cols)
+        shape_time.setdefault(key, [0.0, []])
+        shape_time[key][0] += per[f"{p.name} {p.mt.rows}x{p.mt.cols}"]["us"]
+        shape_time[key][1].append(p)
+    (drows, dcols), (_, dps) = max(shape_time.items(), key=lambda kv: kv[1][0])
+    dus = float(np.mean([per[f"{p.name} {drows}x{dcols}"]["us"] for p in dps]))
+    dbytes = dps[0].sbytes[1]
+    roofline = {"bound": "hbm", "achieved": round(dbytes / dus / 1e3, 1), "peak": PEAK_GBS,
+                "unit": "GB/s", "frac": round(dbytes / dus / 1e3 / PEAK_GBS, 4),
+                "traffic": measured_traffic(drows, dcols),
+                "kernel": f"nm_spmv_rows_kernel {drows}x{dcols} 2:4 fp16 batch 1",
+                "bytes_per_launch": dbytes, "us_per_launch": round(dus, 3),
+                "launches_per_step": len(dps)}
 
-    ms = timings[("sparse", 1)]
+    ms = timings[("sparse", 1, False)]
     res = {
         "metric": METRIC,
         "value": round(layer_bytes[1] / (ms * 1e-3) / 1e9, 1),
@@ -287,23 +375,28 @@ def main():
                                "(q,o 4096x4096; k,v 1024x4096; gate,up 14336x4096; down 4096x14336), "
                                "2:4 fp16, x N(0,1) + 0.1% outlier channels x20",
                    "batch": 1, "pattern": "2:4", "bytes_per_step": layer_bytes[1],
-                   "launches_per_step": len(projs), "timing": "HIP-graph replay per step, "
-                   ">=1 GiB rotation per projection (cache-cold)"},
+                   "launches_per_step": len(projs), "timing": "one HIP graph per step, the 7 "
+                   "launches in series, >=1 GiB rotation per projection (cache-cold)"},
         "frac_of_peak": round(layer_bytes[1] / (ms * 1e-3) / 1e9 / PEAK_GBS, 4),
         "us_per_call": per,
         "roofline": roofline,
     }
+    res["ms_per_step_parallel_branches"] = round(timings[("sparse", 1, True)], 5)
+
+    def best_dense(b):
+        return min(timings[(k, b, par)] for k in ("dense", "torch") for par in (False, True))
+
     if want_dense:
-        res["dense_ms_per_step"] = {"nm_dense_gemv": round(timings[("dense", 1)], 5),
-                                    "torch_linear": round(timings[("torch", 1)], 5)}
-        res["speedup_vs_best_dense"] = round(min(timings[("dense", 1)], timings[("torch", 1)]) / ms, 3)
+        res["dense_ms_per_step"] = {f"{k} {'parallel branches' if par else 'serial'}":
+                                    round(timings[(k, 1, par)], 5)
+                                    for k in ("dense", "torch") for par in (False, True)}
+        res["speedup_vs_best_dense"] = round(best_dense(1) / ms, 3)
     if 4 in batches:
-        ms4 = timings[("sparse", 4)]
-        b4 = {"ms_per_step": round(ms4, 5), "GB/s": round(layer_bytes[4] / (ms4 * 1e-3) / 1e9, 1)}
+        ms4 = timings[("sparse", 4, False)]
+        b4 = {"ms_per_step": round(ms4, 5), "GB/s": round(layer_bytes[4] / (ms4 * 1e-3) / 1e9, 1),
+              "ms_per_step_parallel_branches": round(timings[("sparse", 4, True)], 5)}
         if want_dense:
-            b4["dense_ms_per_step"] = {"nm_dense_gemv": round(timings[("dense", 4)], 5),
-                                       "torch_linear": round(timings[("torch", 4)], 5)}
-            b4["speedup_vs_best_dense"] = round(min(timings[("dense", 4)], timings[("torch", 4)]) / ms4, 3)
+            b4["speedup_vs_best_dense"] = round(best_dense(4) / ms4, 3)
         res["batch4"] = b4
     if not args.no_cpu_baseline:
         gpu_y = {}

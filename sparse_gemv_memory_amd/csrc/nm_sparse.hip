@@ -486,6 +486,111 @@ __global__ __launch_bounds__(1024) void nm_spmv_seg_kernel(
   }
 }
 
+// Dense comparison when x fits the LDS budget, built like the sparse row
+// kernel so that the speedup is measured against an equally tuned dense
+// GEMV: x staged once per workgroup as BP contiguous rows; each wave walks
+// its rows as a two-stage pipeline of load batches (lane l takes 16-byte
+// chunks, 8 columns each, t*64U + l + 64u), with the same raw buffer loads
+// and nt policy as the sparse weights.
+template <int U>
+struct DBatch {
+  uint4 v[U];
+};
+
+template <int U>
+__device__ __forceinline__ void dload_batch(DBatch<U> &bt, const uint4 *wrow, int nch, int t,
+                                            int lane) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void *)wrow, 0, nch * 16, kRsrcWord3);
+  const int so = t * (kWave * U * 16);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    bt.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            r, lane * 16 + u * kWave * 16, so, kStreamAux));
+}
+
+template <bool BF, int BP, int U>
+__device__ __forceinline__ void drun_batch(const char *lds, int K, const DBatch<U> &bt, int q0,
+                                           int nch, float (&acc)[BP]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int q = q0 + kWave * u;
+    const int qc = min(q, nch - 1);
+#pragma unroll
+    for (int b = 0; b < BP; ++b) {
+      const uint4 xq = *reinterpret_cast<const uint4 *>(lds + (size_t)b * K * 2 + (size_t)qc * 16);
+      float a = 0.f;
+      a = dot2<BF>(bt.v[u].x, xq.x, a);
+      a = dot2<BF>(bt.v[u].y, xq.y, a);
+      a = dot2<BF>(bt.v[u].z, xq.z, a);
+      a = dot2<BF>(bt.v[u].w, xq.w, a);
+      acc[b] += q < nch ? a : 0.f;
+    }
+  }
+}
+
+template <bool BF, int BP>
+__global__ __launch_bounds__(1024) void nm_dense_rows_kernel(
+    const uint4 *__restrict__ W, const uint16_t *__restrict__ x, void *__restrict__ y, int B,
+    int64_t R, int K, int rpw, int out_kind) {
+  constexpr int U = 4;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wpg = blockDim.x / kWave;
+  const int nch = K >> 3;  // 16-byte chunks per row
+  const int nb = (nch + kWave * U - 1) / (kWave * U);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t r0 = ((int64_t)blockIdx.x * wpg + wid) * rpw;
+  const int64_t left = R - r0;
+  const int nrows = left <= 0 ? 0 : (left < rpw ? (int)left : rpw);
+  const int nitems = nrows * nb;
+
+  float acc[BP];
+#pragma unroll
+  for (int b = 0; b < BP; ++b) acc[b] = 0.f;
+  if (K == 0) {
+    for (int r = 0; r < nrows; ++r) finish_row<BP>(acc, y, B, R, r0 + r, lane, out_kind);
+    return;
+  }
+  auto item_load = [&](DBatch<U> &bt, int k) {
+    const bool real = k < nitems;
+    const int ii = real ? k / nb : 0, tt = real ? k - ii * nb : 0;
+    const int64_t r = real ? r0 + ii : 0;
+    dload_batch<U>(bt, W + r * nch, real ? nch : 0, tt, lane);
+  };
+  DBatch<U> A, Bt;
+  item_load(A, 0);
+  item_load(Bt, 1);
+  for (int b = 0; b < BP; ++b) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)(b < B ? b : 0) * K);
+    uint4 *dst = reinterpret_cast<uint4 *>(lds + (size_t)b * K * 2);
+    for (int j = threadIdx.x; j < nch; j += blockDim.x)
+      dst[j] = b < B ? src[j] : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  float res[BP];
+#pragma unroll
+  for (int b = 0; b < BP; ++b) res[b] = 0.f;
+  for (int k = 0; k < nitems; k += 2) {
+    const int i = k / nb, t = k - i * nb;
+    drun_batch<BF, BP, U>(lds, K, A, t * kWave * U + lane, nch, acc);
+    if (t == nb - 1) collect_row<BP>(acc, res, i, lane);
+    item_load(A, k + 2);
+    if (k + 1 >= nitems) break;
+    const int i1 = (k + 1) / nb, t1 = (k + 1) - i1 * nb;
+    drun_batch<BF, BP, U>(lds, K, Bt, t1 * kWave * U + lane, nch, acc);
+    if (t1 == nb - 1) collect_row<BP>(acc, res, i1, lane);
+    item_load(Bt, k + 3);
+  }
+  if (lane < nrows) {
+#pragma unroll
+    for (int b = 0; b < BP; ++b)
+      if (b < B) store_out(y, (int64_t)b * R + r0 + lane, res[b], out_kind);
+  }
+}
+
+// Dense comparison when x does not fit the LDS budget in one piece.
 // Dense comparison: lane l handles 16-byte chunks (8 columns) l, l+64, ...
 // of a row; x is staged in LDS as BP contiguous rows of `seg` columns.
 template <bool BF, int BP, int RPW>
@@ -735,7 +840,8 @@ size_t lds_budget(const DevInfo &di) {
 
 // Is this a launch of the single-segment row kernel (all of x in LDS)?
 bool rows_kernel(bool dense, int64_t cols, int seg) {
-  return !dense && seg >= cols;
+  (void)dense;
+  return seg >= cols;
 }
 
 int threads_for_lds(size_t lds) {
@@ -750,14 +856,15 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, bool dense,
   const int bp = pad_batch(batch);
   const size_t budget = lds_budget(di);
   const int smax = max_seg(dense, bp, budget);
-  if (!dense && sparse_lds_bytes(bp, (int)cols) <= budget) {
+  const size_t full = lds_bytes(dense, bp, cols > 0 ? (int)cols : 32);
+  if (full <= budget) {
     // row kernel: x staged once per workgroup.  When the rows split evenly
     // over the CUs, every wave gets the same number of rows rpw (<= 8), with
     // at least two workgroups per CU: x is staged rarely and no CU finishes
     // early.  Otherwise one row per wave, and the hardware balances the
     // workgroups.
     cfg->seg_cols = cols > 0 ? (int)cols : 32;
-    cfg->threads_per_wg = threads_for_lds(sparse_lds_bytes(bp, cfg->seg_cols));
+    cfg->threads_per_wg = threads_for_lds(full);
     const int64_t per_cu_rows = (int64_t)di.cus * (cfg->threads_per_wg / kWave);
     int rpw = 1;
     if (rows % per_cu_rows == 0) {
@@ -787,7 +894,7 @@ nm_status check_cfg(const nm_launch_cfg &c, int64_t cols, bool dense, int bp,
   if (c.seg_cols <= 0 || c.seg_cols % 32 != 0) return NM_ERR_INVALID_ARG;
   if (rows_kernel(dense, cols, c.seg_cols)) {
     if (c.rows_per_wave < 1 || c.rows_per_wave > 64) return NM_ERR_INVALID_ARG;
-    if (sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32) > lds_budget(di)) return NM_ERR_INVALID_ARG;
+    if (lds_bytes(dense, bp, cols > 0 ? (int)cols : 32) > lds_budget(di)) return NM_ERR_INVALID_ARG;
     return NM_OK;
   }
   if (!(c.rows_per_wave == 1 || c.rows_per_wave == 2 || c.rows_per_wave == 4))
@@ -878,6 +985,23 @@ dense_fn pick_dense_bp(int bp, int rpw) {
 
 dense_fn pick_dense(bool bf, int bp, int rpw) {
   return bf ? pick_dense_bp<true>(bp, rpw) : pick_dense_bp<false>(bp, rpw);
+}
+
+typedef void (*dense_rows_fn)(const uint4 *, const uint16_t *, void *, int, int64_t, int, int,
+                              int);
+
+template <bool BF>
+dense_rows_fn pick_dense_rows_bp(int bp) {
+  switch (bp) {
+    case 1: return nm_dense_rows_kernel<BF, 1>;
+    case 2: return nm_dense_rows_kernel<BF, 2>;
+    case 4: return nm_dense_rows_kernel<BF, 4>;
+    default: return nm_dense_rows_kernel<BF, 8>;
+  }
+}
+
+dense_rows_fn pick_dense_rows(bool bf, int bp) {
+  return bf ? pick_dense_rows_bp<true>(bp) : pick_dense_rows_bp<false>(bp);
 }
 
 int sparse_product(const void *values, const uint32_t *bits, const void *X,
@@ -1039,14 +1163,21 @@ int nm_dense_gemv_cfg(const void *W, const void *X, void *Y, int batch,
   st = resolve_cfg(rows, cols, batch, true, user, &cfg);
   if (st != NM_OK) return st;
   const int bp = pad_batch(batch);
-  dense_fn fn = pick_dense(in_dt == NM_BF16, bp, cfg.rows_per_wave);
+  const bool bf = in_dt == NM_BF16;
   const int64_t rows_per_wg = (int64_t)(cfg.threads_per_wg / kWave) * cfg.rows_per_wave;
   const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
   if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
-                     dense_lds_bytes(bp, cfg.seg_cols), (hipStream_t)stream,
-                     (const uint4 *)W, (const uint16_t *)X, Y, batch, rows,
-                     (int)cols, cfg.seg_cols, (int)out_dt);
+  if (rows_kernel(true, cols, cfg.seg_cols)) {
+    hipLaunchKernelGGL(pick_dense_rows(bf, bp), dim3((unsigned)grid), dim3(cfg.threads_per_wg),
+                       dense_lds_bytes(bp, cols > 0 ? (int)cols : 32), (hipStream_t)stream,
+                       (const uint4 *)W, (const uint16_t *)X, Y, batch, rows, (int)cols,
+                       cfg.rows_per_wave, (int)out_dt);
+  } else {
+    hipLaunchKernelGGL(pick_dense(bf, bp, cfg.rows_per_wave), dim3((unsigned)grid),
+                       dim3(cfg.threads_per_wg), dense_lds_bytes(bp, cfg.seg_cols),
+                       (hipStream_t)stream, (const uint4 *)W, (const uint16_t *)X, Y, batch, rows,
+                       (int)cols, cfg.seg_cols, (int)out_dt);
+  }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? NM_OK : hip_fail(e);
 }

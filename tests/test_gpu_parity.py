@@ -170,7 +170,7 @@ def test_spmm_small_matches_oracle(batch, n, m, dtype):
 
 
 CFGS = [(64, 1, 32), (64, 4, 96), (128, 2, 1024), (256, 1, 0), (256, 4, 64),
-        (512, 2, 2080), (1024, 1, 160), (1024, 4, 0)]
+        (512, 2, 2080), (1024, 1, 160), (1024, 4, 0), (64, 3, 0), (256, 7, 0), (128, 64, 0)]
 
 
 @pytest.mark.parametrize("cfg", CFGS)
@@ -188,6 +188,25 @@ def test_launch_shapes_integer_exact(cfg, batch, n, m):
     Y = native.nm_spmm_small(values, bits, t16(X, "f16"), n, m, cfg=cfg)
     want = oracle.masked_gemv(W, keep, X, False)
     assert np.array_equal(f64(Y), want)
+
+
+@pytest.mark.parametrize("cols", [4160, 8224])
+@pytest.mark.parametrize("batch", [1, 2, 8])
+@pytest.mark.parametrize("n,m", [(2, 4), (16, 32)])
+def test_rows_pipeline_several_batches_per_row(cols, batch, n, m):
+    """Rows longer than one load batch (256 chunks), ragged against it, walked
+    by waves owning 1..7 rows: the two-stage pipeline crosses row and batch
+    boundaries in every phase."""
+    rows = 203
+    W = synth.integer_weights(rows, cols, seed=61)
+    keep = synth.random_mask(rows, cols, n, m, seed=62)
+    xi = np.random.default_rng(63).integers(-4, 5, size=(batch, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    values, bits = gpu_pack(W, keep, n, m, "f16")
+    want = oracle.masked_gemv(W, keep, X, False)
+    for cfg in ((64, 1, 0), (64, 3, 0), (256, 5, 0), (256, 7, 0), (1024, 2, 0)):
+        Y = native.nm_spmm_small(values, bits, t16(X, "f16"), n, m, cfg=cfg)
+        assert np.array_equal(f64(Y), want), cfg
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -245,14 +264,19 @@ def test_dense_gemv_matches_oracle(rows, cols, batch, dtype):
         assert rel_l2(f64(Y[b]), want[b]) <= TOL
 
 
-def test_dense_integer_exact():
-    rows, cols = 129, 2080
+@pytest.mark.parametrize("cols", [2080, 8224])
+def test_dense_integer_exact(cols):
+    """Dense kernels (all of x in LDS with any rows per wave, or K walked in
+    segments) give the exact result on integer inputs."""
+    rows = 129
     W = synth.integer_weights(rows, cols, seed=51)
     xi = np.random.default_rng(52).integers(-4, 5, size=(8, cols)).astype(np.float32)
     X = synth.f32_to_16_bits(xi, "f16")
-    for cfg in (None, (64, 4, 96), (1024, 2, 1024)):
-        Y = native.nm_dense_gemv(t16(W, "f16"), t16(X, "f16"), cfg=cfg)
-        assert np.array_equal(f64(Y), oracle.masked_gemv(W, None, X, False))
+    want = oracle.masked_gemv(W, None, X, False)
+    for batch in (1, 3, 8):
+        for cfg in (None, (64, 4, 96), (1024, 2, 1024), (64, 1, 0), (256, 3, 0), (512, 7, 0)):
+            Y = native.nm_dense_gemv(t16(W, "f16"), t16(X[:batch], "f16"), cfg=cfg)
+            assert np.array_equal(f64(Y), want[:batch]), (batch, cfg)
 
 
 def test_zero_columns_give_zero_output():
