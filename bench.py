@@ -53,8 +53,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def t16(a):
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).to(DEV)
+def t16(a, dtype="f16"):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(DEV)
 
 
 def pow2_copies(nbytes):
@@ -72,7 +73,7 @@ class Proj:
         self.keep = synth.topn_mask(self.W, mt.n, mt.m)
         self.X = {b: synth.activations(b, mt.cols, seed=mt.seed, dtype=mt.dtype, outliers=mt.outliers)
                   for b in batches}
-        Wd = t16(self.W)
+        Wd = t16(self.W, mt.dtype)
         values, bits = native.nm_pack(Wd, torch.from_numpy(self.keep).to(DEV), mt.n, mt.m)
         self.sbytes = {b: workloads.sparse_bytes(mt.rows, mt.cols, mt.n, mt.m, b, 4) for b in batches}
         self.dbytes = {b: workloads.dense_bytes(mt.rows, mt.cols, b, 4) for b in batches}
@@ -84,7 +85,7 @@ class Proj:
         self.dense = ([Wd] + [Wd.clone() for _ in range(self.ndc - 1)]) if want_dense else []
         if not want_dense:
             del Wd
-        self.Xd = {b: t16(self.X[b]) for b in batches}
+        self.Xd = {b: t16(self.X[b], mt.dtype) for b in batches}
         self.Y = {b: torch.empty((b, mt.rows), dtype=torch.float32, device=DEV) for b in batches}
         self.args = {}
         log(f"  {self.name:5s} {mt.rows}x{mt.cols}: {self.nc} packed copies "
@@ -94,11 +95,12 @@ class Proj:
         """Launch the sparse product on copy c at batch b (raw C call)."""
         L = native.lib()
         mt = self.mt
+        dt = native.NM_BF16 if mt.dtype == "bf16" else native.NM_F16
         st = L.nm_spmm_small(self.vals[c].data_ptr(), self.bits[c].data_ptr(), self.Xd[b].data_ptr(),
-                             self.Y[b].data_ptr(), b, mt.rows, mt.cols, mt.n, mt.m, native.NM_F16,
+                             self.Y[b].data_ptr(), b, mt.rows, mt.cols, mt.n, mt.m, dt,
                              native.NM_F32, torch.cuda.current_stream().cuda_stream) if b > 1 else \
             L.nm_spmv(self.vals[c].data_ptr(), self.bits[c].data_ptr(), self.Xd[b].data_ptr(),
-                      self.Y[b].data_ptr(), mt.rows, mt.cols, mt.n, mt.m, native.NM_F16,
+                      self.Y[b].data_ptr(), mt.rows, mt.cols, mt.n, mt.m, dt,
                       native.NM_F32, torch.cuda.current_stream().cuda_stream)
         if st != native.NM_OK:
             raise native.NMError(st, f"{self.name} sparse b={b}")
@@ -106,8 +108,9 @@ class Proj:
     def dense_call(self, b, c):
         L = native.lib()
         mt = self.mt
+        dt = native.NM_BF16 if mt.dtype == "bf16" else native.NM_F16
         st = L.nm_dense_gemv(self.dense[c].data_ptr(), self.Xd[b].data_ptr(), self.Y[b].data_ptr(), b,
-                             mt.rows, mt.cols, native.NM_F16, native.NM_F32,
+                             mt.rows, mt.cols, dt, native.NM_F32,
                              torch.cuda.current_stream().cuda_stream)
         if st != native.NM_OK:
             raise native.NMError(st, f"{self.name} dense b={b}")
@@ -272,6 +275,107 @@ def counters_run():
                       "copy_bytes_each_way": n}), flush=True)
 
 
+def shapes_run(cfg_id, args):
+    """Workloads 1, 3 and 4: per-matrix µs/call and GB/s (cache-cold rotation),
+    sparse and dense, at every batch the workload lists."""
+    want_dense = not args.no_dense
+    rows_out = []
+    for mt, batches in workloads.config_matrices(cfg_id):
+        p = Proj(mt, batches, want_dense)
+        for b in batches:
+            us = per_kernel_us(p, Proj.sparse_call, b, p.nc, args.reps)
+            row = {"matrix": mt.name, "rows": mt.rows, "cols": mt.cols, "pattern": f"{mt.n}:{mt.m}",
+                   "dtype": mt.dtype, "batch": b, "us": round(us, 3),
+                   "GB/s": round(p.sbytes[b] / us / 1e3, 1),
+                   "frac_of_peak": round(p.sbytes[b] / us / 1e3 / PEAK_GBS, 4)}
+            if want_dense:
+                dus = per_kernel_us(p, Proj.dense_call, b, p.ndc, args.reps)
+                tus = per_kernel_us(p, Proj.torch_call, b, p.ndc, args.reps)
+                row.update({"dense_us": round(dus, 3), "torch_linear_us": round(tus, 3),
+                            "speedup_vs_best_dense": round(min(dus, tus) / us, 3)})
+            rows_out.append(row)
+            log(f"  {mt.name:14s} {mt.rows:5d}x{mt.cols:5d} {mt.n}:{mt.m} {mt.dtype} b={b}: {us:8.2f} us "
+                f"{row['GB/s']:7.1f} GB/s ({100 * row['frac_of_peak']:.1f}%)"
+                + (f"  dense {row['dense_us']:.2f} torch {row['torch_linear_us']:.2f}" if want_dense else ""))
+        del p
+        torch.cuda.empty_cache()
+    return rows_out
+
+
+def gpu_layer(rows, cols, n, m, seed, want_dense):
+    """A seeded synthetic matrix drawn on the GPU (timing only: the kernels'
+    time does not depend on the values): W = fp16(0.02 z), the n largest |w|
+    of every m kept (ties to the lower column), packed by nm_pack."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    W = (torch.randn((rows, cols), device=DEV, generator=g) * 0.02).half()
+    mag = W.abs().view(rows, cols // m, m).float()
+    pos = torch.arange(m, device=DEV, dtype=torch.float32) * 1e-9  # ties to the lower column
+    idx = (mag - pos).topk(n, dim=-1).indices
+    keep = torch.zeros((rows, cols // m, m), dtype=torch.uint8, device=DEV)
+    keep.scatter_(-1, idx, 1)
+    values, bits = native.nm_pack(W, keep.view(rows, cols), n, m)
+    del keep, mag, idx
+    return values, bits, (W if want_dense else None)
+
+
+def decode_run(args):
+    """Workload 5: 32 stacked Llama-3.1-8B-shaped layers (224 matrices, 2:4
+    fp16, a different seed per matrix), all resident; one token = the 224
+    products chained in one HIP graph, at batch 1, 2, 4 and 8, against the
+    dense fp16 chain (nm_dense_gemv and torch linear)."""
+    want_dense = not args.no_dense
+    mats = [mt for mt, _ in workloads.config_matrices(5)]
+    t0 = time.time()
+    store = []
+    for mt in mats:
+        v, bt, W = gpu_layer(mt.rows, mt.cols, mt.n, mt.m, mt.seed, want_dense)
+        store.append((mt, v, bt, W))
+    torch.cuda.synchronize()
+    log(f"  224 matrices resident ({time.time() - t0:.1f}s): "
+        f"{sum(v.numel() * 2 + b.numel() * 4 for _, v, b, _ in store) / 1e9:.2f} GB packed")
+    L = native.lib()
+    out = {}
+    for B in (1, 2, 4, 8):
+        X = {k: torch.randn((B, k), device=DEV).half() for k in (4096, 14336)}
+        Y = {r: torch.empty((B, r), device=DEV) for r in (1024, 4096, 14336)}
+        def sparse_token():
+            st_ = torch.cuda.current_stream().cuda_stream
+            for mt, v, bt, _ in store:
+                st = L.nm_spmm_small(v.data_ptr(), bt.data_ptr(), X[mt.cols].data_ptr(),
+                                     Y[mt.rows].data_ptr(), B, mt.rows, mt.cols, mt.n, mt.m,
+                                     native.NM_F16, native.NM_F32, st_)
+                assert st == 0, st
+        def dense_token():
+            st_ = torch.cuda.current_stream().cuda_stream
+            for mt, _, _, W in store:
+                st = L.nm_dense_gemv(W.data_ptr(), X[mt.cols].data_ptr(), Y[mt.rows].data_ptr(), B,
+                                     mt.rows, mt.cols, native.NM_F16, native.NM_F32, st_)
+                assert st == 0, st
+        def torch_token():
+            for mt, _, _, W in store:
+                torch.nn.functional.linear(X[mt.cols], W)
+        sbytes = sum(workloads.sparse_bytes(mt.rows, mt.cols, mt.n, mt.m, B, 4) for mt, *_ in store)
+        dbytes = sum(workloads.dense_bytes(mt.rows, mt.cols, B, 4) for mt, *_ in store)
+        res = {}
+        for kind, fn, nbytes in (("sparse", sparse_token, sbytes), ("dense", dense_token, dbytes),
+                                 ("torch_linear", torch_token, dbytes)):
+            if kind != "sparse" and not want_dense:
+                continue
+            g = capture(fn)
+            ms = time_steps([g], args.steps, args.warmup)
+            res[kind] = {"ms_per_token": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            del g
+        if want_dense:
+            res["speedup_vs_best_dense"] = round(
+                min(res["dense"]["ms_per_token"], res["torch_linear"]["ms_per_token"])
+                / res["sparse"]["ms_per_token"], 3)
+        out[f"batch{B}"] = res
+        log(f"  batch {B}: " + ", ".join(f"{k} {v['ms_per_token']} ms/token ({v['GB/s']} GB/s)"
+                                         for k, v in res.items() if isinstance(v, dict)))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +385,12 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch4", action="store_true")
+    ap.add_argument("--workload", default="llama8b-layer",
+                    choices=["llama8b-layer", "single", "patterns", "70b-qwen", "decode-32-layers"],
+                    help="llama8b-layer (default, the headline line): one Llama-3.1-8B layer; "
+                         "single: the 4096x4096 matrix; patterns: 4:8/8:16/16:32 bf16 on the 8B "
+                         "shapes; 70b-qwen: Llama-3.3-70B and Qwen3-32B shapes; "
+                         "decode-32-layers: 32 stacked 8B layers timed per token")
     ap.add_argument("--counters", action="store_true",
                     help="short eager run for rocprofv3 --pmc: the 14336x4096 sparse kernel on "
                          "5 cache-cold copies, then 5 plain copies of 64 MiB (the known-size "
@@ -300,6 +410,16 @@ def main():
 
     if args.counters:
         counters_run()
+        return
+    if args.workload != "llama8b-layer":
+        cfg_id = {"single": 1, "patterns": 3, "70b-qwen": 4, "decode-32-layers": 5}[args.workload]
+        log(f"workload {args.workload} ({cfg_id})")
+        if cfg_id == 5:
+            body = {"per_token": decode_run(args)}
+        else:
+            body = {"per_matrix": shapes_run(cfg_id, args)}
+        print(json.dumps({"metric": METRIC, "workload": args.workload, "n_gpus": 1,
+                          "data": "synthetic", "peak_GB/s": PEAK_GBS, **body}), flush=True)
         return
     batches = (1,) if args.no_batch4 else (1, 4)
     want_dense = not args.no_dense

@@ -41,6 +41,8 @@ constexpr size_t kLdsCap = 160 * 1024;  // LDS one workgroup may use (CU total o
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // acc + w.lo * x.lo + w.hi * x.hi with 16-bit pairs and an fp32 accumulator.
 template <bool BF>
@@ -95,9 +97,9 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v,
 // segment holds the BP batch values of that column in one slot of SB bytes;
 // the 32 slots of a mask word are followed by PB pad bytes, and PB bytes sit
 // in front of word 0.  The pad shifts consecutive words across LDS banks.  A
-// tail of 8 slots keeps the reads of a malformed mask word (fewer set bits
-// than its pattern requires, which walks into the sentinel bits) inside the
-// allocation.
+// tail of 16 slots keeps the reads of a malformed mask word (fewer set bits
+// than its pattern requires: the scan walks into the sentinel bits, an empty
+// 2:4 nibble decodes to column 32) inside the allocation.
 template <int BP>
 struct XLay {
   static constexpr int SB = 2 * BP;
@@ -105,7 +107,7 @@ struct XLay {
   static constexpr int WS = 32 * SB + PB;
   static constexpr int FP = PB;
   static constexpr size_t bytes(int seg_cols) {
-    return FP + (size_t)(seg_cols / 32) * WS + 8 * SB;
+    return FP + (size_t)(seg_cols / 32) * WS + 16 * SB;
   }
 };
 
@@ -178,77 +180,156 @@ __device__ __forceinline__ void stage_x_sparse(char *lds, const uint16_t *__rest
   }
 }
 
-// One lane's 16-byte chunk: 8 kept weights (4 packed pairs in v) whose
-// columns are the 8 lowest set bits of m.  `base` is the LDS byte address of
-// column 0 of the chunk's column range.  Two LSB-scan steps feed one dot2.
-template <bool BF, int BP>
-__device__ __forceinline__ void chunk8(const char *lds, uint32_t base,
-                                       uint32_t m, const uint4 v,
-                                       float (&acc)[BP]) {
-  using L = XLay<BP>;
-  const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-  const char *wb = lds + base;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // m is never zero here (see the callers), so v_ffbl_b32 is well defined
-    const uint32_t c0 = __builtin_ctz(m);
-    m &= m - 1;
-    const uint32_t c1 = __builtin_ctz(m);
-    m &= m - 1;
-    const char *p0 = wb + c0 * L::SB;
-    const char *p1 = wb + c1 * L::SB;
-    if constexpr (BP == 1) {
-      // two 16-bit LDS reads into the low and high halves of one register
-      u16x2_t pr;
-      pr[0] = *reinterpret_cast<const uint16_t *>(p0);
-      pr[1] = *reinterpret_cast<const uint16_t *>(p1);
-      acc[0] = dot2<BF>(vv[j], __builtin_bit_cast(uint32_t, pr), acc[0]);
+typedef __attribute__((address_space(3))) const char *lds_ptr;
+
+// Load a T from an LDS slot given either as a generic pointer into the
+// dynamic LDS array or as an explicit LDS-address-space pointer.
+template <typename T, typename P>
+__device__ __forceinline__ T ld(P p) {
+  if constexpr (__is_same(P, lds_ptr))
+    return *(__attribute__((address_space(3))) const T *)p;
+  else
+    return *reinterpret_cast<const T *>(p);
+}
+
+// x values of a kept pair of a lane's chunk (LDS slots p0, p1), multiplied
+// with the packed weight pair w and accumulated for every batch row.
+template <bool BF, int BP, typename P>
+__device__ __forceinline__ void accum_pair(P p0, P p1, uint32_t w, float (&acc)[BP]) {
+  if constexpr (BP == 1) {
+    // two 16-bit LDS reads into the low and high halves of one register
+    u16x2_t pr;
+    pr[0] = ld<uint16_t>(p0);
+    pr[1] = ld<uint16_t>(p1);
+    acc[0] = dot2<BF>(w, __builtin_bit_cast(uint32_t, pr), acc[0]);
+  } else {
+    uint32_t X0[BP / 2], X1[BP / 2];
+    if constexpr (BP == 2) {
+      X0[0] = ld<uint32_t>(p0);
+      X1[0] = ld<uint32_t>(p1);
+    } else if constexpr (BP == 4) {
+      const u32x2_t a = ld<u32x2_t>(p0);
+      const u32x2_t b = ld<u32x2_t>(p1);
+      X0[0] = a[0]; X0[1] = a[1];
+      X1[0] = b[0]; X1[1] = b[1];
     } else {
-      uint32_t X0[BP / 2], X1[BP / 2];
-      if constexpr (BP == 2) {
-        X0[0] = *reinterpret_cast<const uint32_t *>(p0);
-        X1[0] = *reinterpret_cast<const uint32_t *>(p1);
-      } else if constexpr (BP == 4) {
-        const uint2 a = *reinterpret_cast<const uint2 *>(p0);
-        const uint2 b = *reinterpret_cast<const uint2 *>(p1);
-        X0[0] = a.x; X0[1] = a.y;
-        X1[0] = b.x; X1[1] = b.y;
-      } else {
-        const uint4 a = *reinterpret_cast<const uint4 *>(p0);
-        const uint4 b = *reinterpret_cast<const uint4 *>(p1);
-        X0[0] = a.x; X0[1] = a.y; X0[2] = a.z; X0[3] = a.w;
-        X1[0] = b.x; X1[1] = b.y; X1[2] = b.z; X1[3] = b.w;
-      }
+      const u32x4_t a = ld<u32x4_t>(p0);
+      const u32x4_t b = ld<u32x4_t>(p1);
+      X0[0] = a[0]; X0[1] = a[1]; X0[2] = a[2]; X0[3] = a[3];
+      X1[0] = b[0]; X1[1] = b[1]; X1[2] = b[2]; X1[3] = b[3];
+    }
 #pragma unroll
-      for (int d = 0; d < BP / 2; ++d) {
-        // (x0[b], x1[b]) pairs for batch rows b = 2d and 2d+1
-        const uint32_t lo = (X0[d] & 0xffffu) | (X1[d] << 16);
-        const uint32_t hi = (X0[d] >> 16) | (X1[d] & 0xffff0000u);
-        acc[2 * d] = dot2<BF>(vv[j], lo, acc[2 * d]);
-        acc[2 * d + 1] = dot2<BF>(vv[j], hi, acc[2 * d + 1]);
-      }
+    for (int d = 0; d < BP / 2; ++d) {
+      // (x0[b], x1[b]) pairs for batch rows b = 2d and 2d+1
+      const uint32_t lo = (X0[d] & 0xffffu) | (X1[d] << 16);
+      const uint32_t hi = (X0[d] >> 16) | (X1[d] & 0xffff0000u);
+      acc[2 * d] = dot2<BF>(w, lo, acc[2 * d]);
+      acc[2 * d + 1] = dot2<BF>(w, hi, acc[2 * d + 1]);
     }
   }
 }
 
+// v_ffbl_b32 / v_ffbh_u32 with their hardware meaning for 0 (-1), which the
+// C builtins leave undefined: index of the lowest set bit, and the number of
+// zero bits above the highest set bit.
+__device__ __forceinline__ int ffbl_hw(uint32_t x) {
+  int r;
+  asm("v_ffbl_b32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ int ffbh_hw(uint32_t x) {
+  int r;
+  asm("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Generic fixed-step traversal (item (2)): the chunk's 8 kept weights are
+// the 8 lowest set bits of m; each step takes the lowest set bit as the next
+// kept column and clears it, and two steps feed one pair.
+template <bool BF, int BP>
+__device__ __forceinline__ void chunk8_scan(const char *wb, uint32_t m, const uint4 v,
+                                            float (&acc)[BP]) {
+  const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // m is never zero here (see the callers), so v_ffbl_b32 is well defined
+    const int c0 = __builtin_ctz(m);
+    m &= m - 1;
+    const int c1 = __builtin_ctz(m);
+    m &= m - 1;
+    accum_pair<BF, BP>(wb + c0 * XLay<BP>::SB, wb + c1 * XLay<BP>::SB, vv[j], acc);
+  }
+}
+
+// 2:4: nibble j of the lane's 16 columns holds exactly the pair j of kept
+// weights, so its lowest and highest set bits are their columns: one ffbl and
+// one ffbh per pair replace the serial scan.  A malformed nibble (no set bit)
+// gives columns -1 and 32, inside the LDS pads.
+// base - hz * SB in one v_mad_i32_i24 (the slot of column 31 - hz relative to
+// column 31's slot); hz <= 32 and SB <= 16 fit the 24-bit operands.
+template <int SB>
+__device__ __forceinline__ uint32_t slot_from_top(int hz, uint32_t base31) {
+  uint32_t r;
+  if constexpr (SB == 2)
+    asm("v_mad_i32_i24 %0, %1, -2, %2" : "=v"(r) : "v"(hz), "v"(base31));
+  else if constexpr (SB == 4)
+    asm("v_mad_i32_i24 %0, %1, -4, %2" : "=v"(r) : "v"(hz), "v"(base31));
+  else if constexpr (SB == 8)
+    asm("v_mad_i32_i24 %0, %1, -8, %2" : "=v"(r) : "v"(hz), "v"(base31));
+  else
+    asm("v_mad_i32_i24 %0, %1, -16, %2" : "=v"(r) : "v"(hz), "v"(base31));
+  return r;
+}
+
+template <bool BF, int BP>
+__device__ __forceinline__ void chunk8_nibbles(const char *lds, uint32_t base, uint32_t m,
+                                               const uint4 v, float (&acc)[BP]) {
+  constexpr int SB = XLay<BP>::SB;
+  const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  // LDS addresses as 32-bit integers, so that the slot arithmetic (one
+  // lshl_add and one mad_i24 per pair) yields the final address
+  const uint32_t b0 = (uint32_t)(size_t)(lds_ptr)lds + base;
+  const uint32_t b31 = b0 + 31 * SB;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t n = m & (0xfu << (4 * j));
+    const uint32_t o0 = b0 + (uint32_t)ffbl_hw(n) * SB;
+    const uint32_t o1 = slot_from_top<SB>(ffbh_hw(n), b31);
+    accum_pair<BF, BP>((lds_ptr)(size_t)o0, (lds_ptr)(size_t)o1, vv[j], acc);
+  }
+}
+
+// Pattern kinds: the traversal a kernel is compiled for (Appendix C: one
+// kernel per pattern, with N and M fixed at compile time).
+enum { kPat24 = 0, kPatHalf = 1, kPat1632 = 2 };
+
+__host__ __device__ constexpr int pattern_kind(int m) {
+  return m == 4 ? kPat24 : m == 32 ? kPat1632 : kPatHalf;
+}
+
 // Process value chunk q (< nch) of a row with the lane's registers: select
-// the lane's 16 columns of mask word q >> 1 and run the 8-step scan.
-//   M32 = false (M <= 16): a half-word's 16 columns hold exactly 8 kept
-//         weights, so the odd lane scans the upper 16 bits of the word;
-//   M32 = true (16:32): the 8 kept weights of the odd lane are set bits 8..15
+// the lane's 16 columns of mask word q >> 1 and decode its 8 kept columns.
+//   kPat24, kPatHalf (M <= 16): a half-word's 16 columns hold exactly 8 kept
+//         weights, so the odd lane takes the upper 16 bits of the word;
+//   kPat1632 (16:32): the 8 kept weights of the odd lane are set bits 8..15
 //         of the word, so it first clears the 8 lowest set bits.
-template <bool BF, int BP, bool M32>
+template <bool BF, int BP, int PK>
 __device__ __forceinline__ void chunk(const char *lds, int q, uint32_t mw, const uint4 v,
                                       float (&acc)[BP]) {
   using L = XLay<BP>;
   const uint32_t h = q & 1;
   uint32_t base = L::FP + (uint32_t)(q >> 1) * L::WS;
   uint32_t m = mw;
-  if constexpr (!M32) {
-    // this lane's 16 columns in the low half; the sentinel bits above them
+  if constexpr (PK == kPat24) {
+    m >>= (h << 4);
+    base += h * (16 * L::SB);
+    chunk8_nibbles<BF, BP>(lds, base, m, v, acc);
+  } else if constexpr (PK == kPatHalf) {
+    // the lane's 16 columns in the low half; the sentinel bits above them
     // keep every scan step on a nonzero word
     m = (m >> (h << 4)) | 0xffff0000u;
     base += h * (16 * L::SB);
+    chunk8_scan<BF, BP>(lds + base, m, v, acc);
   } else {
     // a word without exactly 16 set bits is replaced by one that keeps the
     // scan in range (its row's result is then undefined)
@@ -257,8 +338,8 @@ __device__ __forceinline__ void chunk(const char *lds, int q, uint32_t mw, const
 #pragma unroll
       for (int k = 0; k < 8; ++k) m &= m - 1;
     }
+    chunk8_scan<BF, BP>(lds + base, m, v, acc);
   }
-  chunk8<BF, BP>(lds, base, m, v, acc);
 }
 
 // Registers of one load batch: U value chunks and their mask words.
@@ -303,7 +384,7 @@ __device__ __forceinline__ void load_batch(Batch<U> &bt, const uint4 *vrow,
 // computed like any other at the row's last column range, without a branch,
 // and its sum is dropped by a select.  Straight-line code keeps the wait
 // counts of the pipeline exact.
-template <bool BF, int BP, bool M32, int U>
+template <bool BF, int BP, int PK, int U>
 __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, int q0, int nch,
                                           float (&acc)[BP]) {
 #pragma unroll
@@ -313,7 +394,7 @@ __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, i
     float part[BP];
 #pragma unroll
     for (int b = 0; b < BP; ++b) part[b] = 0.f;
-    chunk<BF, BP, M32>(lds, qc, bt.m[u], bt.v[u], part);
+    chunk<BF, BP, PK>(lds, qc, bt.m[u], bt.v[u], part);
 #pragma unroll
     for (int b = 0; b < BP; ++b) acc[b] += q < nch ? part[b] : 0.f;
   }
@@ -347,14 +428,14 @@ __device__ __forceinline__ void collect_row(float (&acc)[BP], float (&res)[BP], 
 // staged once per workgroup; wave w of the grid owns the rpw consecutive rows
 // from w * rpw.  Its work is a sequence of items (row, load batch of U chunks
 // per lane) run as a two-stage software pipeline: the loads of item k+1 are
-// in flight while item k is consumed.  The first item's loads are issued
+// in flight while item k is consumed.  U is chosen per shape so that it
+// divides the row's chunks per lane (no idle load slots in the last batch).  The first item's loads are issued
 // before x is committed to LDS, so the x and weight latencies overlap.
-template <bool BF, int BP, bool M32>
+template <bool BF, int BP, int PK, int U>
 __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
     const uint4 *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int rpw,
     int out_kind) {
-  constexpr int U = 4;
   constexpr int XS = BP == 1 ? 4 : 1;  // x groups per thread held in registers
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & (kWave - 1);
@@ -412,12 +493,12 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   // two-buffer pipeline: while one batch is consumed the other is in flight
   for (int k = 0; k < nitems; k += 2) {
     const int i = k / nb, t = k - i * nb;
-    run_batch<BF, BP, M32, U>(lds, A, t * kWave * U + lane, nch, acc);
+    run_batch<BF, BP, PK, U>(lds, A, t * kWave * U + lane, nch, acc);
     if (t == nb - 1) collect_row<BP>(acc, res, i, lane);
     item_load(A, k + 2);
     if (k + 1 >= nitems) break;
     const int i1 = (k + 1) / nb, t1 = (k + 1) - i1 * nb;
-    run_batch<BF, BP, M32, U>(lds, Bt, t1 * kWave * U + lane, nch, acc);
+    run_batch<BF, BP, PK, U>(lds, Bt, t1 * kWave * U + lane, nch, acc);
     if (t1 == nb - 1) collect_row<BP>(acc, res, i1, lane);
     item_load(Bt, k + 3);
   }
@@ -431,13 +512,10 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
 // Sparse product when x does not fit the LDS budget in one piece.
 // Workgroup g owns rows g*WPG*RPW + i*WPG + wave (i < RPW), processed
 // together; K is walked in segments of `seg` columns, each staged in LDS once
-// per workgroup, and the RPW x BP accumulators live in registers throughout.  Lane l of a wave handles value chunks l, l+64, ... of the
-// segment; chunk q is half (q & 1) of mask word q >> 1.
-//   M32 = false (M <= 16): a half-word's 16 columns hold exactly 8 kept
-//         weights, so the odd lane scans the upper 16 bits of the word;
-//   M32 = true (16:32): the 8 kept weights of the odd lane are set bits 8..15
-//         of the word, so it first clears the 8 lowest set bits.
-template <bool BF, int BP, bool M32, int RPW>
+// per workgroup, and the RPW x BP accumulators live in registers throughout.
+// Lane l of a wave handles value chunks l, l+64, ... of the segment; chunk q
+// is half (q & 1) of mask word q >> 1 (see chunk()).
+template <bool BF, int BP, int PK, int RPW>
 __global__ __launch_bounds__(1024) void nm_spmv_seg_kernel(
     const uint4 *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R,
@@ -475,7 +553,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_seg_kernel(
       }
 #pragma unroll
       for (int i = 0; i < RPW; ++i)
-        run_batch<BF, BP, M32, U>(lds, bt[i], t0 + lane, nch, acc[i]);
+        run_batch<BF, BP, PK, U>(lds, bt[i], t0 + lane, nch, acc[i]);
     }
   }
 
@@ -858,12 +936,21 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, bool dense,
   const int smax = max_seg(dense, bp, budget);
   const size_t full = lds_bytes(dense, bp, cols > 0 ? (int)cols : 32);
   if (full <= budget) {
-    // row kernel: x staged once per workgroup.  When the rows split evenly
-    // over the CUs, every wave gets the same number of rows rpw (<= 8), with
-    // at least two workgroups per CU: x is staged rarely and no CU finishes
-    // early.  Otherwise one row per wave, and the hardware balances the
-    // workgroups.
+    // row kernel: x staged once per workgroup.  Measured on the 8B, 70B and
+    // Qwen3-32B shapes:
+    //  - few rows (<= 32 per CU) split evenly over the CUs: one row per wave
+    //    and exactly two workgroups per CU, as wide as that takes;
+    //  - otherwise, rows split evenly: 256 threads and the same number of
+    //    rows rpw (<= 8) for every wave, at least two workgroups per CU, so
+    //    x is staged rarely and no CU finishes early;
+    //  - otherwise one row per wave, and the hardware balances the groups.
     cfg->seg_cols = cols > 0 ? (int)cols : 32;
+    const int64_t two_per_cu = 2LL * di.cus;
+    if (full <= budget / 2 && rows % two_per_cu == 0 && rows / two_per_cu <= 16) {
+      cfg->threads_per_wg = (int)(rows / two_per_cu) * kWave;
+      cfg->rows_per_wave = 1;
+      return NM_OK;
+    }
     cfg->threads_per_wg = threads_for_lds(full);
     const int64_t per_cu_rows = (int64_t)di.cus * (cfg->threads_per_wg / kWave);
     int rpw = 1;
@@ -890,7 +977,7 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, bool dense,
 nm_status check_cfg(const nm_launch_cfg &c, int64_t cols, bool dense, int bp,
                     const DevInfo &di) {
   const int t = c.threads_per_wg;
-  if (!(t == 64 || t == 128 || t == 256 || t == 512 || t == 1024)) return NM_ERR_INVALID_ARG;
+  if (t < kWave || t > 1024 || t % kWave != 0) return NM_ERR_INVALID_ARG;
   if (c.seg_cols <= 0 || c.seg_cols % 32 != 0) return NM_ERR_INVALID_ARG;
   if (rows_kernel(dense, cols, c.seg_cols)) {
     if (c.rows_per_wave < 1 || c.rows_per_wave > 64) return NM_ERR_INVALID_ARG;
@@ -925,43 +1012,71 @@ typedef void (*rows_fn)(const uint4 *, const uint32_t *, const uint16_t *, void 
 typedef void (*dense_fn)(const uint4 *, const uint16_t *, void *, int, int64_t,
                          int, int, int);
 
-template <bool BF, int BP, bool M32>
+template <bool BF, int BP, int PK>
 seg_fn pick_seg_rpw(int rpw) {
   switch (rpw) {
-    case 1: return nm_spmv_seg_kernel<BF, BP, M32, 1>;
-    case 2: return nm_spmv_seg_kernel<BF, BP, M32, 2>;
-    default: return nm_spmv_seg_kernel<BF, BP, M32, 4>;
+    case 1: return nm_spmv_seg_kernel<BF, BP, PK, 1>;
+    case 2: return nm_spmv_seg_kernel<BF, BP, PK, 2>;
+    default: return nm_spmv_seg_kernel<BF, BP, PK, 4>;
   }
 }
 
-template <bool BF, bool M32>
+template <bool BF, int PK>
 seg_fn pick_seg_bp(int bp, int rpw) {
   switch (bp) {
-    case 1: return pick_seg_rpw<BF, 1, M32>(rpw);
-    case 2: return pick_seg_rpw<BF, 2, M32>(rpw);
-    case 4: return pick_seg_rpw<BF, 4, M32>(rpw);
-    default: return pick_seg_rpw<BF, 8, M32>(rpw);
+    case 1: return pick_seg_rpw<BF, 1, PK>(rpw);
+    case 2: return pick_seg_rpw<BF, 2, PK>(rpw);
+    case 4: return pick_seg_rpw<BF, 4, PK>(rpw);
+    default: return pick_seg_rpw<BF, 8, PK>(rpw);
   }
 }
 
-seg_fn pick_seg(bool bf, bool m32, int bp, int rpw) {
-  if (bf) return m32 ? pick_seg_bp<true, true>(bp, rpw) : pick_seg_bp<true, false>(bp, rpw);
-  return m32 ? pick_seg_bp<false, true>(bp, rpw) : pick_seg_bp<false, false>(bp, rpw);
+template <bool BF>
+seg_fn pick_seg_pk(int pk, int bp, int rpw) {
+  switch (pk) {
+    case kPat24: return pick_seg_bp<BF, kPat24>(bp, rpw);
+    case kPatHalf: return pick_seg_bp<BF, kPatHalf>(bp, rpw);
+    default: return pick_seg_bp<BF, kPat1632>(bp, rpw);
+  }
 }
 
-template <bool BF, bool M32>
-rows_fn pick_rows_bp(int bp) {
+seg_fn pick_seg(bool bf, int pk, int bp, int rpw) {
+  return bf ? pick_seg_pk<true>(pk, bp, rpw) : pick_seg_pk<false>(pk, bp, rpw);
+}
+
+template <bool BF, int PK>
+rows_fn pick_rows_bp(int bp, int u) {
   switch (bp) {
-    case 1: return nm_spmv_rows_kernel<BF, 1, M32>;
-    case 2: return nm_spmv_rows_kernel<BF, 2, M32>;
-    case 4: return nm_spmv_rows_kernel<BF, 4, M32>;
-    default: return nm_spmv_rows_kernel<BF, 8, M32>;
+    case 1:
+      return u == 5 ? nm_spmv_rows_kernel<BF, 1, PK, 5> : nm_spmv_rows_kernel<BF, 1, PK, 4>;
+    case 2: return nm_spmv_rows_kernel<BF, 2, PK, 4>;
+    case 4: return nm_spmv_rows_kernel<BF, 4, PK, 4>;
+    default: return nm_spmv_rows_kernel<BF, 8, PK, 4>;
   }
 }
 
-rows_fn pick_rows(bool bf, bool m32, int bp) {
-  if (bf) return m32 ? pick_rows_bp<true, true>(bp) : pick_rows_bp<true, false>(bp);
-  return m32 ? pick_rows_bp<false, true>(bp) : pick_rows_bp<false, false>(bp);
+template <bool BF>
+rows_fn pick_rows_pk(int pk, int bp, int u) {
+  switch (pk) {
+    case kPat24: return pick_rows_bp<BF, kPat24>(bp, u);
+    case kPatHalf: return pick_rows_bp<BF, kPatHalf>(bp, u);
+    default: return pick_rows_bp<BF, kPat1632>(bp, u);
+  }
+}
+
+rows_fn pick_rows(bool bf, int pk, int bp, int u) {
+  return bf ? pick_rows_pk<true>(pk, bp, u) : pick_rows_pk<false>(pk, bp, u);
+}
+
+// Chunks per lane per load batch of the batch-1 row kernel: 4, or 5 when
+// that divides the row's chunks per lane (K / 1024) and 4 does not, so the
+// row's last batch has no idle slots (K = 5120, 25600).  Measured on the
+// 8B/70B/Qwen shapes: 5 helps the K = 5120k shapes; 7 (for K = 14336) costs
+// occupancy (93 VGPRs) and is slower than a ragged last batch of 4.
+int rows_batch_chunks(int64_t cols, int bp) {
+  if (bp != 1 || cols % 1024 != 0) return 4;
+  const int64_t c = cols / 1024;
+  return (c % 4 != 0 && c % 5 == 0) ? 5 : 4;
 }
 
 template <bool BF, int BP>
@@ -1023,13 +1138,14 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
   st = resolve_cfg(rows, cols, batch, false, user, &cfg);
   if (st != NM_OK) return st;
   const int bp = pad_batch(batch);
-  const bool bf = in_dt == NM_BF16, m32 = m == 32;
+  const bool bf = in_dt == NM_BF16;
+  const int pk = pattern_kind(m);
   const int wpg = cfg.threads_per_wg / kWave;
   if (rows_kernel(false, cols, cfg.seg_cols)) {
     const int64_t rows_per_wg = (int64_t)wpg * cfg.rows_per_wave;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
     if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(pick_rows(bf, m32, bp), dim3((unsigned)grid), dim3(cfg.threads_per_wg),
+    hipLaunchKernelGGL(pick_rows(bf, pk, bp, rows_batch_chunks(cols, bp)), dim3((unsigned)grid), dim3(cfg.threads_per_wg),
                        sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32), (hipStream_t)stream,
                        (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
                        (int)cols, cfg.rows_per_wave, (int)out_dt);
@@ -1037,7 +1153,7 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     const int64_t rows_per_wg = (int64_t)wpg * cfg.rows_per_wave;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
     if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(pick_seg(bf, m32, bp, cfg.rows_per_wave), dim3((unsigned)grid),
+    hipLaunchKernelGGL(pick_seg(bf, pk, bp, cfg.rows_per_wave), dim3((unsigned)grid),
                        dim3(cfg.threads_per_wg), sparse_lds_bytes(bp, cfg.seg_cols),
                        (hipStream_t)stream, (const uint4 *)values, bits, (const uint16_t *)X, Y,
                        batch, rows, (int)cols, cfg.seg_cols, (int)out_dt);

@@ -209,6 +209,24 @@ def test_rows_pipeline_several_batches_per_row(cols, batch, n, m):
         assert np.array_equal(f64(Y), want), cfg
 
 
+@pytest.mark.parametrize("cols", [1024, 2048, 5120, 7168, 14336, 25600])
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (16, 32)])
+def test_batch1_load_batch_sizes_exact(cols, n, m):
+    """The batch-1 kernel sizes its load batches (4 or 5 chunks per lane, full
+    or ragged last batch for these K); every size, crossed with several rows
+    per wave, gives the exact result on integer inputs."""
+    rows = 131
+    W = synth.integer_weights(rows, cols, seed=71)
+    keep = synth.random_mask(rows, cols, n, m, seed=72)
+    xi = np.random.default_rng(73).integers(-4, 5, size=(1, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    values, bits = gpu_pack(W, keep, n, m, "f16")
+    want = oracle.masked_gemv(W, keep, X, False)
+    for cfg in (None, (64, 1, 0), (128, 3, 0), (256, 6, 0)):
+        y = native.nm_spmv(values, bits, t16(X[0], "f16"), n, m, cfg=cfg)
+        assert np.array_equal(f64(y), want[0]), cfg
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("n,m", PATTERNS)
 def test_integer_inputs_bit_exact(n, m, dtype):
