@@ -142,26 +142,47 @@ int nm_dense_gemv(const void *W, const void *X, void *Y, int batch,
                   int64_t rows, int64_t cols, nm_dtype in_dt, nm_dtype out_dt,
                   void *stream);
 
+/* Kernel family of a launch.
+ *   NM_KERNEL_VALU: vector-ALU kernels (every pattern, the dense product);
+ *   NM_KERNEL_MFMA: the 2:4 product on gfx950's sparse matrix cores
+ *                   (v_smfmac_f32_16x16x64), which take a 2:4 tile as its
+ *                   kept values plus a 2-bit in-group position per value
+ *                   (derived on the fly from the bitmask words).  Only for
+ *                   n:m = 2:4, cols % 64 == 0, cols <= 2^25 and
+ *                   rows * cols <= 2^31 - 1. */
+typedef enum { NM_KERNEL_AUTO = 0, NM_KERNEL_VALU = 1, NM_KERNEL_MFMA = 2 } nm_kernel;
+
 /* Launch shape of the sparse and dense kernels, for tuning sweeps.  Fields
  * set to 0 take the library's choice for the shape.
- *   threads_per_wg: 64, 128, 256, 512 or 1024;
- *   rows_per_wave:  1, 2 or 4 rows processed together by one wavefront;
+ * VALU kernels:
+ *   threads_per_wg: a multiple of 64 in 64..1024;
+ *   rows_per_wave:  rows processed by one wavefront (1..64 when x fits LDS
+ *                   whole, else 1, 2 or 4 processed together);
  *   seg_cols:       columns of x staged in LDS at a time (multiple of 32);
- *                   K is walked in segments of this width. */
+ *                   seg_cols >= cols stages all of x once per workgroup.
+ * MFMA kernel (one 16-row tile per workgroup):
+ *   threads_per_wg: waves per workgroup x 64; the waves split K;
+ *   rows_per_wave:  depth of each wave's LDS ring, 2..4 blocks of 256
+ *                   columns (waves x depth x block bytes must fit the LDS);
+ *   seg_cols:       ignored.
+ * kernel: an nm_kernel (0 = the library's choice). */
 typedef struct {
   int threads_per_wg;
   int rows_per_wave;
   int seg_cols;
+  int kernel;
 } nm_launch_cfg;
 
-/* The launch shape nm_spmm_small / nm_dense_gemv would use for a call
- * (dense != 0 selects the dense kernel).  Pure host arithmetic apart from
- * one query of the current device's properties on first use. */
-int nm_default_launch(int64_t rows, int64_t cols, int batch, int dense,
-                      nm_launch_cfg *cfg);
+/* The launch shape nm_spmm_small (pattern n:m) or nm_dense_gemv (dense != 0;
+ * n and m ignored) would use for a call.  Pure host arithmetic apart from one
+ * query of the current device's properties on first use.  Errors as the
+ * product's argument checks. */
+int nm_default_launch(int64_t rows, int64_t cols, int batch, int n, int m,
+                      int dense, nm_launch_cfg *cfg);
 
 /* nm_spmm_small / nm_dense_gemv with an explicit launch shape (cfg may be
- * NULL for the default).  Invalid shapes give NM_ERR_INVALID_ARG. */
+ * NULL for the default).  Invalid shapes give NM_ERR_INVALID_ARG; asking for
+ * the MFMA kernel where it cannot run gives NM_ERR_UNSUPPORTED. */
 int nm_spmm_small_cfg(const void *values, const uint32_t *bits, const void *X,
                       void *Y, int batch, int64_t rows, int64_t cols, int n,
                       int m, nm_dtype in_dt, nm_dtype out_dt,

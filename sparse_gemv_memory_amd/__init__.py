@@ -7,6 +7,9 @@ layer shapes.
 """
 
 from .native import (  # noqa: F401
+    NM_KERNEL_AUTO,
+    NM_KERNEL_MFMA,
+    NM_KERNEL_VALU,
     NMError,
     LaunchCfg,
     nm_default_launch,

@@ -564,6 +564,247 @@ __global__ __launch_bounds__(1024) void nm_spmv_seg_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// 2:4 small batch on the sparse matrix cores.
+//
+// At batch 2..8 the VALU kernel's work per kept weight grows with the batch
+// (one dot2 per token per pair plus the gathers), so for 2:4 the product runs
+// on gfx950's v_smfmac_f32_16x16x64_{f16,bf16}: A is a 16 x 64 2:4-sparse
+// tile given as its kept values plus a 2-bit in-group position per kept
+// value, B a dense 64 x 16 tile, D += A.B in fp32.  The bitmask format maps
+// onto it directly (Method item (1)): a lane's 16 columns of a row hold
+// exactly 8 kept values, 16 contiguous bytes of `values`, and their position
+// codes come from the lane's 16 mask bits.  Operand layout (established on
+// the device against a CPU product): lane l = 16 j + n holds
+//   A: row n of the tile, dense columns 16 j .. 16 j + 15 of the step;
+//   B: column n (the token), dense columns 8 j .. 8 j + 7 and
+//      32 + 8 j .. 32 + 8 j + 7 of the step;
+//   D: rows 4 j .. 4 j + 3 of the tile, column n.
+// N = 16 columns hold the batch; columns beyond it are computed from
+// whatever the lanes hold and never stored.
+//
+// Loads.  A's layout asks one load instruction for 16 rows x 64 bytes,
+// which streams HBM at about half the rate of row-contiguous requests, so
+// every operand goes through LDS: a block (256 columns of the 16-row tile:
+// 4 KiB of values, 512 B of mask words, and 512 B of x per token) is copied
+// by direct-to-LDS buffer loads (buffer_load ... lds, 16 or 4 bytes per
+// lane, lane i's data landing at base + i * size), each instruction reading
+// whole 256-byte row segments.  The 16-byte chunks are XOR-swizzled within a
+// row (values: chunk c of row r at position c ^ r; x: chunk c of token t at
+// c ^ t; mask word w of row r at w ^ (r >> 2 & 7)), so the reads in MFMA
+// layout hit distinct LDS banks.  Each wave streams its own K range through a
+// private ring of NB such blocks with explicit vmcnt waits; the waves of a
+// workgroup split K and add their tiles through LDS at the end.
+
+typedef _Float16 h8v_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h16v_t __attribute__((ext_vector_type(16)));
+typedef __bf16 b8v_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b16v_t __attribute__((ext_vector_type(16)));
+typedef float f4v_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void *lds_vptr;
+
+// 2-bit in-group positions of the 8 kept values of a lane's 16 columns:
+// nibble g (exactly 2 set bits at p0 < p1) -> p0 | p1 << 2 at bits 4g..4g+3.
+// Branch-free: with bits b0..b3 of a nibble, p0 & 1 = ~b0 & b1,
+// p0 >> 1 = ~b0 & ~b1, p1 & 1 = b3 | ~b2, p1 >> 1 = b3 | b2.
+__device__ __forceinline__ int nib_codes(uint32_t m) {
+  const uint32_t s1 = m >> 1, s2 = m >> 2, s3 = m >> 3;
+  const uint32_t c0 = ~m & s1 & 0x1111u;
+  const uint32_t c1 = ~m & ~s1 & 0x1111u;
+  const uint32_t c2 = (s3 | ~s2) & 0x1111u;
+  const uint32_t c3 = (s3 | s2) & 0x1111u;
+  return (int)(c0 | (c1 << 1) | (c2 << 2) | (c3 << 3));
+}
+
+template <bool BF>
+__device__ __forceinline__ f4v_t smfmac(u32x4_t a, u32x4_t b0, u32x4_t b1, int idx, f4v_t c) {
+  const u32x8_t b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+  if constexpr (BF)
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(b8v_t, a),
+                                                    __builtin_bit_cast(b16v_t, b), c, idx, 0, 0);
+  else
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8v_t, a),
+                                                   __builtin_bit_cast(h16v_t, b), c, idx, 0, 0);
+}
+
+constexpr int kMBlkCols = 256;                  // columns per block
+constexpr int kMValBytes = 16 * kMBlkCols;      // 16 rows x 128 values x 2 B
+constexpr int kMMaskBytes = 16 * kMBlkCols / 8;  // 16 rows x 8 words x 4 B
+constexpr int kMXTok = 2 * kMBlkCols;           // x bytes per token per block
+
+// LDS bytes of one ring slot for a padded batch BP (x for BP tokens).
+__host__ __device__ constexpr int mfma_slot_bytes(int bp) {
+  return kMValBytes + kMMaskBytes + kMXTok * bp;
+}
+
+// Direct-to-LDS buffer loads: lane i's 16 (or 4) bytes at voff + soff land
+// at LDS address lds + 16 i (4 i); lds is wave-uniform.  The weights stream
+// with the nt policy, x (read by every workgroup) with the default one.
+__device__ __forceinline__ void lds_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff,
+                                              int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(size_t)lds, 16, voff, soff, 0, 2);
+}
+__device__ __forceinline__ void lds_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff,
+                                             int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(size_t)lds, 4, voff, soff, 0, 2);
+}
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff,
+                                           int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(size_t)lds, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Operands of one 64-column step of the matrix-core kernel.
+struct MfmaOps {
+  u32x4_t a, x0, x1;
+  uint32_t w;
+};
+
+template <bool BF, int BP, int NB>
+__global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
+    const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
+    const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K,
+    int out_kind) {
+  constexpr int XQ = BP / 2;          // x instructions per block (2 tokens each)
+  constexpr int ND = 4 + 2 + XQ;      // direct-to-LDS instructions per block
+  constexpr int SLOT = mfma_slot_bytes(BP);
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int W = blockDim.x / kWave;
+  const int n = lane & 15, j = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int nsteps = K >> 6;                              // 64-column steps
+  const int per = (((nsteps + W - 1) / W) + 3) & ~3;      // whole blocks per wave
+  const int sbeg = min(nsteps, wid * per), send = min(nsteps, sbeg + per);
+  const int mysteps = send - sbeg;
+  const int nblk = (mysteps + 3) >> 2;
+  const uint32_t ring = (uint32_t)(size_t)(lds_ptr)lds + (uint32_t)(wid * NB * SLOT);
+
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)values, 0, (int)(R * (int64_t)K), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)bits, 0, (int)(R * (int64_t)K / 8), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)x, 0, B * K * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t r0 = __builtin_amdgcn_make_buffer_rsrc((void *)values, 0, 0,
+                                                                      kRsrcWord3);
+  // Per-lane source offsets of the wave's first block (bytes).  Rows past R
+  // load row R - 1 (never stored); tokens past B read zeros (range check).
+  int voff[4], boff[2], xoff[XQ];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rr = 4 * q + (lane >> 4);
+    const int64_t r = min(row0 + rr, R - 1);
+    voff[q] = (int)(r * K) + 64 * sbeg + 16 * ((lane & 15) ^ rr);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int rr = 8 * q + (lane >> 3);
+    const int64_t r = min(row0 + rr, R - 1);
+    boff[q] = (int)(r * (K / 8)) + 8 * sbeg + 4 * ((lane & 7) ^ ((rr >> 2) & 7));
+  }
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int t = 2 * q + (lane >> 5);
+    xoff[q] = t * K * 2 + 128 * sbeg + 16 * ((lane & 31) ^ (t & 7));
+  }
+
+  // block b of the wave into ring slot b % NB; b >= nblk loads from
+  // zero-size resources (no memory traffic, same instruction count)
+  auto issue = [&](int b) {
+    const bool real = b < nblk;
+    const __amdgpu_buffer_rsrc_t V = real ? rv : r0, M = real ? rb : r0, X = real ? rx : r0;
+    const uint32_t sl = ring + (uint32_t)((b % NB) * SLOT);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      lds_load16_nt(V, sl + 1024 * q, voff[q], kMValBytes / 16 * b);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      lds_load4_nt(M, sl + kMValBytes + 256 * q, boff[q], kMMaskBytes / 16 * b);
+#pragma unroll
+    for (int q = 0; q < XQ; ++q)
+      lds_load16(X, sl + kMValBytes + kMMaskBytes + 1024 * q, xoff[q], kMXTok * b);
+  };
+
+  // reader addresses within a slot, step 0 (steps add constant offsets only
+  // after the swizzle, so they are recomputed per step)
+  const int tn = min(n, B - 1);
+  f4v_t acc = {0.f, 0.f, 0.f, 0.f};
+  // operands of step s of the block in slot sl
+  auto fetch = [&](uint32_t sl, int s) {
+    MfmaOps o;
+    o.a = ld<u32x4_t>((lds_ptr)(size_t)(sl + n * 256 + 16 * ((4 * s + j) ^ n)));
+    o.w = ld<uint32_t>((lds_ptr)(size_t)(sl + kMValBytes + n * 32 +
+                                         4 * ((2 * s + (j >> 1)) ^ ((n >> 2) & 7))));
+    const uint32_t xb = sl + kMValBytes + kMMaskBytes + tn * kMXTok;
+    o.x0 = ld<u32x4_t>((lds_ptr)(size_t)(xb + 16 * ((8 * s + j) ^ (tn & 7))));
+    o.x1 = ld<u32x4_t>((lds_ptr)(size_t)(xb + 16 * ((8 * s + 4 + j) ^ (tn & 7))));
+    return o;
+  };
+  auto mac = [&](const MfmaOps &o) {
+    acc = smfmac<BF>(o.a, o.x0, o.x1, nib_codes(o.w >> ((j & 1) * 16)), acc);
+  };
+  auto compute = [&](int b) {
+    const uint32_t sl = ring + (uint32_t)((b % NB) * SLOT);
+    const int ns = min(4, mysteps - 4 * b);
+    if (ns == 4) {  // whole block: every LDS read is issued before the first product
+      MfmaOps o[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) o[s] = fetch(sl, s);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) mac(o[s]);
+    } else {  // the wave's ragged last block
+      for (int s = 0; s < ns; ++s) mac(fetch(sl, s));
+    }
+  };
+
+#pragma unroll
+  for (int b = 0; b < NB - 1; ++b) issue(b);
+  for (int b = 0; b < nblk; ++b) {
+    // the slot about to be refilled was read by the previous block's
+    // compute: its LDS reads have returned before the refill is issued
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b + NB - 1);
+    wait_vmcnt<(NB - 1) * ND>();  // block b has landed; NB - 1 blocks stay in flight
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b);
+  }
+  wait_vmcnt<0>();  // the trailing dummy loads still write LDS
+  __builtin_amdgcn_sched_barrier(0);
+
+  // partial tiles of the W waves -> LDS (each wave's own ring) -> wave 0
+  if (W > 1) {
+    wait_lgkmcnt0();
+    float *mine = reinterpret_cast<float *>(lds + wid * NB * SLOT);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mine[i * kWave + lane] = acc[i];
+    __syncthreads();
+    if (wid != 0) return;
+    for (int w = 1; w < W; ++w) {
+      const float *other = reinterpret_cast<const float *>(lds + w * NB * SLOT);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += other[i * kWave + lane];
+    }
+  }
+  if (n < B) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = row0 + 4 * j + i;
+      if (r < R) store_out(y, (int64_t)n * R + r, acc[i], out_kind);
+    }
+  }
+}
+
 // Dense comparison when x fits the LDS budget, built like the sparse row
 // kernel so that the speedup is measured against an equally tuned dense
 // GEMV: x staged once per workgroup as BP contiguous rows; each wave walks
@@ -762,7 +1003,7 @@ __global__ __launch_bounds__(256) void nm_pack_kernel(
   const int wpg = blockDim.x / kWave;
   const uint32_t lb = lane & 31;
   const uint32_t below = (1u << lb) - 1u;
-  const uint32_t gmask = (M == 32) ? 0xffffffffu : ((1u << M) - 1u);
+  const uint32_t gmask = (M == 32) ? 0xffffffffu : ((1u << (M & 31)) - 1u);
   int nbad = 0;
   for (int64_t r = (int64_t)blockIdx.x * wpg + threadIdx.x / kWave; r < R;
        r += (int64_t)gridDim.x * wpg) {
@@ -926,11 +1167,52 @@ int threads_for_lds(size_t lds) {
   return lds <= 40 * 1024 ? 256 : lds <= 80 * 1024 ? 512 : 1024;
 }
 
-nm_status default_cfg(int64_t rows, int64_t cols, int batch, bool dense,
+// Can the 2:4 matrix-core kernel run this shape?  Its buffer resources
+// address the whole values array and the batch's x with 32-bit offsets.
+bool mfma_ok(int64_t rows, int64_t cols, int n, int m) {
+  return n == 2 && m == 4 && cols % 64 == 0 && cols <= (1 << 25) &&
+         rows * cols <= INT32_MAX;
+}
+
+// LDS of the matrix-core kernel: every wave's ring of `nb` blocks.
+size_t mfma_lds_bytes(int waves, int nb, int bp) {
+  return (size_t)waves * nb * mfma_slot_bytes(bp < 2 ? 2 : bp);
+}
+
+// Launch shape of the matrix-core kernel: threads_per_wg / 64 waves split K
+// for one 16-row tile; rows_per_wave is each wave's ring depth (blocks).
+// Measured on the 8B, 70B and Qwen3-32B shapes at batch 2..8: four waves
+// per workgroup is best or within 5% everywhere; a ring of three blocks is
+// best while two such workgroups fit a CU's LDS (batch <= 4), else two.
+void mfma_default(int64_t rows, int64_t cols, int batch, const DevInfo &di,
+                  nm_launch_cfg *cfg) {
+  (void)rows;
+  const int bp = pad_batch(batch) < 2 ? 2 : pad_batch(batch);
+  const int64_t nsteps = cols / 64;
+  const size_t budget = lds_budget(di);
+  int w = 4;
+  while (w > 1 && nsteps / w < 8) --w;  // at least two blocks of K per wave
+  const int nb = 2 * mfma_lds_bytes(w, 3, bp) <= kLdsCap ? 3 : 2;
+  while (w > 1 && mfma_lds_bytes(w, nb, bp) > budget) --w;
+  cfg->kernel = NM_KERNEL_MFMA;
+  cfg->threads_per_wg = w * kWave;
+  cfg->rows_per_wave = nb;
+  cfg->seg_cols = cols > 0 ? (int)cols : 64;
+}
+
+// Batch from which the auto choice takes the matrix-core kernel for 2:4.
+constexpr int kMfmaMinBatch = 2;
+
+nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool dense,
                       nm_launch_cfg *cfg) {
   DevInfo di;
   nm_status st = device_info(&di);
   if (st != NM_OK) return st;
+  if (!dense && batch >= kMfmaMinBatch && mfma_ok(rows, cols, n, m)) {
+    mfma_default(rows, cols, batch, di, cfg);
+    return NM_OK;
+  }
+  cfg->kernel = NM_KERNEL_VALU;
   const int bp = pad_batch(batch);
   const size_t budget = lds_budget(di);
   const int smax = max_seg(dense, bp, budget);
@@ -974,10 +1256,17 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, bool dense,
   return NM_OK;
 }
 
-nm_status check_cfg(const nm_launch_cfg &c, int64_t cols, bool dense, int bp,
-                    const DevInfo &di) {
+nm_status check_cfg(const nm_launch_cfg &c, int64_t rows, int64_t cols, int n, int m,
+                    bool dense, int bp, const DevInfo &di) {
   const int t = c.threads_per_wg;
   if (t < kWave || t > 1024 || t % kWave != 0) return NM_ERR_INVALID_ARG;
+  if (c.kernel == NM_KERNEL_MFMA) {
+    if (dense || !mfma_ok(rows, cols, n, m)) return NM_ERR_UNSUPPORTED;
+    if (c.rows_per_wave < 2 || c.rows_per_wave > 4) return NM_ERR_INVALID_ARG;
+    if (mfma_lds_bytes(t / kWave, c.rows_per_wave, bp) > lds_budget(di)) return NM_ERR_INVALID_ARG;
+    return NM_OK;
+  }
+  if (c.kernel != NM_KERNEL_VALU) return NM_ERR_INVALID_ARG;
   if (c.seg_cols <= 0 || c.seg_cols % 32 != 0) return NM_ERR_INVALID_ARG;
   if (rows_kernel(dense, cols, c.seg_cols)) {
     if (c.rows_per_wave < 1 || c.rows_per_wave > 64) return NM_ERR_INVALID_ARG;
@@ -990,19 +1279,25 @@ nm_status check_cfg(const nm_launch_cfg &c, int64_t cols, bool dense, int bp,
   return NM_OK;
 }
 
-nm_status resolve_cfg(int64_t rows, int64_t cols, int batch, bool dense,
+nm_status resolve_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool dense,
                       const nm_launch_cfg *user, nm_launch_cfg *out) {
-  nm_status st = default_cfg(rows, cols, batch, dense, out);
+  DevInfo di;
+  nm_status st = device_info(&di);
+  if (st != NM_OK) return st;
+  if (user && user->kernel == NM_KERNEL_MFMA && !dense && mfma_ok(rows, cols, n, m))
+    mfma_default(rows, cols, batch, di, out);
+  else if (user && user->kernel == NM_KERNEL_VALU)
+    st = default_cfg(rows, cols, batch, 0, 0, dense, out);  // no pattern: never picks MFMA
+  else
+    st = default_cfg(rows, cols, batch, n, m, dense, out);
   if (st != NM_OK) return st;
   if (user) {
+    if (user->kernel) out->kernel = user->kernel;
     if (user->threads_per_wg) out->threads_per_wg = user->threads_per_wg;
     if (user->rows_per_wave) out->rows_per_wave = user->rows_per_wave;
     if (user->seg_cols) out->seg_cols = user->seg_cols;
   }
-  DevInfo di;
-  st = device_info(&di);
-  if (st != NM_OK) return st;
-  return check_cfg(*out, cols, dense, pad_batch(batch), di);
+  return check_cfg(*out, rows, cols, n, m, dense, pad_batch(batch), di);
 }
 
 typedef void (*seg_fn)(const uint4 *, const uint32_t *, const uint16_t *, void *, int,
@@ -1119,6 +1414,31 @@ dense_rows_fn pick_dense_rows(bool bf, int bp) {
   return bf ? pick_dense_rows_bp<true>(bp) : pick_dense_rows_bp<false>(bp);
 }
 
+typedef void (*mfma_fn)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int,
+                        int64_t, int, int);
+
+template <bool BF, int BP>
+mfma_fn pick_mfma_nb(int nb) {
+  switch (nb) {
+    case 2: return nm_spmm_mfma_kernel<BF, BP, 2>;
+    case 3: return nm_spmm_mfma_kernel<BF, BP, 3>;
+    default: return nm_spmm_mfma_kernel<BF, BP, 4>;
+  }
+}
+
+template <bool BF>
+mfma_fn pick_mfma_bp(int bp, int nb) {
+  switch (bp) {
+    case 2: return pick_mfma_nb<BF, 2>(nb);
+    case 4: return pick_mfma_nb<BF, 4>(nb);
+    default: return pick_mfma_nb<BF, 8>(nb);
+  }
+}
+
+mfma_fn pick_mfma(bool bf, int bp, int nb) {
+  return bf ? pick_mfma_bp<true>(bp, nb) : pick_mfma_bp<false>(bp, nb);
+}
+
 int sparse_product(const void *values, const uint32_t *bits, const void *X,
                    void *Y, int batch, int64_t rows, int64_t cols, int n,
                    int m, nm_dtype in_dt, nm_dtype out_dt,
@@ -1135,10 +1455,21 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     return NM_ERR_ALIGN;
   if (rows == 0) return NM_OK;
   nm_launch_cfg cfg;
-  st = resolve_cfg(rows, cols, batch, false, user, &cfg);
+  st = resolve_cfg(rows, cols, batch, n, m, false, user, &cfg);
   if (st != NM_OK) return st;
   const int bp = pad_batch(batch);
   const bool bf = in_dt == NM_BF16;
+  if (cfg.kernel == NM_KERNEL_MFMA) {
+    const int waves = cfg.threads_per_wg / kWave, nb = cfg.rows_per_wave;
+    const int mbp = bp < 2 ? 2 : bp;
+    const int64_t grid = (rows + 15) / 16;
+    hipLaunchKernelGGL(pick_mfma(bf, mbp, nb), dim3((unsigned)grid), dim3(cfg.threads_per_wg),
+                       mfma_lds_bytes(waves, nb, mbp), (hipStream_t)stream,
+                       (const uint16_t *)values, bits, (const uint16_t *)X, Y, batch, rows,
+                       (int)cols, (int)out_dt);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? NM_OK : hip_fail(e);
+  }
   const int pk = pattern_kind(m);
   const int wpg = cfg.threads_per_wg / kWave;
   if (rows_kernel(false, cols, cfg.seg_cols)) {
@@ -1255,12 +1586,13 @@ int nm_spmm_small_cfg(const void *values, const uint32_t *bits, const void *X,
                         out_dt, cfg, stream);
 }
 
-int nm_default_launch(int64_t rows, int64_t cols, int batch, int dense,
+int nm_default_launch(int64_t rows, int64_t cols, int batch, int n, int m, int dense,
                       nm_launch_cfg *cfg) {
   if (!cfg) return NM_ERR_INVALID_ARG;
   nm_status st = check_dims(rows, cols, batch);
   if (st != NM_OK) return st;
-  return default_cfg(rows, cols, batch, dense != 0, cfg);
+  if (!dense && !pattern_ok(n, m)) return NM_ERR_UNSUPPORTED;
+  return default_cfg(rows, cols, batch, n, m, dense != 0, cfg);
 }
 
 int nm_dense_gemv_cfg(const void *W, const void *X, void *Y, int batch,
@@ -1276,7 +1608,7 @@ int nm_dense_gemv_cfg(const void *W, const void *X, void *Y, int batch,
   if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, ysz)) return NM_ERR_ALIGN;
   if (rows == 0) return NM_OK;
   nm_launch_cfg cfg;
-  st = resolve_cfg(rows, cols, batch, true, user, &cfg);
+  st = resolve_cfg(rows, cols, batch, 0, 0, true, user, &cfg);
   if (st != NM_OK) return st;
   const int bp = pad_batch(batch);
   const bool bf = in_dt == NM_BF16;

@@ -49,12 +49,16 @@ class NMError(RuntimeError):
         super().__init__(msg)
 
 
+NM_KERNEL_AUTO, NM_KERNEL_VALU, NM_KERNEL_MFMA = 0, 1, 2
+
+
 class LaunchCfg(ctypes.Structure):
+    """nm_launch_cfg: (threads_per_wg, rows_per_wave, seg_cols, kernel); 0 = library's choice."""
     _fields_ = [("threads_per_wg", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
-                ("seg_cols", ctypes.c_int)]
+                ("seg_cols", ctypes.c_int), ("kernel", ctypes.c_int)]
 
     def as_tuple(self):
-        return (self.threads_per_wg, self.rows_per_wave, self.seg_cols)
+        return (self.threads_per_wg, self.rows_per_wave, self.seg_cols, self.kernel)
 
 
 _lib = None
@@ -89,7 +93,7 @@ def lib():
     L.nm_dense_gemv.restype = ci
     L.nm_dense_gemv_cfg.argtypes = [p, p, p, ci, i64, i64, ci, ci, ctypes.POINTER(LaunchCfg), p]
     L.nm_dense_gemv_cfg.restype = ci
-    L.nm_default_launch.argtypes = [i64, i64, ci, ci, ctypes.POINTER(LaunchCfg)]
+    L.nm_default_launch.argtypes = [i64, i64, ci, ci, ci, ci, ctypes.POINTER(LaunchCfg)]
     L.nm_default_launch.restype = ci
     _lib = L
     return L
@@ -229,8 +233,9 @@ def nm_dense_gemv(W, X, out_dtype=torch.float32, out=None, cfg=None):
     return Y.reshape(-1) if squeeze else Y
 
 
-def nm_default_launch(rows: int, cols: int, batch: int, dense: bool = False) -> LaunchCfg:
+def nm_default_launch(rows: int, cols: int, batch: int, n: int = 2, m: int = 4,
+                      dense: bool = False) -> LaunchCfg:
     c = LaunchCfg()
-    _check(lib().nm_default_launch(rows, cols, batch, int(bool(dense)), ctypes.byref(c)),
+    _check(lib().nm_default_launch(rows, cols, batch, n, m, int(bool(dense)), ctypes.byref(c)),
            "nm_default_launch")
     return c

@@ -149,6 +149,7 @@ def test_pack_rejects_bad_arguments(L):
 def test_launch_cfg_validation_is_host_only(L):
     from sparse_gemv_memory_amd.native import LaunchCfg
     c = LaunchCfg()
-    assert L.nm_default_launch(8, 48, 1, 0, ctypes.byref(c)) == SHAPE
-    assert L.nm_default_launch(8, 64, 9, 0, ctypes.byref(c)) == INV
-    assert L.nm_default_launch(8, 64, 1, 0, None) == INV
+    assert L.nm_default_launch(8, 48, 1, 2, 4, 0, ctypes.byref(c)) == SHAPE
+    assert L.nm_default_launch(8, 64, 9, 2, 4, 0, ctypes.byref(c)) == INV
+    assert L.nm_default_launch(8, 64, 1, 2, 4, 0, None) == INV
+    assert L.nm_default_launch(8, 64, 1, 3, 4, 0, ctypes.byref(c)) == UNSUP
