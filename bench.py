@@ -239,8 +239,8 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (source sha256, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("d6c83f5e64683961f7b002d9a7bfb52a92c0717590ba35a48a3d7536007e7b05",
-                    66283986),
+    (14336, 4096): ("4620dee35d584b5aa03b98c22605f8bdbb3d68d24758017aea2365cca8356966",
+                    66277691),
 }
 
 
@@ -257,11 +257,12 @@ def measured_traffic(rows, cols):
 def counters_run():
     """Eager launches with known byte counts, for hardware-counter passes."""
     mt = [m for m, _ in workloads.config_matrices(2) if m.name == "gate"][0]
-    p = Proj(mt, (1,), False)
+    p = Proj(mt, (1, 8), False)
     torch.cuda.synchronize()
-    for c in range(5):
-        p.sparse_call(1, c)
-    torch.cuda.synchronize()
+    for b in (1, 8):  # batch 1: the VALU row kernel; batch 8: the matrix-core kernel
+        for c in range(5):
+            p.sparse_call(b, c)
+        torch.cuda.synchronize()
     n = 64 << 20
     src = torch.empty(n, dtype=torch.uint8, device=DEV).fill_(1)
     dst = torch.empty(n, dtype=torch.uint8, device=DEV)
@@ -272,6 +273,8 @@ def counters_run():
     print(json.dumps({"sparse_kernel_bytes_per_launch": p.sbytes[1],
                       "sparse_kernel_read_bytes": p.sbytes[1] - mt.rows * 4,
                       "sparse_kernel_write_bytes": mt.rows * 4,
+                      "batch8_bytes_per_launch": p.sbytes[8],
+                      "batch8_write_bytes": 8 * mt.rows * 4,
                       "copy_bytes_each_way": n}), flush=True)
 
 
