@@ -1220,6 +1220,8 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
   if (full <= budget) {
     // row kernel: x staged once per workgroup.  Measured on the 8B, 70B and
     // Qwen3-32B shapes:
+    //  - very few rows (<= 8 per CU) split evenly over the CUs: one row per
+    //    wave and one workgroup per CU, so x is staged once per CU;
     //  - few rows (<= 32 per CU) split evenly over the CUs: one row per wave
     //    and exactly two workgroups per CU, as wide as that takes;
     //  - otherwise, rows split evenly: 256 threads and the same number of
@@ -1228,6 +1230,11 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
     //  - otherwise one row per wave, and the hardware balances the groups.
     cfg->seg_cols = cols > 0 ? (int)cols : 32;
     const int64_t two_per_cu = 2LL * di.cus;
+    if (rows > 0 && rows % di.cus == 0 && rows / di.cus <= 8) {
+      cfg->threads_per_wg = (int)(rows / di.cus) * kWave;
+      cfg->rows_per_wave = 1;
+      return NM_OK;
+    }
     if (full <= budget / 2 && rows % two_per_cu == 0 && rows / two_per_cu <= 16) {
       cfg->threads_per_wg = (int)(rows / two_per_cu) * kWave;
       cfg->rows_per_wave = 1;
