@@ -628,6 +628,26 @@ __device__ __forceinline__ f4v_t smfmac(u32x4_t a, u32x4_t b0, u32x4_t b1, int i
                                                    __builtin_bit_cast(h16v_t, b), c, idx, 0, 0);
 }
 
+template <bool BF>
+__device__ __forceinline__ f4v_t dmfma(u32x4_t a, u32x4_t b, f4v_t c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8v_t, a),
+                                                  __builtin_bit_cast(b8v_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v_t, a),
+                                                 __builtin_bit_cast(h8v_t, b), c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ void lds_st(uint32_t addr, T v) {
+  *(__attribute__((address_space(3))) T *)(size_t)addr = v;
+}
+
+// Kernel kinds of the matrix-core product.
+constexpr int kMfmaSparse24 = 0;   // 2:4 on v_smfmac
+constexpr int kMfmaDenseHalf = 1;  // 4:8, 8:16: decompressed tile, v_mfma
+constexpr int kMfmaDense1632 = 2;  // 16:32: decompressed tile, v_mfma
+
 constexpr int kMBlkCols = 256;                  // columns per block
 constexpr int kMValBytes = 16 * kMBlkCols;      // 16 rows x 128 values x 2 B
 constexpr int kMMaskBytes = 16 * kMBlkCols / 8;  // 16 rows x 8 words x 4 B
@@ -636,6 +656,16 @@ constexpr int kMXTok = 2 * kMBlkCols;           // x bytes per token per block
 // LDS bytes of one ring slot for a padded batch BP (x for BP tokens).
 __host__ __device__ constexpr int mfma_slot_bytes(int bp) {
   return kMValBytes + kMMaskBytes + kMXTok * bp;
+}
+
+// Dense 16 x 64 tile of the decompressing kinds: rows padded to 144 bytes
+// (64 x 2 + 16), so the 16 rows of a 16-lane read start on distinct banks.
+constexpr int kMTileRow = 144;
+constexpr int kMTileBytes = 16 * kMTileRow;
+
+// LDS of one wave: its ring, and the dense tile of the decompressing kinds.
+__host__ __device__ constexpr int mfma_wave_bytes(int bp, int nb, int kind) {
+  return nb * mfma_slot_bytes(bp) + (kind == kMfmaSparse24 ? 0 : kMTileBytes);
 }
 
 // Direct-to-LDS buffer loads: lane i's 16 (or 4) bytes at voff + soff land
@@ -668,7 +698,7 @@ struct MfmaOps {
   uint32_t w;
 };
 
-template <bool BF, int BP, int NB>
+template <bool BF, int BP, int NB, int KIND>
 __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K,
@@ -687,7 +717,8 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
   const int sbeg = min(nsteps, wid * per), send = min(nsteps, sbeg + per);
   const int mysteps = send - sbeg;
   const int nblk = (mysteps + 3) >> 2;
-  const uint32_t ring = (uint32_t)(size_t)(lds_ptr)lds + (uint32_t)(wid * NB * SLOT);
+  constexpr int WBYTES = mfma_wave_bytes(BP, NB, KIND);
+  const uint32_t ring = (uint32_t)(size_t)(lds_ptr)lds + (uint32_t)(wid * WBYTES);
 
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       (void *)values, 0, (int)(R * (int64_t)K), kRsrcWord3);
@@ -753,10 +784,63 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
   auto mac = [&](const MfmaOps &o) {
     acc = smfmac<BF>(o.a, o.x0, o.x1, nib_codes(o.w >> ((j & 1) * 16)), acc);
   };
+  // Decompressing kinds, step s: lane (j, n) takes chunk 4 s + j of row n
+  // (8 kept values) and the columns of its 8 kept values within its 32-column
+  // mask word: the word's 8 lowest set bits for an even chunk, the next 8 for
+  // an odd one (for M <= 16 simply the word's low or high half).  It zeroes
+  // its 16 columns of the step's dense tile row, writes its 8 values at their
+  // columns (the zeroing of every lane precedes every value write: one
+  // wave's LDS operations complete in order), and the two 16x16x32 products
+  // read the tile in MFMA layout.  (Running a block's four steps phase by
+  // phase on four tiles measured slower: the larger LDS footprint costs more
+  // waves per CU than the overlap gains.)
+  const uint32_t tile = ring + (uint32_t)(NB * SLOT);
+  auto chunk_of = [&](uint32_t sl, int s) {
+    return ld<u32x4_t>((lds_ptr)(size_t)(sl + n * 256 + 16 * ((4 * s + j) ^ n)));
+  };
+  auto word_of = [&](uint32_t sl, int s) {
+    return ld<uint32_t>((lds_ptr)(size_t)(sl + kMValBytes + n * 32 +
+                                          4 * ((2 * s + (j >> 1)) ^ ((n >> 2) & 7))));
+  };
+  auto scatter = [&](uint32_t tile, u32x4_t v, uint32_t w) {
+    uint32_t m;
+    if constexpr (KIND == kMfmaDenseHalf) {
+      m = w & ((j & 1) ? 0xffff0000u : 0x0000ffffu);
+    } else {
+      uint32_t hi = w;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) hi &= hi - 1;
+      m = (j & 1) ? hi : w;
+    }
+    const uint32_t row = tile + (uint32_t)(n * kMTileRow);
+    lds_st<u32x4_t>(row + 32 * j, (u32x4_t){0u, 0u, 0u, 0u});
+    lds_st<u32x4_t>(row + 32 * j + 16, (u32x4_t){0u, 0u, 0u, 0u});
+    const uint32_t wb = row + 64 * (j >> 1);  // column 0 of the lane's word
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = ffbl_hw(m) & 31;  // an exhausted (malformed) word writes column 31
+      m &= m - 1;
+      lds_st<uint16_t>(wb + 2 * c, (uint16_t)(v[k >> 1] >> (16 * (k & 1))));
+    }
+  };
+  auto tile_a = [&](uint32_t tile, int t) {
+    return ld<u32x4_t>((lds_ptr)(size_t)(tile + n * kMTileRow + 64 * t + 16 * j));
+  };
+  auto x_of = [&](uint32_t sl, int s, int t) {
+    const uint32_t xb = sl + kMValBytes + kMMaskBytes + tn * kMXTok;
+    return ld<u32x4_t>((lds_ptr)(size_t)(xb + 16 * ((8 * s + 4 * t + j) ^ (tn & 7))));
+  };
+  auto dense_step = [&](uint32_t sl, int s) {
+    scatter(tile, chunk_of(sl, s), word_of(sl, s));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc = dmfma<BF>(tile_a(tile, t), x_of(sl, s, t), acc);
+  };
   auto compute = [&](int b) {
     const uint32_t sl = ring + (uint32_t)((b % NB) * SLOT);
     const int ns = min(4, mysteps - 4 * b);
-    if (ns == 4) {  // whole block: every LDS read is issued before the first product
+    if constexpr (KIND != kMfmaSparse24) {
+      for (int s = 0; s < ns; ++s) dense_step(sl, s);
+    } else if (ns == 4) {  // whole block: every LDS read is issued before the first product
       MfmaOps o[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) o[s] = fetch(sl, s);
@@ -785,13 +869,13 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
   // partial tiles of the W waves -> LDS (each wave's own ring) -> wave 0
   if (W > 1) {
     wait_lgkmcnt0();
-    float *mine = reinterpret_cast<float *>(lds + wid * NB * SLOT);
+    float *mine = reinterpret_cast<float *>(lds + wid * WBYTES);
 #pragma unroll
     for (int i = 0; i < 4; ++i) mine[i * kWave + lane] = acc[i];
     __syncthreads();
     if (wid != 0) return;
     for (int w = 1; w < W; ++w) {
-      const float *other = reinterpret_cast<const float *>(lds + w * NB * SLOT);
+      const float *other = reinterpret_cast<const float *>(lds + w * WBYTES);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] += other[i * kWave + lane];
     }
@@ -1167,16 +1251,21 @@ int threads_for_lds(size_t lds) {
   return lds <= 40 * 1024 ? 256 : lds <= 80 * 1024 ? 512 : 1024;
 }
 
-// Can the 2:4 matrix-core kernel run this shape?  Its buffer resources
-// address the whole values array and the batch's x with 32-bit offsets.
+// Can the matrix-core kernel run this shape?  Its buffer resources address
+// the whole values array and the batch's x with 32-bit offsets.
 bool mfma_ok(int64_t rows, int64_t cols, int n, int m) {
-  return n == 2 && m == 4 && cols % 64 == 0 && cols <= (1 << 25) &&
-         rows * cols <= INT32_MAX;
+  return pattern_ok(n, m) && cols % 64 == 0 && cols <= (1 << 25) && rows * cols <= INT32_MAX;
 }
 
-// LDS of the matrix-core kernel: every wave's ring of `nb` blocks.
-size_t mfma_lds_bytes(int waves, int nb, int bp) {
-  return (size_t)waves * nb * mfma_slot_bytes(bp < 2 ? 2 : bp);
+// Matrix-core kind of a pattern: 2:4 on the sparse instruction, the others
+// through a decompressed tile.
+int mfma_kind(int n, int m) {
+  return (n == 2 && m == 4) ? kMfmaSparse24 : m == 32 ? kMfmaDense1632 : kMfmaDenseHalf;
+}
+
+// LDS of the matrix-core kernel: every wave's ring of `nb` blocks (and tile).
+size_t mfma_lds_bytes(int waves, int nb, int bp, int kind) {
+  return (size_t)waves * mfma_wave_bytes(bp < 2 ? 2 : bp, nb, kind);
 }
 
 // Launch shape of the matrix-core kernel: threads_per_wg / 64 waves split K
@@ -1184,32 +1273,42 @@ size_t mfma_lds_bytes(int waves, int nb, int bp) {
 // Measured on the 8B, 70B and Qwen3-32B shapes at batch 2..8: four waves
 // per workgroup is best or within 5% everywhere; a ring of three blocks is
 // best while two such workgroups fit a CU's LDS (batch <= 4), else two.
-void mfma_default(int64_t rows, int64_t cols, int batch, const DevInfo &di,
+// For the decompressing kinds (measured on the 8B shapes at batch 2..8) the
+// ring of two blocks is best, with about 8 waves per CU in total, at most 8
+// per workgroup.
+void mfma_default(int64_t rows, int64_t cols, int batch, int kind, const DevInfo &di,
                   nm_launch_cfg *cfg) {
-  (void)rows;
   const int bp = pad_batch(batch) < 2 ? 2 : pad_batch(batch);
   const int64_t nsteps = cols / 64;
+  const int64_t tiles = (rows + 15) / 16;
   const size_t budget = lds_budget(di);
   int w = 4;
+  if (kind != kMfmaSparse24) {
+    const int64_t t = 8LL * di.cus / (tiles > 0 ? tiles : 1);
+    w = t < 1 ? 1 : t > 8 ? 8 : (int)t;
+  }
   while (w > 1 && nsteps / w < 8) --w;  // at least two blocks of K per wave
-  const int nb = 2 * mfma_lds_bytes(w, 3, bp) <= kLdsCap ? 3 : 2;
-  while (w > 1 && mfma_lds_bytes(w, nb, bp) > budget) --w;
+  const int nb = (kind == kMfmaSparse24 && 2 * mfma_lds_bytes(w, 3, bp, kind) <= kLdsCap) ? 3 : 2;
+  while (w > 1 && mfma_lds_bytes(w, nb, bp, kind) > budget) --w;
   cfg->kernel = NM_KERNEL_MFMA;
   cfg->threads_per_wg = w * kWave;
   cfg->rows_per_wave = nb;
   cfg->seg_cols = cols > 0 ? (int)cols : 64;
 }
 
-// Batch from which the auto choice takes the matrix-core kernel for 2:4.
+// Batch from which the auto choice takes the matrix-core kernel: 2:4 on the
+// sparse instruction, the other patterns through the decompressed tile.
 constexpr int kMfmaMinBatch = 2;
+constexpr int kDenseMfmaMinBatch = 5;  // measured: the VALU kernel wins at batch <= 4
 
 nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool dense,
                       nm_launch_cfg *cfg) {
   DevInfo di;
   nm_status st = device_info(&di);
   if (st != NM_OK) return st;
-  if (!dense && batch >= kMfmaMinBatch && mfma_ok(rows, cols, n, m)) {
-    mfma_default(rows, cols, batch, di, cfg);
+  if (!dense && mfma_ok(rows, cols, n, m) &&
+      batch >= (mfma_kind(n, m) == kMfmaSparse24 ? kMfmaMinBatch : kDenseMfmaMinBatch)) {
+    mfma_default(rows, cols, batch, mfma_kind(n, m), di, cfg);
     return NM_OK;
   }
   cfg->kernel = NM_KERNEL_VALU;
@@ -1270,7 +1369,8 @@ nm_status check_cfg(const nm_launch_cfg &c, int64_t rows, int64_t cols, int n, i
   if (c.kernel == NM_KERNEL_MFMA) {
     if (dense || !mfma_ok(rows, cols, n, m)) return NM_ERR_UNSUPPORTED;
     if (c.rows_per_wave < 2 || c.rows_per_wave > 4) return NM_ERR_INVALID_ARG;
-    if (mfma_lds_bytes(t / kWave, c.rows_per_wave, bp) > lds_budget(di)) return NM_ERR_INVALID_ARG;
+    if (mfma_lds_bytes(t / kWave, c.rows_per_wave, bp, mfma_kind(n, m)) > lds_budget(di))
+      return NM_ERR_INVALID_ARG;
     return NM_OK;
   }
   if (c.kernel != NM_KERNEL_VALU) return NM_ERR_INVALID_ARG;
@@ -1292,7 +1392,7 @@ nm_status resolve_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
   nm_status st = device_info(&di);
   if (st != NM_OK) return st;
   if (user && user->kernel == NM_KERNEL_MFMA && !dense && mfma_ok(rows, cols, n, m))
-    mfma_default(rows, cols, batch, di, out);
+    mfma_default(rows, cols, batch, mfma_kind(n, m), di, out);
   else if (user && user->kernel == NM_KERNEL_VALU)
     st = default_cfg(rows, cols, batch, 0, 0, dense, out);  // no pattern: never picks MFMA
   else
@@ -1424,26 +1524,35 @@ dense_rows_fn pick_dense_rows(bool bf, int bp) {
 typedef void (*mfma_fn)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int,
                         int64_t, int, int);
 
-template <bool BF, int BP>
+template <bool BF, int BP, int KIND>
 mfma_fn pick_mfma_nb(int nb) {
   switch (nb) {
-    case 2: return nm_spmm_mfma_kernel<BF, BP, 2>;
-    case 3: return nm_spmm_mfma_kernel<BF, BP, 3>;
-    default: return nm_spmm_mfma_kernel<BF, BP, 4>;
+    case 2: return nm_spmm_mfma_kernel<BF, BP, 2, KIND>;
+    case 3: return nm_spmm_mfma_kernel<BF, BP, 3, KIND>;
+    default: return nm_spmm_mfma_kernel<BF, BP, 4, KIND>;
+  }
+}
+
+template <bool BF, int KIND>
+mfma_fn pick_mfma_bp(int bp, int nb) {
+  switch (bp) {
+    case 2: return pick_mfma_nb<BF, 2, KIND>(nb);
+    case 4: return pick_mfma_nb<BF, 4, KIND>(nb);
+    default: return pick_mfma_nb<BF, 8, KIND>(nb);
   }
 }
 
 template <bool BF>
-mfma_fn pick_mfma_bp(int bp, int nb) {
-  switch (bp) {
-    case 2: return pick_mfma_nb<BF, 2>(nb);
-    case 4: return pick_mfma_nb<BF, 4>(nb);
-    default: return pick_mfma_nb<BF, 8>(nb);
+mfma_fn pick_mfma_kind(int kind, int bp, int nb) {
+  switch (kind) {
+    case kMfmaSparse24: return pick_mfma_bp<BF, kMfmaSparse24>(bp, nb);
+    case kMfmaDenseHalf: return pick_mfma_bp<BF, kMfmaDenseHalf>(bp, nb);
+    default: return pick_mfma_bp<BF, kMfmaDense1632>(bp, nb);
   }
 }
 
-mfma_fn pick_mfma(bool bf, int bp, int nb) {
-  return bf ? pick_mfma_bp<true>(bp, nb) : pick_mfma_bp<false>(bp, nb);
+mfma_fn pick_mfma(bool bf, int kind, int bp, int nb) {
+  return bf ? pick_mfma_kind<true>(kind, bp, nb) : pick_mfma_kind<false>(kind, bp, nb);
 }
 
 int sparse_product(const void *values, const uint32_t *bits, const void *X,
@@ -1470,8 +1579,10 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     const int waves = cfg.threads_per_wg / kWave, nb = cfg.rows_per_wave;
     const int mbp = bp < 2 ? 2 : bp;
     const int64_t grid = (rows + 15) / 16;
-    hipLaunchKernelGGL(pick_mfma(bf, mbp, nb), dim3((unsigned)grid), dim3(cfg.threads_per_wg),
-                       mfma_lds_bytes(waves, nb, mbp), (hipStream_t)stream,
+    const int kind = mfma_kind(n, m);
+    hipLaunchKernelGGL(pick_mfma(bf, kind, mbp, nb), dim3((unsigned)grid),
+                       dim3(cfg.threads_per_wg), mfma_lds_bytes(waves, nb, mbp, kind),
+                       (hipStream_t)stream,
                        (const uint16_t *)values, bits, (const uint16_t *)X, Y, batch, rows,
                        (int)cols, (int)out_dt);
     hipError_t e = hipGetLastError();

@@ -327,46 +327,50 @@ def test_dense_integer_exact(cols):
 
 # ---- 2:4 on the sparse matrix cores ------------------------------------------
 
-# (waves x 64 threads, ring depth in blocks of 256 columns)
-MFMA_CFGS = [(64, 2, 0, MFMA), (64, 4, 0, MFMA), (128, 3, 0, MFMA), (192, 3, 0, MFMA),
-             (256, 2, 0, MFMA), (256, 3, 0, MFMA), (256, 4, 0, MFMA), (448, 2, 0, MFMA),
-             (512, 2, 0, MFMA)]
+# (waves x 64 threads, ring depth in blocks of 256 columns); every shape fits
+# the LDS for every kind at batch 8
+MFMA_CFGS = [(64, 2, 0, MFMA), (64, 4, 0, MFMA), (128, 3, 0, MFMA), (192, 4, 0, MFMA),
+             (256, 2, 0, MFMA), (256, 3, 0, MFMA), (320, 2, 0, MFMA), (384, 2, 0, MFMA)]
+MFMA_CFGS_24 = [(256, 4, 0, MFMA), (448, 2, 0, MFMA), (512, 2, 0, MFMA)]  # 2:4 only (smaller LDS)
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 64), (16, 128), (17, 192), (203, 4160), (257, 2112),
                                        (48, 14336)])
 @pytest.mark.parametrize("batch", [1, 2, 3, 5, 8])
-def test_mfma_integer_exact(rows, cols, batch):
-    """The matrix-core kernel, over ring depths 2..4 and 1..8 waves splitting
-    K (including more waves than 64-column steps, waves left with no steps,
-    and ragged last blocks), gives the exact result on integer inputs; ragged
-    row tiles and tokens beyond the batch are never stored."""
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_mfma_integer_exact(rows, cols, batch, n, m):
+    """The matrix-core kernel (2:4 on the sparse instruction, the other
+    patterns through the decompressed tile), over ring depths 2..4 and 1..8
+    waves splitting K (including more waves than 64-column steps, waves left
+    with no steps, and ragged last blocks), gives the exact result on integer
+    inputs; ragged row tiles and tokens beyond the batch are never stored."""
     W = synth.integer_weights(rows, cols, seed=81)
-    keep = synth.random_mask(rows, cols, 2, 4, seed=82)
+    keep = synth.random_mask(rows, cols, n, m, seed=82)
     xi = np.random.default_rng(83).integers(-4, 5, size=(batch, cols)).astype(np.float32)
     X = synth.f32_to_16_bits(xi, "f16")
-    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    values, bits = gpu_pack(W, keep, n, m, "f16")
     want = oracle.masked_gemv(W, keep, X, False)
-    for cfg in MFMA_CFGS:
-        Y = native.nm_spmm_small(values, bits, t16(X, "f16"), 2, 4, cfg=cfg)
+    for cfg in MFMA_CFGS + (MFMA_CFGS_24 if (n, m) == (2, 4) else []):
+        Y = native.nm_spmm_small(values, bits, t16(X, "f16"), n, m, cfg=cfg)
         assert np.array_equal(f64(Y), want), cfg
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("batch", [2, 4, 7, 8])
 @pytest.mark.parametrize("out", ["f32", "16"])
-def test_mfma_matches_oracle(batch, dtype, out):
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_mfma_matches_oracle(batch, dtype, out, n, m):
     rows, cols = 333, 4096
-    W, keep, X = inputs(rows, cols, 2, 4, dtype, batch, seed=90 + batch)
-    values, bits = gpu_pack(W, keep, 2, 4, dtype)
+    W, keep, X = inputs(rows, cols, n, m, dtype, batch, seed=90 + batch)
+    values, bits = gpu_pack(W, keep, n, m, dtype)
     want = oracle.masked_gemv(W, keep, X, dtype == "bf16")
     cfg = (256, 2, 0, MFMA)
-    Y = native.nm_spmm_small(values, bits, t16(X, dtype), 2, 4, cfg=cfg)
+    Y = native.nm_spmm_small(values, bits, t16(X, dtype), n, m, cfg=cfg)
     for b in range(batch):
         assert rel_l2(f64(Y[b]), want[b]) <= TOL
     if out == "16":
-        Y16 = native.nm_spmm_small(values, bits, t16(X, dtype), 2, 4, out_dtype=TDT[dtype], cfg=cfg)
-        check_16bit_output(Y16, Y, W, keep, X, 2, 4, dtype)
+        Y16 = native.nm_spmm_small(values, bits, t16(X, dtype), n, m, out_dtype=TDT[dtype], cfg=cfg)
+        check_16bit_output(Y16, Y, W, keep, X, n, m, dtype)
 
 
 @pytest.mark.parametrize("kernel", [VALU, MFMA])
@@ -396,10 +400,10 @@ def test_mfma_rejected_where_it_cannot_run():
     with pytest.raises(native.NMError) as e:
         native.nm_spmm_small(values, bits, t16(X, "f16"), 2, 4, cfg=(0, 0, 0, MFMA))
     assert e.value.status == native.NM_ERR_UNSUPPORTED
-    W, keep, X = inputs(rows, 128, 4, 8, "f16", 2, seed=98)
-    values, bits = gpu_pack(W, keep, 4, 8, "f16")
+    W, keep, X = inputs(rows, 96, 16, 32, "f16", 2, seed=98)
+    values, bits = gpu_pack(W, keep, 16, 32, "f16")
     with pytest.raises(native.NMError) as e:
-        native.nm_spmm_small(values, bits, t16(X, "f16"), 4, 8, cfg=(0, 0, 0, MFMA))
+        native.nm_spmm_small(values, bits, t16(X, "f16"), 16, 32, cfg=(0, 0, 0, MFMA))
     assert e.value.status == native.NM_ERR_UNSUPPORTED
     with pytest.raises(native.NMError) as e:
         native.nm_dense_gemv(t16(W, "f16"), t16(X, "f16"), cfg=(0, 0, 0, MFMA))
@@ -414,11 +418,14 @@ def test_mfma_rejected_where_it_cannot_run():
         assert e.value.status == native.NM_ERR_INVALID_ARG, cfg
 
 
-def test_default_launch_picks_mfma_for_2of4_small_batch():
-    c = native.nm_default_launch(14336, 4096, 8, 2, 4)
-    assert c.kernel == MFMA
-    assert native.nm_default_launch(14336, 4096, 1, 2, 4).kernel == VALU
-    assert native.nm_default_launch(14336, 4096, 8, 4, 8).kernel == VALU
+def test_default_launch_picks_matrix_cores_for_small_batch():
+    for n, m in PATTERNS:
+        assert native.nm_default_launch(14336, 4096, 8, n, m).kernel == MFMA, (n, m)
+        assert native.nm_default_launch(14336, 4096, 1, n, m).kernel == VALU, (n, m)
+        want4 = MFMA if (n, m) == (2, 4) else VALU  # the decompressing kinds start at batch 5
+        assert native.nm_default_launch(14336, 4096, 4, n, m).kernel == want4, (n, m)
+    assert native.nm_default_launch(14336, 4080 + 16, 8, 2, 4).kernel == MFMA
+    assert native.nm_default_launch(14336, 4064, 8, 2, 4).kernel == VALU  # K % 64 != 0
     assert native.nm_default_launch(14336, 4096, 8, dense=True).kernel == VALU
 
 
