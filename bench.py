@@ -239,7 +239,7 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (source sha256, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("4620dee35d584b5aa03b98c22605f8bdbb3d68d24758017aea2365cca8356966",
+    (14336, 4096): ("c386188f5341368e0280d1cd7988a44c3ac9274783f7bf61039f87cf9907a820",
                     66277691),
 }
 
