@@ -144,12 +144,16 @@ int nm_dense_gemv(const void *W, const void *X, void *Y, int batch,
 
 /* Kernel family of a launch.
  *   NM_KERNEL_VALU: vector-ALU kernels (every pattern, the dense product);
- *   NM_KERNEL_MFMA: the 2:4 product on gfx950's sparse matrix cores
- *                   (v_smfmac_f32_16x16x64), which take a 2:4 tile as its
- *                   kept values plus a 2-bit in-group position per value
- *                   (derived on the fly from the bitmask words).  Only for
- *                   n:m = 2:4, cols % 64 == 0, cols <= 2^25 and
- *                   rows * cols <= 2^31 - 1. */
+ *   NM_KERNEL_MFMA: the product on gfx950's matrix cores.  2:4 runs on the
+ *                   sparse instruction (v_smfmac_f32_16x16x64), which takes
+ *                   a 2:4 tile as its kept values plus a 2-bit in-group
+ *                   position per value, derived on the fly from the bitmask
+ *                   words.  4:8, 8:16 and 16:32 are expanded into a dense
+ *                   tile in LDS and run on v_mfma_f32_16x16x32.  Only for
+ *                   cols % 64 == 0, cols <= 2^25 and rows * cols <= 2^31 - 1.
+ * The library's choice (NM_KERNEL_AUTO) takes the matrix cores for 2:4 at
+ * batch >= 2 and for the other patterns at batch >= 5 where they can run,
+ * the VALU kernels otherwise. */
 typedef enum { NM_KERNEL_AUTO = 0, NM_KERNEL_VALU = 1, NM_KERNEL_MFMA = 2 } nm_kernel;
 
 /* Launch shape of the sparse and dense kernels, for tuning sweeps.  Fields
@@ -163,7 +167,8 @@ typedef enum { NM_KERNEL_AUTO = 0, NM_KERNEL_VALU = 1, NM_KERNEL_MFMA = 2 } nm_k
  * MFMA kernel (one 16-row tile per workgroup):
  *   threads_per_wg: waves per workgroup x 64; the waves split K;
  *   rows_per_wave:  depth of each wave's LDS ring, 2..4 blocks of 256
- *                   columns (waves x depth x block bytes must fit the LDS);
+ *                   columns (waves x (depth x block bytes + tile bytes)
+ *                   must fit the LDS, else NM_ERR_INVALID_ARG);
  *   seg_cols:       ignored.
  * kernel: an nm_kernel (0 = the library's choice). */
 typedef struct {
