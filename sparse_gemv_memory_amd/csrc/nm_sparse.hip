@@ -11,7 +11,8 @@
 //     next kept column and clears it;
 //   - Appendix C: one kernel per pattern with N and M fixed at compile time.
 // The Triton/A100 kernel described there is prior art only; the design here
-// is for CDNA4:
+// is for CDNA4.  Batch 1 (and every pattern at batch <= 4) runs on the
+// vector ALUs, where the HBM-bound matrix-vector product belongs:
 //   - x is staged once per workgroup in LDS (the paper's kernel read x
 //     through L1 instead) in a padded layout, so the per-nonzero gathers of
 //     a wavefront spread over the LDS banks;
@@ -21,8 +22,11 @@
 //   - each lane walks its half-word in a fixed 8-step LSB scan (v_ffbl_b32),
 //     pairs two gathered x values into one register and accumulates with
 //     v_dot2_f32_{f16,bf16} (fp16/bf16 products are exact in fp32);
-//   - one wavefront per row (or a few rows), reduced across lanes at the end;
-//   - no MFMA: the operation is an HBM-bound matrix-vector product.
+//   - one wavefront per row (or a few rows), reduced across lanes at the end.
+// At batch 2..8 the per-token multiply-adds make that kernel ALU-bound, and
+// the small-batch product moves to the matrix cores (2:4 on the sparse
+// instruction, the other patterns through a decompressed tile), fed from the
+// same stored format through LDS; see nm_spmm_mfma_kernel.
 
 #include <hip/hip_runtime.h>
 
