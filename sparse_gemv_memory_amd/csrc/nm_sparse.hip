@@ -435,12 +435,14 @@ __device__ __forceinline__ void collect_row(float (&acc)[BP], float (&res)[BP], 
 // in flight while item k is consumed.  U is chosen per shape so that it
 // divides the row's chunks per lane (no idle load slots in the last batch).  The first item's loads are issued
 // before x is committed to LDS, so the x and weight latencies overlap.
-template <bool BF, int BP, int PK, int U>
+template <bool BF, int BP, int PK, int U, int XS>
 __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
     const uint4 *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int rpw,
     int out_kind) {
-  constexpr int XS = BP == 1 ? 4 : 1;  // x groups per thread held in registers
+  // XS: x groups per thread held in registers before the weight loads (the
+  // host picks enough for all of x where it can: a group left to the staging
+  // loop below waits for every outstanding load, the weights' included)
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wpg = blockDim.x / kWave;
@@ -1451,27 +1453,30 @@ seg_fn pick_seg(bool bf, int pk, int bp, int rpw) {
 }
 
 template <bool BF, int PK>
-rows_fn pick_rows_bp(int bp, int u) {
+rows_fn pick_rows_bp(int bp, int u, int xs) {
   switch (bp) {
     case 1:
-      return u == 5 ? nm_spmv_rows_kernel<BF, 1, PK, 5> : nm_spmv_rows_kernel<BF, 1, PK, 4>;
-    case 2: return nm_spmv_rows_kernel<BF, 2, PK, 4>;
-    case 4: return nm_spmv_rows_kernel<BF, 4, PK, 4>;
-    default: return nm_spmv_rows_kernel<BF, 8, PK, 4>;
+      if (xs > 4)
+        return u == 5 ? nm_spmv_rows_kernel<BF, 1, PK, 5, 8> : nm_spmv_rows_kernel<BF, 1, PK, 4, 8>;
+      return u == 5 ? nm_spmv_rows_kernel<BF, 1, PK, 5, 4> : nm_spmv_rows_kernel<BF, 1, PK, 4, 4>;
+    case 2: return nm_spmv_rows_kernel<BF, 2, PK, 4, 1>;
+    case 4: return nm_spmv_rows_kernel<BF, 4, PK, 4, 1>;
+    default: return nm_spmv_rows_kernel<BF, 8, PK, 4, 1>;
   }
 }
 
 template <bool BF>
-rows_fn pick_rows_pk(int pk, int bp, int u) {
+rows_fn pick_rows_pk(int pk, int bp, int u, int xs) {
   switch (pk) {
-    case kPat24: return pick_rows_bp<BF, kPat24>(bp, u);
-    case kPatHalf: return pick_rows_bp<BF, kPatHalf>(bp, u);
-    default: return pick_rows_bp<BF, kPat1632>(bp, u);
+    case kPat24: return pick_rows_bp<BF, kPat24>(bp, u, xs);
+    case kPatHalf: return pick_rows_bp<BF, kPatHalf>(bp, u, xs);
+    default: return pick_rows_bp<BF, kPat1632>(bp, u, xs);
   }
 }
 
-rows_fn pick_rows(bool bf, int pk, int bp, int u) {
-  return bf ? pick_rows_pk<true>(pk, bp, u) : pick_rows_pk<false>(pk, bp, u);
+// xs: x groups (8 columns each at batch 1) a thread needs to stage all of x
+rows_fn pick_rows(bool bf, int pk, int bp, int u, int xs) {
+  return bf ? pick_rows_pk<true>(pk, bp, u, xs) : pick_rows_pk<false>(pk, bp, u, xs);
 }
 
 // Chunks per lane per load batch of the batch-1 row kernel: 4, or 5 when
@@ -1598,7 +1603,9 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     const int64_t rows_per_wg = (int64_t)wpg * cfg.rows_per_wave;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
     if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(pick_rows(bf, pk, bp, rows_batch_chunks(cols, bp)), dim3((unsigned)grid), dim3(cfg.threads_per_wg),
+    const int xs = (int)((cols / 8 + cfg.threads_per_wg - 1) / cfg.threads_per_wg);
+    hipLaunchKernelGGL(pick_rows(bf, pk, bp, rows_batch_chunks(cols, bp), xs), dim3((unsigned)grid),
+                       dim3(cfg.threads_per_wg),
                        sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32), (hipStream_t)stream,
                        (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
                        (int)cols, cfg.rows_per_wave, (int)out_dt);

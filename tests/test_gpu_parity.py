@@ -250,7 +250,9 @@ def test_batch1_load_batch_sizes_exact(cols, n, m):
     X = synth.f32_to_16_bits(xi, "f16")
     values, bits = gpu_pack(W, keep, n, m, "f16")
     want = oracle.masked_gemv(W, keep, X, False)
-    for cfg in (None, (64, 1, 0, VALU), (128, 3, 0, VALU), (256, 6, 0, VALU)):
+    # x staged by 4 or 8 groups per thread before the weight loads, with and
+    # without the staging loop for the rest (64..512 threads)
+    for cfg in (None, (64, 1, 0, VALU), (128, 3, 0, VALU), (256, 6, 0, VALU), (512, 1, 0, VALU)):
         y = native.nm_spmv(values, bits, t16(X[0], "f16"), n, m, cfg=cfg)
         assert np.array_equal(f64(y), want[0]), cfg
 
