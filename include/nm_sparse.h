@@ -132,6 +132,28 @@ int nm_spmm_small(const void *values, const uint32_t *bits, const void *X,
                   void *Y, int batch, int64_t rows, int64_t cols, int n, int m,
                   nm_dtype in_dt, nm_dtype out_dt, void *stream);
 
+/* Fused gate/up product with the SwiGLU epilogue: the MLP step around the
+ * sparse product in the decoder layers of the Llama and Qwen models whose
+ * end-to-end decoding the pages time (Experiments, Table 3 paragraph).  The
+ * pages do not describe the layer; silu(gate) * up is those model families'
+ * published MLP.
+ *   H[b][r] = silu(G[b][r]) * U[b][r],  0 <= r < inter,  silu(z) = z / (1 + e^-z),
+ * where G and U are the products (as nm_spmm_small) of the gate and up
+ * projections.  The packed matrix holds 2 * inter rows with the two
+ * projections interleaved: gate row r is packed row 2r and up row r is packed
+ * row 2r + 1 (nm_pack of the row-interleaved dense matrix).  The sums are
+ * fp32; silu is evaluated in fp32 (hardware exp) and H is fp32 or rounded to
+ * in_dt.
+ *   X: batch x cols; H: batch x inter row-major (overwritten).
+ * Other arguments, precision and errors as nm_spmm_small; inter < 0 or
+ * 2 * inter > INT32_MAX gives NM_ERR_INVALID_ARG.  With the VALU kernels the
+ * epilogue needs all of x in LDS (cols * batch * 2 bytes within the LDS
+ * budget; else NM_ERR_UNSUPPORTED) and an even rows_per_wave in an explicit
+ * launch shape (else NM_ERR_INVALID_ARG). */
+int nm_spmm_swiglu(const void *values, const uint32_t *bits, const void *X,
+                   void *H, int batch, int64_t inter, int64_t cols, int n, int m,
+                   nm_dtype in_dt, nm_dtype out_dt, void *stream);
+
 /* Dense comparison, the decode GEMV the sparse kernel replaces (Experiments,
  * Table 3 paragraph: speedups are against the dense model's decode):
  *   Y[b][r] = sum over all c of W[r][c] * X[b][c],  1 <= batch <= 8.
@@ -195,6 +217,12 @@ int nm_spmm_small_cfg(const void *values, const uint32_t *bits, const void *X,
 int nm_dense_gemv_cfg(const void *W, const void *X, void *Y, int batch,
                       int64_t rows, int64_t cols, nm_dtype in_dt,
                       nm_dtype out_dt, const nm_launch_cfg *cfg, void *stream);
+/* nm_spmm_swiglu with an explicit launch shape of its 2 * inter packed rows
+ * (cfg may be NULL). */
+int nm_spmm_swiglu_cfg(const void *values, const uint32_t *bits, const void *X,
+                       void *H, int batch, int64_t inter, int64_t cols, int n,
+                       int m, nm_dtype in_dt, nm_dtype out_dt,
+                       const nm_launch_cfg *cfg, void *stream);
 
 /* Calibration read (measurement only, not part of the product path): loads
  * every byte of buf once with 128-bit loads and writes one word per wavefront

@@ -18,6 +18,11 @@ Functions and the passages they follow (SparseDecoding, arXiv 2610.12327):
   ("Method", "Decoding is dominated by SpMV operations").
 * :func:`decode16` -- binary16 / bfloat16 bit patterns to float64 from the
   format definitions.
+* :func:`silu_mul` / :func:`swiglu_gemv` -- silu(gate) * up on the masked
+  products of a row-interleaved gate/up matrix, the MLP step of the Llama and
+  Qwen decoder layers whose end-to-end decoding the pages time ("Experiments",
+  Table 3 paragraph; the layer itself is those models' published
+  architecture, not spelled out on the pages).
 
 Every function here is pinned in ``tests/test_oracle_pins.py`` against facts
 that do not come from this code (library routines, closed forms, brute force,
@@ -76,6 +81,8 @@ def _load():
     lib.oracle_unpack.restype = ci
     lib.oracle_masked_gemv_f64.argtypes = [p, p, ci, p, ci, i64, i64, p, i64, ci, p]
     lib.oracle_masked_gemv_f64.restype = None
+    lib.oracle_silu_mul_f64.argtypes = [p, p, i64, p]
+    lib.oracle_silu_mul_f64.restype = None
     _lib = lib
     return lib
 
@@ -170,3 +177,24 @@ def masked_gemv(W, keep, x, is_bf16: bool, rows_idx=None, threads: int = 1) -> n
         _ptr(w), None if k is None else _ptr(k), int(bool(is_bf16)), _ptr(xb), batch,
         rows, cols, None if idx is None else _ptr(idx), nrows, int(threads), _ptr(y))
     return y[0] if squeeze else y
+
+
+def silu_mul(g, u) -> np.ndarray:
+    """fp64 h = silu(g) * u elementwise, silu(z) = z / (1 + exp(-z))."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    if g.shape != u.shape:
+        raise ValueError("g and u must have the same shape")
+    h = np.empty_like(g)
+    _load().oracle_silu_mul_f64(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+def swiglu_gemv(W, keep, x, is_bf16: bool, threads: int = 1) -> np.ndarray:
+    """fp64 h[b, r] = silu(g[b, r]) * u[b, r] where g and u are the masked
+    products of rows 2r (gate) and 2r + 1 (up) of the row-interleaved W."""
+    w = _bits16(W)
+    if w.shape[0] % 2:
+        raise ValueError("W must hold (gate, up) row pairs")
+    y = masked_gemv(W, keep, x, is_bf16, threads=threads)
+    return silu_mul(y[..., 0::2], y[..., 1::2])

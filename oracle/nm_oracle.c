@@ -192,3 +192,13 @@ void oracle_masked_gemv_f64(const uint16_t *W, const uint8_t *keep, int is_bf16,
         }
     }
 }
+
+/* ---- the SwiGLU step around the product ------------------------------------ */
+
+/* h[i] = silu(g[i]) * u[i] with silu(z) = z * sigmoid(z) = z / (1 + exp(-z)),
+ * in double.  The MLP of the Llama / Qwen decoder layers timed end to end on
+ * the pages applies this to the gate and up projections (the pages do not
+ * spell the layer out; it is those models' published architecture). */
+void oracle_silu_mul_f64(const double *g, const double *u, int64_t n, double *h) {
+    for (int64_t i = 0; i < n; ++i) h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}

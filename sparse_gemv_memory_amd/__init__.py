@@ -17,5 +17,6 @@ from .native import (  # noqa: F401
     nm_pack,
     nm_packed_bytes,
     nm_spmm_small,
+    nm_spmm_swiglu,
     nm_spmv,
 )

@@ -87,8 +87,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// out_kind: the output nm_dtype in bits 0..7 and the epilogue above them.
+constexpr int kEpiShift = 8;
+constexpr int kEpiNone = 0;
+constexpr int kEpiSwiglu = 1;  // rows 2r, 2r+1 -> silu(row 2r) * row 2r+1
+
 __device__ __forceinline__ void store_out(void *y, int64_t idx, float v,
                                           int kind) {
+  kind &= 0xff;
   if (kind == NM_F32)
     static_cast<float *>(y)[idx] = v;
   else if (kind == NM_F16)
@@ -404,6 +410,9 @@ __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, i
   }
 }
 
+// SiLU in fp32: z * sigmoid(z) = z / (1 + e^-z).
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
 template <int BP>
 __device__ __forceinline__ void finish_row(float (&acc)[BP], void *y, int B, int64_t R,
                                            int64_t r, int lane, int out_kind) {
@@ -460,7 +469,14 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   float acc[BP];
 #pragma unroll
   for (int b = 0; b < BP; ++b) acc[b] = 0.f;
+  const bool swiglu = (out_kind >> kEpiShift) == kEpiSwiglu;
   if (K == 0) {  // every sum is empty
+    if (swiglu) {  // silu(0) * 0 for every pair of the wave (r0 and nrows are even)
+      if (lane == 0)
+        for (int r = 0; r < nrows; r += 2)
+          for (int b = 0; b < B; ++b) store_out(y, (int64_t)b * (R / 2) + (r0 + r) / 2, 0.f, out_kind);
+      return;
+    }
     for (int r = 0; r < nrows; ++r) finish_row<BP>(acc, y, B, R, r0 + r, lane, out_kind);
     return;
   }
@@ -507,6 +523,17 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
     run_batch<BF, BP, PK, U>(lds, Bt, t1 * kWave * U + lane, nch, acc);
     if (t1 == nb - 1) collect_row<BP>(acc, res, i1, lane);
     item_load(Bt, k + 3);
+  }
+  if (swiglu) {
+    // the wave's rows come in (gate, up) pairs at even offsets: lane 2p
+    // takes its up sum from lane 2p + 1 and stores pair p
+#pragma unroll
+    for (int b = 0; b < BP; ++b) {
+      const float u = __shfl_down(res[b], 1);
+      if ((lane & 1) == 0 && lane < nrows && b < B)
+        store_out(y, (int64_t)b * (R / 2) + (r0 + lane) / 2, silu(res[b]) * u, out_kind);
+    }
+    return;
   }
   if (lane < nrows) {
 #pragma unroll
@@ -887,10 +914,19 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     }
   }
   if (n < B) {
+    if ((out_kind >> kEpiShift) == kEpiSwiglu) {
+      // rows 4j, 4j+1 and 4j+2, 4j+3 of the tile are (gate, up) pairs
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = row0 + 4 * j + i;
-      if (r < R) store_out(y, (int64_t)n * R + r, acc[i], out_kind);
+      for (int i = 0; i < 4; i += 2) {
+        const int64_t r = row0 + 4 * j + i;
+        if (r < R) store_out(y, (int64_t)n * (R / 2) + r / 2, silu(acc[i]) * acc[i + 1], out_kind);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = row0 + 4 * j + i;
+        if (r < R) store_out(y, (int64_t)n * R + r, acc[i], out_kind);
+      }
     }
   }
 }
@@ -1307,8 +1343,10 @@ void mfma_default(int64_t rows, int64_t cols, int batch, int kind, const DevInfo
 constexpr int kMfmaMinBatch = 2;
 constexpr int kDenseMfmaMinBatch = 5;  // measured: the VALU kernel wins at batch <= 4
 
+// pair: the rows come in (gate, up) pairs for the SwiGLU epilogue, so a
+// wave of the row kernel must own an even number of rows.
 nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool dense,
-                      nm_launch_cfg *cfg) {
+                      nm_launch_cfg *cfg, bool pair = false) {
   DevInfo di;
   nm_status st = device_info(&di);
   if (st != NM_OK) return st;
@@ -1335,22 +1373,23 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
     //  - otherwise one row per wave, and the hardware balances the groups.
     cfg->seg_cols = cols > 0 ? (int)cols : 32;
     const int64_t two_per_cu = 2LL * di.cus;
-    if (rows > 0 && rows % di.cus == 0 && rows / di.cus <= 8) {
-      cfg->threads_per_wg = (int)(rows / di.cus) * kWave;
-      cfg->rows_per_wave = 1;
+    const int rmin = pair ? 2 : 1;  // rows per wave in the one-row shapes
+    if (rows > 0 && rows % (rmin * di.cus) == 0 && rows / di.cus <= 8) {
+      cfg->threads_per_wg = (int)(rows / (rmin * di.cus)) * kWave;
+      cfg->rows_per_wave = rmin;
       return NM_OK;
     }
-    if (full <= budget / 2 && rows % two_per_cu == 0 && rows / two_per_cu <= 16) {
-      cfg->threads_per_wg = (int)(rows / two_per_cu) * kWave;
-      cfg->rows_per_wave = 1;
+    if (full <= budget / 2 && rows % (rmin * two_per_cu) == 0 && rows / two_per_cu <= 16) {
+      cfg->threads_per_wg = (int)(rows / (rmin * two_per_cu)) * kWave;
+      cfg->rows_per_wave = rmin;
       return NM_OK;
     }
     cfg->threads_per_wg = threads_for_lds(full);
     const int64_t per_cu_rows = (int64_t)di.cus * (cfg->threads_per_wg / kWave);
-    int rpw = 1;
+    int rpw = rmin;
     if (rows % per_cu_rows == 0) {
       const int64_t q = rows / per_cu_rows;  // rows per wave if one workgroup per CU
-      for (int d = 8; d >= 2; --d)
+      for (int d = 8; d >= 2; d -= pair ? 2 : 1)
         if (q % d == 0 && q / d >= 2) { rpw = d; break; }
     }
     cfg->rows_per_wave = rpw;
@@ -1393,16 +1432,16 @@ nm_status check_cfg(const nm_launch_cfg &c, int64_t rows, int64_t cols, int n, i
 }
 
 nm_status resolve_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool dense,
-                      const nm_launch_cfg *user, nm_launch_cfg *out) {
+                      const nm_launch_cfg *user, nm_launch_cfg *out, bool pair = false) {
   DevInfo di;
   nm_status st = device_info(&di);
   if (st != NM_OK) return st;
   if (user && user->kernel == NM_KERNEL_MFMA && !dense && mfma_ok(rows, cols, n, m))
     mfma_default(rows, cols, batch, mfma_kind(n, m), di, out);
   else if (user && user->kernel == NM_KERNEL_VALU)
-    st = default_cfg(rows, cols, batch, 0, 0, dense, out);  // no pattern: never picks MFMA
+    st = default_cfg(rows, cols, batch, 0, 0, dense, out, pair);  // no pattern: never picks MFMA
   else
-    st = default_cfg(rows, cols, batch, n, m, dense, out);
+    st = default_cfg(rows, cols, batch, n, m, dense, out, pair);
   if (st != NM_OK) return st;
   if (user) {
     if (user->kernel) out->kernel = user->kernel;
@@ -1564,10 +1603,12 @@ mfma_fn pick_mfma(bool bf, int kind, int bp, int nb) {
   return bf ? pick_mfma_kind<true>(kind, bp, nb) : pick_mfma_kind<false>(kind, bp, nb);
 }
 
+// epi: kEpiNone, or kEpiSwiglu (rows are (gate, up) pairs, Y has rows / 2
+// columns per token).
 int sparse_product(const void *values, const uint32_t *bits, const void *X,
                    void *Y, int batch, int64_t rows, int64_t cols, int n,
                    int m, nm_dtype in_dt, nm_dtype out_dt,
-                   const nm_launch_cfg *user, void *stream) {
+                   const nm_launch_cfg *user, void *stream, int epi = kEpiNone) {
   nm_status st = check_dims(rows, cols, batch);
   if (st != NM_OK) return st;
   if (!pattern_ok(n, m) || !is16(in_dt) || !out_ok(in_dt, out_dt)) return NM_ERR_UNSUPPORTED;
@@ -1580,8 +1621,15 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     return NM_ERR_ALIGN;
   if (rows == 0) return NM_OK;
   nm_launch_cfg cfg;
-  st = resolve_cfg(rows, cols, batch, n, m, false, user, &cfg);
+  const bool pair = epi == kEpiSwiglu;
+  st = resolve_cfg(rows, cols, batch, n, m, false, user, &cfg, pair);
   if (st != NM_OK) return st;
+  if (pair && cfg.kernel != NM_KERNEL_MFMA) {
+    // the epilogue lives in the row kernel: each wave an even number of rows
+    if (!rows_kernel(false, cols, cfg.seg_cols)) return NM_ERR_UNSUPPORTED;
+    if (cfg.rows_per_wave % 2 != 0) return NM_ERR_INVALID_ARG;
+  }
+  const int out_kind = (int)out_dt | (epi << kEpiShift);
   const int bp = pad_batch(batch);
   const bool bf = in_dt == NM_BF16;
   if (cfg.kernel == NM_KERNEL_MFMA) {
@@ -1593,7 +1641,7 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
                        dim3(cfg.threads_per_wg), mfma_lds_bytes(waves, nb, mbp, kind),
                        (hipStream_t)stream,
                        (const uint16_t *)values, bits, (const uint16_t *)X, Y, batch, rows,
-                       (int)cols, (int)out_dt);
+                       (int)cols, out_kind);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? NM_OK : hip_fail(e);
   }
@@ -1608,7 +1656,7 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
                        dim3(cfg.threads_per_wg),
                        sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32), (hipStream_t)stream,
                        (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
-                       (int)cols, cfg.rows_per_wave, (int)out_dt);
+                       (int)cols, cfg.rows_per_wave, out_kind);
   } else {
     const int64_t rows_per_wg = (int64_t)wpg * cfg.rows_per_wave;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
@@ -1713,6 +1761,21 @@ int nm_spmm_small_cfg(const void *values, const uint32_t *bits, const void *X,
                       const nm_launch_cfg *cfg, void *stream) {
   return sparse_product(values, bits, X, Y, batch, rows, cols, n, m, in_dt,
                         out_dt, cfg, stream);
+}
+
+int nm_spmm_swiglu(const void *values, const uint32_t *bits, const void *X, void *H,
+                   int batch, int64_t inter, int64_t cols, int n, int m, nm_dtype in_dt,
+                   nm_dtype out_dt, void *stream) {
+  return nm_spmm_swiglu_cfg(values, bits, X, H, batch, inter, cols, n, m, in_dt, out_dt,
+                            nullptr, stream);
+}
+
+int nm_spmm_swiglu_cfg(const void *values, const uint32_t *bits, const void *X, void *H,
+                       int batch, int64_t inter, int64_t cols, int n, int m, nm_dtype in_dt,
+                       nm_dtype out_dt, const nm_launch_cfg *cfg, void *stream) {
+  if (inter < 0 || inter > INT32_MAX / 2) return NM_ERR_INVALID_ARG;
+  return sparse_product(values, bits, X, H, batch, 2 * inter, cols, n, m, in_dt, out_dt, cfg,
+                        stream, kEpiSwiglu);
 }
 
 int nm_default_launch(int64_t rows, int64_t cols, int batch, int n, int m, int dense,

@@ -89,6 +89,11 @@ def lib():
     L.nm_spmm_small_cfg.argtypes = [p, p, p, p, ci, i64, i64, ci, ci, ci, ci,
                                     ctypes.POINTER(LaunchCfg), p]
     L.nm_spmm_small_cfg.restype = ci
+    L.nm_spmm_swiglu.argtypes = [p, p, p, p, ci, i64, i64, ci, ci, ci, ci, p]
+    L.nm_spmm_swiglu.restype = ci
+    L.nm_spmm_swiglu_cfg.argtypes = [p, p, p, p, ci, i64, i64, ci, ci, ci, ci,
+                                     ctypes.POINTER(LaunchCfg), p]
+    L.nm_spmm_swiglu_cfg.restype = ci
     L.nm_dense_gemv.argtypes = [p, p, p, ci, i64, i64, ci, ci, p]
     L.nm_dense_gemv.restype = ci
     L.nm_dense_gemv_cfg.argtypes = [p, p, p, ci, i64, i64, ci, ci, ctypes.POINTER(LaunchCfg), p]
@@ -213,6 +218,27 @@ def nm_spmm_small(values, bits, X, n: int, m: int, out_dtype=torch.float32, out=
                                      _DT[out_dtype], _cfg_ptr(cfg), _stream(values.device))
     _check(st, "nm_spmm_small")
     return Y
+
+
+def nm_spmm_swiglu(values, bits, X, n: int, m: int, out_dtype=torch.float32, out=None, cfg=None):
+    """H = silu(G) * U for X of shape (batch, cols), 1 <= batch <= 8, where the
+    packed matrix interleaves gate row r (packed row 2r) and up row r (2r + 1);
+    H has shape (batch, rows // 2)."""
+    rows, cols = _sparse_args(values, bits, X)
+    if rows % 2:
+        raise ValueError("the packed matrix must hold (gate, up) row pairs")
+    if X.dim() != 2 or X.shape[1] != cols:
+        raise ValueError("X must be (batch, cols)")
+    batch, inter = X.shape[0], rows // 2
+    H = out if out is not None else torch.empty((batch, inter), dtype=out_dtype, device=values.device)
+    if tuple(H.shape) != (batch, inter) or H.dtype != out_dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    with torch.cuda.device(values.device):
+        st = lib().nm_spmm_swiglu_cfg(_dev(values, "values"), _dev(bits, "bits"), _dev(X, "X"),
+                                      _dev(H, "H"), batch, inter, cols, n, m, _in_dt(X),
+                                      _DT[out_dtype], _cfg_ptr(cfg), _stream(values.device))
+    _check(st, "nm_spmm_swiglu")
+    return H
 
 
 def nm_dense_gemv(W, X, out_dtype=torch.float32, out=None, cfg=None):

@@ -121,6 +121,25 @@ def test_spmm_small_batch_range(L):
     assert L.nm_spmm_small(P, P, P, P, 2, 8, 96 + 8, 2, 4, F16, F32, None) == SHAPE
 
 
+def _swiglu(L, values=P, bits=P, x=P, h=P, batch=1, inter=4, cols=64, n=2, m=4, i=F16, o=F32):
+    return L.nm_spmm_swiglu(values, bits, x, h, batch, inter, cols, n, m, i, o, None)
+
+
+def test_swiglu_rejects_bad_arguments(L):
+    assert _swiglu(L, inter=-1) == INV
+    assert _swiglu(L, inter=2 ** 30) == INV  # 2 * inter rows exceed INT32_MAX
+    assert _swiglu(L, batch=0) == INV
+    assert _swiglu(L, batch=9) == INV
+    assert _swiglu(L, cols=48) == SHAPE
+    assert _swiglu(L, n=1, m=4) == UNSUP
+    assert _swiglu(L, i=F16, o=BF16) == UNSUP
+    assert _swiglu(L, values=None) == INV
+    assert _swiglu(L, h=None) == INV
+    assert _swiglu(L, x=P + 4) == ALIGN
+    assert _swiglu(L, h=P + 2) == ALIGN
+    assert _swiglu(L, values=None, bits=None, h=None, inter=0) == OK  # nothing to compute
+
+
 def test_dense_rejects_bad_arguments(L):
     assert L.nm_dense_gemv(P, P, P, 0, 8, 64, F16, F32, None) == INV
     assert L.nm_dense_gemv(P, P, P, 9, 8, 64, F16, F32, None) == INV

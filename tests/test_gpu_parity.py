@@ -501,3 +501,87 @@ def test_full_size_sampled_rows(mt, batches):
         wd = oracle.masked_gemv(W, None, X, bf, rows_idx=idx, threads=8)
         for b in range(batch):
             assert rel_l2(Yd[b], wd[b]) <= TOL, (mt, batch, b)
+
+
+# ---- fused gate/up product with the SwiGLU epilogue --------------------------------
+
+def _swiglu_inputs(inter, cols, n, m, dtype, batch, seed):
+    W = synth.weights(2 * inter, cols, seed=seed, dtype=dtype)  # rows 2r gate, 2r+1 up
+    keep = synth.topn_mask(W, n, m)
+    X = synth.activations(batch, cols, seed=seed, dtype=dtype)
+    return W, keep, X
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("batch", [1, 2, 5, 8])
+@pytest.mark.parametrize("n,m", PATTERNS)
+@pytest.mark.parametrize("cols", [2080, 2112])  # 2112: matrix-core eligible at batch >= 2 / 5
+def test_swiglu_matches_oracle(cols, n, m, batch, dtype):
+    inter = 203
+    W, keep, X = _swiglu_inputs(inter, cols, n, m, dtype, batch, seed=100 + batch)
+    values, bits = gpu_pack(W, keep, n, m, dtype)
+    H = native.nm_spmm_swiglu(values, bits, t16(X, dtype), n, m)
+    want = oracle.swiglu_gemv(W, keep, X, dtype == "bf16")
+    assert H.shape == (batch, inter)
+    for b in range(batch):
+        assert rel_l2(f64(H[b]), want[b]) <= TOL
+
+
+SWIGLU_CFGS = [(64, 2, 0, VALU), (256, 4, 0, VALU), (128, 6, 0, VALU), (512, 2, 0, VALU),
+               (256, 2, 0, MFMA), (128, 3, 0, MFMA), (64, 2, 0, MFMA)]
+
+
+@pytest.mark.parametrize("cfg", SWIGLU_CFGS)
+@pytest.mark.parametrize("batch", [1, 3, 8])
+@pytest.mark.parametrize("n,m", [(2, 4), (16, 32)])
+def test_swiglu_epilogue_matches_separate_product(cfg, batch, n, m):
+    """The epilogue equals silu(gate) * up applied on the host to the fp32
+    sums of the same kernel without it (integer inputs: the sums are exact, so
+    only the fp32 silu differs, within a few ulp), for ragged pair counts."""
+    inter, cols = 77, 4160
+    W = synth.integer_weights(2 * inter, cols, seed=110)
+    keep = synth.random_mask(2 * inter, cols, n, m, seed=111)
+    xi = np.random.default_rng(112).integers(-2, 3, size=(batch, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    values, bits = gpu_pack(W, keep, n, m, "f16")
+    Y = f64(native.nm_spmm_small(values, bits, t16(X, "f16"), n, m, cfg=cfg))
+    assert np.array_equal(Y, oracle.masked_gemv(W, keep, X, False))
+    H = f64(native.nm_spmm_swiglu(values, bits, t16(X, "f16"), n, m, cfg=cfg))
+    g = Y[:, 0::2].astype(np.float32)
+    u = Y[:, 1::2].astype(np.float32)
+    with np.errstate(over="ignore"):  # exp(-g) = inf for very negative g: silu -> -0
+        want = (g / (np.float32(1) + np.exp(-g))) * u
+    assert np.allclose(H, want, rtol=1e-5, atol=1e-6 * np.abs(want).max())
+
+
+def test_swiglu_16bit_output_is_rounded_fp32():
+    inter, cols = 150, 2112
+    for dtype in ("f16", "bf16"):
+        for batch in (1, 4):
+            W, keep, X = _swiglu_inputs(inter, cols, 2, 4, dtype, batch, seed=120)
+            values, bits = gpu_pack(W, keep, 2, 4, dtype)
+            H32 = native.nm_spmm_swiglu(values, bits, t16(X, dtype), 2, 4)
+            H16 = native.nm_spmm_swiglu(values, bits, t16(X, dtype), 2, 4, out_dtype=TDT[dtype])
+            assert np.array_equal(u16(H16), round16_f64(f64(H32), dtype)), (dtype, batch)
+
+
+def test_swiglu_rejects_shapes_it_cannot_run():
+    inter, cols = 32, 2112
+    W, keep, X = _swiglu_inputs(inter, cols, 4, 8, "f16", 2, seed=130)
+    values, bits = gpu_pack(W, keep, 4, 8, "f16")
+    with pytest.raises(native.NMError) as e:  # odd rows per wave: pairs would straddle waves
+        native.nm_spmm_swiglu(values, bits, t16(X, "f16"), 4, 8, cfg=(256, 3, 0, VALU))
+    assert e.value.status == native.NM_ERR_INVALID_ARG
+    with pytest.raises(native.NMError) as e:  # K walked in LDS segments: no epilogue there
+        native.nm_spmm_swiglu(values, bits, t16(X, "f16"), 4, 8, cfg=(256, 2, 512, VALU))
+    assert e.value.status == native.NM_ERR_UNSUPPORTED
+
+
+def test_swiglu_zero_columns():
+    for batch in (1, 6):
+        values = torch.empty((8, 0), dtype=torch.float16, device=DEV)
+        bits = torch.empty((8, 0), dtype=torch.int32, device=DEV)
+        X = torch.empty((batch, 0), dtype=torch.float16, device=DEV)
+        H = torch.full((batch, 4), 3.0, device=DEV)
+        native.nm_spmm_swiglu(values, bits, X, 2, 4, out=H)
+        assert torch.count_nonzero(H).item() == 0

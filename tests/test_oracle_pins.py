@@ -8,6 +8,7 @@ fails at least one of them.
 
 import itertools
 import json
+import math
 import os
 
 import numpy as np
@@ -253,3 +254,50 @@ def test_masked_gemv_empty_cols_is_zero():
     x = np.zeros((1, 0), dtype=np.uint16)
     y = oracle.masked_gemv(W, np.zeros((3, 0), np.uint8), x, False)
     assert np.array_equal(y, np.zeros((1, 3)))
+
+
+# ---- silu(gate) * up around the product -------------------------------------------
+
+def test_silu_closed_forms():
+    """silu(z) = z * sigmoid(z): 0 at 0, sigmoid(1) = e / (1 + e) at 1, and
+    z itself (to fp64 precision) for large z."""
+    h = oracle.silu_mul(np.array([0.0, 1.0, 40.0, -40.0]), np.ones(4))
+    assert h[0] == 0.0
+    assert abs(h[1] - math.e / (1.0 + math.e)) <= 1e-16
+    assert h[2] == 40.0
+    assert abs(h[3]) < 1e-15 and h[3] < 0
+
+
+def test_silu_odd_part_is_identity():
+    """silu(z) - silu(-z) = z (sigmoid(z) + sigmoid(-z) = 1): catches a wrong
+    sign in the exponent or a swapped operand."""
+    z = np.random.default_rng(3).normal(0.0, 4.0, size=1000)
+    d = oracle.silu_mul(z, np.ones_like(z)) - oracle.silu_mul(-z, np.ones_like(z))
+    assert np.allclose(d, z, rtol=1e-13, atol=1e-13)
+
+
+def test_silu_mul_is_linear_in_up():
+    rng = np.random.default_rng(4)
+    g, u = rng.normal(size=200), rng.normal(size=200)
+    assert np.allclose(oracle.silu_mul(g, u), oracle.silu_mul(g, np.ones_like(g)) * u,
+                       rtol=1e-15, atol=0)
+
+
+def test_swiglu_gemv_matches_brute_force():
+    """Tiny row-interleaved gate/up matrix, small integers: pure-Python sums
+    and math.exp against the oracle."""
+    rng = np.random.default_rng(5)
+    rows, cols, batch = 6, 32, 2
+    W = synth.f32_to_16_bits(rng.integers(-3, 4, size=(rows, cols)).astype(np.float32), "f16")
+    keep = synth.random_mask(rows, cols, 2, 4, seed=6)
+    X = synth.f32_to_16_bits(rng.integers(-3, 4, size=(batch, cols)).astype(np.float32), "f16")
+    Wf = W.view(np.float16).astype(float)
+    Xf = X.view(np.float16).astype(float)
+    got = oracle.swiglu_gemv(W, keep, X, False)
+    assert got.shape == (batch, rows // 2)
+    for b in range(batch):
+        for r in range(rows // 2):
+            g = sum(Wf[2 * r, c] * Xf[b, c] for c in range(cols) if keep[2 * r, c])
+            u = sum(Wf[2 * r + 1, c] * Xf[b, c] for c in range(cols) if keep[2 * r + 1, c])
+            want = g / (1.0 + math.exp(-g)) * u
+            assert abs(got[b, r] - want) <= 1e-12 * max(1.0, abs(want))
