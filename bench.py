@@ -315,6 +315,18 @@ def shapes_run(cfg_id, args):
     return rows_out
 
 
+def pack_gpu(W, n, m):
+    """nm_pack of a GPU fp16 matrix under the top-n |w| of every m mask
+    (ties to the lower column), the mask drawn on the GPU."""
+    rows, cols = W.shape
+    mag = W.abs().view(rows, cols // m, m).float()
+    pos = torch.arange(m, device=DEV, dtype=torch.float32) * 1e-9
+    idx = (mag - pos).topk(n, dim=-1).indices
+    keep = torch.zeros((rows, cols // m, m), dtype=torch.uint8, device=DEV)
+    keep.scatter_(-1, idx, 1)
+    return native.nm_pack(W, keep.view(rows, cols), n, m)
+
+
 def gpu_layer(rows, cols, n, m, seed, want_dense):
     """A seeded synthetic matrix drawn on the GPU (timing only: the kernels'
     time does not depend on the values): W = fp16(0.02 z), the n largest |w|
@@ -322,14 +334,113 @@ def gpu_layer(rows, cols, n, m, seed, want_dense):
     g = torch.Generator(device=DEV)
     g.manual_seed(seed)
     W = (torch.randn((rows, cols), device=DEV, generator=g) * 0.02).half()
-    mag = W.abs().view(rows, cols // m, m).float()
-    pos = torch.arange(m, device=DEV, dtype=torch.float32) * 1e-9  # ties to the lower column
-    idx = (mag - pos).topk(n, dim=-1).indices
-    keep = torch.zeros((rows, cols // m, m), dtype=torch.uint8, device=DEV)
-    keep.scatter_(-1, idx, 1)
-    values, bits = native.nm_pack(W, keep.view(rows, cols), n, m)
-    del keep, mag, idx
+    values, bits = pack_gpu(W, n, m)
     return values, bits, (W if want_dense else None)
+
+
+def fused_layer_run(args):
+    """The decode-layer step with the gate/up activation: one Llama-3.1-8B
+    layer's products, 2:4 fp16, three ways, each step one HIP graph over one
+    of five resident layers (1.2 GB packed, beyond the 256 MB Infinity Cache):
+      - sparse fused (4 launches): q|k|v row-concatenated into one 6144x4096
+        product, o, gate/up interleaved into one 28672x4096 product with the
+        SwiGLU epilogue (nm_spmm_swiglu, 16-bit h), down on h;
+      - sparse unfused (7 launches + torch silu * mul): the projections one by
+        one, as in the headline step;
+      - dense (torch linear, hipBLASLt): q|k|v and gate|up concatenated, torch
+        silu * mul, down."""
+    L = native.lib()
+    NL = 5
+    hid, inter = 4096, 14336
+    mats = []
+    t0 = time.time()
+    for layer in range(NL):
+        g = torch.Generator(device=DEV)
+        g.manual_seed(7000 + layer)
+        W = {name: (torch.randn((r, c), device=DEV, generator=g) * 0.02).half()
+             for name, r, c in workloads.LLAMA8B_LAYER}
+        qkv = torch.cat([W["q"], W["k"], W["v"]])
+        gu = torch.empty((2 * inter, hid), dtype=torch.float16, device=DEV)
+        gu[0::2] = W["gate"]
+        gu[1::2] = W["up"]
+        d = {"qkv": pack_gpu(qkv, 2, 4), "gu": pack_gpu(gu, 2, 4)}
+        for name in W:
+            d[name] = pack_gpu(W[name], 2, 4)
+        if not args.no_dense:
+            d["dense_qkv"] = qkv
+            d["dense_o"] = W["o"]
+            d["dense_gu"] = torch.cat([W["gate"], W["up"]])
+            d["dense_down"] = W["down"]
+        del W, gu
+        mats.append(d)
+    torch.cuda.synchronize()
+    log(f"  {NL} layers resident ({time.time() - t0:.1f}s)")
+    F16, F32 = native.NM_F16, native.NM_F32
+
+    def spmm(v, bt, X, Y, B, rows, cols, out_dt=F32):
+        st = L.nm_spmm_small(v.data_ptr(), bt.data_ptr(), X.data_ptr(), Y.data_ptr(), B, rows, cols,
+                             2, 4, F16, out_dt, torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
+
+    out = {}
+    for B in (1, 4, 8):
+        x = torch.randn((B, hid), device=DEV).half()
+        xa = torch.randn((B, hid), device=DEV).half()
+        h16 = torch.empty((B, inter), dtype=torch.float16, device=DEV)
+        y_qkv = torch.empty((B, 6144), device=DEV)
+        y = {r: torch.empty((B, r), device=DEV) for r in (1024, 4096, 14336)}
+        yg = torch.empty((B, inter), device=DEV)
+        yu = torch.empty((B, inter), device=DEV)
+
+        def fused(d):
+            spmm(*d["qkv"], x, y_qkv, B, 6144, hid)
+            spmm(*d["o"], xa, y[4096], B, hid, hid)
+            st = L.nm_spmm_swiglu(d["gu"][0].data_ptr(), d["gu"][1].data_ptr(), x.data_ptr(),
+                                  h16.data_ptr(), B, inter, hid, 2, 4, F16, F16,
+                                  torch.cuda.current_stream().cuda_stream)
+            assert st == 0, st
+            spmm(*d["down"], h16, y[4096], B, hid, inter)
+
+        def unfused(d):
+            for name, r in (("q", 4096), ("k", 1024), ("v", 1024)):
+                spmm(*d[name], x, y[r], B, r, hid)
+            spmm(*d["o"], xa, y[4096], B, hid, hid)
+            spmm(*d["gate"], x, yg, B, inter, hid)
+            spmm(*d["up"], x, yu, B, inter, hid)
+            h16.copy_(torch.nn.functional.silu(yg) * yu)
+            spmm(*d["down"], h16, y[4096], B, hid, inter)
+
+        def dense(d):
+            F = torch.nn.functional
+            F.linear(x, d["dense_qkv"])
+            F.linear(xa, d["dense_o"])
+            gu = F.linear(x, d["dense_gu"])
+            h = F.silu(gu[:, :inter]) * gu[:, inter:]
+            F.linear(h, d["dense_down"])
+
+        res = {}
+        for kind, fn in (("sparse_fused", fused), ("sparse_unfused", unfused), ("torch_dense", dense)):
+            if kind == "torch_dense" and args.no_dense:
+                continue
+            graphs = [capture(lambda d=d, fn=fn: fn(d)) for d in mats]
+            ms = time_steps(graphs, args.steps, args.warmup)
+            res[kind] = {"ms_per_step": round(ms, 5), "launches": {"sparse_fused": 4,
+                         "sparse_unfused": 8, "torch_dense": 5}[kind]}
+            del graphs
+        sb = sum(workloads.sparse_bytes(r, c, 2, 4, B, 4) for _, r, c in workloads.LLAMA8B_LAYER)
+        res["sparse_bytes_per_step"] = sb
+        res["fused_GB/s"] = round(sb / (res["sparse_fused"]["ms_per_step"] * 1e-3) / 1e9, 1)
+        res["fused_vs_unfused"] = round(res["sparse_unfused"]["ms_per_step"]
+                                        / res["sparse_fused"]["ms_per_step"], 3)
+        if "torch_dense" in res:
+            res["fused_vs_torch_dense"] = round(res["torch_dense"]["ms_per_step"]
+                                                / res["sparse_fused"]["ms_per_step"], 3)
+        out[f"batch{B}"] = res
+        log(f"  batch {B}: " + ", ".join(f"{k} {v['ms_per_step'] * 1e3:.1f} us" for k, v in res.items()
+                                         if isinstance(v, dict))
+            + f"; fused {res['fused_GB/s']} GB/s, {res['fused_vs_unfused']}x unfused"
+            + (f", {res['fused_vs_torch_dense']}x torch dense" if "torch_dense" in res else ""))
+    return out
 
 
 def decode_run(args):
@@ -399,11 +510,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch4", action="store_true")
     ap.add_argument("--workload", default="llama8b-layer",
-                    choices=["llama8b-layer", "single", "patterns", "70b-qwen", "decode-32-layers"],
+                    choices=["llama8b-layer", "single", "patterns", "70b-qwen", "decode-32-layers",
+                             "llama8b-layer-fused"],
                     help="llama8b-layer (default, the headline line): one Llama-3.1-8B layer; "
                          "single: the 4096x4096 matrix; patterns: 4:8/8:16/16:32 bf16 on the 8B "
                          "shapes; 70b-qwen: Llama-3.3-70B and Qwen3-32B shapes; "
-                         "decode-32-layers: 32 stacked 8B layers timed per token")
+                         "decode-32-layers: 32 stacked 8B layers timed per token; "
+                         "llama8b-layer-fused: the 8B layer step with q|k|v and gate/up fused "
+                         "(SwiGLU epilogue) against the unfused and dense steps")
     ap.add_argument("--counters", action="store_true",
                     help="short eager run for rocprofv3 --pmc: the 14336x4096 sparse kernel on "
                          "5 cache-cold copies, then 5 plain copies of 64 MiB (the known-size "
@@ -423,6 +537,13 @@ def main():
 
     if args.counters:
         counters_run()
+        return
+    if args.workload == "llama8b-layer-fused":
+        log("workload llama8b-layer-fused")
+        body = {"per_step": fused_layer_run(args)}
+        print(json.dumps({"metric": "decode-layer step time, fused vs unfused sparse and dense",
+                          "workload": args.workload, "n_gpus": 1, "data": "synthetic",
+                          "unit": "ms/step", **body}), flush=True)
         return
     if args.workload != "llama8b-layer":
         cfg_id = {"single": 1, "patterns": 3, "70b-qwen": 4, "decode-32-layers": 5}[args.workload]
