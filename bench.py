@@ -447,7 +447,9 @@ def decode_run(args):
     """Workload 5: 32 stacked Llama-3.1-8B-shaped layers (224 matrices, 2:4
     fp16, a different seed per matrix), all resident; one token = the 224
     products chained in one HIP graph, at batch 1, 2, 4 and 8, against the
-    dense fp16 chain (nm_dense_gemv and torch linear)."""
+    dense fp16 chain (nm_dense_gemv and torch linear).  Beside it, the same
+    weights as 32 fused layer steps (q|k|v concatenated, gate/up with the
+    SwiGLU epilogue, 128 launches per token)."""
     want_dense = not args.no_dense
     mats = [mt for mt, _ in workloads.config_matrices(5)]
     t0 = time.time()
@@ -458,6 +460,24 @@ def decode_run(args):
     torch.cuda.synchronize()
     log(f"  224 matrices resident ({time.time() - t0:.1f}s): "
         f"{sum(v.numel() * 2 + b.numel() * 4 for _, v, b, _ in store) / 1e9:.2f} GB packed")
+    # the same weights fused per layer: q|k|v row-concatenated, gate/up
+    # row-interleaved for the SwiGLU epilogue (redrawn from the same seeds)
+    fused = []
+    for layer in range(32):
+        lm = {mt.name: mt for mt in mats[7 * layer:7 * layer + 7]}
+        def redraw(mt):
+            g = torch.Generator(device=DEV)
+            g.manual_seed(mt.seed)
+            return (torch.randn((mt.rows, mt.cols), device=DEV, generator=g) * 0.02).half()
+        qkv = torch.cat([redraw(lm["q"]), redraw(lm["k"]), redraw(lm["v"])])
+        gu = torch.empty((2 * 14336, 4096), dtype=torch.float16, device=DEV)
+        gu[0::2] = redraw(lm["gate"])
+        gu[1::2] = redraw(lm["up"])
+        fused.append({"qkv": pack_gpu(qkv, 2, 4), "gu": pack_gpu(gu, 2, 4),
+                      "o": [(v, bt) for mt, v, bt, _ in store if mt is lm["o"]][0],
+                      "down": [(v, bt) for mt, v, bt, _ in store if mt is lm["down"]][0]})
+        del qkv, gu
+    torch.cuda.synchronize()
     L = native.lib()
     out = {}
     for B in (1, 2, 4, 8):
@@ -479,12 +499,30 @@ def decode_run(args):
         def torch_token():
             for mt, _, _, W in store:
                 torch.nn.functional.linear(X[mt.cols], W)
+        Yqkv = torch.empty((B, 6144), device=DEV)
+        H16 = torch.empty((B, 14336), dtype=torch.float16, device=DEV)
+        def fused_token():
+            st_ = torch.cuda.current_stream().cuda_stream
+            for d in fused:
+                for (v, bt), Xin, Yout, rows, cols in ((d["qkv"], X[4096], Yqkv, 6144, 4096),
+                                                       (d["o"], X[4096], Y[4096], 4096, 4096)):
+                    st = L.nm_spmm_small(v.data_ptr(), bt.data_ptr(), Xin.data_ptr(), Yout.data_ptr(),
+                                         B, rows, cols, 2, 4, native.NM_F16, native.NM_F32, st_)
+                    assert st == 0, st
+                st = L.nm_spmm_swiglu(d["gu"][0].data_ptr(), d["gu"][1].data_ptr(), X[4096].data_ptr(),
+                                      H16.data_ptr(), B, 14336, 4096, 2, 4, native.NM_F16,
+                                      native.NM_F16, st_)
+                assert st == 0, st
+                v, bt = d["down"]
+                st = L.nm_spmm_small(v.data_ptr(), bt.data_ptr(), H16.data_ptr(), Y[4096].data_ptr(),
+                                     B, 4096, 14336, 2, 4, native.NM_F16, native.NM_F32, st_)
+                assert st == 0, st
         sbytes = sum(workloads.sparse_bytes(mt.rows, mt.cols, mt.n, mt.m, B, 4) for mt, *_ in store)
         dbytes = sum(workloads.dense_bytes(mt.rows, mt.cols, B, 4) for mt, *_ in store)
         res = {}
-        for kind, fn, nbytes in (("sparse", sparse_token, sbytes), ("dense", dense_token, dbytes),
-                                 ("torch_linear", torch_token, dbytes)):
-            if kind != "sparse" and not want_dense:
+        for kind, fn, nbytes in (("sparse", sparse_token, sbytes), ("sparse_fused", fused_token, sbytes),
+                                 ("dense", dense_token, dbytes), ("torch_linear", torch_token, dbytes)):
+            if kind in ("dense", "torch_linear") and not want_dense:
                 continue
             g = capture(fn)
             ms = time_steps([g], args.steps, args.warmup)
