@@ -154,6 +154,27 @@ int nm_spmm_swiglu(const void *values, const uint32_t *bits, const void *X,
                    void *H, int batch, int64_t inter, int64_t cols, int n, int m,
                    nm_dtype in_dt, nm_dtype out_dt, void *stream);
 
+/* Calibration side: accumulate the Hessian of the layer-wise reconstruction
+ * objective (Method, OBS paragraph: H = 2 X X^T, shared by all rows; the
+ * decode-time calibration paragraph: X's columns are the layer's input
+ * activations at the decode steps of the dense model, prefill excluded):
+ *   H[i][j] += scale * sum_{t < ntok} X[i][t] * X[j][t],  i, j < d.
+ *   H: device, d x d fp32 row-major, updated in place (both triangles, so
+ *      it stays symmetric); 4-byte aligned.
+ *   X: device, d x ld 16-bit (in_dt = NM_F16 or NM_BF16) row-major, i.e.
+ *      feature-major: column t is the activation of step t; only the first
+ *      ntok columns are read.  ld % 8 == 0 (else NM_ERR_SHAPE), 16-byte
+ *      aligned.
+ *   scale: 2 gives the pages' H; calls with successive batches of columns
+ *      accumulate H over the decode steps.
+ * Products of 16-bit values are exact in fp32; sums are fp32 (matrix cores).
+ * Errors: NM_ERR_INVALID_ARG (negative sizes, ld < ntok, d > 23170 or
+ * d * ld > 2^31 - 1, NULL pointers), NM_ERR_UNSUPPORTED (in_dt),
+ * NM_ERR_ALIGN.  d == 0 or ntok == 0 does nothing.  Asynchronous on stream.
+ * Concurrent calls on the same H race. */
+int nm_hessian_accumulate(float *H, const void *X, int64_t d, int64_t ntok,
+                          int64_t ld, nm_dtype in_dt, float scale, void *stream);
+
 /* Dense comparison, the decode GEMV the sparse kernel replaces (Experiments,
  * Table 3 paragraph: speedups are against the dense model's decode):
  *   Y[b][r] = sum over all c of W[r][c] * X[b][c],  1 <= batch <= 8.

@@ -18,6 +18,10 @@ Functions and the passages they follow (SparseDecoding, arXiv 2610.12327):
   ("Method", "Decoding is dominated by SpMV operations").
 * :func:`decode16` -- binary16 / bfloat16 bit patterns to float64 from the
   format definitions.
+* :func:`hessian` -- H = scale * X X^T over the first ntok columns of a
+  feature-major X (column t = the layer's input at decode step t): the
+  Hessian H = 2 X X^T of the layer-wise objective ("Method", OBS paragraph
+  and the decode-time calibration paragraph), a plain triple loop in fp64.
 * :func:`silu_mul` / :func:`swiglu_gemv` -- silu(gate) * up on the masked
   products of a row-interleaved gate/up matrix, the MLP step of the Llama and
   Qwen decoder layers whose end-to-end decoding the pages time ("Experiments",
@@ -83,6 +87,8 @@ def _load():
     lib.oracle_masked_gemv_f64.restype = None
     lib.oracle_silu_mul_f64.argtypes = [p, p, i64, p]
     lib.oracle_silu_mul_f64.restype = None
+    lib.oracle_hessian_f64.argtypes = [p, ci, i64, i64, i64, ctypes.c_double, ci, p]
+    lib.oracle_hessian_f64.restype = None
     _lib = lib
     return lib
 
@@ -198,3 +204,19 @@ def swiglu_gemv(W, keep, x, is_bf16: bool, threads: int = 1) -> np.ndarray:
         raise ValueError("W must hold (gate, up) row pairs")
     y = masked_gemv(W, keep, x, is_bf16, threads=threads)
     return silu_mul(y[..., 0::2], y[..., 1::2])
+
+
+def hessian(X, ntok=None, scale: float = 2.0, is_bf16: bool = False, threads: int = 1) -> np.ndarray:
+    """fp64 H[i, j] = scale * sum_{t < ntok} X[i, t] X[j, t] for the d x ld
+    16-bit pattern array X (feature-major)."""
+    xb = _bits16(X)
+    if xb.ndim != 2:
+        raise ValueError("X must be 2-D (d, ld)")
+    d, ld = xb.shape
+    ntok = ld if ntok is None else int(ntok)
+    if not 0 <= ntok <= ld:
+        raise ValueError("ntok must be in [0, ld]")
+    H = np.zeros((d, d), dtype=np.float64)
+    _load().oracle_hessian_f64(_ptr(xb), int(bool(is_bf16)), d, ntok, ld, float(scale),
+                               int(threads), _ptr(H))
+    return H

@@ -202,3 +202,22 @@ void oracle_masked_gemv_f64(const uint16_t *W, const uint8_t *keep, int is_bf16,
 void oracle_silu_mul_f64(const double *g, const double *u, int64_t n, double *h) {
     for (int64_t i = 0; i < n; ++i) h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
 }
+
+/* ---- the calibration side: the layer Hessian -------------------------------- */
+
+/* H[i][j] = scale * sum_{t < ntok} x[i][t] * x[j][t] in double, i, j < d, where
+ * X is d x ld 16-bit patterns (feature-major: column t is one decode-step
+ * activation) and H is d x d row-major.  With scale = 2 this is H = 2 X X^T
+ * of the layer-wise reconstruction objective, over the first ntok columns. */
+void oracle_hessian_f64(const uint16_t *X, int is_bf16, int64_t d, int64_t ntok, int64_t ld,
+                        double scale, int threads, double *H) {
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+    for (int64_t i = 0; i < d; ++i) {
+        for (int64_t j = 0; j < d; ++j) {
+            double s = 0.0;
+            for (int64_t t = 0; t < ntok; ++t)
+                s += decode16(X[i * ld + t], is_bf16) * decode16(X[j * ld + t], is_bf16);
+            H[i * d + j] = scale * s;
+        }
+    }
+}

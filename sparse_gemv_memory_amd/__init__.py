@@ -14,6 +14,7 @@ from .native import (  # noqa: F401
     LaunchCfg,
     nm_default_launch,
     nm_dense_gemv,
+    nm_hessian_accumulate,
     nm_pack,
     nm_packed_bytes,
     nm_spmm_small,

@@ -931,6 +931,124 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Calibration side: H += scale * X X^T (the Hessian of the layer-wise
+// reconstruction objective, H = 2 X X^T, with X's columns the layer's input
+// activations at the decode steps; Method, OBS paragraph and the
+// decode-time calibration paragraph).  A GEMM-shaped contraction over
+// tokens, so it runs on the dense matrix cores: X is feature-major (row i =
+// feature i over the tokens), so a 16x16x32 operand lane reads 8 consecutive
+// tokens of one feature, A and B alike.  Each workgroup owns a 128 x 128
+// tile of H in the upper triangle and also writes its mirror; 32-token
+// chunks of the two 128-feature row blocks are staged in LDS (rows padded to
+// 80 bytes, so a 16-lane read hits distinct banks), double-buffered with one
+// barrier per chunk; H is read, added to and written once per call (each
+// element belongs to exactly one workgroup, so there are no atomics).
+
+constexpr int kHTile = 128;     // H tile edge
+constexpr int kHChunk = 32;     // tokens per staged chunk
+constexpr int kHRow = 80;       // LDS bytes per staged feature row (64 + 16 pad)
+constexpr int kHBuf = 2 * kHTile * kHRow;  // one buffer: the i and the j row blocks
+
+template <bool BF>
+__global__ __launch_bounds__(256) void nm_hessian_kernel(float *__restrict__ H,
+                                                         const uint16_t *__restrict__ X, int d,
+                                                         int ntok, int ldx, float scale, int T) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kHBuf];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, q = lane >> 4;
+  // upper-triangle tile (ti <= tj) of this workgroup, row by row
+  int p = blockIdx.x, ti = 0;
+  while (p >= T - ti) { p -= T - ti; ++ti; }
+  const int tj = ti + p;
+  const int i0 = ti * kHTile, j0 = tj * kHTile;
+
+  // staging: piece s of this thread = row (tid + 256 s) / 4 of the i block
+  // (s = 0, 1) or of the j block (s = 2, 3), 16-byte chunk (tid & 3)
+  u32x4_t stg[4];
+  auto load_chunk = [&](int t0) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int piece = tid + 256 * (s & 1);
+      const int row = piece >> 2, c = piece & 3;
+      const int f = ((s >> 1) ? j0 : i0) + row;
+      const int t = t0 + 8 * c;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (f < d && t < ntok) {
+        v = *reinterpret_cast<const u32x4_t *>(X + (int64_t)f * ldx + t);
+        const int left = ntok - t;  // tokens beyond ntok contribute nothing
+        if (left < 8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (2 * e >= left) v[e] = 0u;
+            else if (2 * e + 1 >= left) v[e] &= 0xffffu;
+          }
+        }
+      }
+      stg[s] = v;
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int piece = tid + 256 * (s & 1);
+      const int row = piece >> 2, c = piece & 3;
+      *(__attribute__((address_space(3))) u32x4_t *)(size_t)(
+          (uint32_t)(size_t)(lds_ptr)lds + buf * kHBuf + (s >> 1) * kHTile * kHRow + row * kHRow +
+          16 * c) = stg[s];
+    }
+  };
+
+  const int wi = w & 1, wj = w >> 1;  // this wave's 64 x 64 quarter of the tile
+  f4v_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = (f4v_t){0.f, 0.f, 0.f, 0.f};
+
+  const int nchunks = (ntok + kHChunk - 1) / kHChunk;
+  if (nchunks > 0) load_chunk(0);
+  for (int k = 0; k < nchunks; ++k) {
+    const int buf = k & 1;
+    store_chunk(buf);
+    __syncthreads();  // chunk k is in LDS; every wave is done with chunk k - 1
+    if (k + 1 < nchunks) load_chunk((k + 1) * kHChunk);
+    const uint32_t base = (uint32_t)(size_t)(lds_ptr)lds + buf * kHBuf;
+    u32x4_t av[4], bv[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      av[a] = ld<u32x4_t>((lds_ptr)(size_t)(base + (64 * wi + 16 * a + n) * kHRow + 16 * q));
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      bv[b] = ld<u32x4_t>((lds_ptr)(size_t)(base + kHTile * kHRow +
+                                            (64 * wj + 16 * b + n) * kHRow + 16 * q));
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = dmfma<BF>(av[a], bv[b], acc[a][b]);
+  }
+
+  // H[i][j] += scale * acc (lane: rows 4q..4q+3, column n of each 16 x 16),
+  // and the mirror H[j][i] for tiles off the diagonal
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int ib = i0 + 64 * wi + 16 * a + 4 * q;
+      const int j = j0 + 64 * wj + 16 * b + n;
+      if (j >= d) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (ib + r < d) H[(int64_t)(ib + r) * d + j] += scale * acc[a][b][r];
+      if (ti != tj) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (ib + r < d) H[(int64_t)j * d + ib + r] += scale * acc[a][b][r];
+      }
+    }
+}
+
 // Dense comparison when x fits the LDS budget, built like the sparse row
 // kernel so that the speedup is measured against an equally tuned dense
 // GEMV: x staged once per workgroup as BP contiguous rows; each wave walks
@@ -1776,6 +1894,25 @@ int nm_spmm_swiglu_cfg(const void *values, const uint32_t *bits, const void *X, 
   if (inter < 0 || inter > INT32_MAX / 2) return NM_ERR_INVALID_ARG;
   return sparse_product(values, bits, X, H, batch, 2 * inter, cols, n, m, in_dt, out_dt, cfg,
                         stream, kEpiSwiglu);
+}
+
+int nm_hessian_accumulate(float *H, const void *X, int64_t d, int64_t ntok, int64_t ld,
+                          nm_dtype in_dt, float scale, void *stream) {
+  if (d < 0 || ntok < 0 || ld < ntok) return NM_ERR_INVALID_ARG;
+  if (d > 23170 || d * ld > INT32_MAX) return NM_ERR_INVALID_ARG;  // 32-bit tile and row offsets
+  if (!is16(in_dt)) return NM_ERR_UNSUPPORTED;
+  if (ld % 8 != 0) return NM_ERR_SHAPE;
+  if (d == 0) return NM_OK;
+  if (!H || (!X && ntok > 0)) return NM_ERR_INVALID_ARG;
+  if (!aligned(H, 4) || !aligned(X, 16)) return NM_ERR_ALIGN;
+  if (ntok == 0) return NM_OK;
+  const int T = (int)((d + kHTile - 1) / kHTile);
+  const int64_t grid = (int64_t)T * (T + 1) / 2;
+  auto fn = in_dt == NM_BF16 ? nm_hessian_kernel<true> : nm_hessian_kernel<false>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, H,
+                     (const uint16_t *)X, (int)d, (int)ntok, (int)ld, scale, T);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NM_OK : hip_fail(e);
 }
 
 int nm_default_launch(int64_t rows, int64_t cols, int batch, int n, int m, int dense,

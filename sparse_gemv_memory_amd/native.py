@@ -94,6 +94,8 @@ def lib():
     L.nm_spmm_swiglu_cfg.argtypes = [p, p, p, p, ci, i64, i64, ci, ci, ci, ci,
                                      ctypes.POINTER(LaunchCfg), p]
     L.nm_spmm_swiglu_cfg.restype = ci
+    L.nm_hessian_accumulate.argtypes = [p, p, i64, i64, i64, ci, ctypes.c_float, p]
+    L.nm_hessian_accumulate.restype = ci
     L.nm_dense_gemv.argtypes = [p, p, p, ci, i64, i64, ci, ci, p]
     L.nm_dense_gemv.restype = ci
     L.nm_dense_gemv_cfg.argtypes = [p, p, p, ci, i64, i64, ci, ci, ctypes.POINTER(LaunchCfg), p]
@@ -238,6 +240,23 @@ def nm_spmm_swiglu(values, bits, X, n: int, m: int, out_dtype=torch.float32, out
                                       _dev(H, "H"), batch, inter, cols, n, m, _in_dt(X),
                                       _DT[out_dtype], _cfg_ptr(cfg), _stream(values.device))
     _check(st, "nm_spmm_swiglu")
+    return H
+
+
+def nm_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, ntok: Optional[int] = None,
+                          scale: float = 2.0) -> torch.Tensor:
+    """H += scale * X[:, :ntok] @ X[:, :ntok]^T in place (H: (d, d) fp32; X:
+    (d, ld) fp16/bf16, feature-major: column t is one decode-step activation)."""
+    if H.dtype != torch.float32 or H.dim() != 2 or H.shape[0] != H.shape[1]:
+        raise ValueError("H must be a square float32 matrix")
+    if X.dim() != 2 or X.shape[0] != H.shape[0]:
+        raise ValueError("X must be (d, ld) with d = H's size")
+    d, ld = X.shape
+    ntok = ld if ntok is None else ntok
+    with torch.cuda.device(H.device):
+        st = lib().nm_hessian_accumulate(_dev(H, "H"), _dev(X, "X"), d, ntok, ld, _in_dt(X),
+                                         float(scale), _stream(H.device))
+    _check(st, "nm_hessian_accumulate")
     return H
 
 

@@ -140,6 +140,23 @@ def test_swiglu_rejects_bad_arguments(L):
     assert _swiglu(L, values=None, bits=None, h=None, inter=0) == OK  # nothing to compute
 
 
+def test_hessian_rejects_bad_arguments(L):
+    def h(H=P, X=P, d=64, ntok=16, ld=16, i=F16):
+        return L.nm_hessian_accumulate(H, X, d, ntok, ld, i, 2.0, None)
+    assert h(d=-1) == INV
+    assert h(ntok=-1) == INV
+    assert h(ntok=24, ld=16) == INV  # ld < ntok
+    assert h(d=23171) == INV
+    assert h(ld=12, ntok=12) == SHAPE
+    assert h(i=F32) == UNSUP
+    assert h(H=None) == INV
+    assert h(X=None) == INV
+    assert h(H=P + 2) == ALIGN
+    assert h(X=P + 8) == ALIGN
+    assert h(H=None, X=None, d=0) == OK  # nothing to do
+    assert h(X=None, ntok=0) == OK
+
+
 def test_dense_rejects_bad_arguments(L):
     assert L.nm_dense_gemv(P, P, P, 0, 8, 64, F16, F32, None) == INV
     assert L.nm_dense_gemv(P, P, P, 9, 8, 64, F16, F32, None) == INV

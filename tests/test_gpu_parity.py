@@ -585,3 +585,61 @@ def test_swiglu_zero_columns():
         H = torch.full((batch, 4), 3.0, device=DEV)
         native.nm_spmm_swiglu(values, bits, X, 2, 4, out=H)
         assert torch.count_nonzero(H).item() == 0
+
+
+# ---- the layer Hessian (calibration side) ------------------------------------------
+
+def _hx(d, ld, seed, dtype="f16", ints=True):
+    rng = np.random.default_rng(seed)
+    xf = rng.integers(-3, 4, size=(d, ld)) if ints else rng.normal(size=(d, ld))
+    return synth.f32_to_16_bits(xf.astype(np.float32), dtype)
+
+
+@pytest.mark.parametrize("d", [1, 16, 100, 128, 129, 300])
+@pytest.mark.parametrize("ntok", [1, 7, 8, 31, 32, 33, 100])
+def test_hessian_integer_exact(d, ntok):
+    """Integer activations: every sum is an exact integer in fp32, so
+    H0 + 2 X X^T must match the oracle exactly, ragged tiles, ragged token
+    chunks and columns past ntok (filled with other values) included."""
+    ld = (ntok + 7) // 8 * 8 + 8
+    X = _hx(d, ld, seed=d * 131 + ntok)
+    H0 = np.random.default_rng(d + ntok).integers(-50, 50, size=(d, d)).astype(np.float32)
+    H0 = H0 + H0.T  # a symmetric start
+    H = torch.from_numpy(H0).to(DEV)
+    native.nm_hessian_accumulate(H, t16(X, "f16"), ntok=ntok, scale=2.0)
+    want = H0.astype(np.float64) + oracle.hessian(X, ntok=ntok, scale=2.0)
+    got = H.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_hessian_matches_oracle(dtype):
+    d, ntok = 520, 256
+    X = _hx(d, ntok, seed=7, dtype=dtype, ints=False)
+    H = torch.zeros((d, d), device=DEV)
+    native.nm_hessian_accumulate(H, t16(X, dtype), scale=2.0)
+    want = oracle.hessian(X, scale=2.0, is_bf16=dtype == "bf16", threads=8)
+    got = H.cpu().numpy().astype(np.float64)
+    assert rel_l2(got.ravel(), want.ravel()) <= 1e-6
+    assert np.array_equal(got, got.T)
+
+
+def test_hessian_accumulates_over_calls():
+    """Two calls over the two halves of the columns equal one call over all
+    of them (integer inputs, exact)."""
+    d, ntok = 200, 96
+    X = _hx(d, ntok, seed=9)
+    Xa, Xb = np.ascontiguousarray(X[:, :48]), np.ascontiguousarray(X[:, 48:])
+    H1 = torch.zeros((d, d), device=DEV)
+    native.nm_hessian_accumulate(H1, t16(X, "f16"))
+    H2 = torch.zeros((d, d), device=DEV)
+    native.nm_hessian_accumulate(H2, t16(Xa, "f16"))
+    native.nm_hessian_accumulate(H2, t16(Xb, "f16"))
+    assert torch.equal(H1, H2)
+
+
+def test_hessian_zero_tokens_leaves_h():
+    H = torch.full((33, 33), 1.5, device=DEV)
+    X = torch.zeros((33, 8), dtype=torch.float16, device=DEV)
+    native.nm_hessian_accumulate(H, X, ntok=0)
+    assert torch.all(H == 1.5).item()

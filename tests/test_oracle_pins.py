@@ -301,3 +301,61 @@ def test_swiglu_gemv_matches_brute_force():
             u = sum(Wf[2 * r + 1, c] * Xf[b, c] for c in range(cols) if keep[2 * r + 1, c])
             want = g / (1.0 + math.exp(-g)) * u
             assert abs(got[b, r] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+# ---- the layer Hessian -------------------------------------------------------------
+
+def _x16(a, dtype="f16"):
+    return synth.f32_to_16_bits(np.asarray(a, dtype=np.float32), dtype)
+
+
+def test_hessian_matches_brute_force():
+    rng = np.random.default_rng(21)
+    xf = rng.integers(-3, 4, size=(5, 3)).astype(np.float32)
+    H = oracle.hessian(_x16(xf), scale=2.0)
+    for i in range(5):
+        for j in range(5):
+            want = 2.0 * sum(float(xf[i, t]) * float(xf[j, t]) for t in range(3))
+            assert H[i, j] == want
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_hessian_matches_numpy_matmul(dtype):
+    rng = np.random.default_rng(22)
+    X = _x16(rng.normal(size=(40, 23)), dtype)
+    xd = oracle.decode16(X, dtype == "bf16")
+    H = oracle.hessian(X, scale=2.0, is_bf16=dtype == "bf16")
+    assert np.allclose(H, 2.0 * xd @ xd.T, rtol=1e-13, atol=1e-12)
+
+
+def test_hessian_one_hot_columns():
+    """Column t = e_{i_t}: H = scale * sum_t e_{i_t} e_{i_t}^T (counts on the
+    diagonal)."""
+    d, idx = 7, [0, 3, 3, 6]
+    xf = np.zeros((d, len(idx)), dtype=np.float32)
+    for t, i in enumerate(idx):
+        xf[i, t] = 1.0
+    H = oracle.hessian(_x16(xf), scale=2.0)
+    want = np.zeros((d, d))
+    for i in idx:
+        want[i, i] += 2.0
+    assert np.array_equal(H, want)
+
+
+def test_hessian_is_symmetric_psd_with_trace_identity():
+    rng = np.random.default_rng(23)
+    X = _x16(rng.normal(size=(30, 50)))
+    xd = oracle.decode16(X, False)
+    H = oracle.hessian(X, scale=2.0)
+    assert np.array_equal(H, H.T)
+    assert np.linalg.eigvalsh(H).min() >= -1e-9
+    assert abs(np.trace(H) - 2.0 * float((xd ** 2).sum())) <= 1e-9 * np.trace(H)
+
+
+def test_hessian_reads_only_the_first_ntok_columns():
+    rng = np.random.default_rng(24)
+    X = _x16(rng.normal(size=(9, 16)))
+    Xg = X.copy()
+    Xg[:, 11:] = _x16(rng.normal(size=(9, 5)) * 100)
+    assert np.array_equal(oracle.hessian(X, ntok=11), oracle.hessian(Xg, ntok=11))
+    assert np.array_equal(oracle.hessian(X, ntok=0), np.zeros((9, 9)))
