@@ -443,6 +443,48 @@ def fused_layer_run(args):
     return out
 
 
+def hessian_run(args):
+    """Calibration side: H += 2 X X^T for one layer input width (Llama-3.1-8B:
+    4096 for q/k/v/gate/up, 14336 for down) over batches of decode-step
+    activations.  Per call: the kernel time, the HBM rate of its H traffic
+    (read + write 8 d^2 bytes plus X) and the contraction's flop rate, beside
+    torch (hipBLASLt) doing the same update in fp32 (addmm on fp32 copies of
+    X) and with fp16 inputs (mm, then an fp32 add)."""
+    out = {}
+    for d in (4096, 14336):
+        H = torch.zeros((d, d), device=DEV)
+        for ntok in (16, 64, 256, 1024):
+            X = torch.randn((d, ntok), device=DEV).half()
+            Xf = X.float()
+            L = native.lib()
+            def ours():
+                st = L.nm_hessian_accumulate(H.data_ptr(), X.data_ptr(), d, ntok, ntok, native.NM_F16,
+                                             2.0, torch.cuda.current_stream().cuda_stream)
+                assert st == 0, st
+            def torch32():
+                torch.addmm(H, Xf, Xf.t(), alpha=2.0, out=H)
+            def torch16():
+                H.add_(torch.mm(X, X.t()), alpha=2.0)
+            res = {}
+            for kind, fn in (("nm_hessian", ours), ("torch_addmm_fp32", torch32),
+                             ("torch_mm_fp16_then_add", torch16)):
+                g = capture(fn)
+                ms = time_steps([g], max(10, args.steps // 5), 3)
+                res[kind] = round(ms * 1e3, 2)
+                del g
+            nbytes = 8 * d * d + 2 * d * ntok
+            us = res["nm_hessian"]
+            res.update({"GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, 3),
+                        "TFLOP/s": round(2.0 * d * d * ntok / (us * 1e-6) / 1e12, 1)})
+            out[f"d{d}_ntok{ntok}"] = res
+            log(f"  d={d} ntok={ntok}: " + ", ".join(f"{k} {v}" for k, v in res.items()))
+            del X, Xf
+        del H
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_run(args):
     """Workload 5: 32 stacked Llama-3.1-8B-shaped layers (224 matrices, 2:4
     fp16, a different seed per matrix), all resident; one token = the 224
@@ -549,13 +591,14 @@ def main():
     ap.add_argument("--no-batch4", action="store_true")
     ap.add_argument("--workload", default="llama8b-layer",
                     choices=["llama8b-layer", "single", "patterns", "70b-qwen", "decode-32-layers",
-                             "llama8b-layer-fused"],
+                             "llama8b-layer-fused", "calibration-hessian"],
                     help="llama8b-layer (default, the headline line): one Llama-3.1-8B layer; "
                          "single: the 4096x4096 matrix; patterns: 4:8/8:16/16:32 bf16 on the 8B "
                          "shapes; 70b-qwen: Llama-3.3-70B and Qwen3-32B shapes; "
                          "decode-32-layers: 32 stacked 8B layers timed per token; "
                          "llama8b-layer-fused: the 8B layer step with q|k|v and gate/up fused "
-                         "(SwiGLU epilogue) against the unfused and dense steps")
+                         "(SwiGLU epilogue) against the unfused and dense steps; "
+                         "calibration-hessian: H += 2 X X^T at the 8B input widths")
     ap.add_argument("--counters", action="store_true",
                     help="short eager run for rocprofv3 --pmc: the 14336x4096 sparse kernel on "
                          "5 cache-cold copies, then 5 plain copies of 64 MiB (the known-size "
@@ -582,6 +625,13 @@ def main():
         print(json.dumps({"metric": "decode-layer step time, fused vs unfused sparse and dense",
                           "workload": args.workload, "n_gpus": 1, "data": "synthetic",
                           "unit": "ms/step", **body}), flush=True)
+        return
+    if args.workload == "calibration-hessian":
+        log("workload calibration-hessian")
+        body = {"per_call_us": hessian_run(args)}
+        print(json.dumps({"metric": "Hessian accumulation H += 2 X X^T, us per call",
+                          "workload": args.workload, "n_gpus": 1, "data": "synthetic",
+                          "dtype": "f16 inputs, fp32 H", **body}), flush=True)
         return
     if args.workload != "llama8b-layer":
         cfg_id = {"single": 1, "patterns": 3, "70b-qwen": 4, "decode-32-layers": 5}[args.workload]

@@ -949,12 +949,15 @@ constexpr int kHTile = 128;     // H tile edge
 constexpr int kHChunk = 32;     // tokens per staged chunk
 constexpr int kHRow = 80;       // LDS bytes per staged feature row (64 + 16 pad)
 constexpr int kHBuf = 2 * kHTile * kHRow;  // one buffer: the i and the j row blocks
+constexpr int kHQRow = 64 * 4 + 16;         // epilogue: one wave's 64 x 64 fp32 quarter, padded rows
+constexpr int kHQuarter = 64 * kHQRow;
+constexpr int kHLds = 4 * kHQuarter > 2 * kHBuf ? 4 * kHQuarter : 2 * kHBuf;
 
 template <bool BF>
 __global__ __launch_bounds__(256) void nm_hessian_kernel(float *__restrict__ H,
                                                          const uint16_t *__restrict__ X, int d,
                                                          int ntok, int ldx, float scale, int T) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kHBuf];
+  __shared__ __attribute__((aligned(16))) char lds[kHLds];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, q = lane >> 4;
@@ -1029,24 +1032,81 @@ __global__ __launch_bounds__(256) void nm_hessian_kernel(float *__restrict__ H,
       for (int b = 0; b < 4; ++b) acc[a][b] = dmfma<BF>(av[a], bv[b], acc[a][b]);
   }
 
-  // H[i][j] += scale * acc (lane: rows 4q..4q+3, column n of each 16 x 16),
-  // and the mirror H[j][i] for tiles off the diagonal
+  // Epilogue through LDS: each wave parks its 64 x 64 quarter (lane: rows
+  // 4q..4q+3, column n of each 16 x 16) and then updates H with 16-byte
+  // loads and stores, 16 lanes per 256-byte row segment: H[i][j] += scale *
+  // Q[i][j], and for tiles off the diagonal the mirror H[j][i] += scale *
+  // Q[i][j] from the quarter read column-wise.  Rows or columns past d and
+  // segments that do not fill 4 columns take a scalar path.
+  __syncthreads();  // every wave is done with the staging buffers
+  const uint32_t qb = (uint32_t)(size_t)(lds_ptr)lds + (uint32_t)(w * kHQuarter);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int ib = i0 + 64 * wi + 16 * a + 4 * q;
-      const int j = j0 + 64 * wj + 16 * b + n;
-      if (j >= d) continue;
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (ib + r < d) H[(int64_t)(ib + r) * d + j] += scale * acc[a][b][r];
-      if (ti != tj) {
+        lds_st<float>(qb + (16 * a + 4 * q + r) * kHQRow + 4 * (16 * b + n), scale * acc[a][b][r]);
+  // (each wave reads back only its own quarter: LDS operations of one wave
+  // complete in order, so no barrier is needed here)
+  const int qi0 = i0 + 64 * wi, qj0 = j0 + 64 * wj;
+  const int c4 = lane & 15, rsub = lane >> 4;  // 16 lanes x 16 bytes per row, 4 rows per pass
+  const bool mirror = ti != tj;
+  // whole 16-byte segments (inside the matrix and aligned) take the vector
+  // path; the others (ragged d) are updated element by element
+  auto vec_ok = [&](int64_t row, int col0) {
+    return row < d && col0 + 3 < d && ((((uintptr_t)(H + row * d + col0)) & 15) == 0);
+  };
+  // 16 passes in groups of GP: the H segments of a group (and of its mirror)
+  // are loaded together, so 2 GP loads per lane are in flight, then added to
+  // and stored (GP = 4 keeps the register count, and the main loop's
+  // occupancy, where it is without the epilogue)
+  constexpr int GP = 4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (ib + r < d) H[(int64_t)j * d + ib + r] += scale * acc[a][b][r];
+  for (int g0 = 0; g0 < 16; g0 += GP) {
+  f4v_t hd[16], hm[16];
+#pragma unroll
+  for (int pass = g0; pass < g0 + GP; ++pass) {
+    const int rr = 4 * pass + rsub;
+    hd[pass] = (f4v_t){0.f, 0.f, 0.f, 0.f};
+    hm[pass] = (f4v_t){0.f, 0.f, 0.f, 0.f};
+    if (vec_ok(qi0 + rr, qj0 + 4 * c4))
+      hd[pass] = *reinterpret_cast<const f4v_t *>(H + (int64_t)(qi0 + rr) * d + qj0 + 4 * c4);
+    if (mirror && vec_ok(qj0 + rr, qi0 + 4 * c4))
+      hm[pass] = *reinterpret_cast<const f4v_t *>(H + (int64_t)(qj0 + rr) * d + qi0 + 4 * c4);
+  }
+  // add the quarter (row-wise for H, column-wise for the mirror) and store
+#pragma unroll
+  for (int pass = g0; pass < g0 + GP; ++pass) {
+    const int rr = 4 * pass + rsub;
+    const f4v_t v = ld<f4v_t>((lds_ptr)(size_t)(qb + rr * kHQRow + 16 * c4));
+    float mv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mv[e] = ld<float>((lds_ptr)(size_t)(qb + (4 * c4 + e) * kHQRow + 4 * rr));
+    {
+      const int64_t row = qi0 + rr;
+      const int col0 = qj0 + 4 * c4;
+      if (vec_ok(row, col0)) {
+        *reinterpret_cast<f4v_t *>(H + row * d + col0) = hd[pass] + v;
+      } else if (row < d) {
+        for (int e = 0; e < 4; ++e)
+          if (col0 + e < d) H[row * d + col0 + e] += v[e];
       }
     }
+    if (mirror) {
+      const int64_t row = qj0 + rr;
+      const int col0 = qi0 + 4 * c4;
+      if (vec_ok(row, col0)) {
+        f4v_t h = hm[pass];
+        h[0] += mv[0]; h[1] += mv[1]; h[2] += mv[2]; h[3] += mv[3];
+        *reinterpret_cast<f4v_t *>(H + row * d + col0) = h;
+      } else if (row < d) {
+        for (int e = 0; e < 4; ++e)
+          if (col0 + e < d) H[row * d + col0 + e] += mv[e];
+      }
+    }
+  }
+  }
 }
 
 // Dense comparison when x fits the LDS budget, built like the sparse row
