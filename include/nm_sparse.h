@@ -175,6 +175,27 @@ int nm_spmm_swiglu(const void *values, const uint32_t *bits, const void *X,
 int nm_hessian_accumulate(float *H, const void *X, int64_t d, int64_t ntok,
                           int64_t ld, nm_dtype in_dt, float scale, void *stream);
 
+/* Calibration side: N:M mask selection (the "N:M mask-selection step" of
+ * the pruning solver).  In every group of m consecutive weights of a row,
+ * keep[r][c] = 1 for the n columns with the largest score W[r][c]^2 * s[c],
+ * ties to the lower column, else 0.  The score is computed in fp32 as
+ * (w * w) * s[c]; a NaN score is taken as -inf.
+ * Two per-column weights s give the criteria of the pages' backends ("Method",
+ * OBS paragraph, and the "Experiments" setup naming SparseGPT and Wanda):
+ *   s[c] = H[c][c] for H = 2 X X^T (nm_hessian_accumulate's output, read
+ *          with cstride = cols + 1) ranks by |w| * ||x_c||, Wanda's criterion;
+ *   s[c] = 1 / [H^-1]_cc ranks by the OBS saliency w^2 / [H^-1]_cc of removing
+ *          the weight alone (the compensating update is the solver's, not this
+ *          call's).
+ *   W:    device, rows x cols 16-bit (dt), row-major, 2-byte aligned;
+ *   colw: device fp32, s[c] = colw[c * cstride], 4-byte aligned;
+ *   keep: device, rows x cols bytes (output), ready for nm_pack.
+ * Errors: NM_ERR_INVALID_ARG, NM_ERR_UNSUPPORTED (pattern, dt), NM_ERR_SHAPE
+ * (cols % 32), NM_ERR_ALIGN.  Asynchronous on stream. */
+int nm_select_nm(const void *W, const float *colw, int64_t cstride,
+                 int64_t rows, int64_t cols, int n, int m, nm_dtype dt,
+                 uint8_t *keep, void *stream);
+
 /* Dense comparison, the decode GEMV the sparse kernel replaces (Experiments,
  * Table 3 paragraph: speedups are against the dense model's decode):
  *   Y[b][r] = sum over all c of W[r][c] * X[b][c],  1 <= batch <= 8.

@@ -22,6 +22,11 @@ Functions and the passages they follow (SparseDecoding, arXiv 2610.12327):
   feature-major X (column t = the layer's input at decode step t): the
   Hessian H = 2 X X^T of the layer-wise objective ("Method", OBS paragraph
   and the decode-time calibration paragraph), a plain triple loop in fp64.
+* :func:`select_nm` -- the N:M mask-selection step: in each group of M keep
+  the N weights of largest w^2 * s[c], s = diag(H) for the |w| * ||x_c|| order
+  of the Wanda backend or s = 1 / diag(H^-1) for the OBS saliency of one weight
+  ("Method", OBS paragraph; "Experiments" setup naming SparseGPT and Wanda),
+  chosen greedily one largest score at a time, scores in fp32.
 * :func:`silu_mul` / :func:`swiglu_gemv` -- silu(gate) * up on the masked
   products of a row-interleaved gate/up matrix, the MLP step of the Llama and
   Qwen decoder layers whose end-to-end decoding the pages time ("Experiments",
@@ -89,6 +94,8 @@ def _load():
     lib.oracle_silu_mul_f64.restype = None
     lib.oracle_hessian_f64.argtypes = [p, ci, i64, i64, i64, ctypes.c_double, ci, p]
     lib.oracle_hessian_f64.restype = None
+    lib.oracle_select_nm.argtypes = [p, ci, p, i64, i64, i64, ci, ci, p]
+    lib.oracle_select_nm.restype = ci
     _lib = lib
     return lib
 
@@ -220,3 +227,24 @@ def hessian(X, ntok=None, scale: float = 2.0, is_bf16: bool = False, threads: in
     _load().oracle_hessian_f64(_ptr(xb), int(bool(is_bf16)), d, ntok, ld, float(scale),
                                int(threads), _ptr(H))
     return H
+
+
+def select_nm(W, colw, n: int, m: int, is_bf16: bool, cstride: int = 1) -> np.ndarray:
+    """uint8 keep-mask of the rows x cols 16-bit W: in each group of m columns
+    the n of largest fp32 score (w * w) * s[c], s[c] = colw.flat[c * cstride],
+    ties to the lower column, NaN scores as -inf."""
+    w = _bits16(W)
+    if w.ndim != 2:
+        raise ValueError("W must be 2-D")
+    rows, cols = w.shape
+    cw = np.ascontiguousarray(colw, dtype=np.float32).ravel()
+    if cols and cw.size < (cols - 1) * cstride + 1:
+        raise ValueError("colw too short for cols and cstride")
+    keep = np.zeros((rows, cols), dtype=np.uint8)
+    st = _load().oracle_select_nm(_ptr(w), int(bool(is_bf16)), _ptr(cw), int(cstride), rows, cols,
+                                  int(n), int(m), _ptr(keep))
+    if st == ERR_UNSUPPORTED:
+        raise ValueError(f"pattern {n}:{m} not supported")
+    if st == ERR_SHAPE:
+        raise ValueError("cols must be a multiple of m")
+    return keep

@@ -221,3 +221,40 @@ void oracle_hessian_f64(const uint16_t *X, int is_bf16, int64_t d, int64_t ntok,
         }
     }
 }
+
+/* ---- the calibration side: N:M mask selection ------------------------------- */
+
+/* keep[r][c] for the rows x cols 16-bit W: in each group of m consecutive
+ * columns of a row, choose n columns one at a time, each time the unchosen
+ * column of largest score (w * w) * s[c] (first in column order among equal
+ * scores), s[c] = colw[c * cstride].  The score is a float (fp32) product,
+ * the precision in which the decision is fixed; a NaN score counts as -inf.
+ * With s = diag(H), H = 2 X X^T, this is the |w| * ||x_c|| order of the Wanda
+ * backend; with s = 1 / diag(H^-1), the OBS saliency of removing one weight
+ * ("Method", OBS paragraph). */
+int oracle_select_nm(const uint16_t *W, int is_bf16, const float *colw, int64_t cstride,
+                     int64_t rows, int64_t cols, int n, int m, uint8_t *keep) {
+    if (!oracle_pattern_supported(n, m)) return OR_ERR_UNSUPPORTED;
+    if (cols % m != 0) return OR_ERR_SHAPE;
+    float score[32];
+    int chosen[32];
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t g = 0; g < cols; g += m) {
+            for (int e = 0; e < m; ++e) {
+                const float w = (float)decode16(W[r * cols + g + e], is_bf16);
+                const float ww = w * w;
+                const float sc = ww * colw[(g + e) * cstride];
+                score[e] = isnan(sc) ? -INFINITY : sc;
+                chosen[e] = 0;
+            }
+            for (int k = 0; k < n; ++k) {
+                int best = -1;
+                for (int e = 0; e < m; ++e)
+                    if (!chosen[e] && (best < 0 || score[e] > score[best])) best = e;
+                chosen[best] = 1;
+            }
+            for (int e = 0; e < m; ++e) keep[r * cols + g + e] = (uint8_t)chosen[e];
+        }
+    }
+    return OR_OK;
+}

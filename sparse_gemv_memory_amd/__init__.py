@@ -16,6 +16,7 @@ from .native import (  # noqa: F401
     nm_dense_gemv,
     nm_hessian_accumulate,
     nm_pack,
+    nm_select_nm,
     nm_packed_bytes,
     nm_spmm_small,
     nm_spmm_swiglu,

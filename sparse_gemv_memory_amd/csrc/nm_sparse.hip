@@ -1109,6 +1109,45 @@ __global__ __launch_bounds__(256) void nm_hessian_kernel(float *__restrict__ H,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Calibration side: N:M mask selection.  In every group of M consecutive
+// weights of a row, keep the N with the largest score w^2 * s[c] for a
+// per-column weight s: s = diag(H), H = 2 X X^T, orders the weights by
+// |w| * ||x_c|| (the Wanda backend the pages name); s = 1 / diag(H^-1) gives
+// the OBS saliency of one weight.  Ties go to the lower column.  The score is
+// an fp32 product of exact fp32 values, (w * w) * s, so the decision is
+// reproducible bit for bit; a NaN score is taken as -inf.  One lane per group;
+// a column's rank is the number of columns of its group that beat it.
+
+template <bool BF, int M>
+__global__ __launch_bounds__(256) void nm_select_kernel(const uint16_t *__restrict__ W,
+                                                        const float *__restrict__ colw,
+                                                        int64_t cstride, int64_t groups,
+                                                        int K, int N,
+                                                        uint8_t *__restrict__ keep) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= groups) return;
+  const int64_t gpr = K / M;
+  const int64_t r = g / gpr;
+  const int c0 = (int)(g - r * gpr) * M;
+  float sc[M];
+#pragma unroll
+  for (int c = 0; c < M; ++c) {
+    const uint16_t bits = W[r * K + c0 + c];
+    const float w = BF ? __uint_as_float((uint32_t)bits << 16) : (float)__builtin_bit_cast(_Float16, bits);
+    const float cw = colw[(int64_t)(c0 + c) * cstride];
+    const float s = (w * w) * cw;
+    sc[c] = (s == s) ? s : -__builtin_inff();
+  }
+#pragma unroll
+  for (int c = 0; c < M; ++c) {
+    int rank = 0;
+#pragma unroll
+    for (int e = 0; e < M; ++e) rank += (sc[e] > sc[c]) || (sc[e] == sc[c] && e < c);
+    keep[r * K + c0 + c] = rank < N ? 1 : 0;
+  }
+}
+
 // Dense comparison when x fits the LDS budget, built like the sparse row
 // kernel so that the speedup is measured against an equally tuned dense
 // GEMV: x staged once per workgroup as BP contiguous rows; each wave walks
@@ -1971,6 +2010,33 @@ int nm_hessian_accumulate(float *H, const void *X, int64_t d, int64_t ntok, int6
   auto fn = in_dt == NM_BF16 ? nm_hessian_kernel<true> : nm_hessian_kernel<false>;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, H,
                      (const uint16_t *)X, (int)d, (int)ntok, (int)ld, scale, T);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NM_OK : hip_fail(e);
+}
+
+int nm_select_nm(const void *W, const float *colw, int64_t cstride, int64_t rows, int64_t cols,
+                 int n, int m, nm_dtype dt, uint8_t *keep, void *stream) {
+  if (rows < 0 || cols < 0 || cstride < 1) return NM_ERR_INVALID_ARG;
+  if (!pattern_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
+  if (cols % 32 != 0) return NM_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return NM_OK;
+  if (!W || !colw || !keep) return NM_ERR_INVALID_ARG;
+  if (!aligned(W, 2) || !aligned(colw, 4)) return NM_ERR_ALIGN;
+  if (cols > INT32_MAX) return NM_ERR_INVALID_ARG;
+  const int64_t groups = rows * (cols / m);
+  const int64_t grid = (groups + 255) / 256;
+  if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
+  const bool bf = dt == NM_BF16;
+  auto go = [&](auto fn) {
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                       (const uint16_t *)W, colw, cstride, groups, (int)cols, n, keep);
+  };
+  switch (m) {
+    case 4: bf ? go(nm_select_kernel<true, 4>) : go(nm_select_kernel<false, 4>); break;
+    case 8: bf ? go(nm_select_kernel<true, 8>) : go(nm_select_kernel<false, 8>); break;
+    case 16: bf ? go(nm_select_kernel<true, 16>) : go(nm_select_kernel<false, 16>); break;
+    default: bf ? go(nm_select_kernel<true, 32>) : go(nm_select_kernel<false, 32>); break;
+  }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? NM_OK : hip_fail(e);
 }

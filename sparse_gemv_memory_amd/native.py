@@ -96,6 +96,8 @@ def lib():
     L.nm_spmm_swiglu_cfg.restype = ci
     L.nm_hessian_accumulate.argtypes = [p, p, i64, i64, i64, ci, ctypes.c_float, p]
     L.nm_hessian_accumulate.restype = ci
+    L.nm_select_nm.argtypes = [p, p, i64, i64, i64, ci, ci, ci, p, p]
+    L.nm_select_nm.restype = ci
     L.nm_dense_gemv.argtypes = [p, p, p, ci, i64, i64, ci, ci, p]
     L.nm_dense_gemv.restype = ci
     L.nm_dense_gemv_cfg.argtypes = [p, p, p, ci, i64, i64, ci, ci, ctypes.POINTER(LaunchCfg), p]
@@ -258,6 +260,31 @@ def nm_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, ntok: Optional[int] 
                                          float(scale), _stream(H.device))
     _check(st, "nm_hessian_accumulate")
     return H
+
+
+def nm_select_nm(W: torch.Tensor, colw: torch.Tensor, n: int, m: int,
+                 cstride: int = 1, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Keep-mask (rows, cols) uint8: in each m-group of each row the n columns
+    with the largest fp32 score (W * W) * s, s[c] = colw.flatten()[c * cstride],
+    ties to the lower column.  For a Hessian H (d x d, fp32) pass H and
+    cstride = d + 1 to use its diagonal."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    rows, cols = W.shape
+    if colw.dtype != torch.float32:
+        raise TypeError("colw must be float32")
+    if not colw.is_contiguous():
+        raise ValueError("colw must be contiguous")
+    if cols and colw.numel() < (cols - 1) * cstride + 1:
+        raise ValueError("colw too short for cols and cstride")
+    keep = out if out is not None else torch.empty((rows, cols), dtype=torch.uint8, device=W.device)
+    if keep.shape != (rows, cols) or keep.dtype != torch.uint8:
+        raise ValueError("out must be a (rows, cols) uint8 tensor")
+    with torch.cuda.device(W.device):
+        st = lib().nm_select_nm(_dev(W, "W"), _dev(colw, "colw"), cstride, rows, cols, n, m,
+                                _in_dt(W), _dev(keep, "keep"), _stream(W.device))
+    _check(st, "nm_select_nm")
+    return keep
 
 
 def nm_dense_gemv(W, X, out_dtype=torch.float32, out=None, cfg=None):

@@ -43,7 +43,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("nm_packed_bytes", "nm_pack", "nm_spmv", "nm_spmm_small", "nm_dense_gemv",
-              "nm_status_string"):
+              "nm_status_string", "nm_spmm_swiglu", "nm_hessian_accumulate", "nm_select_nm"):
         assert n in names
 
 
@@ -155,6 +155,25 @@ def test_hessian_rejects_bad_arguments(L):
     assert h(X=P + 8) == ALIGN
     assert h(H=None, X=None, d=0) == OK  # nothing to do
     assert h(X=None, ntok=0) == OK
+
+
+def test_select_rejects_bad_arguments(L):
+    def sel(W=P, c=P, cs=1, rows=4, cols=64, n=2, m=4, dt=F16, k=P):
+        return L.nm_select_nm(W, c, cs, rows, cols, n, m, dt, k, None)
+    assert sel(rows=-1) == INV
+    assert sel(cols=-32) == INV
+    assert sel(cs=0) == INV
+    assert sel(cols=48) == SHAPE
+    assert sel(n=1) == UNSUP
+    assert sel(m=64, n=32) == UNSUP
+    assert sel(dt=F32) == UNSUP
+    assert sel(W=None) == INV
+    assert sel(c=None) == INV
+    assert sel(k=None) == INV
+    assert sel(W=P + 1) == ALIGN
+    assert sel(c=P + 2) == ALIGN
+    assert sel(W=None, c=None, k=None, rows=0) == OK  # nothing to do
+    assert sel(W=None, c=None, k=None, cols=0) == OK
 
 
 def test_dense_rejects_bad_arguments(L):

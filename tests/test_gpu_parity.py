@@ -643,3 +643,89 @@ def test_hessian_zero_tokens_leaves_h():
     X = torch.zeros((33, 8), dtype=torch.float16, device=DEV)
     native.nm_hessian_accumulate(H, X, ntok=0)
     assert torch.all(H == 1.5).item()
+
+
+# ---- N:M mask selection (calibration side) -----------------------------------------
+
+def _sel_w(rows, cols, seed, dtype, kind="normal"):
+    rng = np.random.default_rng(seed)
+    if kind == "ints":
+        a = rng.integers(-4, 5, size=(rows, cols))
+    else:
+        a = rng.normal(size=(rows, cols)) * 0.02
+    return synth.f32_to_16_bits(a.astype(np.float32), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n,m", PATTERNS)
+@pytest.mark.parametrize("rows,cols,cstride", [(1, 32, 1), (37, 96, 1), (300, 4096, 3), (129, 2080, 1)])
+def test_select_matches_oracle_bit_exact(rows, cols, cstride, n, m, dtype):
+    """The keep-mask is an integer result decided in fp32 on both sides:
+    bit-exact, ragged final block of lanes included."""
+    W = _sel_w(rows, cols, seed=rows + cols + m, dtype=dtype)
+    rng = np.random.default_rng(cols * 7 + m)
+    colw = rng.uniform(0.0, 4.0, size=(cols - 1) * cstride + 1).astype(np.float32)
+    keep = native.nm_select_nm(t16(W, dtype), torch.from_numpy(colw).to(DEV), n, m, cstride=cstride)
+    want = oracle.select_nm(W, colw, n, m, dtype == "bf16", cstride=cstride)
+    assert np.array_equal(keep.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_select_ties_and_nan_scores(n, m):
+    """Integer weights and a few distinct column weights make equal scores
+    common (lower column wins); NaN weights and 0 * inf rank last."""
+    rows, cols = 64, 512
+    W = _sel_w(rows, cols, seed=5 + m, dtype="f16", kind="ints")
+    rng = np.random.default_rng(m)
+    W[rng.random((rows, cols)) < 0.05] = 0x7E00  # NaN
+    colw = rng.integers(0, 3, size=cols).astype(np.float32)
+    colw[rng.random(cols) < 0.05] = np.inf
+    keep = native.nm_select_nm(t16(W, "f16"), torch.from_numpy(colw).to(DEV), n, m)
+    want = oracle.select_nm(W, colw, n, m, False)
+    assert np.array_equal(keep.cpu().numpy(), want)
+    assert oracle.count_bad_groups(want, n, m) == 0
+
+
+def test_select_from_gpu_hessian_then_pack():
+    """The calibration step end to end on the device: H = 2 X X^T from
+    integer activations (exact in fp32), selection from its diagonal
+    (cstride = d + 1), then nm_pack; values and bits equal the oracle's
+    pack of the oracle's selection from the oracle's Hessian."""
+    d, ntok, rows, n, m = 256, 40, 96, 2, 4
+    X = _hx(d, ntok, seed=11)
+    H = torch.zeros((d, d), device=DEV)
+    native.nm_hessian_accumulate(H, t16(X, "f16"), scale=2.0)
+    W = _sel_w(rows, d, seed=12, dtype="f16")
+    Wt = t16(W, "f16")
+    keep = native.nm_select_nm(Wt, H, n, m, cstride=d + 1)
+    values, bits = native.nm_pack(Wt, keep, n, m)
+    Hd = np.diag(oracle.hessian(X, scale=2.0)).astype(np.float32)
+    want_keep = oracle.select_nm(W, Hd, n, m, False)
+    st, want_v, want_b = oracle.pack(W, want_keep, n, m)
+    assert st == oracle.OK
+    assert np.array_equal(keep.cpu().numpy(), want_keep)
+    assert np.array_equal(u16(values).ravel(), want_v.ravel())
+    assert np.array_equal(u32(bits).ravel(), want_b.ravel())
+
+
+def test_select_full_size_layer():
+    """A 14336 x 4096 layer (the gate/up shape), fp16 2:4, against the
+    oracle over every group."""
+    rows, cols = 14336, 4096
+    W = synth.weights(rows, cols, seed=77, dtype="f16")
+    colw = np.random.default_rng(78).uniform(0.0, 4.0, size=cols).astype(np.float32)
+    keep = native.nm_select_nm(t16(W, "f16"), torch.from_numpy(colw).to(DEV), 2, 4)
+    want = oracle.select_nm(W, colw, 2, 4, False)
+    assert np.array_equal(keep.cpu().numpy(), want)
+
+
+def test_select_zero_sized_and_rejections():
+    colw = torch.ones(64, device=DEV)
+    k = native.nm_select_nm(torch.zeros((0, 64), dtype=torch.float16, device=DEV), colw, 2, 4)
+    assert k.shape == (0, 64)
+    with pytest.raises(native.NMError):
+        native.nm_select_nm(torch.zeros((4, 48), dtype=torch.float16, device=DEV), colw, 2, 4)
+    with pytest.raises(native.NMError):
+        native.nm_select_nm(torch.zeros((4, 64), dtype=torch.float16, device=DEV), colw, 3, 4)
+    with pytest.raises(ValueError):
+        native.nm_select_nm(torch.zeros((4, 64), dtype=torch.float16, device=DEV), colw, 2, 4, cstride=2)

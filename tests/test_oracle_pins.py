@@ -359,3 +359,144 @@ def test_hessian_reads_only_the_first_ntok_columns():
     Xg[:, 11:] = _x16(rng.normal(size=(9, 5)) * 100)
     assert np.array_equal(oracle.hessian(X, ntok=11), oracle.hessian(Xg, ntok=11))
     assert np.array_equal(oracle.hessian(X, ntok=0), np.zeros((9, 9)))
+
+
+# ---- N:M mask selection -------------------------------------------------------------
+
+SEL_PATTERNS = [(2, 4), (4, 8), (8, 16), (16, 32)]
+
+
+def _topn_by_sort(score, n, m):
+    """Keep the n largest of each m-group, lower column first among equals, by
+    a stable sort of the negated scores (a library routine, not the oracle's
+    one-at-a-time choice)."""
+    rows, cols = score.shape
+    keep = np.zeros((rows, cols), dtype=np.uint8)
+    for r in range(rows):
+        for g in range(0, cols, m):
+            order = np.argsort(-score[r, g:g + m], kind="stable")[:n]
+            keep[r, g + order] = 1
+    return keep
+
+
+@pytest.mark.parametrize("n,m", SEL_PATTERNS)
+def test_select_nm_minimizes_reconstruction_error_for_orthogonal_activations(n, m):
+    """Eq. (1) without the weight update: with X = diag(a) Had (rows of a
+    Hadamard matrix, exactly orthogonal in fp16), ||W X - (W o K) X||_F^2 over
+    each group's C(m, n) choices is smallest at the selected mask when
+    s = diag(2 X X^T).  The error is the direct matrix product, not a score."""
+    import scipy.linalg
+    rng = np.random.default_rng(31)
+    rows, cols, ntok = 3, 2 * m, 64 if 2 * m <= 64 else 2 * m
+    had = scipy.linalg.hadamard(ntok)[:cols].astype(np.float32)
+    a = rng.integers(1, 9, size=cols).astype(np.float32) / 4.0
+    X = _x16(a[:, None] * had)
+    xd = oracle.decode16(X, False)
+    H = oracle.hessian(X, scale=2.0)
+    assert np.array_equal(H, np.diag(np.diag(H)))  # orthogonal rows
+    W = _x16(rng.normal(size=(rows, cols)))
+    wd = oracle.decode16(W, False)
+    keep = oracle.select_nm(W, np.diag(H).astype(np.float32), n, m, False)
+    assert oracle.count_bad_groups(keep, n, m) == 0
+
+    def err(k):
+        return float((((wd * (1 - k)) @ xd) ** 2).sum())
+
+    base = err(keep)
+    checks = 0
+    for r in range(rows):
+        for g in range(0, cols, m):
+            for kept in itertools.combinations(range(m), n):
+                if m > 8 and checks > 4000:
+                    break
+                k = keep.astype(np.float64).copy()
+                k[r, g:g + m] = 0
+                k[r, [g + e for e in kept]] = 1
+                assert err(k) >= base * (1 - 1e-12)
+                checks += 1
+    assert checks > 0
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n,m", SEL_PATTERNS)
+def test_select_nm_unit_column_weight_is_magnitude_pruning(n, m, dtype):
+    """s = 1: keep the n largest |w| per group (w^2 is exact in fp32 for
+    16-bit inputs); integer weights make ties common and the lower column
+    wins them."""
+    rng = np.random.default_rng(32)
+    W = _x16(rng.integers(-4, 5, size=(6, 4 * m)), dtype)
+    wd = oracle.decode16(W, dtype == "bf16")
+    keep = oracle.select_nm(W, np.ones(4 * m, np.float32), n, m, dtype == "bf16")
+    assert np.array_equal(keep, _topn_by_sort(np.abs(wd), n, m))
+
+
+@pytest.mark.parametrize("n,m", SEL_PATTERNS)
+def test_select_nm_equal_magnitudes_follow_column_weight(n, m):
+    rng = np.random.default_rng(33)
+    W = _x16(np.where(rng.random((5, 2 * m)) < 0.5, -1.0, 1.0))
+    s = rng.integers(0, 6, size=2 * m).astype(np.float32)
+    keep = oracle.select_nm(W, s, n, m, False)
+    assert np.array_equal(keep, _topn_by_sort(np.broadcast_to(s, (5, 2 * m)), n, m))
+
+
+def test_select_nm_matches_wanda_order_from_activation_norms():
+    """s = diag(2 X X^T) ranks by |w| * ||x_c||, the norm taken directly from
+    X in fp64; groups whose n-th and (n+1)-th scores are within 1e-5 of each
+    other are skipped (fp32 against fp64)."""
+    rng = np.random.default_rng(34)
+    n, m, rows, cols = 2, 4, 40, 64
+    X = _x16(rng.normal(size=(cols, 30)) * rng.uniform(0.2, 3.0, size=(cols, 1)))
+    W = _x16(rng.normal(size=(rows, cols)))
+    H = oracle.hessian(X, scale=2.0)
+    keep = oracle.select_nm(W, np.diag(H).astype(np.float32), n, m, False)
+    wanda = np.abs(oracle.decode16(W, False)) * np.linalg.norm(oracle.decode16(X, False), axis=1)
+    want = _topn_by_sort(wanda, n, m)
+    compared = 0
+    for r in range(rows):
+        for g in range(0, cols, m):
+            srt = np.sort(wanda[r, g:g + m])[::-1]
+            if srt[n - 1] - srt[n] <= 1e-5 * srt[n - 1]:
+                continue
+            assert np.array_equal(keep[r, g:g + m], want[r, g:g + m])
+            compared += 1
+    assert compared > rows * cols // m * 0.9
+
+
+def test_select_nm_invariants():
+    rng = np.random.default_rng(35)
+    n, m, d = 4, 8, 64
+    W = _x16(rng.normal(size=(12, d)))
+    s = rng.uniform(0.1, 5.0, size=d).astype(np.float32)
+    keep = oracle.select_nm(W, s, n, m, False)
+    assert oracle.count_bad_groups(keep, n, m) == 0
+    assert int(keep.sum()) == 12 * d // 2
+    # the sign of a weight does not matter
+    assert np.array_equal(oracle.select_nm(W ^ np.uint16(0x8000), s, n, m, False), keep)
+    # a power-of-two scale of s does not change the order
+    assert np.array_equal(oracle.select_nm(W, s * 4, n, m, False), keep)
+    # reading s as the diagonal of a matrix (stride d + 1)
+    S = np.diag(s).astype(np.float32) + rng.normal(size=(d, d)).astype(np.float32) * 9
+    np.fill_diagonal(S, s)
+    assert np.array_equal(oracle.select_nm(W, S, n, m, False, cstride=d + 1), keep)
+    # permuting the columns of a group (with s) permutes its selection
+    perm = np.concatenate([g + rng.permutation(m) for g in range(0, d, m)])
+    assert np.array_equal(oracle.select_nm(W[:, perm], s[perm], n, m, False), keep[:, perm])
+
+
+def test_select_nm_nan_scores_rank_last():
+    nan16 = 0x7E00
+    W = _x16([[1.0, 3.0, 2.0, 4.0, 1.0, 0.0, 1.0, 1.0]])
+    W[0, 3] = nan16  # NaN weight
+    s = np.array([1, 1, 1, 1, 1, np.inf, 1, 1], np.float32)  # 0 * inf = NaN
+    keep = oracle.select_nm(W, s, 2, 4, False)
+    assert keep.tolist() == [[0, 1, 1, 0, 1, 0, 1, 0]]
+    Wn = np.full((1, 4), nan16, np.uint16)
+    assert oracle.select_nm(Wn, np.ones(4, np.float32), 2, 4, False).tolist() == [[1, 1, 0, 0]]
+
+
+def test_select_nm_rejects_bad_pattern_and_shape():
+    W = _x16(np.ones((2, 8)))
+    with pytest.raises(ValueError):
+        oracle.select_nm(W, np.ones(8, np.float32), 1, 4, False)
+    with pytest.raises(ValueError):
+        oracle.select_nm(_x16(np.ones((2, 6))), np.ones(6, np.float32), 2, 4, False)
