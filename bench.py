@@ -449,7 +449,9 @@ def hessian_run(args):
     activations.  Per call: the kernel time, the HBM rate of its H traffic
     (read + write 8 d^2 bytes plus X) and the contraction's flop rate, beside
     torch (hipBLASLt) doing the same update in fp32 (addmm on fp32 copies of
-    X) and with fp16 inputs (mm, then an fp32 add)."""
+    X) and with fp16 inputs (mm, then an fp32 add).  Then the 2:4 mask
+    selection of the layer that reads each width, scored with H's diagonal,
+    beside torch's topk over groups of 4 and a scatter."""
     out = {}
     for d in (4096, 14336):
         H = torch.zeros((d, d), device=DEV)
@@ -480,7 +482,31 @@ def hessian_run(args):
             out[f"d{d}_ntok{ntok}"] = res
             log(f"  d={d} ntok={ntok}: " + ", ".join(f"{k} {v}" for k, v in res.items()))
             del X, Xf
-        del H
+        # the 2:4 selection of the layer that reads this width, scored with
+        # H's diagonal (|w| * ||x_c|| order), against torch's group topk
+        rows = 14336 if d == 4096 else 4096
+        W = (torch.randn((rows, d), device=DEV) * 0.02).half()
+        keep = torch.empty((rows, d), dtype=torch.uint8, device=DEV)
+        hd = H.diagonal()
+        def sel_ours():
+            st = L.nm_select_nm(W.data_ptr(), H.data_ptr(), d + 1, rows, d, 2, 4, native.NM_F16,
+                                keep.data_ptr(), torch.cuda.current_stream().cuda_stream)
+            assert st == 0, st
+        def sel_torch():
+            sc = (W.float().square() * hd).view(rows, d // 4, 4)
+            idx = sc.topk(2, dim=-1).indices
+            keep.view(rows, d // 4, 4).zero_().scatter_(-1, idx, 1)
+        res = {}
+        for kind, fn in (("nm_select_nm", sel_ours), ("torch_topk_scatter", sel_torch)):
+            g = capture(fn)
+            ms = time_steps([g], max(10, args.steps // 5), 3)
+            res[kind] = round(ms * 1e3, 2)
+            del g
+        nbytes = 3 * rows * d + 4 * d
+        res.update({"GB/s": round(nbytes / (res["nm_select_nm"] * 1e-6) / 1e9, 1)})
+        out[f"select_2of4_{rows}x{d}"] = res
+        log(f"  select 2:4 {rows}x{d}: " + ", ".join(f"{k} {v}" for k, v in res.items()))
+        del H, W, keep
         torch.cuda.empty_cache()
     return out
 
