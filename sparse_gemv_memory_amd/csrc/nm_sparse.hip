@@ -310,8 +310,9 @@ __device__ __forceinline__ void chunk8_nibbles(const char *lds, uint32_t base, u
 }
 
 // Pattern kinds: the traversal a kernel is compiled for (Appendix C: one
-// kernel per pattern, with N and M fixed at compile time).
-enum { kPat24 = 0, kPatHalf = 1, kPat1632 = 2 };
+// kernel per pattern, with N and M fixed at compile time).  kPat24x is 2:4 at
+// batch 1 in the row kernel, with x stored plainly (see chunk24x).
+enum { kPat24 = 0, kPatHalf = 1, kPat1632 = 2, kPat24x = 3 };
 
 __host__ __device__ constexpr int pattern_kind(int m) {
   return m == 4 ? kPat24 : m == 32 ? kPat1632 : kPatHalf;
@@ -323,10 +324,51 @@ __host__ __device__ constexpr int pattern_kind(int m) {
 //         weights, so the odd lane takes the upper 16 bits of the word;
 //   kPat1632 (16:32): the 8 kept weights of the odd lane are set bits 8..15
 //         of the word, so it first clears the 8 lowest set bits.
+// 2:4 at batch 1 with x stored plainly in LDS (column c at byte 2c): the
+// chunk's 16 columns are 32 contiguous bytes, read with two 16-byte LDS loads
+// instead of one 2-byte gather per kept weight.  Pair j of the chunk is the
+// two kept weights of nibble j, at in-group positions p0 < p1; its x operand
+// {x[4j+p0], x[4j+p1]} is cut out of the group's two words by one v_perm
+// with byte selector [2p0, 2p0+1, 2p1, 2p1+1].  The positions come from two
+// 8-entry byte tables (themselves read with v_perm) indexed by n >> 1, which
+// is unique for the six nibbles with two set bits (3, 5, 6, 9, 10, 12 ->
+// 1..6).  No LDS address depends on the mask, so a malformed mask word only
+// makes its row's sum undefined.
+constexpr uint32_t kPos0Lo = 0x02000000u, kPos0Hi = 0x00040200u;  // n >> 1 -> 2 p0
+constexpr uint32_t kPos1Lo = 0x04040200u, kPos1Hi = 0x00060606u;  // n >> 1 -> 2 p1
+
+template <bool BF>
+__device__ __forceinline__ void chunk24x(const char *lds, int q, uint32_t mw, const uint4 v,
+                                         float &acc) {
+  const uint32_t m = (mw >> ((q & 1) << 4)) & 0xffffu;
+  const lds_ptr xb = (lds_ptr)lds + 32 * q;
+  const u32x4_t xa = ld<u32x4_t>(xb), xc = ld<u32x4_t>(xb + 16);
+  const uint32_t X[8] = {xa[0], xa[1], xa[2], xa[3], xc[0], xc[1], xc[2], xc[3]};
+  // table indices n >> 1 of nibbles 0, 2, 1, 3 in bytes 0..3
+  const uint32_t t = m >> 1;
+  const uint32_t S = (t & 0x0707u) | (((t >> 4) & 0x0707u) << 16);
+  const uint32_t P0 = __builtin_amdgcn_perm(kPos0Hi, kPos0Lo, S);
+  const uint32_t P1 = __builtin_amdgcn_perm(kPos1Hi, kPos1Lo, S);
+  const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  // selector bytes [b, b, 4 + b, 4 + b] with b the byte of nibble j in P0 / P1
+  constexpr uint32_t kPick[4] = {0x04040000u, 0x06060202u, 0x05050101u, 0x07070303u};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sel = __builtin_amdgcn_perm(P1, P0, kPick[j]) | 0x01000100u;
+    const uint32_t xs = __builtin_amdgcn_perm(X[2 * j + 1], X[2 * j], sel);
+    acc = dot2<BF>(vv[j], xs, acc);
+  }
+}
+
 template <bool BF, int BP, int PK>
 __device__ __forceinline__ void chunk(const char *lds, int q, uint32_t mw, const uint4 v,
                                       float (&acc)[BP]) {
   using L = XLay<BP>;
+  if constexpr (PK == kPat24x) {
+    static_assert(BP == 1, "the plain x layout is for batch 1");
+    chunk24x<BF>(lds, q, mw, v, acc[0]);
+    return;
+  }
   const uint32_t h = q & 1;
   uint32_t base = L::FP + (uint32_t)(q >> 1) * L::WS;
   uint32_t m = mw;
@@ -503,10 +545,19 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   item_load(A, 0);
   item_load(Bt, 1);
   // clamped groups rewrite group ngx-1 with the same data it already holds
+  if constexpr (PK == kPat24x) {  // plain layout: group g at byte 16 g
 #pragma unroll
-  for (int s = 0; s < XS; ++s)
-    xgroup_store<BP>(lds, xg[s], min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1));
-  stage_x_sparse<BP>(lds, x, B, K, 0, K, threadIdx.x + XS * blockDim.x, blockDim.x);
+    for (int s = 0; s < XS; ++s)
+      reinterpret_cast<uint4 *>(lds)[min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1)] =
+          xg[s].r[0];
+    for (int g = threadIdx.x + XS * blockDim.x; g < ngx; g += blockDim.x)
+      reinterpret_cast<uint4 *>(lds)[g] = reinterpret_cast<const uint4 *>(x)[g];
+  } else {
+#pragma unroll
+    for (int s = 0; s < XS; ++s)
+      xgroup_store<BP>(lds, xg[s], min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1));
+    stage_x_sparse<BP>(lds, x, B, K, 0, K, threadIdx.x + XS * blockDim.x, blockDim.x);
+  }
   __syncthreads();
 
   float res[BP];  // lane i holds the sums of the wave's row i
@@ -1722,9 +1773,16 @@ rows_fn pick_rows_bp(int bp, int u, int xs) {
 }
 
 template <bool BF>
+rows_fn pick_rows_24x(int u, int xs) {
+  if (xs > 4)
+    return u == 5 ? nm_spmv_rows_kernel<BF, 1, kPat24x, 5, 8> : nm_spmv_rows_kernel<BF, 1, kPat24x, 4, 8>;
+  return u == 5 ? nm_spmv_rows_kernel<BF, 1, kPat24x, 5, 4> : nm_spmv_rows_kernel<BF, 1, kPat24x, 4, 4>;
+}
+
+template <bool BF>
 rows_fn pick_rows_pk(int pk, int bp, int u, int xs) {
   switch (pk) {
-    case kPat24: return pick_rows_bp<BF, kPat24>(bp, u, xs);
+    case kPat24: return bp == 1 ? pick_rows_24x<BF>(u, xs) : pick_rows_bp<BF, kPat24>(bp, u, xs);
     case kPatHalf: return pick_rows_bp<BF, kPatHalf>(bp, u, xs);
     default: return pick_rows_bp<BF, kPat1632>(bp, u, xs);
   }

@@ -273,6 +273,28 @@ def test_integer_inputs_bit_exact(n, m, dtype):
     assert np.array_equal(f64(Y), want)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_24_batch1_malformed_mask_words_stay_in_their_row(dtype):
+    """2:4 at batch 1 reads x by chunk, never at an address taken from the
+    mask, so mask words without two set bits per nibble (0, all ones, three
+    bits) only make their own row's sum undefined: every other row stays
+    exact (integer inputs)."""
+    rows, cols = 300, 4096
+    W = synth.integer_weights(rows, cols, seed=21, dtype=dtype)
+    keep = synth.random_mask(rows, cols, 2, 4, seed=22)
+    xi = np.random.default_rng(23).integers(-4, 5, size=cols).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, dtype)
+    values, bits = gpu_pack(W, keep, 2, 4, dtype)
+    bad = [0, 7, 150, 299]
+    b = bits.clone()
+    for i, r in enumerate(bad):
+        b[r, (37 * i) % b.shape[1]] = [0, -1, 0x77777777, 0x1][i]
+    y = f64(native.nm_spmv(values, b, t16(X, dtype), 2, 4))
+    want = oracle.masked_gemv(W, keep, X, dtype == "bf16")
+    good = np.setdiff1d(np.arange(rows), bad)
+    assert np.array_equal(y[good], want[good])
+
+
 @pytest.mark.parametrize("n,m", PATTERNS)
 def test_one_hot_x_selects_a_column(n, m):
     """x = e_j gives y[r] = W[r, j] * keep[r, j] exactly: pins the bit ->
