@@ -1633,8 +1633,12 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
     // Qwen3-32B shapes:
     //  - very few rows (<= 8 per CU) split evenly over the CUs: one row per
     //    wave and one workgroup per CU, so x is staged once per CU;
-    //  - few rows (<= 32 per CU) split evenly over the CUs: one row per wave
-    //    and exactly two workgroups per CU, as wide as that takes;
+    //  - few rows (<= 32 per CU) split evenly over the CUs: exactly two
+    //    workgroups per CU; for the sparse product at batch 1 with
+    //    K <= 16384, 4 or else 2 rows per wave while a
+    //    workgroup keeps at least 4 waves (a longer pipeline per wave: 70B q
+    //    8192x8192 -20%, Qwen3 q and 8B down 4-5%, 8B q/o 3%), otherwise one
+    //    row per wave (better or equal at K >= 25600);
     //  - otherwise, rows split evenly: 256 threads and the same number of
     //    rows rpw (<= 8) for every wave, at least two workgroups per CU, so
     //    x is staged rarely and no CU finishes early;
@@ -1648,8 +1652,12 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
       return NM_OK;
     }
     if (full <= budget / 2 && rows % (rmin * two_per_cu) == 0 && rows / two_per_cu <= 16) {
-      cfg->threads_per_wg = (int)(rows / (rmin * two_per_cu)) * kWave;
-      cfg->rows_per_wave = rmin;
+      int rpw = rmin;
+      if (!dense && bp == 1 && cols <= 16384)
+        for (int r = 4; r >= 2; r -= 2)
+          if (rows % (r * two_per_cu) == 0 && rows / (r * two_per_cu) >= 4) { rpw = r; break; }
+      cfg->threads_per_wg = (int)(rows / (rpw * two_per_cu)) * kWave;
+      cfg->rows_per_wave = rpw;
       return NM_OK;
     }
     cfg->threads_per_wg = threads_for_lds(full);
