@@ -237,7 +237,7 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 # source they were taken on.  Any change to the source makes the figure stale,
 # and it is then reported as null.
 MEASURED_TRAFFIC = {
-    # (rows, cols): (code_digest of the kernel source, bytes per launch); see
+    # (rows, cols): (kernel_digest() when measured, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
     (14336, 4096): ("a1e9db3a0a0209ca194721024b8b973b2dd228c8d31c5c955fb07e31a3240275",
                     66277691),
@@ -255,9 +255,16 @@ def code_digest(text: str) -> str:
     return hashlib.sha256(text.encode()).hexdigest()
 
 
+def kernel_digest():
+    """code_digest of the product kernels' source: nm_sparse.hip and the
+    device helpers it includes."""
+    csrc = os.path.join(ROOT, "sparse_gemv_memory_amd", "csrc")
+    return code_digest("".join(open(os.path.join(csrc, f)).read()
+                               for f in ("nm_sparse.hip", "nm_device.h")))
+
+
 def measured_traffic(rows, cols):
-    src = os.path.join(ROOT, "sparse_gemv_memory_amd", "csrc", "nm_sparse.hip")
-    digest = code_digest(open(src).read())
+    digest = kernel_digest()
     entry = MEASURED_TRAFFIC.get((rows, cols))
     if entry and entry[0] == digest:
         return entry[1]

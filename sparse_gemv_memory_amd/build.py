@@ -1,4 +1,4 @@
-"""Build libnm_sparse.so from csrc/nm_sparse.hip with hipcc for gfx950.
+"""Build libnm_sparse.so from the HIP sources in csrc/ with hipcc for gfx950.
 
 The library is built in-tree (next to this file) so that it travels with the
 source tree; nothing is installed.
@@ -11,7 +11,10 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "nm_sparse.hip")
+CSRC = os.path.join(HERE, "csrc")
+# translation units of the library (headers next to them are included)
+SRCS = [os.path.join(CSRC, f) for f in ("nm_sparse.hip", "nm_prefill.hip")
+        if os.path.exists(os.path.join(CSRC, f))]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libnm_sparse.so")
 ARCH = "gfx950"
@@ -37,7 +40,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile the HIP library (always rebuilds) and return its path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", "-o", tmp, *SRCS]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")

@@ -1,0 +1,34 @@
+// nm_host.h -- host-side helpers shared by the library's translation units:
+// argument checks and the record of the last HIP error behind NM_ERR_HIP
+// (read by nm_last_hip_error).  Defined in nm_sparse.hip; not exported from
+// the shared library.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "nm_sparse.h"
+
+#define NM_INTERNAL __attribute__((visibility("hidden")))
+
+namespace nm_host {
+
+// HIP error code of the last call that returned NM_ERR_HIP on this thread.
+extern thread_local int g_last_hip NM_INTERNAL;
+
+// Record e and return NM_ERR_HIP.
+NM_INTERNAL nm_status hip_fail(hipError_t e);
+
+// A 50% pattern the kernels are built for: N = M/2, M in {4, 8, 16, 32}.
+NM_INTERNAL bool pattern_ok(int n, int m);
+
+NM_INTERNAL bool is16(nm_dtype d);
+
+// fp32 output, or the input's own 16-bit type.
+NM_INTERNAL bool out_ok(nm_dtype in, nm_dtype out);
+
+NM_INTERNAL bool aligned(const void *p, uintptr_t a);
+
+}  // namespace nm_host

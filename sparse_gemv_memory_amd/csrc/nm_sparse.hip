@@ -36,72 +36,35 @@
 #include <mutex>
 
 #include "nm_sparse.h"
+#include "nm_device.h"
+#include "nm_host.h"
+
+namespace nm_host {
+
+thread_local int g_last_hip = 0;
+
+nm_status hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return NM_ERR_HIP;
+}
+
+bool pattern_ok(int n, int m) {
+  return (m == 4 || m == 8 || m == 16 || m == 32) && 2 * n == m;
+}
+
+bool is16(nm_dtype d) { return d == NM_F16 || d == NM_BF16; }
+
+bool out_ok(nm_dtype in, nm_dtype out) { return out == NM_F32 || out == in; }
+
+bool aligned(const void *p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+}  // namespace nm_host
 
 namespace {
 
-constexpr int kWave = 64;
-constexpr size_t kLdsCap = 160 * 1024;  // LDS one workgroup may use (CU total on gfx950)
-
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// acc + w.lo * x.lo + w.hi * x.hi with 16-bit pairs and an fp32 accumulator.
-template <bool BF>
-__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
-  if constexpr (BF)
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, w),
-                                           __builtin_bit_cast(b2_t, x), acc,
-                                           false);
-  else
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w),
-                                  __builtin_bit_cast(h2_t, x), acc, false);
-}
-
-// v + (v of the DPP-selected lane); rows outside ROW_MASK add 0.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_add(float v) {
-  const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false);
-  return v + __int_as_float(t);
-}
-
-// Sum over the 64 lanes with DPP moves only (no LDS traffic); the result is
-// valid in lane 63.
-__device__ __forceinline__ float wave_sum_to_63(float v) {
-  v = dpp_add<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]: pairs
-  v = dpp_add<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]: quads
-  v = dpp_add<0x141, 0xf>(v);  // row_half_mirror: 8 lanes
-  v = dpp_add<0x140, 0xf>(v);  // row_mirror: 16 lanes (a row)
-  v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
-  v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
-  return v;
-}
-
-// fp32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// out_kind: the output nm_dtype in bits 0..7 and the epilogue above them.
-constexpr int kEpiShift = 8;
-constexpr int kEpiNone = 0;
-constexpr int kEpiSwiglu = 1;  // rows 2r, 2r+1 -> silu(row 2r) * row 2r+1
-
-__device__ __forceinline__ void store_out(void *y, int64_t idx, float v,
-                                          int kind) {
-  kind &= 0xff;
-  if (kind == NM_F32)
-    static_cast<float *>(y)[idx] = v;
-  else if (kind == NM_F16)
-    static_cast<_Float16 *>(y)[idx] = (_Float16)v;  // v_cvt_f16_f32, RNE
-  else
-    static_cast<uint16_t *>(y)[idx] = f32_to_bf16_rne(v);
-}
+using namespace nm_host;
 
 // LDS layout of a segment of x for the sparse kernel.  Column c of the
 // segment holds the BP batch values of that column in one slot of SB bytes;
@@ -190,18 +153,6 @@ __device__ __forceinline__ void stage_x_sparse(char *lds, const uint16_t *__rest
   }
 }
 
-typedef __attribute__((address_space(3))) const char *lds_ptr;
-
-// Load a T from an LDS slot given either as a generic pointer into the
-// dynamic LDS array or as an explicit LDS-address-space pointer.
-template <typename T, typename P>
-__device__ __forceinline__ T ld(P p) {
-  if constexpr (__is_same(P, lds_ptr))
-    return *(__attribute__((address_space(3))) const T *)p;
-  else
-    return *reinterpret_cast<const T *>(p);
-}
-
 // x values of a kept pair of a lane's chunk (LDS slots p0, p1), multiplied
 // with the packed weight pair w and accumulated for every batch row.
 template <bool BF, int BP, typename P>
@@ -237,20 +188,6 @@ __device__ __forceinline__ void accum_pair(P p0, P p1, uint32_t w, float (&acc)[
       acc[2 * d + 1] = dot2<BF>(w, hi, acc[2 * d + 1]);
     }
   }
-}
-
-// v_ffbl_b32 / v_ffbh_u32 with their hardware meaning for 0 (-1), which the
-// C builtins leave undefined: index of the lowest set bit, and the number of
-// zero bits above the highest set bit.
-__device__ __forceinline__ int ffbl_hw(uint32_t x) {
-  int r;
-  asm("v_ffbl_b32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
-}
-__device__ __forceinline__ int ffbh_hw(uint32_t x) {
-  int r;
-  asm("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
 }
 
 // Generic fixed-step traversal (item (2)): the chunk's 8 kept weights are
@@ -401,14 +338,6 @@ struct Batch {
   uint32_t m[U];
 };
 
-// Word 3 of a raw buffer resource for the gfx9 family (gfx950): untyped
-// 32-bit data, no swizzle; with stride 0 the range check is per byte offset.
-constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy of the weight loads: nt (non-temporal).  Every weight byte is
-// read exactly once per call, and streaming it with nt measured 7-9% more
-// HBM read bandwidth on gfx950 than the default policy.
-constexpr int kStreamAux = 2;
-
 // Load batch t of a row segment: lane l gets value chunks t*64U + l + 64u
 // (u < U) and their mask words.  Raw buffer loads: the resource holds the
 // segment's base and byte size, so the per-lane offsets are loop-invariant,
@@ -451,9 +380,6 @@ __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, i
     for (int b = 0; b < BP; ++b) acc[b] += q < nch ? part[b] : 0.f;
   }
 }
-
-// SiLU in fp32: z * sigmoid(z) = z / (1 + e^-z).
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 template <int BP>
 __device__ __forceinline__ void finish_row(float (&acc)[BP], void *y, int B, int64_t R,
@@ -680,54 +606,6 @@ __global__ __launch_bounds__(1024) void nm_spmv_seg_kernel(
 // private ring of NB such blocks with explicit vmcnt waits; the waves of a
 // workgroup split K and add their tiles through LDS at the end.
 
-typedef _Float16 h8v_t __attribute__((ext_vector_type(8)));
-typedef _Float16 h16v_t __attribute__((ext_vector_type(16)));
-typedef __bf16 b8v_t __attribute__((ext_vector_type(8)));
-typedef __bf16 b16v_t __attribute__((ext_vector_type(16)));
-typedef float f4v_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void *lds_vptr;
-
-// 2-bit in-group positions of the 8 kept values of a lane's 16 columns:
-// nibble g (exactly 2 set bits at p0 < p1) -> p0 | p1 << 2 at bits 4g..4g+3.
-// Branch-free: with bits b0..b3 of a nibble, p0 & 1 = ~b0 & b1,
-// p0 >> 1 = ~b0 & ~b1, p1 & 1 = b3 | ~b2, p1 >> 1 = b3 | b2.
-__device__ __forceinline__ int nib_codes(uint32_t m) {
-  const uint32_t s1 = m >> 1, s2 = m >> 2, s3 = m >> 3;
-  const uint32_t c0 = ~m & s1 & 0x1111u;
-  const uint32_t c1 = ~m & ~s1 & 0x1111u;
-  const uint32_t c2 = (s3 | ~s2) & 0x1111u;
-  const uint32_t c3 = (s3 | s2) & 0x1111u;
-  return (int)(c0 | (c1 << 1) | (c2 << 2) | (c3 << 3));
-}
-
-template <bool BF>
-__device__ __forceinline__ f4v_t smfmac(u32x4_t a, u32x4_t b0, u32x4_t b1, int idx, f4v_t c) {
-  const u32x8_t b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-  if constexpr (BF)
-    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(b8v_t, a),
-                                                    __builtin_bit_cast(b16v_t, b), c, idx, 0, 0);
-  else
-    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8v_t, a),
-                                                   __builtin_bit_cast(h16v_t, b), c, idx, 0, 0);
-}
-
-template <bool BF>
-__device__ __forceinline__ f4v_t dmfma(u32x4_t a, u32x4_t b, f4v_t c) {
-  if constexpr (BF)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8v_t, a),
-                                                  __builtin_bit_cast(b8v_t, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v_t, a),
-                                                 __builtin_bit_cast(h8v_t, b), c, 0, 0, 0);
-}
-
-template <typename T>
-__device__ __forceinline__ void lds_st(uint32_t addr, T v) {
-  *(__attribute__((address_space(3))) T *)(size_t)addr = v;
-}
-
-// Kernel kinds of the matrix-core product.
 constexpr int kMfmaSparse24 = 0;   // 2:4 on v_smfmac
 constexpr int kMfmaDenseHalf = 1;  // 4:8, 8:16: decompressed tile, v_mfma
 constexpr int kMfmaDense1632 = 2;  // 16:32: decompressed tile, v_mfma
@@ -751,30 +629,6 @@ constexpr int kMTileBytes = 16 * kMTileRow;
 __host__ __device__ constexpr int mfma_wave_bytes(int bp, int nb, int kind) {
   return nb * mfma_slot_bytes(bp) + (kind == kMfmaSparse24 ? 0 : kMTileBytes);
 }
-
-// Direct-to-LDS buffer loads: lane i's 16 (or 4) bytes at voff + soff land
-// at LDS address lds + 16 i (4 i); lds is wave-uniform.  The weights stream
-// with the nt policy, x (read by every workgroup) with the default one.
-__device__ __forceinline__ void lds_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff,
-                                              int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(size_t)lds, 16, voff, soff, 0, 2);
-}
-__device__ __forceinline__ void lds_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff,
-                                             int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(size_t)lds, 4, voff, soff, 0, 2);
-}
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff,
-                                           int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(size_t)lds, 16, voff, soff, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left at their maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // Operands of one 64-column step of the matrix-core kernel.
 struct MfmaOps {
@@ -1461,13 +1315,6 @@ __global__ __launch_bounds__(1024) void nm_stream_read_kernel(const char *__rest
 // ---------------------------------------------------------------------------
 // host side
 
-thread_local int g_last_hip = 0;
-
-nm_status hip_fail(hipError_t e) {
-  g_last_hip = (int)e;
-  return NM_ERR_HIP;
-}
-
 struct DevInfo {
   bool init = false;
   int cus = 0;
@@ -1496,18 +1343,6 @@ nm_status device_info(DevInfo *out) {
   }
   *out = d;
   return NM_OK;
-}
-
-bool pattern_ok(int n, int m) {
-  return (m == 4 || m == 8 || m == 16 || m == 32) && 2 * n == m;
-}
-
-bool is16(nm_dtype d) { return d == NM_F16 || d == NM_BF16; }
-
-bool out_ok(nm_dtype in, nm_dtype out) { return out == NM_F32 || out == in; }
-
-bool aligned(const void *p, uintptr_t a) {
-  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
 // Argument checks common to the products; nothing here touches HIP.
@@ -1970,7 +1805,7 @@ const char *nm_status_string(int status) {
   }
 }
 
-int nm_last_hip_error(void) { return g_last_hip; }
+int nm_last_hip_error(void) { return nm_host::g_last_hip; }
 
 int nm_packed_bytes(int64_t rows, int64_t cols, int n, int m, nm_dtype dt,
                     size_t *values_bytes, size_t *bits_bytes) {
