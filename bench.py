@@ -239,8 +239,8 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("a1e9db3a0a0209ca194721024b8b973b2dd228c8d31c5c955fb07e31a3240275",
-                    66277691),
+    (14336, 4096): ("77c901379f58f3b24c52e99fabfe7ace42e3891bdec91d18b99dc8d6d82b0ed4",
+                    66260289),
 }
 
 
