@@ -518,6 +518,65 @@ def hessian_run(args):
     return out
 
 
+def prefill_run(args):
+    """Prefill-side contrast: the 8B gate (14336x4096) and down (4096x14336)
+    shapes, 2:4 fp16, as the batch of tokens grows, against the dense GEMM.
+    Per batch: nm_spmm_prefill (sparse matrix cores, GEMM tiling), the decode
+    entry point nm_spmm_small (batch <= 8), nm_dense_gemv (batch <= 8) and
+    torch linear (hipBLASLt) on the dense weights; four resident copies of
+    each (cache-cold at small batch), us per call and dense-equivalent
+    TFLOP/s (2 R K B / time)."""
+    out = {}
+    L = native.lib()
+    for name, R, K in (("gate", 14336, 4096), ("down", 4096, 14336)):
+        mats = [gpu_layer(R, K, 2, 4, 1000 + i, True) for i in range(4)]
+        res = {}
+        for B in (1, 8, 16, 64, 128, 256, 512, 1024, 2048, 4096):
+            X = torch.randn((B, K), device=DEV).half()
+            Y = torch.empty((B, R), device=DEV)
+            Yh = torch.empty((B, R), dtype=torch.float16, device=DEV)
+            def run(fn):
+                g = capture(lambda: [fn(i) for i in range(8)])
+                ms = time_steps([g], max(5, args.steps // 10), 2) / 8
+                del g
+                return ms * 1e3
+            def pre(i):
+                v, b, _ = mats[i % 4]
+                st = L.nm_spmm_prefill(v.data_ptr(), b.data_ptr(), X.data_ptr(), Y.data_ptr(), B, R,
+                                       K, 2, 4, native.NM_F16, native.NM_F32,
+                                       torch.cuda.current_stream().cuda_stream)
+                assert st == 0, st
+            def dense(i):
+                torch.nn.functional.linear(X, mats[i % 4][2], out=Yh)
+            row = {"nm_spmm_prefill": round(run(pre), 2), "torch_linear": round(run(dense), 2)}
+            if B <= 8:
+                def small(i):
+                    v, b, _ = mats[i % 4]
+                    st = L.nm_spmm_small_cfg(v.data_ptr(), b.data_ptr(), X.data_ptr(), Y.data_ptr(), B,
+                                             R, K, 2, 4, native.NM_F16, native.NM_F32, None,
+                                             torch.cuda.current_stream().cuda_stream)
+                    assert st == 0, st
+                def dgemv(i):
+                    st = L.nm_dense_gemv_cfg(mats[i % 4][2].data_ptr(), X.data_ptr(), Y.data_ptr(), B,
+                                             R, K, native.NM_F16, native.NM_F32, None,
+                                             torch.cuda.current_stream().cuda_stream)
+                    assert st == 0, st
+                row["nm_spmm_small"] = round(run(small), 2)
+                row["nm_dense_gemv"] = round(run(dgemv), 2)
+            best_sparse = min(v for k, v in row.items() if k.startswith("nm_spmm"))
+            best_dense = min(v for k, v in row.items() if k in ("torch_linear", "nm_dense_gemv"))
+            row["prefill_TFLOP/s"] = round(2.0 * R * K * B / (row["nm_spmm_prefill"] * 1e-6) / 1e12, 1)
+            row["dense_TFLOP/s"] = round(2.0 * R * K * B / (row["torch_linear"] * 1e-6) / 1e12, 1)
+            row["speedup_best_sparse_vs_best_dense"] = round(best_dense / best_sparse, 3)
+            res[B] = row
+            log(f"  {name} {R}x{K} B={B}: " + ", ".join(f"{k} {v}" for k, v in row.items()))
+            del X, Y, Yh
+        out[f"{name} {R}x{K}"] = res
+        del mats
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_run(args):
     """Workload 5: 32 stacked Llama-3.1-8B-shaped layers (224 matrices, 2:4
     fp16, a different seed per matrix), all resident; one token = the 224
@@ -624,14 +683,16 @@ def main():
     ap.add_argument("--no-batch4", action="store_true")
     ap.add_argument("--workload", default="llama8b-layer",
                     choices=["llama8b-layer", "single", "patterns", "70b-qwen", "decode-32-layers",
-                             "llama8b-layer-fused", "calibration-hessian"],
+                             "llama8b-layer-fused", "calibration-hessian", "prefill-contrast"],
                     help="llama8b-layer (default, the headline line): one Llama-3.1-8B layer; "
                          "single: the 4096x4096 matrix; patterns: 4:8/8:16/16:32 bf16 on the 8B "
                          "shapes; 70b-qwen: Llama-3.3-70B and Qwen3-32B shapes; "
                          "decode-32-layers: 32 stacked 8B layers timed per token; "
                          "llama8b-layer-fused: the 8B layer step with q|k|v and gate/up fused "
                          "(SwiGLU epilogue) against the unfused and dense steps; "
-                         "calibration-hessian: H += 2 X X^T at the 8B input widths")
+                         "calibration-hessian: H += 2 X X^T at the 8B input widths; "
+                         "prefill-contrast: 2:4 gate/down shapes as the batch grows to 4096 "
+                         "tokens, sparse matrix cores against the dense GEMM")
     ap.add_argument("--counters", action="store_true",
                     help="short eager run for rocprofv3 --pmc: the 14336x4096 sparse kernel on "
                          "5 cache-cold copies, then 5 plain copies of 64 MiB (the known-size "
@@ -658,6 +719,14 @@ def main():
         print(json.dumps({"metric": "decode-layer step time, fused vs unfused sparse and dense",
                           "workload": args.workload, "n_gpus": 1, "data": "synthetic",
                           "unit": "ms/step", **body}), flush=True)
+        return
+    if args.workload == "prefill-contrast":
+        log("workload prefill-contrast")
+        body = {"per_call_us": prefill_run(args)}
+        print(json.dumps({"metric": "2:4 product us per call as the batch grows, sparse vs dense",
+                          "workload": args.workload, "n_gpus": 1, "data": "synthetic",
+                          "dtype": "f16 inputs, fp32 sparse output, f16 torch output", **body}),
+              flush=True)
         return
     if args.workload == "calibration-hessian":
         log("workload calibration-hessian")

@@ -266,6 +266,26 @@ int nm_spmm_swiglu_cfg(const void *values, const uint32_t *bits, const void *X,
                        int m, nm_dtype in_dt, nm_dtype out_dt,
                        const nm_launch_cfg *cfg, void *stream);
 
+/* Prefill-side product on the sparse matrix cores: Y = X . W^T for 2:4 W and
+ * any number of tokens.  The pages contrast the structured-sparsity matrix
+ * path with the dense GEMM: it gains in prefill and loses in decode
+ * ("Introduction" and Figure 1(b)); this entry point is that path here, fed
+ * from the same stored format.  A GEMM tiling (256 rows x 128 tokens per
+ * workgroup, v_smfmac_f32_16x16x64) reuses each weight byte for up to 128
+ * tokens, where the decode entry points stream the weights once per call for
+ * at most 8 tokens.
+ *   values, bits: nm_pack output for 2:4 (rows x cols/2 and rows x cols/32),
+ *                 device; values and X 16-byte aligned, bits 4-byte aligned;
+ *   X:            device, batch x cols, in_dt, row-major (token-major);
+ *   Y:            device, batch x rows, out_dt (NM_F32 or in_dt), row-major;
+ *   cols % 64 == 0; rows * cols and batch * cols * 2 at most INT32_MAX.
+ * batch == 0 or rows == 0 does nothing; cols == 0 writes zeros.
+ * Errors: NM_ERR_INVALID_ARG, NM_ERR_UNSUPPORTED (not 2:4, dtypes),
+ * NM_ERR_SHAPE (cols % 64), NM_ERR_ALIGN, NM_ERR_HIP.  Asynchronous on stream. */
+int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, void *Y,
+                    int64_t batch, int64_t rows, int64_t cols, int n, int m,
+                    nm_dtype in_dt, nm_dtype out_dt, void *stream);
+
 /* Calibration read (measurement only, not part of the product path): loads
  * every byte of buf once with 128-bit loads and writes one word per wavefront
  * of the grid to out (grid * threads_per_wg / 64 uint32, device), so the

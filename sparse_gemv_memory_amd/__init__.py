@@ -19,6 +19,7 @@ from .native import (  # noqa: F401
     nm_select_nm,
     nm_packed_bytes,
     nm_spmm_small,
+    nm_spmm_prefill,
     nm_spmm_swiglu,
     nm_spmv,
 )

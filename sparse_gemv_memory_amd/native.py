@@ -94,6 +94,8 @@ def lib():
     L.nm_spmm_swiglu_cfg.argtypes = [p, p, p, p, ci, i64, i64, ci, ci, ci, ci,
                                      ctypes.POINTER(LaunchCfg), p]
     L.nm_spmm_swiglu_cfg.restype = ci
+    L.nm_spmm_prefill.argtypes = [p, p, p, p, i64, i64, i64, ci, ci, ci, ci, p]
+    L.nm_spmm_prefill.restype = ci
     L.nm_hessian_accumulate.argtypes = [p, p, i64, i64, i64, ci, ctypes.c_float, p]
     L.nm_hessian_accumulate.restype = ci
     L.nm_select_nm.argtypes = [p, p, i64, i64, i64, ci, ci, ci, p, p]
@@ -221,6 +223,24 @@ def nm_spmm_small(values, bits, X, n: int, m: int, out_dtype=torch.float32, out=
                                      _dev(Y, "Y"), batch, rows, cols, n, m, _in_dt(X),
                                      _DT[out_dtype], _cfg_ptr(cfg), _stream(values.device))
     _check(st, "nm_spmm_small")
+    return Y
+
+
+def nm_spmm_prefill(values, bits, X, n: int = 2, m: int = 4, out_dtype=torch.float32, out=None):
+    """Y = X . W_sparse^T for X of shape (batch, cols), any batch (2:4 only),
+    on the sparse matrix cores with a GEMM tiling."""
+    rows, cols = _sparse_args(values, bits, X)
+    if X.dim() != 2 or X.shape[1] != cols:
+        raise ValueError("X must be (batch, cols)")
+    batch = X.shape[0]
+    Y = out if out is not None else torch.empty((batch, rows), dtype=out_dtype, device=values.device)
+    if tuple(Y.shape) != (batch, rows) or Y.dtype != out_dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    with torch.cuda.device(values.device):
+        st = lib().nm_spmm_prefill(_dev(values, "values"), _dev(bits, "bits"), _dev(X, "X"),
+                                   _dev(Y, "Y"), batch, rows, cols, n, m, _in_dt(X),
+                                   _DT[out_dtype], _stream(values.device))
+    _check(st, "nm_spmm_prefill")
     return Y
 
 

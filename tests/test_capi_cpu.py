@@ -43,7 +43,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("nm_packed_bytes", "nm_pack", "nm_spmv", "nm_spmm_small", "nm_dense_gemv",
-              "nm_status_string", "nm_spmm_swiglu", "nm_hessian_accumulate", "nm_select_nm"):
+              "nm_status_string", "nm_spmm_swiglu", "nm_hessian_accumulate", "nm_select_nm",
+              "nm_spmm_prefill"):
         assert n in names
 
 
@@ -155,6 +156,27 @@ def test_hessian_rejects_bad_arguments(L):
     assert h(X=P + 8) == ALIGN
     assert h(H=None, X=None, d=0) == OK  # nothing to do
     assert h(X=None, ntok=0) == OK
+
+
+def test_prefill_rejects_bad_arguments(L):
+    def pf(v=P, b=P, x=P, y=P, batch=16, rows=64, cols=128, n=2, m=4, i=F16, o=F32):
+        return L.nm_spmm_prefill(v, b, x, y, batch, rows, cols, n, m, i, o, None)
+    assert pf(batch=-1) == INV
+    assert pf(rows=-1) == INV
+    assert pf(n=4, m=8) == UNSUP  # the sparse instruction is 2:4
+    assert pf(n=1) == UNSUP
+    assert pf(i=F32) == UNSUP
+    assert pf(o=BF16) == UNSUP  # f16 input, bf16 output
+    assert pf(cols=96) == SHAPE
+    assert pf(rows=1 << 20, cols=1 << 12) == INV  # rows * cols > INT32_MAX
+    assert pf(batch=1 << 20, cols=1 << 11) == INV  # batch * cols * 2 > INT32_MAX
+    assert pf(y=None) == INV
+    assert pf(v=None) == INV
+    assert pf(x=P + 8) == ALIGN
+    assert pf(v=P + 8) == ALIGN
+    assert pf(y=P + 2) == ALIGN
+    assert pf(batch=0, v=None, b=None, x=None, y=None) == OK
+    assert pf(rows=0, v=None, b=None, x=None, y=None) == OK
 
 
 def test_select_rejects_bad_arguments(L):

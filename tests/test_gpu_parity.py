@@ -751,3 +751,99 @@ def test_select_zero_sized_and_rejections():
         native.nm_select_nm(torch.zeros((4, 64), dtype=torch.float16, device=DEV), colw, 3, 4)
     with pytest.raises(ValueError):
         native.nm_select_nm(torch.zeros((4, 64), dtype=torch.float16, device=DEV), colw, 2, 4, cstride=2)
+
+
+# ---- prefill-side product (2:4 on the sparse matrix cores, any batch) ----------------
+
+PREFILL_SHAPES = [(1, 64, 1), (16, 128, 16), (300, 320, 17), (257, 1024, 130), (512, 4096, 128),
+                  (100, 64, 300), (640, 2112, 257)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("rows,cols,batch", PREFILL_SHAPES)
+def test_prefill_integer_exact(rows, cols, batch, dtype):
+    """Integer weights and activations: every partial sum is an exact integer
+    in fp32, so the product must equal the oracle exactly, ragged row and
+    token tiles and several K steps included."""
+    W = synth.integer_weights(rows, cols, seed=rows + cols, dtype=dtype)
+    keep = synth.random_mask(rows, cols, 2, 4, seed=batch)
+    xi = np.random.default_rng(rows * batch).integers(-4, 5, size=(batch, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, dtype)
+    values, bits = gpu_pack(W, keep, 2, 4, dtype)
+    Y = native.nm_spmm_prefill(values, bits, t16(X, dtype))
+    want = oracle.masked_gemv(W, keep, X, dtype == "bf16", threads=8)
+    assert np.array_equal(f64(Y), want)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_matches_oracle(dtype):
+    rows, cols, batch = 700, 1536, 200
+    W, keep, X = inputs(rows, cols, 2, 4, dtype, batch, seed=31)
+    values, bits = gpu_pack(W, keep, 2, 4, dtype)
+    Y = f64(native.nm_spmm_prefill(values, bits, t16(X, dtype)))
+    want = oracle.masked_gemv(W, keep, X, dtype == "bf16", threads=8)
+    for b in range(batch):
+        assert rel_l2(Y[b], want[b]) <= TOL
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_16bit_output_is_rounded_fp32(dtype):
+    rows, cols, batch = 300, 512, 40
+    W, keep, X = inputs(rows, cols, 2, 4, dtype, batch, seed=32)
+    values, bits = gpu_pack(W, keep, 2, 4, dtype)
+    Xt = t16(X, dtype)
+    Y32 = native.nm_spmm_prefill(values, bits, Xt)
+    Y16 = native.nm_spmm_prefill(values, bits, Xt, out_dtype=TDT[dtype])
+    assert torch.equal(Y16, Y32.to(TDT[dtype]))
+
+
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_prefill_agrees_with_decode_kernels(batch):
+    rows, cols = 1000, 4096
+    W, keep, X = inputs(rows, cols, 2, 4, "f16", batch, seed=33)
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    Xt = t16(X, "f16")
+    a = f64(native.nm_spmm_prefill(values, bits, Xt))
+    b = f64(native.nm_spmm_small(values, bits, Xt, 2, 4))
+    for t in range(batch):
+        assert rel_l2(a[t], b[t]) <= 1e-5
+
+
+def test_prefill_full_size_sampled_rows():
+    """14336 x 4096 (the gate/up shape) at 256 tokens, 384 rows against the
+    oracle one by one."""
+    rows, cols, batch = 14336, 4096, 256
+    W = synth.weights(rows, cols, seed=41, dtype="f16")
+    keep = synth.topn_mask(W, 2, 4)
+    X = synth.activations(batch, cols, seed=42, dtype="f16")
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    Y = f64(native.nm_spmm_prefill(values, bits, t16(X, "f16")))
+    idx = np.sort(np.random.default_rng(43).choice(rows, SAMPLE_ROWS, replace=False))
+    idx[0], idx[-1] = 0, rows - 1
+    want = oracle.masked_gemv(W, keep, X, False, rows_idx=idx, threads=8)
+    got = Y[:, idx]
+    for b in range(batch):
+        assert rel_l2(got[b], want[b]) <= TOL
+
+
+def test_prefill_zero_columns_and_empty_batch():
+    values = torch.zeros((40, 0), dtype=torch.float16, device=DEV)
+    bits = torch.zeros((40, 0), dtype=torch.int32, device=DEV)
+    Y = torch.full((5, 40), 3.0, device=DEV)
+    native.nm_spmm_prefill(values, bits, torch.zeros((5, 0), dtype=torch.float16, device=DEV), out=Y)
+    assert torch.count_nonzero(Y).item() == 0
+    W, keep, X = inputs(40, 64, 2, 4, "f16", 1, seed=5)
+    v, b = gpu_pack(W, keep, 2, 4, "f16")
+    Y0 = native.nm_spmm_prefill(v, b, torch.zeros((0, 64), dtype=torch.float16, device=DEV))
+    assert Y0.shape == (0, 40)
+
+
+def test_prefill_rejects_what_it_cannot_run():
+    W, keep, X = inputs(32, 128, 4, 8, "f16", 4, seed=6)
+    v, b = gpu_pack(W, keep, 4, 8, "f16")
+    with pytest.raises(native.NMError):
+        native.nm_spmm_prefill(v, b, t16(X, "f16"), 4, 8)
+    W, keep, X = inputs(32, 96, 2, 4, "f16", 4, seed=7)
+    v, b = gpu_pack(W, keep, 2, 4, "f16")
+    with pytest.raises(native.NMError):
+        native.nm_spmm_prefill(v, b, t16(X, "f16"))
