@@ -836,223 +836,6 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Calibration side: H += scale * X X^T (the Hessian of the layer-wise
-// reconstruction objective, H = 2 X X^T, with X's columns the layer's input
-// activations at the decode steps; Method, OBS paragraph and the
-// decode-time calibration paragraph).  A GEMM-shaped contraction over
-// tokens, so it runs on the dense matrix cores: X is feature-major (row i =
-// feature i over the tokens), so a 16x16x32 operand lane reads 8 consecutive
-// tokens of one feature, A and B alike.  Each workgroup owns a 128 x 128
-// tile of H in the upper triangle and also writes its mirror; 32-token
-// chunks of the two 128-feature row blocks are staged in LDS (rows padded to
-// 80 bytes, so a 16-lane read hits distinct banks), double-buffered with one
-// barrier per chunk; H is read, added to and written once per call (each
-// element belongs to exactly one workgroup, so there are no atomics).
-
-constexpr int kHTile = 128;     // H tile edge
-constexpr int kHChunk = 32;     // tokens per staged chunk
-constexpr int kHRow = 80;       // LDS bytes per staged feature row (64 + 16 pad)
-constexpr int kHBuf = 2 * kHTile * kHRow;  // one buffer: the i and the j row blocks
-constexpr int kHQRow = 64 * 4 + 16;         // epilogue: one wave's 64 x 64 fp32 quarter, padded rows
-constexpr int kHQuarter = 64 * kHQRow;
-constexpr int kHLds = 4 * kHQuarter > 2 * kHBuf ? 4 * kHQuarter : 2 * kHBuf;
-
-template <bool BF>
-__global__ __launch_bounds__(256) void nm_hessian_kernel(float *__restrict__ H,
-                                                         const uint16_t *__restrict__ X, int d,
-                                                         int ntok, int ldx, float scale, int T) {
-  __shared__ __attribute__((aligned(16))) char lds[kHLds];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, q = lane >> 4;
-  // upper-triangle tile (ti <= tj) of this workgroup, row by row
-  int p = blockIdx.x, ti = 0;
-  while (p >= T - ti) { p -= T - ti; ++ti; }
-  const int tj = ti + p;
-  const int i0 = ti * kHTile, j0 = tj * kHTile;
-
-  // staging: piece s of this thread = row (tid + 256 s) / 4 of the i block
-  // (s = 0, 1) or of the j block (s = 2, 3), 16-byte chunk (tid & 3)
-  u32x4_t stg[4];
-  auto load_chunk = [&](int t0) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int piece = tid + 256 * (s & 1);
-      const int row = piece >> 2, c = piece & 3;
-      const int f = ((s >> 1) ? j0 : i0) + row;
-      const int t = t0 + 8 * c;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (f < d && t < ntok) {
-        v = *reinterpret_cast<const u32x4_t *>(X + (int64_t)f * ldx + t);
-        const int left = ntok - t;  // tokens beyond ntok contribute nothing
-        if (left < 8) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (2 * e >= left) v[e] = 0u;
-            else if (2 * e + 1 >= left) v[e] &= 0xffffu;
-          }
-        }
-      }
-      stg[s] = v;
-    }
-  };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int piece = tid + 256 * (s & 1);
-      const int row = piece >> 2, c = piece & 3;
-      *(__attribute__((address_space(3))) u32x4_t *)(size_t)(
-          (uint32_t)(size_t)(lds_ptr)lds + buf * kHBuf + (s >> 1) * kHTile * kHRow + row * kHRow +
-          16 * c) = stg[s];
-    }
-  };
-
-  const int wi = w & 1, wj = w >> 1;  // this wave's 64 x 64 quarter of the tile
-  f4v_t acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = (f4v_t){0.f, 0.f, 0.f, 0.f};
-
-  const int nchunks = (ntok + kHChunk - 1) / kHChunk;
-  if (nchunks > 0) load_chunk(0);
-  for (int k = 0; k < nchunks; ++k) {
-    const int buf = k & 1;
-    store_chunk(buf);
-    __syncthreads();  // chunk k is in LDS; every wave is done with chunk k - 1
-    if (k + 1 < nchunks) load_chunk((k + 1) * kHChunk);
-    const uint32_t base = (uint32_t)(size_t)(lds_ptr)lds + buf * kHBuf;
-    u32x4_t av[4], bv[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-      av[a] = ld<u32x4_t>((lds_ptr)(size_t)(base + (64 * wi + 16 * a + n) * kHRow + 16 * q));
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      bv[b] = ld<u32x4_t>((lds_ptr)(size_t)(base + kHTile * kHRow +
-                                            (64 * wj + 16 * b + n) * kHRow + 16 * q));
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = dmfma<BF>(av[a], bv[b], acc[a][b]);
-  }
-
-  // Epilogue through LDS: each wave parks its 64 x 64 quarter (lane: rows
-  // 4q..4q+3, column n of each 16 x 16) and then updates H with 16-byte
-  // loads and stores, 16 lanes per 256-byte row segment: H[i][j] += scale *
-  // Q[i][j], and for tiles off the diagonal the mirror H[j][i] += scale *
-  // Q[i][j] from the quarter read column-wise.  Rows or columns past d and
-  // segments that do not fill 4 columns take a scalar path.
-  __syncthreads();  // every wave is done with the staging buffers
-  const uint32_t qb = (uint32_t)(size_t)(lds_ptr)lds + (uint32_t)(w * kHQuarter);
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        lds_st<float>(qb + (16 * a + 4 * q + r) * kHQRow + 4 * (16 * b + n), scale * acc[a][b][r]);
-  // (each wave reads back only its own quarter: LDS operations of one wave
-  // complete in order, so no barrier is needed here)
-  const int qi0 = i0 + 64 * wi, qj0 = j0 + 64 * wj;
-  const int c4 = lane & 15, rsub = lane >> 4;  // 16 lanes x 16 bytes per row, 4 rows per pass
-  const bool mirror = ti != tj;
-  // whole 16-byte segments (inside the matrix and aligned) take the vector
-  // path; the others (ragged d) are updated element by element
-  auto vec_ok = [&](int64_t row, int col0) {
-    return row < d && col0 + 3 < d && ((((uintptr_t)(H + row * d + col0)) & 15) == 0);
-  };
-  // 16 passes in groups of GP: the H segments of a group (and of its mirror)
-  // are loaded together, so 2 GP loads per lane are in flight, then added to
-  // and stored (GP = 4 keeps the register count, and the main loop's
-  // occupancy, where it is without the epilogue)
-  constexpr int GP = 4;
-#pragma unroll
-  for (int g0 = 0; g0 < 16; g0 += GP) {
-  f4v_t hd[16], hm[16];
-#pragma unroll
-  for (int pass = g0; pass < g0 + GP; ++pass) {
-    const int rr = 4 * pass + rsub;
-    hd[pass] = (f4v_t){0.f, 0.f, 0.f, 0.f};
-    hm[pass] = (f4v_t){0.f, 0.f, 0.f, 0.f};
-    if (vec_ok(qi0 + rr, qj0 + 4 * c4))
-      hd[pass] = *reinterpret_cast<const f4v_t *>(H + (int64_t)(qi0 + rr) * d + qj0 + 4 * c4);
-    if (mirror && vec_ok(qj0 + rr, qi0 + 4 * c4))
-      hm[pass] = *reinterpret_cast<const f4v_t *>(H + (int64_t)(qj0 + rr) * d + qi0 + 4 * c4);
-  }
-  // add the quarter (row-wise for H, column-wise for the mirror) and store
-#pragma unroll
-  for (int pass = g0; pass < g0 + GP; ++pass) {
-    const int rr = 4 * pass + rsub;
-    const f4v_t v = ld<f4v_t>((lds_ptr)(size_t)(qb + rr * kHQRow + 16 * c4));
-    float mv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mv[e] = ld<float>((lds_ptr)(size_t)(qb + (4 * c4 + e) * kHQRow + 4 * rr));
-    {
-      const int64_t row = qi0 + rr;
-      const int col0 = qj0 + 4 * c4;
-      if (vec_ok(row, col0)) {
-        *reinterpret_cast<f4v_t *>(H + row * d + col0) = hd[pass] + v;
-      } else if (row < d) {
-        for (int e = 0; e < 4; ++e)
-          if (col0 + e < d) H[row * d + col0 + e] += v[e];
-      }
-    }
-    if (mirror) {
-      const int64_t row = qj0 + rr;
-      const int col0 = qi0 + 4 * c4;
-      if (vec_ok(row, col0)) {
-        f4v_t h = hm[pass];
-        h[0] += mv[0]; h[1] += mv[1]; h[2] += mv[2]; h[3] += mv[3];
-        *reinterpret_cast<f4v_t *>(H + row * d + col0) = h;
-      } else if (row < d) {
-        for (int e = 0; e < 4; ++e)
-          if (col0 + e < d) H[row * d + col0 + e] += mv[e];
-      }
-    }
-  }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Calibration side: N:M mask selection.  In every group of M consecutive
-// weights of a row, keep the N with the largest score w^2 * s[c] for a
-// per-column weight s: s = diag(H), H = 2 X X^T, orders the weights by
-// |w| * ||x_c|| (the Wanda backend the pages name); s = 1 / diag(H^-1) gives
-// the OBS saliency of one weight.  Ties go to the lower column.  The score is
-// an fp32 product of exact fp32 values, (w * w) * s, so the decision is
-// reproducible bit for bit; a NaN score is taken as -inf.  One lane per group;
-// a column's rank is the number of columns of its group that beat it.
-
-template <bool BF, int M>
-__global__ __launch_bounds__(256) void nm_select_kernel(const uint16_t *__restrict__ W,
-                                                        const float *__restrict__ colw,
-                                                        int64_t cstride, int64_t groups,
-                                                        int K, int N,
-                                                        uint8_t *__restrict__ keep) {
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= groups) return;
-  const int64_t gpr = K / M;
-  const int64_t r = g / gpr;
-  const int c0 = (int)(g - r * gpr) * M;
-  float sc[M];
-#pragma unroll
-  for (int c = 0; c < M; ++c) {
-    const uint16_t bits = W[r * K + c0 + c];
-    const float w = BF ? __uint_as_float((uint32_t)bits << 16) : (float)__builtin_bit_cast(_Float16, bits);
-    const float cw = colw[(int64_t)(c0 + c) * cstride];
-    const float s = (w * w) * cw;
-    sc[c] = (s == s) ? s : -__builtin_inff();
-  }
-#pragma unroll
-  for (int c = 0; c < M; ++c) {
-    int rank = 0;
-#pragma unroll
-    for (int e = 0; e < M; ++e) rank += (sc[e] > sc[c]) || (sc[e] == sc[c] && e < c);
-    keep[r * K + c0 + c] = rank < N ? 1 : 0;
-  }
-}
-
 // Dense comparison when x fits the LDS budget, built like the sparse row
 // kernel so that the speedup is measured against an equally tuned dense
 // GEMV: x staged once per workgroup as BP contiguous rows; each wave walks
@@ -1894,52 +1677,6 @@ int nm_spmm_swiglu_cfg(const void *values, const uint32_t *bits, const void *X, 
   if (inter < 0 || inter > INT32_MAX / 2) return NM_ERR_INVALID_ARG;
   return sparse_product(values, bits, X, H, batch, 2 * inter, cols, n, m, in_dt, out_dt, cfg,
                         stream, kEpiSwiglu);
-}
-
-int nm_hessian_accumulate(float *H, const void *X, int64_t d, int64_t ntok, int64_t ld,
-                          nm_dtype in_dt, float scale, void *stream) {
-  if (d < 0 || ntok < 0 || ld < ntok) return NM_ERR_INVALID_ARG;
-  if (d > 23170 || d * ld > INT32_MAX) return NM_ERR_INVALID_ARG;  // 32-bit tile and row offsets
-  if (!is16(in_dt)) return NM_ERR_UNSUPPORTED;
-  if (ld % 8 != 0) return NM_ERR_SHAPE;
-  if (d == 0) return NM_OK;
-  if (!H || (!X && ntok > 0)) return NM_ERR_INVALID_ARG;
-  if (!aligned(H, 4) || !aligned(X, 16)) return NM_ERR_ALIGN;
-  if (ntok == 0) return NM_OK;
-  const int T = (int)((d + kHTile - 1) / kHTile);
-  const int64_t grid = (int64_t)T * (T + 1) / 2;
-  auto fn = in_dt == NM_BF16 ? nm_hessian_kernel<true> : nm_hessian_kernel<false>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, H,
-                     (const uint16_t *)X, (int)d, (int)ntok, (int)ld, scale, T);
-  hipError_t e = hipGetLastError();
-  return e == hipSuccess ? NM_OK : hip_fail(e);
-}
-
-int nm_select_nm(const void *W, const float *colw, int64_t cstride, int64_t rows, int64_t cols,
-                 int n, int m, nm_dtype dt, uint8_t *keep, void *stream) {
-  if (rows < 0 || cols < 0 || cstride < 1) return NM_ERR_INVALID_ARG;
-  if (!pattern_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
-  if (cols % 32 != 0) return NM_ERR_SHAPE;
-  if (rows == 0 || cols == 0) return NM_OK;
-  if (!W || !colw || !keep) return NM_ERR_INVALID_ARG;
-  if (!aligned(W, 2) || !aligned(colw, 4)) return NM_ERR_ALIGN;
-  if (cols > INT32_MAX) return NM_ERR_INVALID_ARG;
-  const int64_t groups = rows * (cols / m);
-  const int64_t grid = (groups + 255) / 256;
-  if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
-  const bool bf = dt == NM_BF16;
-  auto go = [&](auto fn) {
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
-                       (const uint16_t *)W, colw, cstride, groups, (int)cols, n, keep);
-  };
-  switch (m) {
-    case 4: bf ? go(nm_select_kernel<true, 4>) : go(nm_select_kernel<false, 4>); break;
-    case 8: bf ? go(nm_select_kernel<true, 8>) : go(nm_select_kernel<false, 8>); break;
-    case 16: bf ? go(nm_select_kernel<true, 16>) : go(nm_select_kernel<false, 16>); break;
-    default: bf ? go(nm_select_kernel<true, 32>) : go(nm_select_kernel<false, 32>); break;
-  }
-  hipError_t e = hipGetLastError();
-  return e == hipSuccess ? NM_OK : hip_fail(e);
 }
 
 int nm_default_launch(int64_t rows, int64_t cols, int batch, int n, int m, int dense,
