@@ -239,7 +239,7 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("77c901379f58f3b24c52e99fabfe7ace42e3891bdec91d18b99dc8d6d82b0ed4",
+    (14336, 4096): ("e437ed69efc714a20c13f95b48cdc1eb65426af49bfdcbb3962b3b89ce12f3fe",
                     66260289),
 }
 
