@@ -57,18 +57,43 @@ __host__ __device__ constexpr int prefill_lds(int ns) { return ns * kPStage; }
 #endif
 constexpr int kPrefillStages = NM_PREFILL_STAGES;  // ring depth (LDS: 34 KiB per step)
 
+// An LDS read the compiler may not repeat or drop: the fragments of the next
+// step are read once, into registers, while the current step's products run.
+template <typename T>
+__device__ __forceinline__ T vld(uint32_t addr) {
+  return *(volatile __attribute__((address_space(3))) T *)(size_t)addr;
+}
+
+// Direct-to-LDS load of 4 bytes per lane with the default cache policy: the
+// weights are reused by every token tile of their row tile, so they must stay
+// in L2 (the streaming policy of the decode kernels measured 20% slower here).
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(size_t)lds, 4, voff, soff, 0, 0);
+}
+
 template <bool BF, int NS>
 __global__ __launch_bounds__(256) void nm_spmm_prefill_kernel(
     const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
-    const uint16_t *__restrict__ x, void *__restrict__ y, int B, int R, int K, int ntt,
+    const uint16_t *__restrict__ x, void *__restrict__ y, int B, int R, int K, int nrt, int ntt,
     int out_kind) {
-  static_assert(NS >= 2 && (NS - 2) * kPDma < 64, "ring depth");
+  static_assert(NS >= 3 && (NS - 2) * kPDma < 64, "ring depth");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15, j = lane >> 4;
-  const int rt = blockIdx.x / ntt, tt = blockIdx.x - rt * ntt;
+  // Tile of this workgroup.  Workgroups go to the 8 XCDs round-robin
+  // (block b on XCD b % 8), and each XCD has its own L2: XCD x takes a
+  // contiguous range of tiles, ordered by groups of 4 row tiles x all token
+  // tiles, so the workgroups running together on one XCD share their
+  // weights and activations through its L2.
+  const int T = nrt * ntt;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int tile = xcd * (T / 8) + min(xcd, T % 8) + slot;
+  const int group = tile / (4 * ntt);
+  const int first_r = 4 * group, gr = min(nrt - first_r, 4);
+  const int in = tile - group * 4 * ntt;
+  const int rt = first_r + in % gr, tt = in / gr;
   const int row0 = rt * kPRows, tok0 = tt * kPToks;
   const int nk = K >> 6;
   const uint32_t base = (uint32_t)(size_t)(lds_ptr)lds;
@@ -124,10 +149,10 @@ __global__ __launch_bounds__(256) void nm_spmm_prefill_kernel(
     const __amdgpu_buffer_rsrc_t V = real ? rv : r0, M = real ? rb : r0, X = real ? rx : r0;
     const uint32_t st = base + (uint32_t)((s % NS) * kPStage);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lds_load16_nt(V, st + 1024 * (4 * q + w), voff[q], 64 * s);
+    for (int q = 0; q < 4; ++q) lds_load16(V, st + 1024 * (4 * q + w), voff[q], 64 * s);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
-      lds_load4_nt(M, st + kPValBytes + 256 * (4 * q + w), moff[q], 8 * s);
+      lds_load4(M, st + kPValBytes + 256 * (4 * q + w), moff[q], 8 * s);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       lds_load16(X, st + kPValBytes + kPMaskBytes + 1024 * (4 * q + w), xoff[q], 128 * s);
@@ -140,40 +165,67 @@ __global__ __launch_bounds__(256) void nm_spmm_prefill_kernel(
     for (int t = 0; t < 4; ++t) acc[i][t] = (f4v_t){0.f, 0.f, 0.f, 0.f};
 
   const int wr = w & 1, wc = w >> 1;
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s);
-  for (int s = 0; s < nk; ++s) {
-    // step s has landed (NS - 2 younger steps stay in flight); after the
-    // barrier every wave's part of it is in LDS, and every wave is done
-    // with step s - 1 (its LDS reads fed the products already), whose slot
-    // is refilled next.  A bare s_barrier: __syncthreads() would add a
-    // workgroup fence, i.e. wait for every load in flight.
-    wait_vmcnt<(NS - 2) * kPDma>();
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue(s + NS - 1);
-    const uint32_t st = base + (uint32_t)((s % NS) * kPStage);
-    // A operands of the wave's 8 row tiles
+  // operands of one step: A fragments and raw mask words of the 8 row tiles,
+  // B fragments of the 4 token tiles
+  struct Frag {
     u32x4_t a[8];
-    int idx[8];
+    uint32_t mw[8];
+    u32x4_t b[4][2];
+  };
+  auto read_frags = [&](Frag &f, int s) {
+    const uint32_t st = base + (uint32_t)((s % NS) * kPStage);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 128 * wr + 16 * i + n;
-      a[i] = ld<u32x4_t>((lds_ptr)(size_t)(st + r * kPValRow + 16 * (j ^ ((r >> 2) & 3))));
-      const uint32_t mw = ld<uint32_t>((lds_ptr)(size_t)(st + kPValBytes + r * 8 + 4 * (j >> 1)));
-      idx[i] = nib_codes(mw >> ((j & 1) * 16));
+      f.a[i] = vld<u32x4_t>(st + r * kPValRow + 16 * (j ^ ((r >> 2) & 3)));
+      f.mw[i] = vld<uint32_t>(st + kPValBytes + r * 8 + 4 * (j >> 1));
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int tk = 64 * wc + 16 * t + n;
       const uint32_t xr = st + kPValBytes + kPMaskBytes + tk * kPXRow;
       const int sw = (tk >> 1) & 7;
-      const u32x4_t b0 = ld<u32x4_t>((lds_ptr)(size_t)(xr + 16 * (j ^ sw)));
-      const u32x4_t b1 = ld<u32x4_t>((lds_ptr)(size_t)(xr + 16 * ((4 + j) ^ sw)));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][t] = smfmac<BF>(a[i], b0, b1, idx[i], acc[i][t]);
+      f.b[t][0] = vld<u32x4_t>(xr + 16 * (j ^ sw));
+      f.b[t][1] = vld<u32x4_t>(xr + 16 * ((4 + j) ^ sw));
     }
+  };
+  // Software pipeline: the products of step s run while the fragments of
+  // step s + 1 are read from LDS.  Steps s + 2 .. s + NS - 1 are in flight.
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  wait_vmcnt<(NS - 2) * kPDma>();  // step 0 has landed
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  Frag cur;
+  read_frags(cur, 0);
+  for (int s = 0; s < nk; ++s) {
+    // step s + 1 has landed (NS - 3 younger steps stay in flight); the
+    // fragments of step s are in registers, so after the barrier every
+    // wave is done with slot (s - 1) % NS, which is refilled next
+    wait_vmcnt<(NS - 3) * kPDma>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(s + NS - 1);
+    Frag nxt;
+    read_frags(nxt, s + 1);
+    int idx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) idx[i] = nib_codes(cur.mw[i] >> ((j & 1) * 16));
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[i][t] = smfmac<BF>(cur.a[i], cur.b[t][0], cur.b[t][1], idx[i], acc[i][t]);
+    // issue order: one product, one LDS read of the next step, 24 times,
+    // then the last 8 products
+#pragma unroll
+    for (int k = 0; k < 24; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    cur = nxt;
   }
   wait_vmcnt<0>();  // the trailing dummy loads still write LDS
 
@@ -215,7 +267,7 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
   auto go = [&](auto fn) {
     hipLaunchKernelGGL(fn, dim3((unsigned)(nrt * ntt)), dim3(256), prefill_lds(NS), (hipStream_t)stream,
                        (const uint16_t *)values, bits, (const uint16_t *)X, Y, (int)batch,
-                       (int)rows, (int)cols, (int)ntt, (int)out_dt);
+                       (int)rows, (int)cols, (int)nrt, (int)ntt, (int)out_dt);
   };
   if (in_dt == NM_BF16)
     go(nm_spmm_prefill_kernel<true, NS>);
