@@ -106,6 +106,8 @@ def lib():
     L.nm_dense_gemv_cfg.restype = ci
     L.nm_default_launch.argtypes = [i64, i64, ci, ci, ci, ci, ctypes.POINTER(LaunchCfg)]
     L.nm_default_launch.restype = ci
+    L.nm_stream_read.argtypes = [p, sz, p, ci, ci, p]
+    L.nm_stream_read.restype = ci
     _lib = L
     return L
 
@@ -331,3 +333,20 @@ def nm_default_launch(rows: int, cols: int, batch: int, n: int = 2, m: int = 4,
     _check(lib().nm_default_launch(rows, cols, batch, n, m, int(bool(dense)), ctypes.byref(c)),
            "nm_default_launch")
     return c
+
+
+def nm_stream_read(buf: torch.Tensor, out: torch.Tensor, grid: int = 512, threads_per_wg: int = 256,
+                   nbytes: Optional[int] = None):
+    """Read nbytes (default: all) of buf once with the calibration read kernel;
+    out (int32 or uint32, at least grid * threads_per_wg / 64 elements)
+    receives one word per wave."""
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    if out.numel() * out.element_size() < 4 * grid * (threads_per_wg // 64):
+        raise ValueError("out needs one 4-byte word per wave of the grid")
+    with torch.cuda.device(buf.device):
+        st = lib().nm_stream_read(_dev(buf, "buf"), nbytes, _dev(out, "out"), grid,
+                                  threads_per_wg, _stream(buf.device))
+    _check(st, "nm_stream_read")
+

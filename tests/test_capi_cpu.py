@@ -53,6 +53,13 @@ def test_library_exports_every_declared_function(L):
     assert missing == []
 
 
+def test_binding_declares_every_argument_type(L):
+    # an undeclared ctypes function masks Python ints to 32 bits, which would
+    # turn a 64-bit device address into a wild pointer
+    undeclared = [n for n in _declared() if getattr(L, n).argtypes is None]
+    assert undeclared == []
+
+
 def test_status_strings(L):
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert L.nm_status_string(s).decode().startswith("NM_")
