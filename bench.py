@@ -239,8 +239,8 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("e437ed69efc714a20c13f95b48cdc1eb65426af49bfdcbb3962b3b89ce12f3fe",
-                    66260289),
+    (14336, 4096): ("07da70420d80528af7ddd5ed9be6f3a0830f89ff9cf4c8de1c1a000489997057",
+                    66270525),
 }
 
 

@@ -248,8 +248,12 @@ __device__ __forceinline__ void chunk8_nibbles(const char *lds, uint32_t base, u
 
 // Pattern kinds: the traversal a kernel is compiled for (Appendix C: one
 // kernel per pattern, with N and M fixed at compile time).  kPat24x is 2:4 at
-// batch 1 in the row kernel, with x stored plainly (see chunk24x).
-enum { kPat24 = 0, kPatHalf = 1, kPat1632 = 2, kPat24x = 3 };
+// batch 1 in the row kernel, with x stored plainly (see chunk24x); kPat24xE
+// is the same where the load batches divide the row exactly (no chunk of a
+// batch lies past the row end, so the guards of run_batch are left out).
+enum { kPat24 = 0, kPatHalf = 1, kPat1632 = 2, kPat24x = 3, kPat24xE = 4 };
+
+__host__ __device__ constexpr bool plain_x(int pk) { return pk == kPat24x || pk == kPat24xE; }
 
 __host__ __device__ constexpr int pattern_kind(int m) {
   return m == 4 ? kPat24 : m == 32 ? kPat1632 : kPatHalf;
@@ -274,12 +278,12 @@ __host__ __device__ constexpr int pattern_kind(int m) {
 constexpr uint32_t kPos0Lo = 0x02000000u, kPos0Hi = 0x00040200u;  // n >> 1 -> 2 p0
 constexpr uint32_t kPos1Lo = 0x04040200u, kPos1Hi = 0x00060606u;  // n >> 1 -> 2 p1
 
+// chunk24x_ops takes the chunk's 32 bytes of x (xa: columns 0..7, xc:
+// columns 8..15) already read from LDS.
 template <bool BF>
-__device__ __forceinline__ void chunk24x(const char *lds, int q, uint32_t mw, const uint4 v,
-                                         float &acc) {
+__device__ __forceinline__ void chunk24x_ops(int q, uint32_t mw, const uint4 v, const u32x4_t xa,
+                                             const u32x4_t xc, float &acc) {
   const uint32_t m = (mw >> ((q & 1) << 4)) & 0xffffu;
-  const lds_ptr xb = (lds_ptr)lds + 32 * q;
-  const u32x4_t xa = ld<u32x4_t>(xb), xc = ld<u32x4_t>(xb + 16);
   const uint32_t X[8] = {xa[0], xa[1], xa[2], xa[3], xc[0], xc[1], xc[2], xc[3]};
   // table indices n >> 1 of nibbles 0, 2, 1, 3 in bytes 0..3
   const uint32_t t = m >> 1;
@@ -297,11 +301,18 @@ __device__ __forceinline__ void chunk24x(const char *lds, int q, uint32_t mw, co
   }
 }
 
+template <bool BF>
+__device__ __forceinline__ void chunk24x(const char *lds, int q, uint32_t mw, const uint4 v,
+                                         float &acc) {
+  const lds_ptr xb = (lds_ptr)lds + 32 * q;
+  chunk24x_ops<BF>(q, mw, v, ld<u32x4_t>(xb), ld<u32x4_t>(xb + 16), acc);
+}
+
 template <bool BF, int BP, int PK>
 __device__ __forceinline__ void chunk(const char *lds, int q, uint32_t mw, const uint4 v,
                                       float (&acc)[BP]) {
   using L = XLay<BP>;
-  if constexpr (PK == kPat24x) {
+  if constexpr (plain_x(PK)) {
     static_assert(BP == 1, "the plain x layout is for batch 1");
     chunk24x<BF>(lds, q, mw, v, acc[0]);
     return;
@@ -344,7 +355,9 @@ struct Batch {
 // the batch offset is a scalar, and a chunk past the end reads zeros (the
 // hardware range check) without touching memory.  nch = 0 makes a dummy
 // batch that keeps the wait counts uniform and costs no memory traffic.
-template <int U>
+// MF: the mask words are issued before the values, so the first chunk of a
+// batch waits for one value load less.
+template <int U, bool MF = false>
 __device__ __forceinline__ void load_batch(Batch<U> &bt, const uint4 *vrow,
                                            const uint32_t *brow, int nch, int t, int lane) {
   const __amdgpu_buffer_rsrc_t rv =
@@ -352,6 +365,17 @@ __device__ __forceinline__ void load_batch(Batch<U> &bt, const uint4 *vrow,
   const __amdgpu_buffer_rsrc_t rb =
       __builtin_amdgcn_make_buffer_rsrc((void *)brow, 0, nch * 2, kRsrcWord3);
   const int sv = t * (kWave * U * 16), sb = t * (kWave * U * 2);
+  if constexpr (MF) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      bt.m[u] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lane >> 1) * 4 + u * kWave * 2, sb,
+                                                     kStreamAux);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      bt.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rv, lane * 16 + u * kWave * 16, sv, kStreamAux));
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     bt.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -368,6 +392,32 @@ __device__ __forceinline__ void load_batch(Batch<U> &bt, const uint4 *vrow,
 template <bool BF, int BP, int PK, int U>
 __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, int q0, int nch,
                                           float (&acc)[BP]) {
+  if constexpr (plain_x(PK)) {
+    // the x operands of every chunk first: their LDS addresses do not depend
+    // on the loaded data, so the reads overlap the wait for the batch
+    constexpr bool exact = PK == kPat24xE;
+    u32x4_t xa[U], xc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + kWave * u;
+      const lds_ptr xb = (lds_ptr)lds + 32 * (exact ? q : min(q, nch - 1));
+      xa[u] = ld<u32x4_t>(xb);
+      xc[u] = ld<u32x4_t>(xb + 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + kWave * u;
+      if constexpr (exact) {
+        chunk24x_ops<BF>(q, bt.m[u], bt.v[u], xa[u], xc[u], acc[0]);
+      } else {
+        float part = 0.f;
+        chunk24x_ops<BF>(min(q, nch - 1), bt.m[u], bt.v[u], xa[u], xc[u], part);
+        acc[0] += q < nch ? part : 0.f;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int q = q0 + kWave * u;
@@ -465,13 +515,13 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
     const bool real = k < nitems;
     const int ii = real ? k / nb : 0, tt = real ? k - ii * nb : 0;
     const int64_t r = real ? r0 + ii : 0;
-    load_batch<U>(bt, values + r * cpr, bits + r * wpr, real ? nch : 0, tt, lane);
+    load_batch<U, plain_x(PK)>(bt, values + r * cpr, bits + r * wpr, real ? nch : 0, tt, lane);
   };
   Batch<U> A, Bt;
   item_load(A, 0);
   item_load(Bt, 1);
   // clamped groups rewrite group ngx-1 with the same data it already holds
-  if constexpr (PK == kPat24x) {  // plain layout: group g at byte 16 g
+  if constexpr (plain_x(PK)) {  // plain layout: group g at byte 16 g
 #pragma unroll
     for (int s = 0; s < XS; ++s)
       reinterpret_cast<uint4 *>(lds)[min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1)] =
@@ -1398,25 +1448,32 @@ rows_fn pick_rows_bp(int bp, int u, int xs) {
   }
 }
 
-template <bool BF>
-rows_fn pick_rows_24x(int u, int xs) {
+template <bool BF, int PK>
+rows_fn pick_rows_24x_xs(int u, int xs) {
   if (xs > 4)
-    return u == 5 ? nm_spmv_rows_kernel<BF, 1, kPat24x, 5, 8> : nm_spmv_rows_kernel<BF, 1, kPat24x, 4, 8>;
-  return u == 5 ? nm_spmv_rows_kernel<BF, 1, kPat24x, 5, 4> : nm_spmv_rows_kernel<BF, 1, kPat24x, 4, 4>;
+    return u == 5 ? nm_spmv_rows_kernel<BF, 1, PK, 5, 8> : nm_spmv_rows_kernel<BF, 1, PK, 4, 8>;
+  return u == 5 ? nm_spmv_rows_kernel<BF, 1, PK, 5, 4> : nm_spmv_rows_kernel<BF, 1, PK, 4, 4>;
 }
 
 template <bool BF>
-rows_fn pick_rows_pk(int pk, int bp, int u, int xs) {
+rows_fn pick_rows_24x(int u, int xs, bool exact) {
+  return exact ? pick_rows_24x_xs<BF, kPat24xE>(u, xs) : pick_rows_24x_xs<BF, kPat24x>(u, xs);
+}
+
+template <bool BF>
+rows_fn pick_rows_pk(int pk, int bp, int u, int xs, bool exact) {
   switch (pk) {
-    case kPat24: return bp == 1 ? pick_rows_24x<BF>(u, xs) : pick_rows_bp<BF, kPat24>(bp, u, xs);
+    case kPat24: return bp == 1 ? pick_rows_24x<BF>(u, xs, exact) : pick_rows_bp<BF, kPat24>(bp, u, xs);
     case kPatHalf: return pick_rows_bp<BF, kPatHalf>(bp, u, xs);
     default: return pick_rows_bp<BF, kPat1632>(bp, u, xs);
   }
 }
 
-// xs: x groups (8 columns each at batch 1) a thread needs to stage all of x
-rows_fn pick_rows(bool bf, int pk, int bp, int u, int xs) {
-  return bf ? pick_rows_pk<true>(pk, bp, u, xs) : pick_rows_pk<false>(pk, bp, u, xs);
+// xs: x groups (8 columns each at batch 1) a thread needs to stage all of x;
+// exact: the row's value chunks are a whole number of load batches (only the
+// 2:4 batch-1 kernel has a separate kind for it)
+rows_fn pick_rows(bool bf, int pk, int bp, int u, int xs, bool exact) {
+  return bf ? pick_rows_pk<true>(pk, bp, u, xs, exact) : pick_rows_pk<false>(pk, bp, u, xs, exact);
 }
 
 // Chunks per lane per load batch of the batch-1 row kernel: 4, or 5 when
@@ -1553,7 +1610,9 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
     if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
     const int xs = (int)((cols / 8 + cfg.threads_per_wg - 1) / cfg.threads_per_wg);
-    hipLaunchKernelGGL(pick_rows(bf, pk, bp, rows_batch_chunks(cols, bp), xs), dim3((unsigned)grid),
+    const int ub = rows_batch_chunks(cols, bp);
+    const bool exact = cols % (1024LL * ub) == 0;  // 16 columns per chunk, 64 lanes
+    hipLaunchKernelGGL(pick_rows(bf, pk, bp, ub, xs, exact), dim3((unsigned)grid),
                        dim3(cfg.threads_per_wg),
                        sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32), (hipStream_t)stream,
                        (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
