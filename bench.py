@@ -239,7 +239,7 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("07da70420d80528af7ddd5ed9be6f3a0830f89ff9cf4c8de1c1a000489997057",
+    (14336, 4096): ("a41b0913a27900c4ac644d5d047ab30daefcd81ed6dc5863cbffa9ef888196a5",
                     66270525),
 }
 

@@ -389,32 +389,37 @@ __device__ __forceinline__ void load_batch(Batch<U> &bt, const uint4 *vrow,
 // computed like any other at the row's last column range, without a branch,
 // and its sum is dropped by a select.  Straight-line code keeps the wait
 // counts of the pipeline exact.
+// qb (plain-x kinds): the batch's first chunk, t * 64 * U, a wave-uniform
+// value.  A batch that ends inside the row takes the guard-free code; in the
+// row's last batch, groups of 64 chunks wholly past the row end are skipped by
+// a uniform branch.
 template <bool BF, int BP, int PK, int U>
 __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, int q0, int nch,
-                                          float (&acc)[BP]) {
+                                          float (&acc)[BP], int qb = 0) {
   if constexpr (plain_x(PK)) {
-    // the x operands of every chunk first: their LDS addresses do not depend
-    // on the loaded data, so the reads overlap the wait for the batch
-    constexpr bool exact = PK == kPat24xE;
-    u32x4_t xa[U], xc[U];
+    if (PK == kPat24xE || qb + kWave * U <= nch) {
+      // the x operands of every chunk first: their LDS addresses do not
+      // depend on the loaded data, so the reads overlap the wait for the batch
+      u32x4_t xa[U], xc[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = q0 + kWave * u;
-      const lds_ptr xb = (lds_ptr)lds + 32 * (exact ? q : min(q, nch - 1));
-      xa[u] = ld<u32x4_t>(xb);
-      xc[u] = ld<u32x4_t>(xb + 16);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = q0 + kWave * u;
-      if constexpr (exact) {
-        chunk24x_ops<BF>(q, bt.m[u], bt.v[u], xa[u], xc[u], acc[0]);
-      } else {
-        float part = 0.f;
-        chunk24x_ops<BF>(min(q, nch - 1), bt.m[u], bt.v[u], xa[u], xc[u], part);
-        acc[0] += q < nch ? part : 0.f;
+      for (int u = 0; u < U; ++u) {
+        const lds_ptr xb = (lds_ptr)lds + 32 * (q0 + kWave * u);
+        xa[u] = ld<u32x4_t>(xb);
+        xc[u] = ld<u32x4_t>(xb + 16);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        chunk24x_ops<BF>(q0 + kWave * u, bt.m[u], bt.v[u], xa[u], xc[u], acc[0]);
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (qb + kWave * u >= nch) break;
+      const int q = q0 + kWave * u;
+      float part = 0.f;
+      chunk24x<BF>(lds, min(q, nch - 1), bt.m[u], bt.v[u], part);
+      acc[0] += q < nch ? part : 0.f;
     }
     return;
   }
@@ -542,12 +547,12 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   // two-buffer pipeline: while one batch is consumed the other is in flight
   for (int k = 0; k < nitems; k += 2) {
     const int i = k / nb, t = k - i * nb;
-    run_batch<BF, BP, PK, U>(lds, A, t * kWave * U + lane, nch, acc);
+    run_batch<BF, BP, PK, U>(lds, A, t * kWave * U + lane, nch, acc, t * kWave * U);
     if (t == nb - 1) collect_row<BP>(acc, res, i, lane);
     item_load(A, k + 2);
     if (k + 1 >= nitems) break;
     const int i1 = (k + 1) / nb, t1 = (k + 1) - i1 * nb;
-    run_batch<BF, BP, PK, U>(lds, Bt, t1 * kWave * U + lane, nch, acc);
+    run_batch<BF, BP, PK, U>(lds, Bt, t1 * kWave * U + lane, nch, acc, t1 * kWave * U);
     if (t1 == nb - 1) collect_row<BP>(acc, res, i1, lane);
     item_load(Bt, k + 3);
   }
