@@ -91,9 +91,13 @@ void oracle_decode16(const uint16_t *in, int64_t count, int is_bf16, double *out
 
 /* ---- format checks ------------------------------------------------------ */
 
-/* Only the 50% patterns the pages evaluate: N = M/2, M in {4, 8, 16, 32}. */
+/* N:M patterns whose groups tile an aligned 32-bit word: M in {4, 8, 16, 32}
+ * and 0 < N < M.  The pages evaluate the 50% ones (N = M/2); at any N the
+ * same format holds, each aligned word then carrying exactly 32*N/M kept
+ * columns (the fixed-count argument of "Method", item (2), which the pages
+ * make at 50%). */
 int oracle_pattern_supported(int n, int m) {
-    return (m == 4 || m == 8 || m == 16 || m == 32) && 2 * n == m;
+    return (m == 4 || m == 8 || m == 16 || m == 32) && n > 0 && n < m;
 }
 
 /* Number of M-groups of `keep` that do not hold exactly N kept entries.
@@ -234,7 +238,8 @@ void oracle_hessian_f64(const uint16_t *X, int is_bf16, int64_t d, int64_t ntok,
  * ("Method", OBS paragraph). */
 int oracle_select_nm(const uint16_t *W, int is_bf16, const float *colw, int64_t cstride,
                      int64_t rows, int64_t cols, int n, int m, uint8_t *keep) {
-    if (!oracle_pattern_supported(n, m)) return OR_ERR_UNSUPPORTED;
+    /* the calibration side is built for the 50% patterns only */
+    if (!oracle_pattern_supported(n, m) || 2 * n != m) return OR_ERR_UNSUPPORTED;
     if (cols % m != 0) return OR_ERR_SHAPE;
     float score[32];
     int chosen[32];

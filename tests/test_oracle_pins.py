@@ -139,8 +139,12 @@ def test_pack_rejects_bad_inputs():
     bad[1, 5] ^= 1  # one group now holds 1 or 3
     assert oracle.pack(W, bad, 2, 4)[0] == oracle.ERR_MASK
     assert oracle.count_bad_groups(bad, 2, 4) == 1
-    assert oracle.pack(W, keep, 1, 4)[0] == oracle.ERR_UNSUPPORTED
-    assert oracle.pack(W, keep, 3, 8)[0] == oracle.ERR_UNSUPPORTED
+    # patterns outside 0 < N < M, M in {4, 8, 16, 32}
+    for n, m in [(0, 4), (4, 4), (2, 6), (3, 12), (32, 64)]:
+        assert oracle.pack(W, keep, n, m)[0] == oracle.ERR_UNSUPPORTED
+    # a valid 2:4 mask is not a valid 1:4 or 3:4 mask
+    assert oracle.pack(W, keep, 1, 4)[0] == oracle.ERR_MASK
+    assert oracle.pack(W, keep, 3, 4)[0] == oracle.ERR_MASK
     assert oracle.pack(W[:, :48], keep[:, :48], 2, 4)[0] == oracle.ERR_SHAPE
 
 
@@ -176,6 +180,110 @@ def test_packed_size_is_pattern_independent():
         assert st == oracle.OK
         sizes.add((values.nbytes, bits.nbytes))
     assert sizes == {(8 * 128 * 2, 8 * 8 * 4)}
+
+
+# ---- densities other than 50% (N:M with M | 32, any 0 < N < M) ------------------
+
+OTHER_DENSITIES = [(1, 4), (3, 4), (1, 8), (3, 8), (7, 8), (5, 16), (1, 32), (31, 32)]
+
+
+@pytest.mark.parametrize("n,m", OTHER_DENSITIES)
+def test_pack_other_densities_match_brute_force(n, m):
+    rows, cols = 6, 160
+    W = synth.weights(rows, cols, seed=17)
+    keep = synth.random_mask(rows, cols, n, m, seed=19)
+    st, values, bits = oracle.pack(W, keep, n, m)
+    assert st == oracle.OK
+    bv, bb = _brute_pack(W, keep)
+    assert values.shape == (rows, cols * n // m)
+    assert np.array_equal(values, bv)
+    assert np.array_equal(bits, bb)
+
+
+@pytest.mark.parametrize("n,m", OTHER_DENSITIES)
+def test_every_word_has_32n_over_m_set_bits(n, m):
+    """Fixed count per aligned word at any N:M with M | 32, so word w's values
+    start at w * 32N/M of the row ("Method", item (2), generalised)."""
+    W = synth.weights(16, 256, seed=23)
+    keep = synth.topn_mask(W, n, m)
+    st, values, bits = oracle.pack(W, keep, n, m)
+    assert st == oracle.OK
+    pop = np.unpackbits(bits.view(np.uint8).reshape(bits.shape + (4,)), axis=-1).sum(axis=-1)
+    p = 32 * n // m
+    assert np.all(pop == p)
+    # with W[r, c] = c the values of word w are its kept columns, at w * p
+    Wc = np.broadcast_to(np.arange(256, dtype=np.uint16), keep.shape).copy()
+    st, vc, _ = oracle.pack(Wc, keep, n, m)
+    assert st == oracle.OK
+    for w in range(256 // 32):
+        cols = np.nonzero(keep[0, 32 * w:32 * w + 32])[0] + 32 * w
+        assert np.array_equal(vc[0, w * p:(w + 1) * p], cols.astype(np.uint16))
+
+
+@pytest.mark.parametrize("n,m", OTHER_DENSITIES)
+def test_unpack_inverts_pack_other_densities(n, m):
+    W = synth.weights(9, 96, seed=29, dtype="bf16")
+    keep = synth.random_mask(9, 96, n, m, seed=31)
+    st, values, bits = oracle.pack(W, keep, n, m)
+    assert st == oracle.OK
+    st, W2, k2 = oracle.unpack(values, bits, 96, n, m)
+    assert st == oracle.OK
+    assert np.array_equal(k2, keep)
+    assert np.array_equal(W2, np.where(keep != 0, W, 0).astype(np.uint16))
+
+
+def test_packed_size_scales_with_density():
+    """Values take K*N/M 16-bit words per row, the mask K/32 words whatever
+    the density: 16*N/M + 1 bits per column in all."""
+    W = synth.weights(4, 512, seed=37)
+    for n, m in OTHER_DENSITIES + [(2, 4)]:
+        st, values, bits = oracle.pack(W, synth.topn_mask(W, n, m), n, m)
+        assert st == oracle.OK
+        assert values.nbytes == 4 * 512 * n // m * 2
+        assert bits.nbytes == 4 * 512 // 8
+
+
+@pytest.mark.parametrize("n,m", [(1, 4), (3, 4), (5, 16)])
+def test_masked_gemv_from_packed_form_other_densities(n, m):
+    """The product read back from the packed form, walked word by word with
+    the lowest-set-bit scan in pure Python, equals the oracle's dense masked
+    product (a second formulation of the same sum)."""
+    rows, cols = 5, 96
+    W = synth.weights(rows, cols, seed=41)
+    keep = synth.topn_mask(W, n, m)
+    x = synth.activations(2, cols, seed=43)
+    st, values, bits = oracle.pack(W, keep, n, m)
+    assert st == oracle.OK
+    vf = _f64(values, False)
+    xf = _f64(x, False)
+    p = 32 * n // m
+    y = np.zeros((2, rows))
+    for r in range(rows):
+        for w in range(cols // 32):
+            word, j = int(bits[r, w]), 0
+            while word:
+                c = (word & -word).bit_length() - 1
+                word &= word - 1
+                y[:, r] += vf[r, w * p + j] * xf[:, 32 * w + c]
+                j += 1
+            assert j == p
+    assert np.allclose(oracle.masked_gemv(W, keep, x, False), y, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,m", [(1, 4), (3, 4), (3, 8)])
+def test_topn_mask_other_densities_brute_force(n, m):
+    """The harness mask at other densities: per group the n largest |w|,
+    ties to the lower column, against a sort of every group."""
+    W = synth.weights(3, 64, seed=47)
+    W[0, :m] = W[0, 0]  # a group of equal magnitudes
+    keep = synth.topn_mask(W, n, m)
+    mag = (W & 0x7FFF).astype(np.int64)
+    for r in range(3):
+        for g in range(64 // m):
+            idx = sorted(range(m), key=lambda j: (-mag[r, g * m + j], j))[:n]
+            want = np.zeros(m, np.uint8)
+            want[idx] = 1
+            assert np.array_equal(keep[r, g * m:(g + 1) * m], want)
 
 
 # ---- the product ----------------------------------------------------------------
