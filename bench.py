@@ -79,7 +79,7 @@ class Proj:
         self.dbytes = {b: workloads.dense_bytes(mt.rows, mt.cols, b, 4) for b in batches}
         packed = values.numel() * 2 + bits.numel() * 4
         self.nc = pow2_copies(packed)
-        self.vals = [values] + [values.clone() for _ in range(self.nc - 1)]
+        self.vals = [values] + [native.clone_packed(values) for _ in range(self.nc - 1)]
         self.bits = [bits] + [bits.clone() for _ in range(self.nc - 1)]
         self.ndc = pow2_copies(Wd.numel() * 2) if want_dense else 0
         self.dense = ([Wd] + [Wd.clone() for _ in range(self.ndc - 1)]) if want_dense else []
@@ -295,12 +295,13 @@ def counters_run():
                       "copy_bytes_each_way": n}), flush=True)
 
 
-def shapes_run(cfg_id, args):
-    """Workloads 1, 3 and 4: per-matrix µs/call and GB/s (cache-cold rotation),
-    sparse and dense, at every batch the workload lists."""
+def shapes_run(cfg_id, args, mats=None):
+    """Workloads 1, 3 and 4 (and the other densities): per-matrix µs/call and
+    GB/s (cache-cold rotation), sparse and dense, at every batch the workload
+    lists."""
     want_dense = not args.no_dense
     rows_out = []
-    for mt, batches in workloads.config_matrices(cfg_id):
+    for mt, batches in (mats if mats is not None else workloads.config_matrices(cfg_id)):
         p = Proj(mt, batches, want_dense)
         for b in batches:
             us = per_kernel_us(p, Proj.sparse_call, b, p.nc, args.reps)
@@ -683,7 +684,8 @@ def main():
     ap.add_argument("--no-batch4", action="store_true")
     ap.add_argument("--workload", default="llama8b-layer",
                     choices=["llama8b-layer", "single", "patterns", "70b-qwen", "decode-32-layers",
-                             "llama8b-layer-fused", "calibration-hessian", "prefill-contrast"],
+                             "llama8b-layer-fused", "calibration-hessian", "prefill-contrast",
+                             "densities"],
                     help="llama8b-layer (default, the headline line): one Llama-3.1-8B layer; "
                          "single: the 4096x4096 matrix; patterns: 4:8/8:16/16:32 bf16 on the 8B "
                          "shapes; 70b-qwen: Llama-3.3-70B and Qwen3-32B shapes; "
@@ -692,7 +694,9 @@ def main():
                          "(SwiGLU epilogue) against the unfused and dense steps; "
                          "calibration-hessian: H += 2 X X^T at the 8B input widths; "
                          "prefill-contrast: 2:4 gate/down shapes as the batch grows to 4096 "
-                         "tokens, sparse matrix cores against the dense GEMM")
+                         "tokens, sparse matrix cores against the dense GEMM; densities: "
+                         "1:4, 3:4, 1:8, 3:8 fp16 on the 8B gate and down shapes (generic "
+                         "window kernel) against the dense GEMV")
     ap.add_argument("--counters", action="store_true",
                     help="short eager run for rocprofv3 --pmc: the 14336x4096 sparse kernel on "
                          "5 cache-cold copies, then 5 plain copies of 64 MiB (the known-size "
@@ -734,6 +738,13 @@ def main():
         print(json.dumps({"metric": "Hessian accumulation H += 2 X X^T, us per call",
                           "workload": args.workload, "n_gpus": 1, "data": "synthetic",
                           "dtype": "f16 inputs, fp32 H", **body}), flush=True)
+        return
+    if args.workload == "densities":
+        log("workload densities (1:4, 3:4, 1:8, 3:8 on the 8B gate and down shapes)")
+        body = {"per_matrix": shapes_run(0, args, mats=workloads.density_matrices())}
+        print(json.dumps({"metric": METRIC.replace("2:4", "N:M at densities other than 50%"),
+                          "workload": args.workload, "n_gpus": 1, "data": "synthetic",
+                          "peak_GB/s": PEAK_GBS, **body}), flush=True)
         return
     if args.workload != "llama8b-layer":
         cfg_id = {"single": 1, "patterns": 3, "70b-qwen": 4, "decode-32-layers": 5}[args.workload]

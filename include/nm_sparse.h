@@ -78,10 +78,22 @@ const char *nm_status_string(int status);
  * calling thread, 0 if none. */
 int nm_last_hip_error(void);
 
+/* Patterns.  Every entry point taking n, m accepts the 50% patterns the
+ * pages evaluate, N = M/2 with M in {4, 8, 16, 32} ("Experiments", Table 3
+ * paragraph).  nm_packed_bytes, nm_pack, nm_spmv, nm_spmm_small(_cfg) and
+ * nm_default_launch also accept any 0 < N < M with M in {4, 8, 16, 32}: every
+ * aligned 32-bit mask word then holds exactly P = 32N/M set bits, so word w's
+ * values start at w*P of the row and each word is walked in P fixed steps
+ * (the fixed-count argument of Method item (2), which the pages make at 50%).
+ * Those densities run on a generic kernel (values staged per 64-word window
+ * in LDS); the other entry points reject them with NM_ERR_UNSUPPORTED. */
+
 /* Sizes in bytes of the packed buffers of an R x K matrix under pattern N:M
  * with 16-bit elements of type dt (Method item (1): K*N/M values and K/32
  * words per row).  Pure host arithmetic.
- *   values_bytes = rows * cols * n / m * 2,  bits_bytes = rows * cols / 8.
+ *   values_bytes = rows * cols * n / m * 2 rounded up to a multiple of 16
+ *                  (the rounding adds bytes only at densities other than 50%),
+ *   bits_bytes = rows * cols / 8.
  * Errors: NM_ERR_INVALID_ARG (negative sizes, NULL outputs),
  * NM_ERR_UNSUPPORTED (pattern, dt not 16-bit), NM_ERR_SHAPE (cols % 32). */
 int nm_packed_bytes(int64_t rows, int64_t cols, int n, int m, nm_dtype dt,
@@ -92,7 +104,8 @@ int nm_packed_bytes(int64_t rows, int64_t cols, int n, int m, nm_dtype dt,
  *           row-major, 2-byte aligned; copied as raw bit patterns, so -0.0,
  *           subnormals, inf and NaN survive unchanged;
  *   keep:   device, rows x cols bytes, row-major; nonzero = kept;
- *   values: device, rows x cols*n/m 16-bit elements (output), 16-byte aligned;
+ *   values: device, rows x cols*n/m 16-bit elements (output), 16-byte aligned,
+ *           allocated with at least nm_packed_bytes' values_bytes;
  *   bits:   device, rows x cols/32 uint32 (output), 4-byte aligned.
  * The mask decides what is kept, never the value: a kept zero is stored.
  * Validates that every M-group of every row keeps exactly N entries.  The
@@ -108,9 +121,10 @@ int nm_pack(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
  * decoding-specialised N:M SpMV):
  *   y[r] = sum over kept columns c of row r of W[r][c] * x[c],  r < rows.
  *   values, bits: as produced by nm_pack for pattern n:m (values 16-byte
- *           aligned, bits 4-byte aligned); bits must hold exactly 16 set bits
- *           per word -- a word that does not yields an unspecified result for
- *           its row but no access outside the buffers;
+ *           aligned and allocated with nm_packed_bytes' values_bytes, bits
+ *           4-byte aligned); bits must hold exactly 32n/m set bits per word
+ *           -- a word that does not yields an unspecified result for its row
+ *           but no access outside the buffers;
  *   x:      device, cols elements of in_dt, 16-byte aligned;
  *   y:      device, rows elements of out_dt (overwritten), aligned to its
  *           element size.

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 # translation units of the library (headers next to them are included)
-SRCS = [os.path.join(CSRC, f) for f in ("nm_sparse.hip", "nm_prefill.hip", "nm_calib.hip")
+SRCS = [os.path.join(CSRC, f) for f in ("nm_sparse.hip", "nm_prefill.hip", "nm_calib.hip", "nm_generic.hip")
         if os.path.exists(os.path.join(CSRC, f))]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libnm_sparse.so")

@@ -1,0 +1,319 @@
+// nm_generic.hip -- N:M bitmask product at densities other than 50%.
+//
+// "SparseDecoding: Decoding-Aware Pruning for Accurate and Efficient LLM
+// Inference", Method, kernel subsection: item (1) "Bitmask indexing" stores
+// one bit per column and the kept weights in increasing column order; item
+// (2) "Fixed-step bitmask traversal" rests on every aligned 32-bit word of a
+// 50% N:M row holding the same number of set bits.  The same holds for any
+// N:M pattern with M dividing 32: each word holds exactly P = 32 N / M set
+// bits, so word w's values start at w * P within the row (no prefix sums) and
+// each word is walked in P fixed steps, each taking the lowest set bit as the
+// next kept column and clearing it.  The stored format is the one of the 50%
+// kinds, with row stride K * N / M values.
+//
+// Kernel design (gfx950).  One wavefront walks a window of 64 mask words of a
+// row, one word per lane.  The window's values are one contiguous run of 64 P
+// values; the wave copies it from HBM straight into its LDS buffer with
+// 16-byte direct-to-LDS buffer loads (range-checked, so nothing outside the
+// window's 16-byte-aligned span is read), double-buffered so the next
+// window's copy is in flight while this one is consumed.  Lane l then reads
+// its P values at l * P from LDS and the x values of its kept columns from
+// the LDS copy of x (column-major slots of all batch rows), and accumulates
+// pairs with v_dot2_f32_{f16,bf16} (the products are exact in fp32).  x is
+// staged per workgroup in segments when all of it does not fit the LDS
+// budget.
+
+#include "nm_device.h"
+#include "nm_host.h"
+
+namespace {
+
+constexpr int kWinWords = 64;  // mask words per window (one per lane)
+
+// Chunks of 16 bytes (8 values) one window can span: 64 P values plus up to
+// 7 values of alignment slack in front.
+__host__ __device__ constexpr int win_chunks(int p) { return 8 * p + 1; }
+// Direct-to-LDS load instructions per window (64 chunks each).
+__host__ __device__ constexpr int win_loads(int p) { return (win_chunks(p) + 63) / 64; }
+
+// x segment [s0, s0 + S) of every batch row into LDS: column c of the
+// segment at byte c * 2 * BP, batch row b at + 2 b (rows >= B hold zeros).
+template <int BP>
+__device__ __forceinline__ void stage_x_cols(char *lds, const uint16_t *__restrict__ x, int B,
+                                             int K, int s0, int S) {
+  for (int g = threadIdx.x; g < S / 8; g += blockDim.x) {
+    uint4 r[BP];
+#pragma unroll
+    for (int b = 0; b < BP; ++b) {
+      const int bb = b < B ? b : B - 1;
+      r[b] = reinterpret_cast<const uint4 *>(x + (int64_t)bb * K + s0)[g];
+      if (b >= B) r[b] = make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (BP == 1) {
+      reinterpret_cast<uint4 *>(lds)[g] = r[0];
+    } else {
+      uint16_t *d = reinterpret_cast<uint16_t *>(lds) + (size_t)8 * g * BP;
+#pragma unroll
+      for (int b = 0; b < BP; ++b) {
+        uint16_t h[8];
+        __builtin_memcpy(h, &r[b], 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e * BP + b] = h[e];
+      }
+    }
+  }
+}
+
+// Kept pair (columns c0, c1 of the segment; packed weights w) for every
+// batch row.
+template <bool BF, int BP>
+__device__ __forceinline__ void pair_acc(const char *lds, int c0, int c1, uint32_t w,
+                                         float (&acc)[BP]) {
+  const lds_ptr x0 = (lds_ptr)lds + c0 * (2 * BP), x1 = (lds_ptr)lds + c1 * (2 * BP);
+  if constexpr (BP == 1) {
+    u16x2_t pr;
+    pr[0] = ld<uint16_t>(x0);
+    pr[1] = ld<uint16_t>(x1);
+    acc[0] = dot2<BF>(w, __builtin_bit_cast(uint32_t, pr), acc[0]);
+  } else {
+    uint32_t a[BP / 2], b[BP / 2];
+    if constexpr (BP == 2) {
+      a[0] = ld<uint32_t>(x0);
+      b[0] = ld<uint32_t>(x1);
+    } else if constexpr (BP == 4) {
+      const u32x2_t p = ld<u32x2_t>(x0), q = ld<u32x2_t>(x1);
+      a[0] = p[0]; a[1] = p[1];
+      b[0] = q[0]; b[1] = q[1];
+    } else {
+      const u32x4_t p = ld<u32x4_t>(x0), q = ld<u32x4_t>(x1);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) { a[d] = p[d]; b[d] = q[d]; }
+    }
+#pragma unroll
+    for (int d = 0; d < BP / 2; ++d) {
+      acc[2 * d] = dot2<BF>(w, (a[d] & 0xffffu) | (b[d] << 16), acc[2 * d]);
+      acc[2 * d + 1] = dot2<BF>(w, (a[d] >> 16) | (b[d] & 0xffff0000u), acc[2 * d + 1]);
+    }
+  }
+}
+
+// One kept weight v (low half; the high half is 0 and meets an x of 0, so the
+// pair product adds exactly v * x).
+template <bool BF, int BP>
+__device__ __forceinline__ void single_acc(const char *lds, int c0, uint32_t v,
+                                           float (&acc)[BP]) {
+  const lds_ptr x0 = (lds_ptr)lds + c0 * (2 * BP);
+#pragma unroll
+  for (int b = 0; b < BP; ++b)
+    acc[b] = dot2<BF>(v, (uint32_t)ld<uint16_t>(x0 + 2 * b), acc[b]);
+}
+
+// Wave w of the grid owns rows w * rpw .. + rpw - 1.  Its work per segment of
+// x is a sequence of items (row i, window t); the copy of item k + 1 is in
+// flight while item k is consumed.  Lane i accumulates the sums of the wave's
+// row i across segments (rpw <= 64).
+template <bool BF, int BP, int NI>
+__global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
+    const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
+    const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int P,
+    int seg, int rpw, int out_kind) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wpg = blockDim.x / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t r0 = ((int64_t)blockIdx.x * wpg + wid) * rpw;
+  const int64_t left = R - r0;
+  const int nrows = left <= 0 ? 0 : (left < rpw ? (int)left : rpw);
+  const int W = K >> 5;                   // mask words per row
+  const int64_t vstride = (int64_t)W * P;  // values per row
+  const uint32_t xbytes = ((uint32_t)seg * (2 * BP) + 15u) & ~15u;
+  // LDS address of the wave's two window buffers (NI KiB each)
+  const uint32_t wbuf = (uint32_t)(size_t)(lds_ptr)lds + xbytes + (uint32_t)wid * (2 * NI * 1024);
+
+  float res[BP];
+#pragma unroll
+  for (int b = 0; b < BP; ++b) res[b] = 0.f;
+
+  for (int s0 = 0; s0 < K; s0 += seg) {
+    const int S = K - s0 < seg ? K - s0 : seg;
+    __syncthreads();  // every wave is done with the previous segment's x
+    stage_x_cols<BP>(lds, x, B, K, s0, S);
+    __syncthreads();
+    const int sw0 = s0 >> 5, sw = S >> 5;
+    const int nwin = (sw + kWinWords - 1) / kWinWords;
+    const int nitems = nrows * nwin;
+
+    // Issue item k (a dummy past the last item: empty ranges, no memory
+    // traffic, so the wait counts below stay the same for every item).
+    auto issue = [&](int k, uint32_t &mword) {
+      const bool real = k < nitems;
+      const int i = real ? k / nwin : 0, t = real ? k - i * nwin : 0;
+      const int64_t r = r0 + i;
+      const int w0 = sw0 + t * kWinWords;
+      const int nw = real ? min(kWinWords, sw - t * kWinWords) : 0;
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(bits + r * W + w0), 0, nw * 4, kRsrcWord3);
+      mword = __builtin_amdgcn_raw_buffer_load_b32(rb, lane * 4, 0, kStreamAux);
+      const int64_t vs = r * vstride + (int64_t)w0 * P;
+      const int64_t a0 = vs & ~(int64_t)7;
+      const int nch = real ? (int)((vs + (int64_t)nw * P - a0 + 7) >> 3) : 0;
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(values + a0), 0, nch * 16, kRsrcWord3);
+      const uint32_t dst = wbuf + (uint32_t)(k & 1) * (NI * 1024);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) lds_load16_nt(rv, dst + j * 1024, lane * 16 + j * 1024, 0);
+    };
+
+    float acc[BP];
+#pragma unroll
+    for (int b = 0; b < BP; ++b) acc[b] = 0.f;
+    uint32_t mA, mB;
+    issue(0, mA);
+    issue(1, mB);
+    for (int k = 0; k < nitems; ++k) {
+      // item k's mask word and window copy have landed (item k + 1's
+      // 1 + NI loads may still be in flight)
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<1 + NI>();
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t mw = (k & 1) ? mB : mA;
+      const int i = k / nwin, t = k - i * nwin;
+      const int64_t r = r0 + i;
+      const int w0 = sw0 + t * kWinWords;
+      const int nw = min(kWinWords, sw - t * kWinWords);
+      if (lane < nw) {
+        const int64_t vs = r * vstride + (int64_t)w0 * P;
+        const uint32_t vb = wbuf + (uint32_t)(k & 1) * (NI * 1024) +
+                            2u * (uint32_t)((vs & 7) + (int64_t)lane * P);
+        const int cb = (t * kWinWords + lane) * 32;  // segment column of the word's bit 0
+        uint32_t m = mw;
+        int j = 0;
+        for (; j + 1 < P; j += 2) {
+          const int c0 = ffbl_hw(m) & 31;
+          m &= m - 1;
+          const int c1 = ffbl_hw(m) & 31;
+          m &= m - 1;
+          const uint32_t v0 = ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * j));
+          const uint32_t v1 = ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * j + 2));
+          pair_acc<BF, BP>(lds, cb + c0, cb + c1, v0 | (v1 << 16), acc);
+        }
+        if (j < P) {
+          const int c0 = ffbl_hw(m) & 31;
+          single_acc<BF, BP>(lds, cb + c0, ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * j)), acc);
+        }
+      }
+      if (t == nwin - 1) {  // the row's part of this segment is complete
+#pragma unroll
+        for (int b = 0; b < BP; ++b) {
+          const float s = wave_sum_to_63(acc[b]);
+          const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kWave - 1));
+          res[b] += lane == i ? sv : 0.f;
+          acc[b] = 0.f;
+        }
+      }
+      // the buffer of item k is read out before item k + 2 overwrites it
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_sched_barrier(0);
+      if (k & 1) issue(k + 2, mB); else issue(k + 2, mA);
+    }
+    // the dummy items' copies land before the buffers are reused
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (lane < nrows) {
+#pragma unroll
+    for (int b = 0; b < BP; ++b)
+      if (b < B) store_out(y, (int64_t)b * R + r0 + lane, res[b], out_kind);
+  }
+}
+
+using fixed_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int,
+                          int64_t, int, int, int, int, int);
+
+template <bool BF, int BP>
+fixed_fn pick_fixed_ni(int ni) {
+  switch (ni) {
+    case 1: return nm_spmv_fixed_kernel<BF, BP, 1>;
+    case 2: return nm_spmv_fixed_kernel<BF, BP, 2>;
+    case 3: return nm_spmv_fixed_kernel<BF, BP, 3>;
+    default: return nm_spmv_fixed_kernel<BF, BP, 4>;
+  }
+}
+
+template <bool BF>
+fixed_fn pick_fixed_bp(int bp, int ni) {
+  switch (bp) {
+    case 1: return pick_fixed_ni<BF, 1>(ni);
+    case 2: return pick_fixed_ni<BF, 2>(ni);
+    case 4: return pick_fixed_ni<BF, 4>(ni);
+    default: return pick_fixed_ni<BF, 8>(ni);
+  }
+}
+
+int pad_b(int b) { return b <= 1 ? 1 : b <= 2 ? 2 : b <= 4 ? 4 : 8; }
+
+size_t fixed_lds_bytes(int bp, int seg, int waves, int ni) {
+  return (((size_t)seg * 2 * bp + 15) & ~(size_t)15) + (size_t)waves * 2 * ni * 1024;
+}
+
+}  // namespace
+
+namespace nm_host {
+
+bool pattern_any_ok(int n, int m) {
+  return (m == 4 || m == 8 || m == 16 || m == 32) && n >= 1 && n < m;
+}
+
+nm_status generic_default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, int cus,
+                              size_t lds_budget, nm_launch_cfg *cfg) {
+  const int p = 32 * n / m, ni = win_loads(p), bp = pad_b(batch), waves = 4;
+  cfg->kernel = NM_KERNEL_VALU;
+  cfg->threads_per_wg = waves * kWave;
+  // about two workgroups per CU, at most 8 rows per wave
+  int64_t rpw = rows / ((int64_t)2 * cus * waves);
+  cfg->rows_per_wave = (int)(rpw < 1 ? 1 : rpw > 8 ? 8 : rpw);
+  const size_t wave_area = fixed_lds_bytes(bp, 0, waves, ni);
+  if (fixed_lds_bytes(bp, (int)cols, waves, ni) <= lds_budget) {
+    cfg->seg_cols = cols > 0 ? (int)cols : 32;
+  } else {
+    // widest multiple of 2048 columns (whole windows) that fits
+    const int64_t s = (int64_t)((lds_budget - wave_area) / (2 * bp)) / 2048 * 2048;
+    cfg->seg_cols = (int)(s < 2048 ? 2048 : s);
+  }
+  return NM_OK;
+}
+
+nm_status generic_check_cfg(const nm_launch_cfg &c, int batch, int n, int m,
+                            size_t lds_budget) {
+  const int t = c.threads_per_wg;
+  if (c.kernel != NM_KERNEL_VALU) return NM_ERR_UNSUPPORTED;
+  if (t < kWave || t > 1024 || t % kWave != 0) return NM_ERR_INVALID_ARG;
+  if (c.rows_per_wave < 1 || c.rows_per_wave > kWave) return NM_ERR_INVALID_ARG;
+  if (c.seg_cols <= 0 || c.seg_cols % 32 != 0) return NM_ERR_INVALID_ARG;
+  const int p = 32 * n / m;
+  if (fixed_lds_bytes(pad_b(batch), c.seg_cols, t / kWave, win_loads(p)) > lds_budget)
+    return NM_ERR_INVALID_ARG;
+  return NM_OK;
+}
+
+nm_status generic_launch(const void *values, const uint32_t *bits, const void *X, void *Y,
+                         int batch, int64_t rows, int64_t cols, int n, int m, nm_dtype in_dt,
+                         nm_dtype out_dt, const nm_launch_cfg &cfg, void *stream) {
+  const int p = 32 * n / m, ni = win_loads(p), bp = pad_b(batch);
+  const int waves = cfg.threads_per_wg / kWave;
+  const int64_t rows_per_wg = (int64_t)waves * cfg.rows_per_wave;
+  const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+  if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
+  const int seg = cfg.seg_cols < cols ? cfg.seg_cols : (int)cols;
+  const fixed_fn fn = in_dt == NM_BF16 ? pick_fixed_bp<true>(bp, ni) : pick_fixed_bp<false>(bp, ni);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
+                     fixed_lds_bytes(bp, seg, waves, ni), (hipStream_t)stream,
+                     (const uint16_t *)values, bits, (const uint16_t *)X, Y, batch, rows,
+                     (int)cols, p, seg, cfg.rows_per_wave, (int)out_dt);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NM_OK : hip_fail(e);
+}
+
+}  // namespace nm_host

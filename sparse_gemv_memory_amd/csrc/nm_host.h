@@ -24,6 +24,23 @@ NM_INTERNAL nm_status hip_fail(hipError_t e);
 // A 50% pattern the kernels are built for: N = M/2, M in {4, 8, 16, 32}.
 NM_INTERNAL bool pattern_ok(int n, int m);
 
+// Any N:M pattern the format holds: M in {4, 8, 16, 32}, 1 <= N < M (each
+// aligned 32-bit mask word then holds exactly 32 N / M set bits).
+NM_INTERNAL bool pattern_any_ok(int n, int m);
+
+// The product for the patterns other than 50% (nm_generic.hip): launch
+// shape (threads_per_wg, rows_per_wave, seg_cols; kernel NM_KERNEL_VALU), its
+// check against the LDS budget, and the launch itself (arguments already
+// checked by the caller).
+NM_INTERNAL nm_status generic_default_cfg(int64_t rows, int64_t cols, int batch, int n, int m,
+                                          int cus, size_t lds_budget, nm_launch_cfg *cfg);
+NM_INTERNAL nm_status generic_check_cfg(const nm_launch_cfg &c, int batch, int n, int m,
+                                        size_t lds_budget);
+NM_INTERNAL nm_status generic_launch(const void *values, const uint32_t *bits, const void *X,
+                                     void *Y, int batch, int64_t rows, int64_t cols, int n, int m,
+                                     nm_dtype in_dt, nm_dtype out_dt, const nm_launch_cfg &cfg,
+                                     void *stream);
+
 NM_INTERNAL bool is16(nm_dtype d);
 
 // fp32 output, or the input's own 16-bit type.

@@ -1083,19 +1083,20 @@ __global__ __launch_bounds__(1024) void nm_dense_kernel(
 template <int M>
 __global__ __launch_bounds__(256) void nm_pack_kernel(
     const uint16_t *__restrict__ W, const uint8_t *__restrict__ keep,
-    int64_t R, int K, uint16_t *__restrict__ values,
+    int64_t R, int K, int N, uint16_t *__restrict__ values,
     uint32_t *__restrict__ bits, int *__restrict__ bad) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wpg = blockDim.x / kWave;
   const uint32_t lb = lane & 31;
   const uint32_t below = (1u << lb) - 1u;
   const uint32_t gmask = (M == 32) ? 0xffffffffu : ((1u << (M & 31)) - 1u);
+  const uint32_t P = 32 / M * N;  // values per 32-bit mask word
   int nbad = 0;
   for (int64_t r = (int64_t)blockIdx.x * wpg + threadIdx.x / kWave; r < R;
        r += (int64_t)gridDim.x * wpg) {
     const uint16_t *wr = W + r * K;
     const uint8_t *kr = keep + r * K;
-    uint16_t *vr = values + r * (K / 2);
+    uint16_t *vr = values + r * (K / 32) * P;
     uint32_t *br = bits + r * (K / 32);
     for (int c0 = 0; c0 < K; c0 += kWave) {
       const int c = c0 + lane;
@@ -1106,10 +1107,10 @@ __global__ __launch_bounds__(256) void nm_pack_kernel(
       const uint32_t word = (lane < 32) ? (uint32_t)bal : (uint32_t)(bal >> 32);
       const uint32_t slot = __popc(word & below);
       const int64_t wg = (c0 >> 5) + (lane >> 5);
-      if (kept && slot < 16) vr[wg * 16 + slot] = wv;
+      if (kept && slot < P) vr[wg * P + slot] = wv;
       if (in && lb == 0) br[wg] = word;
       bool badg = false;
-      if (in && (lb % M) == 0) badg = __popc((word >> lb) & gmask) != M / 2;
+      if (in && (lb % M) == 0) badg = __popc((word >> lb) & gmask) != N;
       nbad += badg ? 1 : 0;
     }
   }
@@ -1574,7 +1575,8 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
                    const nm_launch_cfg *user, void *stream, int epi = kEpiNone) {
   nm_status st = check_dims(rows, cols, batch);
   if (st != NM_OK) return st;
-  if (!pattern_ok(n, m) || !is16(in_dt) || !out_ok(in_dt, out_dt)) return NM_ERR_UNSUPPORTED;
+  if (!pattern_any_ok(n, m) || !is16(in_dt) || !out_ok(in_dt, out_dt)) return NM_ERR_UNSUPPORTED;
+  if (!pattern_ok(n, m) && epi != kEpiNone) return NM_ERR_UNSUPPORTED;
   const bool empty_w = rows == 0 || cols == 0;
   if ((!values && !empty_w) || (!bits && !empty_w) || (!X && cols != 0) ||
       (!Y && rows != 0))
@@ -1584,6 +1586,22 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     return NM_ERR_ALIGN;
   if (rows == 0) return NM_OK;
   nm_launch_cfg cfg;
+  if (!pattern_ok(n, m)) {  // densities other than 50%: the generic kernel
+    DevInfo di;
+    st = device_info(&di);
+    if (st != NM_OK) return st;
+    st = generic_default_cfg(rows, cols, batch, n, m, di.cus, lds_budget(di), &cfg);
+    if (st != NM_OK) return st;
+    if (user) {
+      if (user->kernel) cfg.kernel = user->kernel;
+      if (user->threads_per_wg) cfg.threads_per_wg = user->threads_per_wg;
+      if (user->rows_per_wave) cfg.rows_per_wave = user->rows_per_wave;
+      if (user->seg_cols) cfg.seg_cols = user->seg_cols;
+    }
+    st = generic_check_cfg(cfg, batch, n, m, lds_budget(di));
+    if (st != NM_OK) return st;
+    return generic_launch(values, bits, X, Y, batch, rows, cols, n, m, in_dt, out_dt, cfg, stream);
+  }
   const bool pair = epi == kEpiSwiglu;
   st = resolve_cfg(rows, cols, batch, n, m, false, user, &cfg, pair);
   if (st != NM_OK) return st;
@@ -1657,11 +1675,13 @@ int nm_last_hip_error(void) { return nm_host::g_last_hip; }
 int nm_packed_bytes(int64_t rows, int64_t cols, int n, int m, nm_dtype dt,
                     size_t *values_bytes, size_t *bits_bytes) {
   if (rows < 0 || cols < 0 || !values_bytes || !bits_bytes) return NM_ERR_INVALID_ARG;
-  if (!pattern_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
+  if (!pattern_any_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
   if (cols % 32 != 0) return NM_ERR_SHAPE;
   if (rows > INT32_MAX || cols > INT32_MAX) return NM_ERR_INVALID_ARG;
   const uint64_t rc = (uint64_t)rows * (uint64_t)cols;
-  *values_bytes = (size_t)(rc / (uint64_t)m * (uint64_t)n * 2u);
+  // rows x cols*n/m values, rounded up to 16 bytes (a whole last chunk for
+  // the 16-byte loads; already whole at 50%)
+  *values_bytes = (size_t)((rc / (uint64_t)m * (uint64_t)n * 2u + 15u) & ~(uint64_t)15);
   *bits_bytes = (size_t)(rc / 8u);
   return NM_OK;
 }
@@ -1671,7 +1691,7 @@ int nm_pack(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
             void *stream) {
   if (rows < 0 || cols < 0) return NM_ERR_INVALID_ARG;
   if (rows > INT32_MAX || cols > INT32_MAX) return NM_ERR_INVALID_ARG;
-  if (!pattern_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
+  if (!pattern_any_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
   if (cols % 32 != 0) return NM_ERR_SHAPE;
   const bool empty = rows == 0 || cols == 0;
   if (!empty && (!W || !keep || !values || !bits)) return NM_ERR_INVALID_ARG;
@@ -1691,10 +1711,10 @@ int nm_pack(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
     const uint16_t *w16 = (const uint16_t *)W;
     uint16_t *v16 = (uint16_t *)values;
     switch (m) {
-      case 4: hipLaunchKernelGGL(nm_pack_kernel<4>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, v16, bits, dbad); break;
-      case 8: hipLaunchKernelGGL(nm_pack_kernel<8>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, v16, bits, dbad); break;
-      case 16: hipLaunchKernelGGL(nm_pack_kernel<16>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, v16, bits, dbad); break;
-      default: hipLaunchKernelGGL(nm_pack_kernel<32>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, v16, bits, dbad); break;
+      case 4: hipLaunchKernelGGL(nm_pack_kernel<4>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
+      case 8: hipLaunchKernelGGL(nm_pack_kernel<8>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
+      case 16: hipLaunchKernelGGL(nm_pack_kernel<16>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
+      default: hipLaunchKernelGGL(nm_pack_kernel<32>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
     }
     e = hipGetLastError();
   }
@@ -1748,7 +1768,13 @@ int nm_default_launch(int64_t rows, int64_t cols, int batch, int n, int m, int d
   if (!cfg) return NM_ERR_INVALID_ARG;
   nm_status st = check_dims(rows, cols, batch);
   if (st != NM_OK) return st;
-  if (!dense && !pattern_ok(n, m)) return NM_ERR_UNSUPPORTED;
+  if (!dense && !pattern_any_ok(n, m)) return NM_ERR_UNSUPPORTED;
+  if (!dense && !pattern_ok(n, m)) {
+    DevInfo di;
+    st = device_info(&di);
+    if (st != NM_OK) return st;
+    return generic_default_cfg(rows, cols, batch, n, m, di.cus, lds_budget(di), cfg);
+  }
   return default_cfg(rows, cols, batch, n, m, dense != 0, cfg);
 }
 

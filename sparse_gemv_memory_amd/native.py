@@ -167,7 +167,7 @@ def nm_pack(W: torch.Tensor, keep: torch.Tensor, n: int, m: int):
     rows, cols = W.shape
     dt = _in_dt(W)
     vcols = cols * n // m if m > 0 and n >= 0 else 0  # the library validates n, m
-    values = torch.empty((rows, vcols), dtype=W.dtype, device=W.device)
+    values = _packed_values(rows, vcols, _padded_elems(rows, cols, n, m, W.dtype), W.dtype, W.device)
     bits = torch.empty((rows, cols // 32), dtype=torch.int32, device=W.device)
     with torch.cuda.device(W.device):
         st = lib().nm_pack(_dev(W, "W"), _dev(keep, "keep"), rows, cols, n, m, dt,
@@ -176,7 +176,32 @@ def nm_pack(W: torch.Tensor, keep: torch.Tensor, n: int, m: int):
     return values, bits
 
 
-def _sparse_args(values, bits, X):
+def _padded_elems(rows: int, cols: int, n: int, m: int, dtype) -> int:
+    """16-bit elements of nm_packed_bytes' values size (the row-major values
+    rounded up to 16 bytes); 0 for a pattern the library rejects."""
+    vb = ctypes.c_size_t()
+    bb = ctypes.c_size_t()
+    st = lib().nm_packed_bytes(rows, cols, n, m, _DT[dtype], ctypes.byref(vb), ctypes.byref(bb))
+    return vb.value // 2 if st == NM_OK else 0
+
+
+def _packed_values(rows: int, vcols: int, elems: int, dtype, device) -> torch.Tensor:
+    """A (rows, vcols) tensor whose storage holds max(elems, rows * vcols)
+    elements (the packed-size padding stays allocated behind the view)."""
+    flat = torch.empty((max(elems, rows * vcols),), dtype=dtype, device=device)
+    return flat[:rows * vcols].view(rows, vcols)
+
+
+def clone_packed(values: torch.Tensor) -> torch.Tensor:
+    """A copy of packed values that keeps nm_packed_bytes' padding (a plain
+    clone() allocates only rows * cols*n/m elements)."""
+    out = torch.empty((values.untyped_storage().nbytes() // 2 - values.storage_offset(),),
+                      dtype=values.dtype, device=values.device)
+    out[:values.numel()].copy_(values.reshape(-1))
+    return out[:values.numel()].view(values.shape)
+
+
+def _sparse_args(values, bits, X, n, m):
     if values.dim() != 2 or bits.dim() != 2 or values.shape[0] != bits.shape[0]:
         raise ValueError("values and bits must be 2-D with the same number of rows")
     if bits.dtype not in (torch.int32, torch.uint32):
@@ -185,14 +210,19 @@ def _sparse_args(values, bits, X):
         raise TypeError("values and x must have the same dtype")
     rows = values.shape[0]
     cols = bits.shape[1] * 32
-    if values.shape[1] * 2 != cols:
-        raise ValueError("values must hold cols/2 elements per row (50% N:M)")
+    if m <= 0 or n < 0 or values.shape[1] != cols * n // m:
+        raise ValueError("values must hold cols*n/m elements per row")
+    need = _padded_elems(rows, cols, n, m, values.dtype)
+    have = values.untyped_storage().nbytes() // 2 - values.storage_offset()
+    if values.is_contiguous() and have < need:
+        raise ValueError("values must be allocated with nm_packed_bytes' size (nm_pack's "
+                         "output, or clone_packed of it)")
     return rows, cols
 
 
 def nm_spmv(values, bits, x, n: int, m: int, out_dtype=torch.float32, out=None, cfg=None):
     """y = W_sparse . x for one token; x has shape (cols,) or (1, cols)."""
-    rows, cols = _sparse_args(values, bits, x)
+    rows, cols = _sparse_args(values, bits, x, n, m)
     if x.numel() != cols:
         raise ValueError("x must have cols elements")
     y = out if out is not None else torch.empty((rows,), dtype=out_dtype, device=values.device)
@@ -213,7 +243,7 @@ def nm_spmv(values, bits, x, n: int, m: int, out_dtype=torch.float32, out=None, 
 
 def nm_spmm_small(values, bits, X, n: int, m: int, out_dtype=torch.float32, out=None, cfg=None):
     """Y = X . W_sparse^T for X of shape (batch, cols), 1 <= batch <= 8."""
-    rows, cols = _sparse_args(values, bits, X)
+    rows, cols = _sparse_args(values, bits, X, n, m)
     if X.dim() != 2 or X.shape[1] != cols:
         raise ValueError("X must be (batch, cols)")
     batch = X.shape[0]
@@ -231,7 +261,7 @@ def nm_spmm_small(values, bits, X, n: int, m: int, out_dtype=torch.float32, out=
 def nm_spmm_prefill(values, bits, X, n: int = 2, m: int = 4, out_dtype=torch.float32, out=None):
     """Y = X . W_sparse^T for X of shape (batch, cols), any batch (2:4 only),
     on the sparse matrix cores with a GEMM tiling."""
-    rows, cols = _sparse_args(values, bits, X)
+    rows, cols = _sparse_args(values, bits, X, n, m)
     if X.dim() != 2 or X.shape[1] != cols:
         raise ValueError("X must be (batch, cols)")
     batch = X.shape[0]
@@ -250,7 +280,7 @@ def nm_spmm_swiglu(values, bits, X, n: int, m: int, out_dtype=torch.float32, out
     """H = silu(G) * U for X of shape (batch, cols), 1 <= batch <= 8, where the
     packed matrix interleaves gate row r (packed row 2r) and up row r (2r + 1);
     H has shape (batch, rows // 2)."""
-    rows, cols = _sparse_args(values, bits, X)
+    rows, cols = _sparse_args(values, bits, X, n, m)
     if rows % 2:
         raise ValueError("the packed matrix must hold (gate, up) row pairs")
     if X.dim() != 2 or X.shape[1] != cols:

@@ -39,6 +39,10 @@ QWEN32B_SHAPES = (
 
 PATTERNS_50 = ((2, 4), (4, 8), (8, 16), (16, 32))
 
+# N:M densities other than 50% (M | 32): the same format with 32N/M kept
+# columns per mask word.
+OTHER_DENSITIES = ((1, 4), (3, 4), (1, 8), (3, 8))
+
 
 @dataclass(frozen=True)
 class Matrix:
@@ -91,6 +95,19 @@ def config_matrices(config: int):
                 out.append((mt, (1, 2, 4, 8)))
         return out
     raise ValueError(f"no workload {config}")
+
+
+def density_matrices():
+    """The 8B gate (14336x4096) and down (4096x14336) shapes at the densities
+    other than 50%, fp16, batch 1 and 8 (seeds from workload 6)."""
+    from .synth import layer_seed
+    out = []
+    for j, (n, m) in enumerate(OTHER_DENSITIES):
+        for i, (name, r, c) in enumerate(LLAMA8B_LAYER):
+            if name in ("gate", "down"):
+                out.append((Matrix(f"{name}.{n}:{m}", r, c, n, m, "f16", layer_seed(6, j, i), True),
+                            (1, 8)))
+    return out
 
 
 def sparse_bytes(rows: int, cols: int, n: int, m: int, batch: int, out_bytes: int) -> int:

@@ -80,8 +80,13 @@ def test_packed_bytes_closed_form(L):
     assert _pb(L, 0, 4096, 2, 4) == (OK, 0, 0)
     assert _pb(L, 3, 0, 2, 4, BF16) == (OK, 0, 0)
     assert _pb(L, 4, 48, 2, 4)[0] == SHAPE
-    assert _pb(L, 4, 64, 1, 4)[0] == UNSUP
-    assert _pb(L, 4, 64, 3, 6)[0] == UNSUP
+    # other densities: K*N/M values per row, the total rounded up to 16 bytes
+    assert _pb(L, 14336, 4096, 1, 4) == (OK, 14336 * 4096 // 2, 14336 * 4096 // 8)
+    assert _pb(L, 14336, 4096, 3, 4) == (OK, 14336 * 4096 * 3 // 2, 14336 * 4096 // 8)
+    assert _pb(L, 1, 32, 1, 32) == (OK, 16, 4)  # 2 bytes of values, padded
+    assert _pb(L, 3, 64, 5, 16) == (OK, 128, 24)  # 3 * 20 values = 120 bytes -> 128
+    for n, m in ((0, 4), (4, 4), (3, 6), (2, 64), (-1, 4)):
+        assert _pb(L, 4, 64, n, m)[0] == UNSUP
     assert _pb(L, 4, 64, 2, 4, F32)[0] == UNSUP
     assert _pb(L, -1, 64, 2, 4)[0] == INV
     assert L.nm_packed_bytes(1, 32, 2, 4, F16, None, None) == INV
@@ -96,7 +101,8 @@ def test_spmv_rejects_bad_arguments(L):
     assert _spmv(L, cols=-32) == INV
     assert _spmv(L, cols=48) == SHAPE
     assert _spmv(L, cols=2 ** 31) == INV
-    assert _spmv(L, n=1, m=4) == UNSUP
+    assert _spmv(L, n=3, m=6) == UNSUP
+    assert _spmv(L, n=0, m=4) == UNSUP
     assert _spmv(L, n=32, m=64) == UNSUP
     assert _spmv(L, n=4, m=4) == UNSUP
     assert _spmv(L, i=F32) == UNSUP
@@ -219,7 +225,8 @@ def test_pack_rejects_bad_arguments(L):
         return L.nm_pack(W, keep, rows, cols, n, m, dt, v, b, None)
     assert pack(rows=-1) == INV
     assert pack(cols=96 + 16) == SHAPE
-    assert pack(n=2, m=8) == UNSUP
+    assert pack(n=2, m=6) == UNSUP
+    assert pack(n=8, m=8) == UNSUP
     assert pack(dt=F32) == UNSUP
     assert pack(W=None) == INV
     assert pack(keep=None) == INV
@@ -236,4 +243,5 @@ def test_launch_cfg_validation_is_host_only(L):
     assert L.nm_default_launch(8, 48, 1, 2, 4, 0, ctypes.byref(c)) == SHAPE
     assert L.nm_default_launch(8, 64, 9, 2, 4, 0, ctypes.byref(c)) == INV
     assert L.nm_default_launch(8, 64, 1, 2, 4, 0, None) == INV
-    assert L.nm_default_launch(8, 64, 1, 3, 4, 0, ctypes.byref(c)) == UNSUP
+    assert L.nm_default_launch(8, 64, 1, 3, 6, 0, ctypes.byref(c)) == UNSUP
+    assert L.nm_default_launch(8, 64, 1, 4, 4, 0, ctypes.byref(c)) == UNSUP
