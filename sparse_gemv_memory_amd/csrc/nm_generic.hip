@@ -33,7 +33,10 @@ constexpr int kWinWords = 64;  // mask words per window (one per lane)
 // Chunks of 16 bytes (8 values) one window can span: 64 P values plus up to
 // 7 values of alignment slack in front.
 __host__ __device__ constexpr int win_chunks(int p) { return 8 * p + 1; }
-// Direct-to-LDS load instructions per window (64 chunks each).
+// Direct-to-LDS load instructions per window (64 chunks each).  A buffer of
+// win_loads * 1 KiB >= 16 (8p + 1) bytes is a multiple of 128 bytes, so it
+// also holds the up to 7 slots past lane 63's last value that the 8-step
+// groups of the traversal read (and drop).
 __host__ __device__ constexpr int win_loads(int p) { return (win_chunks(p) + 63) / 64; }
 
 // x segment [s0, s0 + S) of every batch row into LDS: column c of the
@@ -62,6 +65,13 @@ __device__ __forceinline__ void stage_x_cols(char *lds, const uint16_t *__restri
       }
     }
   }
+}
+
+// Sum of v over the wave, the same value in every lane (the DPP reduction
+// into lane 63, then a read of lane 63 executed by the whole wave).
+__device__ __forceinline__ float wave_total(float v) {
+  const float s = wave_sum_to_63(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kWave - 1));
 }
 
 // Kept pair (columns c0, c1 of the segment; packed weights w) for every
@@ -187,26 +197,33 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
                             2u * (uint32_t)((vs & 7) + (int64_t)lane * P);
         const int cb = (t * kWinWords + lane) * 32;  // segment column of the word's bit 0
         uint32_t m = mw;
-        int j = 0;
-        for (; j + 1 < P; j += 2) {
-          const int c0 = ffbl_hw(m) & 31;
-          m &= m - 1;
-          const int c1 = ffbl_hw(m) & 31;
-          m &= m - 1;
-          const uint32_t v0 = ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * j));
-          const uint32_t v1 = ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * j + 2));
-          pair_acc<BF, BP>(lds, cb + c0, cb + c1, v0 | (v1 << 16), acc);
-        }
-        if (j < P) {
-          const int c0 = ffbl_hw(m) & 31;
-          single_acc<BF, BP>(lds, cb + c0, ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * j)), acc);
+        // eight scan steps at a time: the columns first (a short VALU chain),
+        // then every LDS read of the group, then the products.  Steps past P
+        // read slots inside the buffer (see win_loads) and are dropped.
+        for (int j0 = 0; j0 < P; j0 += 8) {
+          int c[8];
+          uint32_t v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            c[e] = cb + (ffbl_hw(m) & 31);
+            m &= m - 1;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * (j0 + e)));
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const int left = P - j0 - e;  // steps of this pair still inside P
+            if (left >= 2)
+              pair_acc<BF, BP>(lds, c[e], c[e + 1], v[e] | (v[e + 1] << 16), acc);
+            else if (left == 1)
+              single_acc<BF, BP>(lds, c[e], v[e], acc);
+          }
         }
       }
       if (t == nwin - 1) {  // the row's part of this segment is complete
 #pragma unroll
         for (int b = 0; b < BP; ++b) {
-          const float s = wave_sum_to_63(acc[b]);
-          const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kWave - 1));
+          const float sv = wave_total(acc[b]);
           res[b] += lane == i ? sv : 0.f;
           acc[b] = 0.f;
         }
@@ -228,6 +245,198 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
       if (b < B) store_out(y, (int64_t)b * R + r0 + lane, res[b], out_kind);
   }
 }
+
+// Direct kernel for the common densities (P = 4, 8, 12, 24 kept columns per
+// word: 1:8, 1:4, 3:8, 3:4) when all of x fits the LDS budget.  Lane l of a
+// wave owns mask words t * 64 U + 64 u + l of its row (u < U): the word and
+// its 2P value bytes (one contiguous run per word, 8- or 16-byte aligned) are
+// loaded straight into registers with raw buffer loads (range-checked at the
+// row end), two load batches in flight per wave, and the word is walked in
+// P unrolled steps, each kept pair meeting its x values from LDS in one dot2.
+template <int P>
+struct WordVals {
+  static constexpr int kBytes = 2 * P;                  // value bytes per word
+  static constexpr int kWidth = kBytes % 16 == 0 ? 16 : 8;  // bytes per load
+  static constexpr int kLoads = kBytes / kWidth;
+  static constexpr int kRegs = kBytes / 4;
+};
+
+template <int P, int U>
+struct WordBatch {
+  uint32_t m[U];
+  uint32_t v[U][WordVals<P>::kRegs];
+};
+
+template <int P, int U>
+__device__ __forceinline__ void word_batch_load(WordBatch<P, U> &bt, const uint16_t *vrow,
+                                                const uint32_t *brow, int nw, int t, int lane) {
+  using V = WordVals<P>;
+  // resources from the batch's first word to the row end: the range check
+  // (vector offsets) zeroes the words past the row
+  const int w0 = t * kWave * U, left = nw - w0 > 0 ? nw - w0 : 0;
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(brow + w0), 0, left * 4, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(vrow + (int64_t)w0 * P), 0, left * V::kBytes, kRsrcWord3);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    bt.m[u] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lane + kWave * u) * 4, 0, kStreamAux);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int l = 0; l < V::kLoads; ++l) {
+      const int off = (lane + kWave * u) * V::kBytes + l * V::kWidth;
+      if constexpr (V::kWidth == 16) {
+        const u32x4_t q = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kStreamAux));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bt.v[u][4 * l + e] = q[e];
+      } else {
+        const u32x2_t q = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, kStreamAux));
+        bt.v[u][2 * l] = q[0];
+        bt.v[u][2 * l + 1] = q[1];
+      }
+    }
+  }
+}
+
+// The P kept weights of one word (mask m, values v) against x columns
+// cb + bit position.
+template <bool BF, int BP, int P>
+__device__ __forceinline__ void word_acc(const char *lds, int cb, uint32_t m,
+                                         const uint32_t (&v)[WordVals<P>::kRegs],
+                                         float (&acc)[BP]) {
+  int c[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    c[j] = cb + (ffbl_hw(m) & 31);
+    m &= m - 1;
+  }
+#pragma unroll
+  for (int j = 0; j < P; j += 2) pair_acc<BF, BP>(lds, c[j], c[j + 1], v[j / 2], acc);
+}
+
+template <bool BF, int BP, int P, int U>
+__global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
+    const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
+    const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int rpw,
+    int out_kind) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wpg = blockDim.x / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t r0 = ((int64_t)blockIdx.x * wpg + wid) * rpw;
+  const int64_t left = R - r0;
+  const int nrows = left <= 0 ? 0 : (left < rpw ? (int)left : rpw);
+  const int W = K >> 5;
+  const int nb = (W + kWave * U - 1) / (kWave * U);  // load batches per row
+  const int nitems = nrows * nb;
+
+  stage_x_cols<BP>(lds, x, B, K, 0, K);
+  __syncthreads();
+
+  auto item_load = [&](WordBatch<P, U> &bt, int k) {
+    const bool real = k < nitems;
+    const int i = real ? k / nb : 0, t = real ? k - i * nb : 0;
+    const int64_t r = real ? r0 + i : 0;
+    word_batch_load<P, U>(bt, values + r * W * P, bits + r * W, real ? W : 0, t, lane);
+  };
+  auto consume = [&](const WordBatch<P, U> &bt, int t, float (&acc)[BP]) {
+    const int wb = t * kWave * U;  // the batch's first word (wave-uniform)
+    if (wb + kWave * U <= W) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        word_acc<BF, BP, P>(lds, (wb + kWave * u + lane) * 32, bt.m[u], bt.v[u], acc);
+      return;
+    }
+    // the row's last batch: words past the row end read zeros and are dropped
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (wb + kWave * u >= W) break;
+      const int w = wb + kWave * u + lane;
+      float part[BP];
+#pragma unroll
+      for (int b = 0; b < BP; ++b) part[b] = 0.f;
+      word_acc<BF, BP, P>(lds, min(w, W - 1) * 32, bt.m[u], bt.v[u], part);
+#pragma unroll
+      for (int b = 0; b < BP; ++b) acc[b] += w < W ? part[b] : 0.f;
+    }
+  };
+
+  float acc[BP], res[BP];
+#pragma unroll
+  for (int b = 0; b < BP; ++b) acc[b] = res[b] = 0.f;
+  WordBatch<P, U> A, Bt;
+  item_load(A, 0);
+  item_load(Bt, 1);
+  for (int k = 0; k < nitems; k += 2) {
+    {
+      const int i = k / nb, t = k - i * nb;
+      consume(A, t, acc);
+      if (t == nb - 1) {
+#pragma unroll
+        for (int b = 0; b < BP; ++b) {
+          // the lane-63 read is taken by every lane: inside a select on the
+          // lane it would let the reduction's last step run for lane i only
+          const float sv = wave_total(acc[b]);
+          res[b] = lane == i ? sv : res[b];
+          acc[b] = 0.f;
+        }
+      }
+    }
+    item_load(A, k + 2);
+    if (k + 1 >= nitems) break;
+    {
+      const int i = (k + 1) / nb, t = (k + 1) - i * nb;
+      consume(Bt, t, acc);
+      if (t == nb - 1) {
+#pragma unroll
+        for (int b = 0; b < BP; ++b) {
+          // the lane-63 read is taken by every lane: inside a select on the
+          // lane it would let the reduction's last step run for lane i only
+          const float sv = wave_total(acc[b]);
+          res[b] = lane == i ? sv : res[b];
+          acc[b] = 0.f;
+        }
+      }
+    }
+    item_load(Bt, k + 3);
+  }
+  if (lane < nrows) {
+#pragma unroll
+    for (int b = 0; b < BP; ++b)
+      if (b < B) store_out(y, (int64_t)b * R + r0 + lane, res[b], out_kind);
+  }
+}
+
+using fixedp_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int,
+                           int64_t, int, int, int);
+
+// The densities with a direct kernel, and its words per lane per load batch.
+__host__ __device__ constexpr bool direct_p(int p) { return p == 4 || p == 8 || p == 12 || p == 24; }
+
+template <bool BF, int BP>
+fixedp_fn pick_fixedp_p(int p) {
+  switch (p) {
+    case 4: return nm_spmv_fixedp_kernel<BF, BP, 4, 4>;
+    case 8: return nm_spmv_fixedp_kernel<BF, BP, 8, 4>;
+    case 12: return nm_spmv_fixedp_kernel<BF, BP, 12, 2>;
+    default: return nm_spmv_fixedp_kernel<BF, BP, 24, 2>;
+  }
+}
+
+template <bool BF>
+fixedp_fn pick_fixedp(int bp, int p) {
+  switch (bp) {
+    case 1: return pick_fixedp_p<BF, 1>(p);
+    case 2: return pick_fixedp_p<BF, 2>(p);
+    case 4: return pick_fixedp_p<BF, 4>(p);
+    default: return pick_fixedp_p<BF, 8>(p);
+  }
+}
+
+size_t fixedp_lds_bytes(int bp, int64_t cols) { return (size_t)cols * 2 * bp; }
 
 using fixed_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int,
                           int64_t, int, int, int, int, int);
@@ -307,6 +516,17 @@ nm_status generic_launch(const void *values, const uint32_t *bits, const void *X
   const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
   if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
   const int seg = cfg.seg_cols < cols ? cfg.seg_cols : (int)cols;
+  if (direct_p(p) && seg == cols && cols > 0) {
+    // all of x in LDS (its bytes are within the checked window-kernel bytes)
+    const fixedp_fn fn =
+        in_dt == NM_BF16 ? pick_fixedp<true>(bp, p) : pick_fixedp<false>(bp, p);
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
+                       fixedp_lds_bytes(bp, cols), (hipStream_t)stream, (const uint16_t *)values,
+                       bits, (const uint16_t *)X, Y, batch, rows, (int)cols, cfg.rows_per_wave,
+                       (int)out_dt);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? NM_OK : hip_fail(e);
+  }
   const fixed_fn fn = in_dt == NM_BF16 ? pick_fixed_bp<true>(bp, ni) : pick_fixed_bp<false>(bp, ni);
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
                      fixed_lds_bytes(bp, seg, waves, ni), (hipStream_t)stream,

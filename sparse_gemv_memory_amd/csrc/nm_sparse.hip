@@ -351,36 +351,39 @@ struct Batch {
 
 // Load batch t of a row segment: lane l gets value chunks t*64U + l + 64u
 // (u < U) and their mask words.  Raw buffer loads: the resource holds the
-// segment's base and byte size, so the per-lane offsets are loop-invariant,
-// the batch offset is a scalar, and a chunk past the end reads zeros (the
-// hardware range check) without touching memory.  nch = 0 makes a dummy
+// batch's base and the bytes left in the segment, so the per-lane offsets are
+// loop-invariant and a chunk past the end reads zeros (the hardware range
+// check) without touching memory.  nch = 0 makes a dummy
 // batch that keeps the wait counts uniform and costs no memory traffic.
 // MF: the mask words are issued before the values, so the first chunk of a
 // batch waits for one value load less.
 template <int U, bool MF = false>
 __device__ __forceinline__ void load_batch(Batch<U> &bt, const uint4 *vrow,
                                            const uint32_t *brow, int nch, int t, int lane) {
+  // the resources start at the batch (scalar arithmetic) and end at the row
+  // end, so the range check, which covers the vector offsets, zeroes every
+  // chunk past the row
+  const int c0 = t * (kWave * U), left = nch - c0 > 0 ? nch - c0 : 0;
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void *)vrow, 0, nch * 16, kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void *)(vrow + c0), 0, left * 16, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc((void *)brow, 0, nch * 2, kRsrcWord3);
-  const int sv = t * (kWave * U * 16), sb = t * (kWave * U * 2);
+      __builtin_amdgcn_make_buffer_rsrc((void *)(brow + c0 / 2), 0, left * 2, kRsrcWord3);
   if constexpr (MF) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      bt.m[u] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lane >> 1) * 4 + u * kWave * 2, sb,
+      bt.m[u] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lane >> 1) * 4 + u * kWave * 2, 0,
                                                      kStreamAux);
 #pragma unroll
     for (int u = 0; u < U; ++u)
       bt.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rv, lane * 16 + u * kWave * 16, sv, kStreamAux));
+                                              rv, lane * 16 + u * kWave * 16, 0, kStreamAux));
     return;
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     bt.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rv, lane * 16 + u * kWave * 16, sv, kStreamAux));
-    bt.m[u] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lane >> 1) * 4 + u * kWave * 2, sb,
+                                            rv, lane * 16 + u * kWave * 16, 0, kStreamAux));
+    bt.m[u] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lane >> 1) * 4 + u * kWave * 2, 0,
                                                    kStreamAux);
   }
 }
@@ -905,13 +908,15 @@ struct DBatch {
 template <int U>
 __device__ __forceinline__ void dload_batch(DBatch<U> &bt, const uint4 *wrow, int nch, int t,
                                             int lane) {
+  // the resource starts at the batch and ends at the row end (the range check
+  // covers the vector offsets only)
+  const int c0 = t * (kWave * U), left = nch - c0 > 0 ? nch - c0 : 0;
   const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void *)wrow, 0, nch * 16, kRsrcWord3);
-  const int so = t * (kWave * U * 16);
+      __builtin_amdgcn_make_buffer_rsrc((void *)(wrow + c0), 0, left * 16, kRsrcWord3);
 #pragma unroll
   for (int u = 0; u < U; ++u)
     bt.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            r, lane * 16 + u * kWave * 16, so, kStreamAux));
+                                            r, lane * 16 + u * kWave * 16, 0, kStreamAux));
 }
 
 template <bool BF, int BP, int U>
