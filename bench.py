@@ -239,8 +239,8 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("a41b0913a27900c4ac644d5d047ab30daefcd81ed6dc5863cbffa9ef888196a5",
-                    66270525),
+    (14336, 4096): ("c3073046669a0e990960b3198540199bc22b7188910dbf14b932e4942813fe4f",
+                    66260289),
 }
 
 

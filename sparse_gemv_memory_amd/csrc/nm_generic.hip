@@ -39,11 +39,25 @@ __host__ __device__ constexpr int win_chunks(int p) { return 8 * p + 1; }
 // groups of the traversal read (and drop).
 __host__ __device__ constexpr int win_loads(int p) { return (win_chunks(p) + 63) / 64; }
 
-// x segment [s0, s0 + S) of every batch row into LDS: column c of the
-// segment at byte c * 2 * BP, batch row b at + 2 b (rows >= B hold zeros).
+// LDS image of a segment of x: bit b of the segment's word w (column
+// 32 w + b) holds the BP batch values of that column in one slot of SB bytes
+// at w * WS + b * SB; each word's 32 slots are followed by PB pad bytes, so
+// the words that the 64 lanes of a wave gather from at once (one word per
+// lane) start in different LDS banks.
+template <int BP>
+struct XCols {
+  static constexpr int SB = 2 * BP;
+  static constexpr int PB = SB < 4 ? 4 : SB;
+  static constexpr int WS = 32 * SB + PB;
+  static constexpr size_t bytes(int seg_cols) { return (size_t)(seg_cols / 32) * WS; }
+};
+
+// x segment [s0, s0 + S) of every batch row into the XCols<BP> image (rows
+// >= B hold zeros), one 8-column group at a time.
 template <int BP>
 __device__ __forceinline__ void stage_x_cols(char *lds, const uint16_t *__restrict__ x, int B,
                                              int K, int s0, int S) {
+  using L = XCols<BP>;
   for (int g = threadIdx.x; g < S / 8; g += blockDim.x) {
     uint4 r[BP];
 #pragma unroll
@@ -52,10 +66,15 @@ __device__ __forceinline__ void stage_x_cols(char *lds, const uint16_t *__restri
       r[b] = reinterpret_cast<const uint4 *>(x + (int64_t)bb * K + s0)[g];
       if (b >= B) r[b] = make_uint4(0, 0, 0, 0);
     }
-    if constexpr (BP == 1) {
-      reinterpret_cast<uint4 *>(lds)[g] = r[0];
+    char *dst = lds + (g >> 2) * L::WS + (8 * g & 31) * L::SB;
+    if constexpr (BP == 1) {  // 4-byte aligned: four dword stores
+      uint32_t *d = reinterpret_cast<uint32_t *>(dst);
+      d[0] = r[0].x;
+      d[1] = r[0].y;
+      d[2] = r[0].z;
+      d[3] = r[0].w;
     } else {
-      uint16_t *d = reinterpret_cast<uint16_t *>(lds) + (size_t)8 * g * BP;
+      uint16_t *d = reinterpret_cast<uint16_t *>(dst);
 #pragma unroll
       for (int b = 0; b < BP; ++b) {
         uint16_t h[8];
@@ -74,12 +93,12 @@ __device__ __forceinline__ float wave_total(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kWave - 1));
 }
 
-// Kept pair (columns c0, c1 of the segment; packed weights w) for every
-// batch row.
+// Kept pair (x slots at byte offsets a0, a1 of the XCols image; packed
+// weights w) for every batch row.
 template <bool BF, int BP>
-__device__ __forceinline__ void pair_acc(const char *lds, int c0, int c1, uint32_t w,
+__device__ __forceinline__ void pair_acc(const char *lds, int a0, int a1, uint32_t w,
                                          float (&acc)[BP]) {
-  const lds_ptr x0 = (lds_ptr)lds + c0 * (2 * BP), x1 = (lds_ptr)lds + c1 * (2 * BP);
+  const lds_ptr x0 = (lds_ptr)lds + a0, x1 = (lds_ptr)lds + a1;
   if constexpr (BP == 1) {
     u16x2_t pr;
     pr[0] = ld<uint16_t>(x0);
@@ -110,9 +129,9 @@ __device__ __forceinline__ void pair_acc(const char *lds, int c0, int c1, uint32
 // One kept weight v (low half; the high half is 0 and meets an x of 0, so the
 // pair product adds exactly v * x).
 template <bool BF, int BP>
-__device__ __forceinline__ void single_acc(const char *lds, int c0, uint32_t v,
+__device__ __forceinline__ void single_acc(const char *lds, int a0, uint32_t v,
                                            float (&acc)[BP]) {
-  const lds_ptr x0 = (lds_ptr)lds + c0 * (2 * BP);
+  const lds_ptr x0 = (lds_ptr)lds + a0;
 #pragma unroll
   for (int b = 0; b < BP; ++b)
     acc[b] = dot2<BF>(v, (uint32_t)ld<uint16_t>(x0 + 2 * b), acc[b]);
@@ -136,7 +155,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
   const int nrows = left <= 0 ? 0 : (left < rpw ? (int)left : rpw);
   const int W = K >> 5;                   // mask words per row
   const int64_t vstride = (int64_t)W * P;  // values per row
-  const uint32_t xbytes = ((uint32_t)seg * (2 * BP) + 15u) & ~15u;
+  const uint32_t xbytes = ((uint32_t)XCols<BP>::bytes(seg) + 15u) & ~15u;
   // LDS address of the wave's two window buffers (NI KiB each)
   const uint32_t wbuf = (uint32_t)(size_t)(lds_ptr)lds + xbytes + (uint32_t)wid * (2 * NI * 1024);
 
@@ -195,7 +214,8 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
         const int64_t vs = r * vstride + (int64_t)w0 * P;
         const uint32_t vb = wbuf + (uint32_t)(k & 1) * (NI * 1024) +
                             2u * (uint32_t)((vs & 7) + (int64_t)lane * P);
-        const int cb = (t * kWinWords + lane) * 32;  // segment column of the word's bit 0
+        // byte offset of the word's x slots in the segment's image
+        const int cb = (t * kWinWords + lane) * XCols<BP>::WS;
         uint32_t m = mw;
         // eight scan steps at a time: the columns first (a short VALU chain),
         // then every LDS read of the group, then the products.  Steps past P
@@ -205,7 +225,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
           uint32_t v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            c[e] = cb + (ffbl_hw(m) & 31);
+            c[e] = cb + (ffbl_hw(m) & 31) * XCols<BP>::SB;
             m &= m - 1;
           }
 #pragma unroll
@@ -301,16 +321,16 @@ __device__ __forceinline__ void word_batch_load(WordBatch<P, U> &bt, const uint1
   }
 }
 
-// The P kept weights of one word (mask m, values v) against x columns
-// cb + bit position.
+// The P kept weights of one word (mask m, values v) against the word's x
+// slots at byte offset xw of the XCols image.
 template <bool BF, int BP, int P>
-__device__ __forceinline__ void word_acc(const char *lds, int cb, uint32_t m,
+__device__ __forceinline__ void word_acc(const char *lds, int xw, uint32_t m,
                                          const uint32_t (&v)[WordVals<P>::kRegs],
                                          float (&acc)[BP]) {
   int c[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) {
-    c[j] = cb + (ffbl_hw(m) & 31);
+    c[j] = xw + (ffbl_hw(m) & 31) * XCols<BP>::SB;
     m &= m - 1;
   }
 #pragma unroll
@@ -347,7 +367,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
     if (wb + kWave * U <= W) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        word_acc<BF, BP, P>(lds, (wb + kWave * u + lane) * 32, bt.m[u], bt.v[u], acc);
+        word_acc<BF, BP, P>(lds, (wb + kWave * u + lane) * XCols<BP>::WS, bt.m[u], bt.v[u], acc);
       return;
     }
     // the row's last batch: words past the row end read zeros and are dropped
@@ -358,7 +378,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
       float part[BP];
 #pragma unroll
       for (int b = 0; b < BP; ++b) part[b] = 0.f;
-      word_acc<BF, BP, P>(lds, min(w, W - 1) * 32, bt.m[u], bt.v[u], part);
+      word_acc<BF, BP, P>(lds, min(w, W - 1) * XCols<BP>::WS, bt.m[u], bt.v[u], part);
 #pragma unroll
       for (int b = 0; b < BP; ++b) acc[b] += w < W ? part[b] : 0.f;
     }
@@ -436,7 +456,16 @@ fixedp_fn pick_fixedp(int bp, int p) {
   }
 }
 
-size_t fixedp_lds_bytes(int bp, int64_t cols) { return (size_t)cols * 2 * bp; }
+size_t xcols_bytes(int bp, int64_t cols) {
+  switch (bp) {
+    case 1: return XCols<1>::bytes((int)cols);
+    case 2: return XCols<2>::bytes((int)cols);
+    case 4: return XCols<4>::bytes((int)cols);
+    default: return XCols<8>::bytes((int)cols);
+  }
+}
+
+size_t fixedp_lds_bytes(int bp, int64_t cols) { return xcols_bytes(bp, cols); }
 
 using fixed_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int,
                           int64_t, int, int, int, int, int);
@@ -463,8 +492,10 @@ fixed_fn pick_fixed_bp(int bp, int ni) {
 
 int pad_b(int b) { return b <= 1 ? 1 : b <= 2 ? 2 : b <= 4 ? 4 : 8; }
 
+size_t xcols_bytes(int bp, int64_t cols);
+
 size_t fixed_lds_bytes(int bp, int seg, int waves, int ni) {
-  return (((size_t)seg * 2 * bp + 15) & ~(size_t)15) + (size_t)waves * 2 * ni * 1024;
+  return ((xcols_bytes(bp, seg) + 15) & ~(size_t)15) + (size_t)waves * 2 * ni * 1024;
 }
 
 }  // namespace
@@ -488,7 +519,8 @@ nm_status generic_default_cfg(int64_t rows, int64_t cols, int batch, int n, int 
     cfg->seg_cols = cols > 0 ? (int)cols : 32;
   } else {
     // widest multiple of 2048 columns (whole windows) that fits
-    const int64_t s = (int64_t)((lds_budget - wave_area) / (2 * bp)) / 2048 * 2048;
+    const size_t ws = xcols_bytes(bp, 32);  // bytes per 32-column word
+    const int64_t s = (int64_t)((lds_budget - wave_area - 16) / ws) * 32 / 2048 * 2048;
     cfg->seg_cols = (int)(s < 2048 ? 2048 : s);
   }
   return NM_OK;
