@@ -239,8 +239,8 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("c3073046669a0e990960b3198540199bc22b7188910dbf14b932e4942813fe4f",
-                    66260289),
+    (14336, 4096): ("ad1a58765a6a1f563c39e7f8058c25f9cc6c9468ce500dc4284e219450f37256",
+                    66272572),
 }
 
 

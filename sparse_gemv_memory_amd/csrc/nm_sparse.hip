@@ -1290,6 +1290,8 @@ void mfma_default(int64_t rows, int64_t cols, int batch, int kind, const DevInfo
 constexpr int kMfmaMinBatch = 2;
 constexpr int kDenseMfmaMinBatch = 5;  // measured: the VALU kernel wins at batch <= 4
 
+int rows_batch_chunks(int64_t cols, int bp);
+
 // pair: the rows come in (gate, up) pairs for the SwiGLU epilogue, so a
 // wave of the row kernel must own an even number of rows.
 nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool dense,
@@ -1332,7 +1334,9 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
     }
     if (full <= budget / 2 && rows % (rmin * two_per_cu) == 0 && rows / two_per_cu <= 16) {
       int rpw = rmin;
-      if (!dense && bp == 1 && cols <= 16384)
+      // (2:4 rows whose load batches hold 2 chunks per lane keep one row per
+      // wave: 8 waves per workgroup measured 3% faster for K = 14336)
+      if (!dense && bp == 1 && cols <= 16384 && !(m == 4 && rows_batch_chunks(cols, bp) == 2))
         for (int r = 4; r >= 2; r -= 2)
           if (rows % (r * two_per_cu) == 0 && rows / (r * two_per_cu) >= 4) { rpw = r; break; }
       cfg->threads_per_wg = (int)(rows / (rpw * two_per_cu)) * kWave;
@@ -1459,11 +1463,18 @@ rows_fn pick_rows_bp(int bp, int u, int xs) {
   }
 }
 
+template <bool BF, int PK, int XS>
+rows_fn pick_rows_24x_u(int u) {
+  switch (u) {
+    case 2: return nm_spmv_rows_kernel<BF, 1, PK, 2, XS>;
+    case 5: return nm_spmv_rows_kernel<BF, 1, PK, 5, XS>;
+    default: return nm_spmv_rows_kernel<BF, 1, PK, 4, XS>;
+  }
+}
+
 template <bool BF, int PK>
 rows_fn pick_rows_24x_xs(int u, int xs) {
-  if (xs > 4)
-    return u == 5 ? nm_spmv_rows_kernel<BF, 1, PK, 5, 8> : nm_spmv_rows_kernel<BF, 1, PK, 4, 8>;
-  return u == 5 ? nm_spmv_rows_kernel<BF, 1, PK, 5, 4> : nm_spmv_rows_kernel<BF, 1, PK, 4, 4>;
+  return xs > 4 ? pick_rows_24x_u<BF, PK, 8>(u) : pick_rows_24x_u<BF, PK, 4>(u);
 }
 
 template <bool BF>
@@ -1488,14 +1499,18 @@ rows_fn pick_rows(bool bf, int pk, int bp, int u, int xs, bool exact) {
 }
 
 // Chunks per lane per load batch of the batch-1 row kernel: 4, or 5 when
-// that divides the row's chunks per lane (K / 1024) and 4 does not, so the
-// row's last batch has no idle slots (K = 5120, 25600).  Measured on the
-// 8B/70B/Qwen shapes: 5 helps the K = 5120k shapes; 7 (for K = 14336) costs
-// occupancy (93 VGPRs) and is slower than a ragged last batch of 4.
+// that divides the row's chunks per lane (K / 1024) and 4 does not, or 2 when
+// neither does but 2 does, so the row's last batch has no idle slots
+// (K = 5120, 25600: 5; K = 14336: 2, with one row per wave, see default_cfg).
+// Measured on the 8B/70B/Qwen shapes: 5 helps the K = 5120k shapes; for
+// K = 14336, 2 (12.0 us) beats a ragged last batch of 4 (12.4 us), and 7 costs
+// occupancy and is slower than both.
 int rows_batch_chunks(int64_t cols, int bp) {
   if (bp != 1 || cols % 1024 != 0) return 4;
   const int64_t c = cols / 1024;
-  return (c % 4 != 0 && c % 5 == 0) ? 5 : 4;
+  if (c % 4 == 0) return 4;
+  if (c % 5 == 0) return 5;
+  return c % 2 == 0 ? 2 : 4;
 }
 
 template <bool BF, int BP>
