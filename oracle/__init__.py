@@ -88,6 +88,12 @@ def _load():
     lib.oracle_pack.restype = ci
     lib.oracle_unpack.argtypes = [p, p, i64, i64, ci, ci, p, p]
     lib.oracle_unpack.restype = ci
+    lib.oracle_bitmask_row_ptr.argtypes = [p, i64, i64, p]
+    lib.oracle_bitmask_row_ptr.restype = None
+    lib.oracle_pack_bitmask.argtypes = [p, p, i64, i64, p, p, p]
+    lib.oracle_pack_bitmask.restype = ci
+    lib.oracle_unpack_bitmask.argtypes = [p, p, p, i64, i64, p, p]
+    lib.oracle_unpack_bitmask.restype = ci
     lib.oracle_masked_gemv_f64.argtypes = [p, p, ci, p, ci, i64, i64, p, i64, ci, p]
     lib.oracle_masked_gemv_f64.restype = None
     lib.oracle_silu_mul_f64.argtypes = [p, p, i64, p]
@@ -156,6 +162,35 @@ def unpack(values, bits, cols: int, n: int, m: int):
     W = np.zeros((rows, cols), dtype=np.uint16)
     keep = np.zeros((rows, cols), dtype=np.uint8)
     st = _load().oracle_unpack(_ptr(v), _ptr(b), rows, cols, n, m, _ptr(W), _ptr(keep))
+    return st, W, keep
+
+
+def pack_bitmask(W, keep):
+    """Unstructured bitmask pack of any keep-mask.  Returns (status, values
+    uint16[row_ptr[-1]], bits uint32[rows, cols/32], row_ptr int64[rows+1])."""
+    w = _bits16(W)
+    k = _keep_u8(keep)
+    rows, cols = w.shape
+    if k.shape != w.shape:
+        raise ValueError("W and keep must have the same shape")
+    row_ptr = np.zeros(rows + 1, dtype=np.int64)
+    _load().oracle_bitmask_row_ptr(_ptr(k), rows, cols, _ptr(row_ptr))
+    values = np.zeros(int(row_ptr[-1]), dtype=np.uint16)
+    bits = np.zeros((rows, cols // 32), dtype=np.uint32)
+    st = _load().oracle_pack_bitmask(_ptr(w), _ptr(k), rows, cols, _ptr(row_ptr), _ptr(values),
+                                     _ptr(bits))
+    return st, values, bits, row_ptr
+
+
+def unpack_bitmask(values, bits, row_ptr, cols: int):
+    """Return (status, W uint16[rows, cols], keep uint8[rows, cols])."""
+    v = _bits16(values)
+    b = np.ascontiguousarray(bits, dtype=np.uint32)
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+    rows = b.shape[0]
+    W = np.zeros((rows, cols), dtype=np.uint16)
+    keep = np.zeros((rows, cols), dtype=np.uint8)
+    st = _load().oracle_unpack_bitmask(_ptr(v), _ptr(b), _ptr(rp), rows, cols, _ptr(W), _ptr(keep))
     return st, W, keep
 
 

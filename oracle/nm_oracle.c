@@ -171,6 +171,68 @@ int oracle_unpack(const uint16_t *values, const uint32_t *bits, int64_t rows, in
     return OR_OK;
 }
 
+/* ---- unstructured bitmasks (any keep mask) ------------------------------- */
+
+/* The same bitmask format for an arbitrary keep mask (the pages evaluate 50%
+ * unstructured pruning for quality, "Experiments"): each row's kept weights
+ * in increasing column order, rows one after another, row r starting at
+ * values[row_ptr[r]]; row_ptr has rows + 1 entries, row_ptr[0] = 0 and
+ * row_ptr[rows] = the number of kept weights.  A word's count now varies, so
+ * its values start at the row's start plus the set bits of the words before
+ * it. */
+void oracle_bitmask_row_ptr(const uint8_t *keep, int64_t rows, int64_t cols,
+                            int64_t *row_ptr) {
+    row_ptr[0] = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t cnt = 0;
+        for (int64_t c = 0; c < cols; ++c) cnt += keep[r * cols + c] != 0;
+        row_ptr[r + 1] = row_ptr[r] + cnt;
+    }
+}
+
+int oracle_pack_bitmask(const uint16_t *W, const uint8_t *keep, int64_t rows, int64_t cols,
+                        const int64_t *row_ptr, uint16_t *values, uint32_t *bits) {
+    if (cols % 32 != 0) return OR_ERR_SHAPE;
+    const int64_t wrow = cols / 32;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t j = row_ptr[r];
+        for (int64_t w = 0; w < wrow; ++w) {
+            uint32_t word = 0;
+            for (int b = 0; b < 32; ++b) {
+                int64_t c = 32 * w + b;
+                if (keep[r * cols + c]) {
+                    word |= (uint32_t)1 << b;
+                    values[j++] = W[r * cols + c];
+                }
+            }
+            bits[r * wrow + w] = word;
+        }
+        if (j != row_ptr[r + 1]) return OR_ERR_MASK;
+    }
+    return OR_OK;
+}
+
+int oracle_unpack_bitmask(const uint16_t *values, const uint32_t *bits, const int64_t *row_ptr,
+                          int64_t rows, int64_t cols, uint16_t *W, uint8_t *keep) {
+    if (cols % 32 != 0) return OR_ERR_SHAPE;
+    const int64_t wrow = cols / 32;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t j = row_ptr[r];
+        for (int64_t c = 0; c < cols; ++c) {
+            int set = (bits[r * wrow + c / 32] >> (c % 32)) & 1u;
+            if (set) {
+                if (j >= row_ptr[r + 1]) return OR_ERR_MASK;
+                W[r * cols + c] = values[j++];
+            } else {
+                W[r * cols + c] = 0;
+            }
+            keep[r * cols + c] = (uint8_t)set;
+        }
+        if (j != row_ptr[r + 1]) return OR_ERR_MASK;
+    }
+    return OR_OK;
+}
+
 /* ---- the product ---------------------------------------------------------- */
 
 /* y[b][i] = sum_{c=0}^{cols-1} [keep[r][c] != 0] * W[r][c] * x[b][c], r = row_idx[i]

@@ -92,6 +92,24 @@ def topn_mask(w_bits: np.ndarray, n: int, m: int, chunk_rows: int = 4096) -> np.
     return keep
 
 
+def topk_row_mask(w_bits: np.ndarray, frac: float = 0.5) -> np.ndarray:
+    """uint8 unstructured keep-mask: per row the round(frac * cols) largest
+    magnitudes, ties to the lower column (key magnitude * 2**20 + (2**20 - 1
+    - column), distinct within a row for cols <= 2**20)."""
+    w = np.ascontiguousarray(w_bits).view(np.uint16)
+    rows, cols = w.shape
+    k = int(round(frac * cols))
+    if cols > (1 << 20) or not (0 <= k <= cols):
+        raise ValueError("bad shape or fraction")
+    keep = np.zeros((rows, cols), dtype=np.uint8)
+    if k == 0:
+        return keep
+    key = ((w & 0x7FFF).astype(np.int64) << 20) | ((1 << 20) - 1 - np.arange(cols, dtype=np.int64))
+    idx = np.argpartition(-key, k - 1, axis=1)[:, :k]
+    np.put_along_axis(keep, idx, 1, axis=1)
+    return keep
+
+
 def activations(batch: int, cols: int, seed: int, dtype: str = F16,
                 outliers: bool = True) -> np.ndarray:
     """(batch, cols) uint16 bit patterns of N(0, 1) activations."""

@@ -286,6 +286,117 @@ def test_topn_mask_other_densities_brute_force(n, m):
             assert np.array_equal(keep[r, g * m:(g + 1) * m], want)
 
 
+# ---- unstructured bitmasks (any keep mask, row offsets) -------------------------
+
+def _brute_pack_bitmask(W, keep):
+    """Rows' kept values concatenated, from the list of kept columns."""
+    rows, cols = W.shape
+    vals, ptr = [], [0]
+    for r in range(rows):
+        kept = [c for c in range(cols) if keep[r, c]]
+        vals += [int(W[r, c]) for c in kept]
+        ptr.append(len(vals))
+    words = [[sum(1 << b for b in range(32) if keep[r, 32 * w + b]) for w in range(cols // 32)]
+             for r in range(rows)]
+    return (np.array(vals, dtype=np.uint16), np.array(words, dtype=np.uint32),
+            np.array(ptr, dtype=np.int64))
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (5, 96), (9, 160)])
+def test_pack_bitmask_matches_brute_force(rows, cols):
+    W = synth.weights(rows, cols, seed=53)
+    rng = np.random.default_rng(rows + cols)
+    keep = (rng.random((rows, cols)) < 0.5).astype(np.uint8)
+    keep[0, :] = 0            # an empty row
+    if rows > 1:
+        keep[1, :] = 1        # a full row
+    st, values, bits, row_ptr = oracle.pack_bitmask(W, keep)
+    assert st == oracle.OK
+    bv, bb, bp = _brute_pack_bitmask(W, keep)
+    assert np.array_equal(values, bv)
+    assert np.array_equal(bits, bb)
+    assert np.array_equal(row_ptr, bp)
+
+
+def test_pack_bitmask_offsets_are_prefix_popcounts():
+    """Word w of row r starts at row_ptr[r] plus the set bits of the row's
+    words before w (the per-word prefix offsets the format needs once the
+    count per word varies)."""
+    W = np.broadcast_to(np.arange(256, dtype=np.uint16), (6, 256)).copy()
+    keep = synth.topk_row_mask(synth.weights(6, 256, seed=59), 0.5)
+    st, values, bits, row_ptr = oracle.pack_bitmask(W, keep)
+    assert st == oracle.OK
+    assert np.array_equal(np.diff(row_ptr), keep.sum(axis=1))
+    for r in range(6):
+        off = row_ptr[r]
+        for w in range(8):
+            word = int(bits[r, w])
+            cols = [32 * w + b for b in range(32) if word >> b & 1]
+            assert list(values[off:off + len(cols)]) == cols
+            off += len(cols)
+        assert off == row_ptr[r + 1]
+
+
+def test_unpack_bitmask_inverts_pack():
+    W = synth.weights(7, 128, seed=61, dtype="bf16")
+    keep = synth.topk_row_mask(W, 0.5)
+    st, values, bits, row_ptr = oracle.pack_bitmask(W, keep)
+    assert st == oracle.OK
+    st, W2, k2 = oracle.unpack_bitmask(values, bits, row_ptr, 128)
+    assert st == oracle.OK
+    assert np.array_equal(k2, keep)
+    assert np.array_equal(W2, np.where(keep != 0, W, 0).astype(np.uint16))
+
+
+def test_pack_bitmask_of_an_nm_mask_is_the_nm_pack():
+    """An N:M mask is a special unstructured mask: the same values and words,
+    rows at stride K*N/M."""
+    W = synth.weights(5, 128, seed=67)
+    keep = synth.topn_mask(W, 2, 4)
+    st, values, bits, row_ptr = oracle.pack_bitmask(W, keep)
+    st2, v2, b2 = oracle.pack(W, keep, 2, 4)
+    assert st == st2 == oracle.OK
+    assert np.array_equal(values, v2.reshape(-1))
+    assert np.array_equal(bits, b2)
+    assert np.array_equal(row_ptr, np.arange(6) * 64)
+
+
+def test_topk_row_mask_keeps_the_larger_half_per_row():
+    W = synth.weights(4, 64, seed=71)
+    W[0, :] = W[0, 0]  # all ties: the lower columns win
+    keep = synth.topk_row_mask(W, 0.5)
+    assert np.all(keep.sum(axis=1) == 32)
+    assert np.array_equal(keep[0], np.r_[np.ones(32), np.zeros(32)].astype(np.uint8))
+    mag = (W & 0x7FFF).astype(np.int64)
+    for r in range(1, 4):
+        order = sorted(range(64), key=lambda c: (-mag[r, c], c))[:32]
+        want = np.zeros(64, np.uint8)
+        want[order] = 1
+        assert np.array_equal(keep[r], want)
+
+
+def test_masked_gemv_from_bitmask_form():
+    """The product re-walked from the unstructured packed form equals the
+    dense masked product."""
+    rows, cols = 6, 96
+    W = synth.weights(rows, cols, seed=73)
+    keep = synth.topk_row_mask(W, 0.5)
+    x = synth.activations(2, cols, seed=73)
+    st, values, bits, row_ptr = oracle.pack_bitmask(W, keep)
+    vf, xf = _f64(values, False), _f64(x, False)
+    y = np.zeros((2, rows))
+    for r in range(rows):
+        j = row_ptr[r]
+        for w in range(cols // 32):
+            word = int(bits[r, w])
+            while word:
+                c = (word & -word).bit_length() - 1
+                word &= word - 1
+                y[:, r] += vf[j] * xf[:, 32 * w + c]
+                j += 1
+    assert np.allclose(oracle.masked_gemv(W, keep, x, False), y, rtol=1e-12, atol=1e-12)
+
+
 # ---- the product ----------------------------------------------------------------
 
 def _f64(bits, bf16):
