@@ -323,6 +323,71 @@ def shapes_run(cfg_id, args, mats=None):
     return rows_out
 
 
+def bitmask_run(args):
+    """Unstructured 50% bitmasks (per-row largest half) on the 8B gate and down
+    shapes, batch 1 and 8: µs/call and GB/s, cache-cold rotation, against the
+    2:4 kernel's bytes and the dense products."""
+    out = []
+    for i, (name, rows, cols) in enumerate(workloads.LLAMA8B_LAYER):
+        if name not in ("gate", "down"):
+            continue
+        seed = synth.layer_seed(7, 0, i)
+        W = synth.weights(rows, cols, seed=seed)
+        keep = synth.topk_row_mask(W, 0.5)
+        Wd = t16(W)
+        values, bits, offs = native.nm_pack_bitmask(Wd, torch.from_numpy(keep).to(DEV))
+        nbytes_w = values.numel() * 2 + bits.numel() * 4 + offs.numel() * 8
+        nc = pow2_copies(nbytes_w)
+        vals = [values] + [native.clone_packed(values) for _ in range(nc - 1)]
+        bts = [bits] + [bits.clone() for _ in range(nc - 1)]
+        ndc = pow2_copies(Wd.numel() * 2)
+        dense = [Wd] + [Wd.clone() for _ in range(ndc - 1)]
+        for b in (1, 8):
+            X = t16(synth.activations(b, cols, seed=seed))
+            Y = torch.empty((b, rows), dtype=torch.float32, device=DEV)
+            L = native.lib()
+
+            def call(c, X=X, Y=Y, b=b):
+                st = L.nm_spmm_bitmask(vals[c].data_ptr(), bts[c].data_ptr(), offs.data_ptr(),
+                                       X.data_ptr(), Y.data_ptr(), b, rows, cols, native.NM_F16,
+                                       native.NM_F32, torch.cuda.current_stream().cuda_stream)
+                if st != native.NM_OK:
+                    raise native.NMError(st, "nm_spmm_bitmask")
+
+            def dcall(c, X=X, Y=Y, b=b):
+                st = L.nm_dense_gemv(dense[c].data_ptr(), X.data_ptr(), Y.data_ptr(), b, rows, cols,
+                                     native.NM_F16, native.NM_F32, torch.cuda.current_stream().cuda_stream)
+                if st != native.NM_OK:
+                    raise native.NMError(st, "nm_dense_gemv")
+
+            g = capture(lambda: [call(c) for c in range(nc)])
+            gd = capture(lambda: [dcall(c) for c in range(ndc)])
+            gt = capture(lambda: [torch.nn.functional.linear(X, dense[c]) for c in range(ndc)])
+            res = {}
+            for key, graph, n in (("us", g, nc), ("dense_us", gd, ndc), ("torch_linear_us", gt, ndc)):
+                graph.replay()
+                torch.cuda.synchronize()
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.reps)]
+                for a, z in evs:
+                    a.record()
+                    graph.replay()
+                    z.record()
+                torch.cuda.synchronize()
+                res[key] = round(1e3 * float(np.median([a.elapsed_time(z) for a, z in evs])) / n, 3)
+            nbytes = nbytes_w + b * cols * 2 + b * rows * 4
+            row = {"matrix": f"{name} 50% unstructured", "rows": rows, "cols": cols, "batch": b,
+                   "bytes": nbytes, **res, "GB/s": round(nbytes / res["us"] / 1e3, 1),
+                   "frac_of_peak": round(nbytes / res["us"] / 1e3 / PEAK_GBS, 4)}
+            out.append(row)
+            log(f"  {name:5s} {rows}x{cols} 50% unstructured b={b}: {res['us']:8.2f} us "
+                f"{row['GB/s']:7.1f} GB/s ({100 * row['frac_of_peak']:.1f}%)  dense {res['dense_us']:.2f} "
+                f"torch {res['torch_linear_us']:.2f}")
+        del vals, bts, dense
+        torch.cuda.empty_cache()
+    return out
+
+
 def pack_gpu(W, n, m):
     """nm_pack of a GPU fp16 matrix under the top-n |w| of every m mask
     (ties to the lower column), the mask drawn on the GPU."""
@@ -685,7 +750,7 @@ def main():
     ap.add_argument("--workload", default="llama8b-layer",
                     choices=["llama8b-layer", "single", "patterns", "70b-qwen", "decode-32-layers",
                              "llama8b-layer-fused", "calibration-hessian", "prefill-contrast",
-                             "densities"],
+                             "densities", "unstructured"],
                     help="llama8b-layer (default, the headline line): one Llama-3.1-8B layer; "
                          "single: the 4096x4096 matrix; patterns: 4:8/8:16/16:32 bf16 on the 8B "
                          "shapes; 70b-qwen: Llama-3.3-70B and Qwen3-32B shapes; "
@@ -696,7 +761,8 @@ def main():
                          "prefill-contrast: 2:4 gate/down shapes as the batch grows to 4096 "
                          "tokens, sparse matrix cores against the dense GEMM; densities: "
                          "1:4, 3:4, 1:8, 3:8 fp16 on the 8B gate and down shapes (generic "
-                         "window kernel) against the dense GEMV")
+                         "window kernel) against the dense GEMV; unstructured: 50% per-row "
+                         "bitmasks on the same shapes")
     ap.add_argument("--counters", action="store_true",
                     help="short eager run for rocprofv3 --pmc: the 14336x4096 sparse kernel on "
                          "5 cache-cold copies, then 5 plain copies of 64 MiB (the known-size "
@@ -738,6 +804,13 @@ def main():
         print(json.dumps({"metric": "Hessian accumulation H += 2 X X^T, us per call",
                           "workload": args.workload, "n_gpus": 1, "data": "synthetic",
                           "dtype": "f16 inputs, fp32 H", **body}), flush=True)
+        return
+    if args.workload == "unstructured":
+        log("workload unstructured (50% per-row bitmasks on the 8B gate and down shapes)")
+        body = {"per_matrix": bitmask_run(args)}
+        print(json.dumps({"metric": METRIC.replace("2:4", "50% unstructured bitmask"),
+                          "workload": args.workload, "n_gpus": 1, "data": "synthetic",
+                          "peak_GB/s": PEAK_GBS, **body}), flush=True)
         return
     if args.workload == "densities":
         log("workload densities (1:4, 3:4, 1:8, 3:8 on the 8B gate and down shapes)")

@@ -280,6 +280,42 @@ int nm_spmm_swiglu_cfg(const void *values, const uint32_t *bits, const void *X,
                        int m, nm_dtype in_dt, nm_dtype out_dt,
                        const nm_launch_cfg *cfg, void *stream);
 
+/* Unstructured bitmasks: the bitmask format of Method item (1) for any keep
+ * mask (the pages evaluate 50% unstructured pruning for quality,
+ * "Experiments").  Values are the kept weights in column order, rows one
+ * after another; bits as for N:M.  A word's count now varies, so an offset
+ * index replaces the fixed row stride: offs[r * nwr + t] is the index in
+ * values of the first kept weight of window t of row r, a window being 64
+ * mask words (2048 columns) and nwr = ceil(cols / 2048); offs has rows * nwr
+ * + 1 entries and the last one is the number of kept weights.  offs[r * nwr]
+ * is the row's start (the CSR row pointer).
+ *
+ * nm_bitmask_offsets: fills offs (device, int64, rows * nwr + 1 entries,
+ *   8-byte aligned) from keep (device, rows x cols bytes, nonzero = kept) and
+ *   writes the number of kept weights to *total (host).  Synchronous on
+ *   `stream`.
+ * nm_pack_bitmask: with offs from nm_bitmask_offsets, writes values (device,
+ *   16-byte aligned, at least total elements rounded up to a multiple of 8:
+ *   the product reads whole 16-byte chunks) and bits (device, rows x cols/32
+ *   uint32).  Raw 16-bit patterns are moved.  Synchronous; allocates and frees
+ *   4 bytes of device memory for its check; NM_ERR_MASK when keep and offs
+ *   disagree (values then unspecified, nothing outside a window's range
+ *   written).
+ * nm_spmm_bitmask: Y[b][r] = sum over kept c of W[r][c] * X[b][c] for
+ *   1 <= batch <= 8, X batch x cols, Y batch x rows (as nm_spmm_small);
+ *   fp32 accumulation; asynchronous on `stream`.  Words inconsistent with
+ *   offs give unspecified results for their rows but no access outside the
+ *   buffers.
+ * Errors as nm_spmm_small (cols % 32 != 0 gives NM_ERR_SHAPE). */
+int nm_bitmask_offsets(const uint8_t *keep, int64_t rows, int64_t cols, int64_t *offs,
+                       int64_t *total, void *stream);
+int nm_pack_bitmask(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
+                    nm_dtype dt, const int64_t *offs, void *values, uint32_t *bits,
+                    void *stream);
+int nm_spmm_bitmask(const void *values, const uint32_t *bits, const int64_t *offs,
+                    const void *X, void *Y, int batch, int64_t rows, int64_t cols,
+                    nm_dtype in_dt, nm_dtype out_dt, void *stream);
+
 /* Prefill-side product on the sparse matrix cores: Y = X . W^T for 2:4 W and
  * any number of tokens.  The pages contrast the structured-sparsity matrix
  * path with the dense GEMM: it gains in prefill and loses in decode

@@ -23,6 +23,8 @@
 // staged per workgroup in segments when all of it does not fit the LDS
 // budget.
 
+#include <mutex>
+
 #include "nm_device.h"
 #include "nm_host.h"
 
@@ -141,11 +143,17 @@ __device__ __forceinline__ void single_acc(const char *lds, int a0, uint32_t v,
 // x is a sequence of items (row i, window t); the copy of item k + 1 is in
 // flight while item k is consumed.  Lane i accumulates the sums of the wave's
 // row i across segments (rpw <= 64).
-template <bool BF, int BP, int NI>
+// UN: unstructured bitmask (any keep mask).  A word's count varies, so offs
+// holds the value index of every 64-word window of every row (row r, window
+// t at offs[r * nwr + t], nwr = windows per row, offs[R * nwr] = all kept
+// values); lane l of a window finds its values at the window's start plus
+// the set bits of the window's words before it (a wave prefix sum), and
+// walks popc(word) steps.  seg is then a multiple of 64 words.
+template <bool BF, int BP, int NI, bool UN = false>
 __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
     const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int P,
-    int seg, int rpw, int out_kind) {
+    int seg, int rpw, int out_kind, const int64_t *__restrict__ offs = nullptr) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wpg = blockDim.x / kWave;
@@ -154,7 +162,8 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
   const int64_t left = R - r0;
   const int nrows = left <= 0 ? 0 : (left < rpw ? (int)left : rpw);
   const int W = K >> 5;                   // mask words per row
-  const int64_t vstride = (int64_t)W * P;  // values per row
+  const int64_t vstride = (int64_t)W * P;  // values per row (N:M)
+  const int nwr = (W + kWinWords - 1) / kWinWords;  // windows per row (UN)
   const uint32_t xbytes = ((uint32_t)XCols<BP>::bytes(seg) + 15u) & ~15u;
   // LDS address of the wave's two window buffers (NI KiB each)
   const uint32_t wbuf = (uint32_t)(size_t)(lds_ptr)lds + xbytes + (uint32_t)wid * (2 * NI * 1024);
@@ -183,9 +192,19 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
       const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(bits + r * W + w0), 0, nw * 4, kRsrcWord3);
       mword = __builtin_amdgcn_raw_buffer_load_b32(rb, lane * 4, 0, kStreamAux);
-      const int64_t vs = r * vstride + (int64_t)w0 * P;
+      int64_t vs, cnt;
+      if constexpr (UN) {
+        // a dummy item reads entry 0 (always present) and uses none of it
+        const int64_t wi = real ? r * nwr + (w0 / kWinWords) : 0;
+        const int64_t a = offs[wi], b = offs[wi + (real ? 1 : 0)];
+        vs = real ? a : 0;
+        cnt = real ? b - a : 0;
+      } else {
+        vs = r * vstride + (int64_t)w0 * P;
+        cnt = (int64_t)nw * P;
+      }
       const int64_t a0 = vs & ~(int64_t)7;
-      const int nch = real ? (int)((vs + (int64_t)nw * P - a0 + 7) >> 3) : 0;
+      const int nch = real ? (int)((vs + cnt - a0 + 7) >> 3) : 0;
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(values + a0), 0, nch * 16, kRsrcWord3);
       const uint32_t dst = wbuf + (uint32_t)(k & 1) * (NI * 1024);
@@ -210,17 +229,32 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
       const int64_t r = r0 + i;
       const int w0 = sw0 + t * kWinWords;
       const int nw = min(kWinWords, sw - t * kWinWords);
+      // the lane's count and the offset of its values in the window
+      int pl = P, ol = lane * P;
+      int64_t vs;
+      if constexpr (UN) {
+        pl = __popc(mw);  // words past the row read 0
+        int incl = pl;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+          const int t2 = __shfl_up(incl, d, kWave);
+          incl += lane >= d ? t2 : 0;
+        }
+        ol = incl - pl;
+        vs = offs[r * nwr + (w0 / kWinWords)];
+      } else {
+        vs = r * vstride + (int64_t)w0 * P;
+      }
       if (lane < nw) {
-        const int64_t vs = r * vstride + (int64_t)w0 * P;
         const uint32_t vb = wbuf + (uint32_t)(k & 1) * (NI * 1024) +
-                            2u * (uint32_t)((vs & 7) + (int64_t)lane * P);
+                            2u * (uint32_t)((vs & 7) + (int64_t)ol);
         // byte offset of the word's x slots in the segment's image
         const int cb = (t * kWinWords + lane) * XCols<BP>::WS;
         uint32_t m = mw;
         // eight scan steps at a time: the columns first (a short VALU chain),
         // then every LDS read of the group, then the products.  Steps past P
         // read slots inside the buffer (see win_loads) and are dropped.
-        for (int j0 = 0; j0 < P; j0 += 8) {
+        for (int j0 = 0; j0 < pl; j0 += 8) {
           int c[8];
           uint32_t v[8];
 #pragma unroll
@@ -232,7 +266,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
           for (int e = 0; e < 8; ++e) v[e] = ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * (j0 + e)));
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            const int left = P - j0 - e;  // steps of this pair still inside P
+            const int left = pl - j0 - e;  // steps of this pair still inside the count
             if (left >= 2)
               pair_acc<BF, BP>(lds, c[e], c[e + 1], v[e] | (v[e + 1] << 16), acc);
             else if (left == 1)
@@ -467,8 +501,95 @@ size_t xcols_bytes(int bp, int64_t cols) {
 
 size_t fixedp_lds_bytes(int bp, int64_t cols) { return xcols_bytes(bp, cols); }
 
+// ---- unstructured bitmasks: window offsets and pack ------------------------
+
+// Kept entries of window t of row r (64 words = 2048 columns), one wave per
+// window: cnt[r * nwr + t].
+__global__ __launch_bounds__(256) void nm_bitmask_count_kernel(const uint8_t *__restrict__ keep,
+                                                               int64_t R, int K,
+                                                               int64_t *__restrict__ cnt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nwr = (K / 32 + kWinWords - 1) / kWinWords;
+  const int64_t nwave = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t q = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; q < R * nwr;
+       q += nwave) {
+    const int64_t r = q / nwr;
+    const int c0 = (int)(q - r * nwr) * kWinWords * 32;
+    const int c1 = min(c0 + kWinWords * 32, K);
+    int n = 0;
+    for (int c = c0 + lane; c < c1; c += kWave) n += keep[r * K + c] != 0;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) n += __shfl_xor(n, o, kWave);
+    if (lane == 0) cnt[q] = n;
+  }
+}
+
+// offs[0] = 0, offs[i + 1] = offs[i] + cnt[i] for i < n: one workgroup of
+// 1024 threads, each scanning a contiguous block; cnt may alias offs + 1.
+__global__ __launch_bounds__(1024) void nm_bitmask_scan_kernel(int64_t *__restrict__ offs,
+                                                               int64_t n) {
+  __shared__ int64_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t b0 = t * per < n ? t * per : n, b1 = b0 + per < n ? b0 + per : n;
+  int64_t sum = 0;
+  for (int64_t i = b0; i < b1; ++i) sum += offs[i + 1];
+  part[t] = sum;
+  __syncthreads();
+  if (t == 0) {
+    int64_t run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int64_t v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    offs[0] = 0;
+  }
+  __syncthreads();
+  int64_t run = part[t];
+  for (int64_t i = b0; i < b1; ++i) {
+    run += offs[i + 1];
+    offs[i + 1] = run;
+  }
+}
+
+// Pack one window per wave: bit b of word w <-> column 32 w + b, kept values
+// in column order from offs[window].  A window whose kept count does not
+// match its offsets bumps *bad (the write stays inside the window's range).
+__global__ __launch_bounds__(256) void nm_pack_bitmask_kernel(
+    const uint16_t *__restrict__ W, const uint8_t *__restrict__ keep, int64_t R, int K,
+    const int64_t *__restrict__ offs, uint16_t *__restrict__ values, uint32_t *__restrict__ bits,
+    int *__restrict__ bad) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nwr = (K / 32 + kWinWords - 1) / kWinWords;
+  const int64_t nwave = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
+  int nbad = 0;
+  for (int64_t q = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; q < R * nwr;
+       q += nwave) {
+    const int64_t r = q / nwr;
+    const int c0 = (int)(q - r * nwr) * kWinWords * 32;
+    const int c1 = min(c0 + kWinWords * 32, K);
+    const int64_t vs = offs[q], cnt = offs[q + 1] - vs;
+    int64_t run = 0;
+    for (int c = c0; c < c1; c += kWave) {  // K % 32 == 0: whole words
+      const int col = c + lane;
+      const bool in = col < c1;
+      const bool kept = in && keep[r * K + col] != 0;
+      const uint64_t bal = __ballot(kept);
+      const int64_t j = run + __popcll(bal & below);
+      if (kept && j < cnt) values[vs + j] = W[r * K + col];
+      if (in && (lane & 31) == 0)
+        bits[r * (K / 32) + col / 32] = (uint32_t)(bal >> (lane & 32));
+      run += __popcll(bal);
+    }
+    nbad += run != cnt ? 1 : 0;
+  }
+  if (lane == 0 && nbad) atomicAdd(bad, nbad);
+}
+
 using fixed_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int,
-                          int64_t, int, int, int, int, int);
+                          int64_t, int, int, int, int, int, const int64_t *);
 
 template <bool BF, int BP>
 fixed_fn pick_fixed_ni(int ni) {
@@ -539,6 +660,85 @@ nm_status generic_check_cfg(const nm_launch_cfg &c, int batch, int n, int m,
   return NM_OK;
 }
 
+nm_status bitmask_offsets(const uint8_t *keep, int64_t rows, int64_t cols, int64_t *offs,
+                          int64_t *total, void *stream) {
+  const int nwr = (int)((cols / 32 + kWinWords - 1) / kWinWords);
+  const int64_t n = rows * nwr;
+  hipStream_t s = (hipStream_t)stream;
+  if (n > 0) {
+    int64_t grid = (n + 3) / 4;
+    if (grid > (1 << 20)) grid = 1 << 20;
+    hipLaunchKernelGGL(nm_bitmask_count_kernel, dim3((unsigned)grid), dim3(256), 0, s, keep, rows,
+                       (int)cols, offs + 1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  hipLaunchKernelGGL(nm_bitmask_scan_kernel, dim3(1), dim3(1024), 0, s, offs, n);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(total, offs + n, sizeof(int64_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? NM_OK : hip_fail(e);
+}
+
+nm_status bitmask_pack(const uint16_t *W, const uint8_t *keep, int64_t rows, int64_t cols,
+                       const int64_t *offs, uint16_t *values, uint32_t *bits, void *stream) {
+  const int nwr = (int)((cols / 32 + kWinWords - 1) / kWinWords);
+  const int64_t n = rows * nwr;
+  hipStream_t s = (hipStream_t)stream;
+  int *dbad = nullptr;
+  hipError_t e = hipMalloc((void **)&dbad, sizeof(int));
+  if (e != hipSuccess) return hip_fail(e);
+  int hbad = 0;
+  e = hipMemsetAsync(dbad, 0, sizeof(int), s);
+  if (e == hipSuccess) {
+    int64_t grid = (n + 3) / 4;
+    if (grid > (1 << 20)) grid = 1 << 20;
+    hipLaunchKernelGGL(nm_pack_bitmask_kernel, dim3((unsigned)grid), dim3(256), 0, s, W, keep,
+                       rows, (int)cols, offs, values, bits, dbad);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipMemcpyAsync(&hbad, dbad, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  const hipError_t ef = hipFree(dbad);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ef != hipSuccess) return hip_fail(ef);
+  return hbad ? NM_ERR_MASK : NM_OK;
+}
+
+nm_status bitmask_launch(const void *values, const uint32_t *bits, const int64_t *offs,
+                         const void *X, void *Y, int batch, int64_t rows, int64_t cols,
+                         nm_dtype in_dt, nm_dtype out_dt, int cus, size_t lds_budget,
+                         void *stream) {
+  constexpr int kNI = 5;  // a window holds up to 64 x 32 values (+ alignment)
+  const int bp = pad_b(batch), waves = 4;
+  int64_t rpw = rows / ((int64_t)2 * cus * waves);
+  rpw = rpw < 1 ? 1 : rpw > 8 ? 8 : rpw;
+  int64_t seg = cols;
+  if (fixed_lds_bytes(bp, (int)cols, waves, kNI) > lds_budget) {
+    const size_t wave_area = fixed_lds_bytes(bp, 0, waves, kNI);
+    seg = (int64_t)((lds_budget - wave_area - 16) / xcols_bytes(bp, 32)) * 32 / 2048 * 2048;
+    if (seg < 2048) return NM_ERR_UNSUPPORTED;
+  }
+  const int64_t grid = (rows + waves * rpw - 1) / (waves * rpw);
+  if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
+  using un_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int, int64_t,
+                         int, int, int, int, int, const int64_t *);
+  un_fn fn;
+  const bool bf = in_dt == NM_BF16;
+  switch (bp) {
+    case 1: fn = bf ? nm_spmv_fixed_kernel<true, 1, kNI, true> : nm_spmv_fixed_kernel<false, 1, kNI, true>; break;
+    case 2: fn = bf ? nm_spmv_fixed_kernel<true, 2, kNI, true> : nm_spmv_fixed_kernel<false, 2, kNI, true>; break;
+    case 4: fn = bf ? nm_spmv_fixed_kernel<true, 4, kNI, true> : nm_spmv_fixed_kernel<false, 4, kNI, true>; break;
+    default: fn = bf ? nm_spmv_fixed_kernel<true, 8, kNI, true> : nm_spmv_fixed_kernel<false, 8, kNI, true>; break;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(waves * kWave),
+                     fixed_lds_bytes(bp, (int)seg, waves, kNI), (hipStream_t)stream,
+                     (const uint16_t *)values, bits, (const uint16_t *)X, Y, batch, rows, (int)cols,
+                     0, (int)seg, (int)rpw, (int)out_dt, offs);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NM_OK : hip_fail(e);
+}
+
 nm_status generic_launch(const void *values, const uint32_t *bits, const void *X, void *Y,
                          int batch, int64_t rows, int64_t cols, int n, int m, nm_dtype in_dt,
                          nm_dtype out_dt, const nm_launch_cfg &cfg, void *stream) {
@@ -563,9 +763,99 @@ nm_status generic_launch(const void *values, const uint32_t *bits, const void *X
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
                      fixed_lds_bytes(bp, seg, waves, ni), (hipStream_t)stream,
                      (const uint16_t *)values, bits, (const uint16_t *)X, Y, batch, rows,
-                     (int)cols, p, seg, cfg.rows_per_wave, (int)out_dt);
+                     (int)cols, p, seg, cfg.rows_per_wave, (int)out_dt, (const int64_t *)nullptr);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? NM_OK : hip_fail(e);
 }
 
 }  // namespace nm_host
+
+namespace {
+
+// Compute units and the LDS one workgroup may use, per device (queried once).
+struct GenDev {
+  int cus = 0;
+  size_t lds = 0;
+};
+GenDev g_gen_dev[64];
+std::mutex g_gen_mu;
+
+nm_status gen_device(GenDev *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return nm_host::hip_fail(e);
+  if (dev < 0 || dev >= 64) return NM_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_gen_mu);
+  GenDev &d = g_gen_dev[dev];
+  if (d.cus == 0) {
+    int cus = 0, lds = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return nm_host::hip_fail(e);
+    d.lds = (size_t)lds < kLdsCap ? (size_t)lds : kLdsCap;
+    d.cus = cus;
+  }
+  *out = d;
+  return NM_OK;
+}
+
+nm_status bitmask_dims(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0 || rows > INT32_MAX || cols > INT32_MAX) return NM_ERR_INVALID_ARG;
+  if (cols % 32 != 0) return NM_ERR_SHAPE;
+  const int64_t nwr = (cols / 32 + kWinWords - 1) / kWinWords;
+  if (rows * nwr > ((int64_t)1 << 40)) return NM_ERR_INVALID_ARG;
+  return NM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nm_bitmask_offsets(const uint8_t *keep, int64_t rows, int64_t cols, int64_t *offs,
+                       int64_t *total, void *stream) {
+  nm_status st = bitmask_dims(rows, cols);
+  if (st != NM_OK) return st;
+  if (!offs || !total || (!keep && rows > 0 && cols > 0)) return NM_ERR_INVALID_ARG;
+  if (!nm_host::aligned(offs, 8)) return NM_ERR_ALIGN;
+  return nm_host::bitmask_offsets(keep, rows, cols, offs, total, stream);
+}
+
+int nm_pack_bitmask(const void *W, const uint8_t *keep, int64_t rows, int64_t cols, nm_dtype dt,
+                    const int64_t *offs, void *values, uint32_t *bits, void *stream) {
+  nm_status st = bitmask_dims(rows, cols);
+  if (st != NM_OK) return st;
+  if (!nm_host::is16(dt)) return NM_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return NM_OK;
+  if (!W || !keep || !offs || !values || !bits) return NM_ERR_INVALID_ARG;
+  if (!nm_host::aligned(W, 2) || !nm_host::aligned(offs, 8) || !nm_host::aligned(values, 16) ||
+      !nm_host::aligned(bits, 4))
+    return NM_ERR_ALIGN;
+  return nm_host::bitmask_pack((const uint16_t *)W, keep, rows, cols, offs, (uint16_t *)values,
+                               bits, stream);
+}
+
+int nm_spmm_bitmask(const void *values, const uint32_t *bits, const int64_t *offs, const void *X,
+                    void *Y, int batch, int64_t rows, int64_t cols, nm_dtype in_dt,
+                    nm_dtype out_dt, void *stream) {
+  nm_status st = bitmask_dims(rows, cols);
+  if (st != NM_OK) return st;
+  if (batch < 1 || batch > 8) return NM_ERR_INVALID_ARG;
+  if (!nm_host::is16(in_dt) || !nm_host::out_ok(in_dt, out_dt)) return NM_ERR_UNSUPPORTED;
+  const bool empty_w = rows == 0 || cols == 0;
+  if ((!values && !empty_w) || (!bits && !empty_w) || (!offs && !empty_w) || (!X && cols != 0) ||
+      (!Y && rows != 0))
+    return NM_ERR_INVALID_ARG;
+  const uintptr_t ysz = out_dt == NM_F32 ? 4 : 2;
+  if (!nm_host::aligned(values, 16) || !nm_host::aligned(bits, 4) || !nm_host::aligned(offs, 8) ||
+      !nm_host::aligned(X, 16) || !nm_host::aligned(Y, ysz))
+    return NM_ERR_ALIGN;
+  if (rows == 0) return NM_OK;
+  GenDev d;
+  st = gen_device(&d);
+  if (st != NM_OK) return st;
+  return nm_host::bitmask_launch(values, bits, offs, X, Y, batch, rows, cols, in_dt, out_dt, d.cus,
+                                 d.lds, stream);
+}
+
+}  // extern "C"
+

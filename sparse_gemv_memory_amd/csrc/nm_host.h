@@ -36,6 +36,16 @@ NM_INTERNAL nm_status generic_default_cfg(int64_t rows, int64_t cols, int batch,
                                           int cus, size_t lds_budget, nm_launch_cfg *cfg);
 NM_INTERNAL nm_status generic_check_cfg(const nm_launch_cfg &c, int batch, int n, int m,
                                         size_t lds_budget);
+// Unstructured bitmasks (nm_generic.hip): window offsets, pack, product.
+NM_INTERNAL nm_status bitmask_offsets(const uint8_t *keep, int64_t rows, int64_t cols,
+                                      int64_t *offs, int64_t *total, void *stream);
+NM_INTERNAL nm_status bitmask_pack(const uint16_t *W, const uint8_t *keep, int64_t rows,
+                                   int64_t cols, const int64_t *offs, uint16_t *values,
+                                   uint32_t *bits, void *stream);
+NM_INTERNAL nm_status bitmask_launch(const void *values, const uint32_t *bits,
+                                     const int64_t *offs, const void *X, void *Y, int batch,
+                                     int64_t rows, int64_t cols, nm_dtype in_dt, nm_dtype out_dt,
+                                     int cus, size_t lds_budget, void *stream);
 NM_INTERNAL nm_status generic_launch(const void *values, const uint32_t *bits, const void *X,
                                      void *Y, int batch, int64_t rows, int64_t cols, int n, int m,
                                      nm_dtype in_dt, nm_dtype out_dt, const nm_launch_cfg &cfg,

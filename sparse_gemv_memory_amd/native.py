@@ -106,6 +106,12 @@ def lib():
     L.nm_dense_gemv_cfg.restype = ci
     L.nm_default_launch.argtypes = [i64, i64, ci, ci, ci, ci, ctypes.POINTER(LaunchCfg)]
     L.nm_default_launch.restype = ci
+    L.nm_bitmask_offsets.argtypes = [p, i64, i64, p, ctypes.POINTER(i64), p]
+    L.nm_bitmask_offsets.restype = ci
+    L.nm_pack_bitmask.argtypes = [p, p, i64, i64, ci, p, p, p, p]
+    L.nm_pack_bitmask.restype = ci
+    L.nm_spmm_bitmask.argtypes = [p, p, p, p, p, ci, i64, i64, ci, ci, p]
+    L.nm_spmm_bitmask.restype = ci
     L.nm_stream_read.argtypes = [p, sz, p, ci, ci, p]
     L.nm_stream_read.restype = ci
     _lib = L
@@ -379,4 +385,67 @@ def nm_stream_read(buf: torch.Tensor, out: torch.Tensor, grid: int = 512, thread
         st = lib().nm_stream_read(_dev(buf, "buf"), nbytes, _dev(out, "out"), grid,
                                   threads_per_wg, _stream(buf.device))
     _check(st, "nm_stream_read")
+
+
+def _vptr(values: torch.Tensor) -> Optional[int]:
+    """Device address of packed values; an empty view (no kept weight) still
+    passes its padded storage, which the library never reads as data."""
+    if values.numel() == 0 and values.untyped_storage().nbytes() > 0:
+        return values.untyped_storage().data_ptr()
+    return _dev(values, "values")
+
+
+def nm_pack_bitmask(W: torch.Tensor, keep: torch.Tensor):
+    """Unstructured bitmask pack of a (rows, cols) fp16/bf16 W under any keep
+    mask.  Returns (values, bits, offs): values 1-D of W's dtype (the kept
+    weights, rows one after another; storage padded to 16 bytes), bits
+    (rows, cols/32) int32, offs int64 (rows * ceil(cols/2048) + 1 window
+    offsets)."""
+    if W.dim() != 2 or keep.shape != W.shape:
+        raise ValueError("W must be 2-D and keep must have its shape")
+    if keep.dtype not in (torch.uint8, torch.bool, torch.int8):
+        raise TypeError("keep must be uint8, int8 or bool")
+    rows, cols = W.shape
+    dt = _in_dt(W)
+    nwr = (cols // 32 + 63) // 64
+    offs = torch.empty((rows * nwr + 1,), dtype=torch.int64, device=W.device)
+    total = ctypes.c_int64()
+    with torch.cuda.device(W.device):
+        _check(lib().nm_bitmask_offsets(_dev(keep, "keep"), rows, cols, _dev(offs, "offs"),
+                                        ctypes.byref(total), _stream(W.device)), "nm_bitmask_offsets")
+        n = total.value
+        values = _packed_values(1, n, max(8, (n + 7) // 8 * 8), W.dtype, W.device).view(n)
+        bits = torch.empty((rows, cols // 32), dtype=torch.int32, device=W.device)
+        _check(lib().nm_pack_bitmask(_dev(W, "W"), _dev(keep, "keep"), rows, cols, dt,
+                                     _dev(offs, "offs"), _vptr(values), _dev(bits, "bits"),
+                                     _stream(W.device)), "nm_pack_bitmask")
+    return values, bits, offs
+
+
+def nm_spmm_bitmask(values, bits, offs, X, out_dtype=torch.float32, out=None):
+    """Y = X . W^T for an unstructured bitmask matrix (nm_pack_bitmask's
+    output); X of shape (batch, cols) with 1 <= batch <= 8, or (cols,)."""
+    if bits.dim() != 2 or bits.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("bits must be (rows, cols/32) int32")
+    rows, cols = bits.shape[0], bits.shape[1] * 32
+    nwr = (cols // 32 + 63) // 64
+    if offs.dtype != torch.int64 or offs.numel() != rows * nwr + 1:
+        raise ValueError("offs must hold rows * ceil(cols/2048) + 1 int64 offsets")
+    if values.dtype != X.dtype:
+        raise TypeError("values and X must have the same dtype")
+    have = values.untyped_storage().nbytes() // 2 - values.storage_offset()
+    if values.numel() and have < (values.numel() + 7) // 8 * 8:
+        raise ValueError("values must keep nm_pack_bitmask's 16-byte padding")
+    squeeze = X.dim() == 1
+    X2 = X.reshape(1, -1) if squeeze else X
+    if X2.shape[1] != cols:
+        raise ValueError("X must have cols columns")
+    batch = X2.shape[0]
+    Y = out if out is not None else torch.empty((batch, rows), dtype=out_dtype, device=X.device)
+    with torch.cuda.device(X.device):
+        st = lib().nm_spmm_bitmask(_vptr(values), _dev(bits, "bits"), _dev(offs, "offs"),
+                                   _dev(X2, "X"), _dev(Y, "Y"), batch, rows, cols, _in_dt(X2),
+                                   _DT[out_dtype], _stream(X.device))
+    _check(st, "nm_spmm_bitmask")
+    return Y.reshape(-1) if squeeze else Y
 

@@ -245,3 +245,29 @@ def test_launch_cfg_validation_is_host_only(L):
     assert L.nm_default_launch(8, 64, 1, 2, 4, 0, None) == INV
     assert L.nm_default_launch(8, 64, 1, 3, 6, 0, ctypes.byref(c)) == UNSUP
     assert L.nm_default_launch(8, 64, 1, 4, 4, 0, ctypes.byref(c)) == UNSUP
+
+
+def test_bitmask_entry_points_reject_bad_arguments(L):
+    total = ctypes.c_int64()
+    off = L.nm_bitmask_offsets
+    assert off(P, 4, 48, P, ctypes.byref(total), None) == SHAPE
+    assert off(P, -1, 64, P, ctypes.byref(total), None) == INV
+    assert off(P, 4, 64, None, ctypes.byref(total), None) == INV
+    assert off(P, 4, 64, P + 4, ctypes.byref(total), None) == ALIGN
+    pack = L.nm_pack_bitmask
+    assert pack(P, P, 4, 48, F16, P, P, P, None) == SHAPE
+    assert pack(P, P, 4, 64, F32, P, P, P, None) == UNSUP
+    assert pack(None, P, 4, 64, F16, P, P, P, None) == INV
+    assert pack(P, P, 4, 64, F16, P, P + 8, P, None) == ALIGN
+    assert pack(None, None, 0, 64, F16, None, None, None, None) == OK
+    spmm = L.nm_spmm_bitmask
+    assert spmm(P, P, P, P, P, 0, 4, 64, F16, F32, None) == INV
+    assert spmm(P, P, P, P, P, 9, 4, 64, F16, F32, None) == INV
+    assert spmm(P, P, P, P, P, 1, 4, 48, F16, F32, None) == SHAPE
+    assert spmm(P, P, P, P, P, 1, 4, 64, F32, F32, None) == UNSUP
+    assert spmm(P, P, P, P, P, 1, 4, 64, F16, BF16, None) == UNSUP
+    assert spmm(P, P, None, P, P, 1, 4, 64, F16, F32, None) == INV
+    assert spmm(P, P, P + 4, P, P, 1, 4, 64, F16, F32, None) == ALIGN
+    assert spmm(P + 8, P, P, P, P, 1, 4, 64, F16, F32, None) == ALIGN
+    assert spmm(None, None, None, P, None, 1, 0, 64, F16, F32, None) == OK
+
