@@ -356,22 +356,34 @@ __device__ __forceinline__ void word_batch_load(WordBatch<P, U> &bt, const uint1
 }
 
 // The P kept weights of one word (mask m, values v) against the word's x
-// slots at byte offset xw of the XCols image.
-template <bool BF, int BP, int P>
+// slots at byte offset xw of the XCols image.  CH independent scans: with
+// M <= 8 every byte of a valid word holds P / 4 kept columns (CH = 4), with
+// M = 16 every half-word P / 2 (CH = 2); value j of chain h is value
+// h * P / CH + j of the word (column order).  The chains are independent, so
+// their steps overlap instead of forming one P-step dependence chain.  A
+// malformed word only makes its row's sum undefined: every column stays in
+// its chain's span.
+template <bool BF, int BP, int P, int CH>
 __device__ __forceinline__ void word_acc(const char *lds, int xw, uint32_t m,
                                          const uint32_t (&v)[WordVals<P>::kRegs],
                                          float (&acc)[BP]) {
+  constexpr int Q = P / CH, SPAN = 32 / CH;
+  static_assert(Q * CH == P, "chains split the word's kept columns evenly");
   int c[P];
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    c[j] = xw + (ffbl_hw(m) & 31) * XCols<BP>::SB;
-    m &= m - 1;
+  for (int h = 0; h < CH; ++h) {
+    uint32_t mh = CH == 1 ? m : (m >> (SPAN * h)) & ((1u << (SPAN & 31)) - 1u);
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      c[h * Q + j] = xw + (SPAN * h + (ffbl_hw(mh) & (SPAN - 1))) * XCols<BP>::SB;
+      mh &= mh - 1;
+    }
   }
 #pragma unroll
   for (int j = 0; j < P; j += 2) pair_acc<BF, BP>(lds, c[j], c[j + 1], v[j / 2], acc);
 }
 
-template <bool BF, int BP, int P, int U>
+template <bool BF, int BP, int P, int U, int CH>
 __global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
     const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int rpw,
@@ -401,7 +413,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
     if (wb + kWave * U <= W) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        word_acc<BF, BP, P>(lds, (wb + kWave * u + lane) * XCols<BP>::WS, bt.m[u], bt.v[u], acc);
+        word_acc<BF, BP, P, CH>(lds, (wb + kWave * u + lane) * XCols<BP>::WS, bt.m[u], bt.v[u], acc);
       return;
     }
     // the row's last batch: words past the row end read zeros and are dropped
@@ -412,7 +424,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
       float part[BP];
 #pragma unroll
       for (int b = 0; b < BP; ++b) part[b] = 0.f;
-      word_acc<BF, BP, P>(lds, min(w, W - 1) * XCols<BP>::WS, bt.m[u], bt.v[u], part);
+      word_acc<BF, BP, P, CH>(lds, min(w, W - 1) * XCols<BP>::WS, bt.m[u], bt.v[u], part);
 #pragma unroll
       for (int b = 0; b < BP; ++b) acc[b] += w < W ? part[b] : 0.f;
     }
@@ -470,23 +482,31 @@ using fixedp_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *,
 // The densities with a direct kernel, and its words per lane per load batch.
 __host__ __device__ constexpr bool direct_p(int p) { return p == 4 || p == 8 || p == 12 || p == 24; }
 
-template <bool BF, int BP>
+template <bool BF, int BP, int CH>
 fixedp_fn pick_fixedp_p(int p) {
   switch (p) {
-    case 4: return nm_spmv_fixedp_kernel<BF, BP, 4, 4>;
-    case 8: return nm_spmv_fixedp_kernel<BF, BP, 8, 4>;
-    case 12: return nm_spmv_fixedp_kernel<BF, BP, 12, 2>;
-    default: return nm_spmv_fixedp_kernel<BF, BP, 24, 2>;
+    case 4: return nm_spmv_fixedp_kernel<BF, BP, 4, 4, CH>;
+    case 8: return nm_spmv_fixedp_kernel<BF, BP, 8, 4, CH>;
+    case 12: return nm_spmv_fixedp_kernel<BF, BP, 12, 2, CH>;
+    default: return nm_spmv_fixedp_kernel<BF, BP, 24, 2, CH>;
   }
 }
 
+// ch: independent scan chains per word (4 for M <= 8, 2 for M = 16, 1 for
+// M = 32)
+template <bool BF, int BP>
+fixedp_fn pick_fixedp_ch(int p, int ch) {
+  return ch == 4 ? pick_fixedp_p<BF, BP, 4>(p) : ch == 2 ? pick_fixedp_p<BF, BP, 2>(p)
+                                                         : pick_fixedp_p<BF, BP, 1>(p);
+}
+
 template <bool BF>
-fixedp_fn pick_fixedp(int bp, int p) {
+fixedp_fn pick_fixedp(int bp, int p, int ch) {
   switch (bp) {
-    case 1: return pick_fixedp_p<BF, 1>(p);
-    case 2: return pick_fixedp_p<BF, 2>(p);
-    case 4: return pick_fixedp_p<BF, 4>(p);
-    default: return pick_fixedp_p<BF, 8>(p);
+    case 1: return pick_fixedp_ch<BF, 1>(p, ch);
+    case 2: return pick_fixedp_ch<BF, 2>(p, ch);
+    case 4: return pick_fixedp_ch<BF, 4>(p, ch);
+    default: return pick_fixedp_ch<BF, 8>(p, ch);
   }
 }
 
@@ -750,8 +770,9 @@ nm_status generic_launch(const void *values, const uint32_t *bits, const void *X
   const int seg = cfg.seg_cols < cols ? cfg.seg_cols : (int)cols;
   if (direct_p(p) && seg == cols && cols > 0) {
     // all of x in LDS (its bytes are within the checked window-kernel bytes)
+    const int ch = m <= 8 ? 4 : m == 16 ? 2 : 1;
     const fixedp_fn fn =
-        in_dt == NM_BF16 ? pick_fixedp<true>(bp, p) : pick_fixedp<false>(bp, p);
+        in_dt == NM_BF16 ? pick_fixedp<true>(bp, p, ch) : pick_fixedp<false>(bp, p, ch);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
                        fixedp_lds_bytes(bp, cols), (hipStream_t)stream, (const uint16_t *)values,
                        bits, (const uint16_t *)X, Y, batch, rows, (int)cols, cfg.rows_per_wave,
