@@ -751,15 +751,18 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     const bool real = b < nblk;
     const __amdgpu_buffer_rsrc_t V = real ? rv : r0, M = real ? rb : r0, X = real ? rx : r0;
     const uint32_t sl = ring + (uint32_t)((b % NB) * SLOT);
+    // the block offset goes into the vector offset, which the range check
+    // covers (the scalar offset is not checked): a wave's last block may
+    // reach past its K range, and on the last rows past the arrays
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      lds_load16_nt(V, sl + 1024 * q, voff[q], kMValBytes / 16 * b);
+      lds_load16_nt(V, sl + 1024 * q, voff[q] + kMValBytes / 16 * b, 0);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
-      lds_load4_nt(M, sl + kMValBytes + 256 * q, boff[q], kMMaskBytes / 16 * b);
+      lds_load4_nt(M, sl + kMValBytes + 256 * q, boff[q] + kMMaskBytes / 16 * b, 0);
 #pragma unroll
     for (int q = 0; q < XQ; ++q)
-      lds_load16(X, sl + kMValBytes + kMMaskBytes + 1024 * q, xoff[q], kMXTok * b);
+      lds_load16(X, sl + kMValBytes + kMMaskBytes + 1024 * q, xoff[q] + kMXTok * b, 0);
   };
 
   // reader addresses within a slot, step 0 (steps add constant offsets only
