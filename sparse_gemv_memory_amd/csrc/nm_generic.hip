@@ -301,12 +301,15 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
 }
 
 // Direct kernel for the common densities (P = 4, 8, 12, 24 kept columns per
-// word: 1:8, 1:4, 3:8, 3:4) when all of x fits the LDS budget.  Lane l of a
-// wave owns mask words t * 64 U + 64 u + l of its row (u < U): the word and
-// its 2P value bytes (one contiguous run per word, 8- or 16-byte aligned) are
-// loaded straight into registers with raw buffer loads (range-checked at the
-// row end), two load batches in flight per wave, and the word is walked in
-// P unrolled steps, each kept pair meeting its x values from LDS in one dot2.
+// word: 1:8, 1:4, 3:8, 3:4).  Lane l of a wave owns mask words
+// t * 64 U + 64 u + l of its row's part of the x segment (u < U): the word
+// and its 2P value bytes (one contiguous run per word, 8- or 16-byte aligned)
+// are loaded straight into registers with raw buffer loads (range-checked at
+// the segment end), two load batches in flight per wave, and the word is
+// walked in P unrolled steps, each kept pair meeting its x values from LDS in
+// one dot2.  When all of x does not fit the LDS budget, K is walked in
+// segments of seg columns; lane i carries the sums of the wave's row i across
+// segments.
 template <int P>
 struct WordVals {
   static constexpr int kBytes = 2 * P;                  // value bytes per word
@@ -383,11 +386,13 @@ __device__ __forceinline__ void word_acc(const char *lds, int xw, uint32_t m,
   for (int j = 0; j < P; j += 2) pair_acc<BF, BP>(lds, c[j], c[j + 1], v[j / 2], acc);
 }
 
-template <bool BF, int BP, int P, int U, int CH>
+// SEGS: x in several segments (a build of its own, so that the one-segment
+// case keeps the straight-line code of a single pass).
+template <bool BF, int BP, int P, int U, int CH, bool SEGS>
 __global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
     const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int rpw,
-    int out_kind) {
+    int out_kind, int seg) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wpg = blockDim.x / kWave;
@@ -396,78 +401,92 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
   const int64_t left = R - r0;
   const int nrows = left <= 0 ? 0 : (left < rpw ? (int)left : rpw);
   const int W = K >> 5;
-  const int nb = (W + kWave * U - 1) / (kWave * U);  // load batches per row
-  const int nitems = nrows * nb;
 
-  stage_x_cols<BP>(lds, x, B, K, 0, K);
-  __syncthreads();
+  float res[BP];
+#pragma unroll
+  for (int b = 0; b < BP; ++b) res[b] = 0.f;
 
-  auto item_load = [&](WordBatch<P, U> &bt, int k) {
-    const bool real = k < nitems;
-    const int i = real ? k / nb : 0, t = real ? k - i * nb : 0;
-    const int64_t r = real ? r0 + i : 0;
-    word_batch_load<P, U>(bt, values + r * W * P, bits + r * W, real ? W : 0, t, lane);
-  };
-  auto consume = [&](const WordBatch<P, U> &bt, int t, float (&acc)[BP]) {
-    const int wb = t * kWave * U;  // the batch's first word (wave-uniform)
-    if (wb + kWave * U <= W) {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        word_acc<BF, BP, P, CH>(lds, (wb + kWave * u + lane) * XCols<BP>::WS, bt.m[u], bt.v[u], acc);
-      return;
-    }
-    // the row's last batch: words past the row end read zeros and are dropped
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (wb + kWave * u >= W) break;
-      const int w = wb + kWave * u + lane;
-      float part[BP];
-#pragma unroll
-      for (int b = 0; b < BP; ++b) part[b] = 0.f;
-      word_acc<BF, BP, P, CH>(lds, min(w, W - 1) * XCols<BP>::WS, bt.m[u], bt.v[u], part);
-#pragma unroll
-      for (int b = 0; b < BP; ++b) acc[b] += w < W ? part[b] : 0.f;
-    }
-  };
+  auto segment = [&](const int s0, const int S) {
+    if (s0 > 0) __syncthreads();  // every wave is done with the previous segment's x
+    stage_x_cols<BP>(lds, x, B, K, s0, S);
+    __syncthreads();
+    const int sw0 = s0 >> 5, sw = S >> 5;  // the segment's first word and its words
+    const int nb = (sw + kWave * U - 1) / (kWave * U);  // load batches per row and segment
+    const int nitems = nrows * nb;
 
-  float acc[BP], res[BP];
+    auto item_load = [&](WordBatch<P, U> &bt, int k) {
+      const bool real = k < nitems;
+      const int i = real ? k / nb : 0, t = real ? k - i * nb : 0;
+      const int64_t r = real ? r0 + i : 0;
+      word_batch_load<P, U>(bt, values + (r * W + sw0) * P, bits + r * W + sw0, real ? sw : 0, t,
+                            lane);
+    };
+    auto consume = [&](const WordBatch<P, U> &bt, int t, float (&acc)[BP]) {
+      const int wb = t * kWave * U;  // the batch's first word in the segment (wave-uniform)
+      if (wb + kWave * U <= sw) {
 #pragma unroll
-  for (int b = 0; b < BP; ++b) acc[b] = res[b] = 0.f;
-  WordBatch<P, U> A, Bt;
-  item_load(A, 0);
-  item_load(Bt, 1);
-  for (int k = 0; k < nitems; k += 2) {
-    {
-      const int i = k / nb, t = k - i * nb;
-      consume(A, t, acc);
-      if (t == nb - 1) {
+        for (int u = 0; u < U; ++u)
+          word_acc<BF, BP, P, CH>(lds, (wb + kWave * u + lane) * XCols<BP>::WS, bt.m[u], bt.v[u], acc);
+        return;
+      }
+      // the segment's last batch: words past its end read zeros and are dropped
 #pragma unroll
-        for (int b = 0; b < BP; ++b) {
-          // the lane-63 read is taken by every lane: inside a select on the
-          // lane it would let the reduction's last step run for lane i only
-          const float sv = wave_total(acc[b]);
-          res[b] = lane == i ? sv : res[b];
-          acc[b] = 0.f;
+      for (int u = 0; u < U; ++u) {
+        if (wb + kWave * u >= sw) break;
+        const int w = wb + kWave * u + lane;
+        float part[BP];
+#pragma unroll
+        for (int b = 0; b < BP; ++b) part[b] = 0.f;
+        word_acc<BF, BP, P, CH>(lds, min(w, sw - 1) * XCols<BP>::WS, bt.m[u], bt.v[u], part);
+#pragma unroll
+        for (int b = 0; b < BP; ++b) acc[b] += w < sw ? part[b] : 0.f;
+      }
+    };
+
+    float acc[BP];
+#pragma unroll
+    for (int b = 0; b < BP; ++b) acc[b] = 0.f;
+    WordBatch<P, U> A, Bt;
+    item_load(A, 0);
+    item_load(Bt, 1);
+    for (int k = 0; k < nitems; k += 2) {
+      {
+        const int i = k / nb, t = k - i * nb;
+        consume(A, t, acc);
+        if (t == nb - 1) {
+#pragma unroll
+          for (int b = 0; b < BP; ++b) {
+            // the lane-63 read is taken by every lane: inside a select on the
+            // lane it would let the reduction's last step run for lane i only
+            const float sv = wave_total(acc[b]);
+            res[b] += lane == i ? sv : 0.f;
+            acc[b] = 0.f;
+          }
         }
       }
-    }
-    item_load(A, k + 2);
-    if (k + 1 >= nitems) break;
-    {
-      const int i = (k + 1) / nb, t = (k + 1) - i * nb;
-      consume(Bt, t, acc);
-      if (t == nb - 1) {
+      item_load(A, k + 2);
+      if (k + 1 >= nitems) break;
+      {
+        const int i = (k + 1) / nb, t = (k + 1) - i * nb;
+        consume(Bt, t, acc);
+        if (t == nb - 1) {
 #pragma unroll
-        for (int b = 0; b < BP; ++b) {
-          // the lane-63 read is taken by every lane: inside a select on the
-          // lane it would let the reduction's last step run for lane i only
-          const float sv = wave_total(acc[b]);
-          res[b] = lane == i ? sv : res[b];
-          acc[b] = 0.f;
+          for (int b = 0; b < BP; ++b) {
+            // the lane-63 read is taken by every lane: inside a select on the
+            // lane it would let the reduction's last step run for lane i only
+            const float sv = wave_total(acc[b]);
+            res[b] += lane == i ? sv : 0.f;
+            acc[b] = 0.f;
+          }
         }
       }
+      item_load(Bt, k + 3);
     }
-    item_load(Bt, k + 3);
+  };
+  if constexpr (SEGS) {
+    for (int s0 = 0; s0 < K; s0 += seg) segment(s0, K - s0 < seg ? K - s0 : seg);
+  } else {
+    segment(0, K);
   }
   if (lane < nrows) {
 #pragma unroll
@@ -477,37 +496,42 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
 }
 
 using fixedp_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int,
-                           int64_t, int, int, int);
+                           int64_t, int, int, int, int);
 
 // The densities with a direct kernel, and its words per lane per load batch.
 __host__ __device__ constexpr bool direct_p(int p) { return p == 4 || p == 8 || p == 12 || p == 24; }
 
-template <bool BF, int BP, int CH>
+template <bool BF, int BP, int CH, bool SEGS>
 fixedp_fn pick_fixedp_p(int p) {
   switch (p) {
-    case 4: return nm_spmv_fixedp_kernel<BF, BP, 4, 4, CH>;
-    case 8: return nm_spmv_fixedp_kernel<BF, BP, 8, 4, CH>;
-    case 12: return nm_spmv_fixedp_kernel<BF, BP, 12, 2, CH>;
-    default: return nm_spmv_fixedp_kernel<BF, BP, 24, 2, CH>;
+    case 4: return nm_spmv_fixedp_kernel<BF, BP, 4, 4, CH, SEGS>;
+    case 8: return nm_spmv_fixedp_kernel<BF, BP, 8, 4, CH, SEGS>;
+    case 12: return nm_spmv_fixedp_kernel<BF, BP, 12, 2, CH, SEGS>;
+    default: return nm_spmv_fixedp_kernel<BF, BP, 24, 2, CH, SEGS>;
   }
 }
 
 // ch: independent scan chains per word (4 for M <= 8, 2 for M = 16, 1 for
 // M = 32)
-template <bool BF, int BP>
+template <bool BF, int BP, bool SEGS>
 fixedp_fn pick_fixedp_ch(int p, int ch) {
-  return ch == 4 ? pick_fixedp_p<BF, BP, 4>(p) : ch == 2 ? pick_fixedp_p<BF, BP, 2>(p)
-                                                         : pick_fixedp_p<BF, BP, 1>(p);
+  return ch == 4 ? pick_fixedp_p<BF, BP, 4, SEGS>(p)
+                 : ch == 2 ? pick_fixedp_p<BF, BP, 2, SEGS>(p) : pick_fixedp_p<BF, BP, 1, SEGS>(p);
+}
+
+template <bool BF, bool SEGS>
+fixedp_fn pick_fixedp_bp(int bp, int p, int ch) {
+  switch (bp) {
+    case 1: return pick_fixedp_ch<BF, 1, SEGS>(p, ch);
+    case 2: return pick_fixedp_ch<BF, 2, SEGS>(p, ch);
+    case 4: return pick_fixedp_ch<BF, 4, SEGS>(p, ch);
+    default: return pick_fixedp_ch<BF, 8, SEGS>(p, ch);
+  }
 }
 
 template <bool BF>
-fixedp_fn pick_fixedp(int bp, int p, int ch) {
-  switch (bp) {
-    case 1: return pick_fixedp_ch<BF, 1>(p, ch);
-    case 2: return pick_fixedp_ch<BF, 2>(p, ch);
-    case 4: return pick_fixedp_ch<BF, 4>(p, ch);
-    default: return pick_fixedp_ch<BF, 8>(p, ch);
-  }
+fixedp_fn pick_fixedp(int bp, int p, int ch, bool segs) {
+  return segs ? pick_fixedp_bp<BF, true>(bp, p, ch) : pick_fixedp_bp<BF, false>(bp, p, ch);
 }
 
 size_t xcols_bytes(int bp, int64_t cols) {
@@ -649,8 +673,27 @@ bool pattern_any_ok(int n, int m) {
 
 nm_status generic_default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, int cus,
                               size_t lds_budget, nm_launch_cfg *cfg) {
-  const int p = 32 * n / m, ni = win_loads(p), bp = pad_b(batch), waves = 4;
+  const int p = 32 * n / m, ni = win_loads(p), bp = pad_b(batch);
   cfg->kernel = NM_KERNEL_VALU;
+  if (direct_p(p)) {
+    // x in as few equal segments as fit the budget.  Workgroups of 4 waves,
+    // about two per CU, unless only one x image fits a CU's LDS or there are
+    // at most 16 rows per CU: then 16 waves, one row each, so that a CU still
+    // holds 16 waves (measured: 2.0-2.4x faster at K = 14336, batch 4-8).
+    const int64_t w = cols / 32;
+    const int64_t maxw = (int64_t)((lds_budget - 16) / xcols_bytes(bp, 32));
+    const int64_t nseg = w <= maxw ? 1 : (w + maxw - 1) / maxw;
+    const int64_t segw = (w + nseg - 1) / nseg;
+    cfg->seg_cols = segw > 0 ? (int)(segw * 32) : 32;
+    const size_t xb = fixedp_lds_bytes(bp, cfg->seg_cols);
+    const size_t per_cu = xb > 0 ? kLdsCap / xb : 16;
+    const int waves = (per_cu < 2 || rows <= (int64_t)16 * cus) ? 16 : 4;
+    cfg->threads_per_wg = waves * kWave;
+    int64_t rpw = rows / ((int64_t)2 * cus * waves);
+    cfg->rows_per_wave = (int)(rpw < 1 ? 1 : rpw > 8 ? 8 : rpw);
+    return NM_OK;
+  }
+  const int waves = 4;
   cfg->threads_per_wg = waves * kWave;
   // about two workgroups per CU, at most 8 rows per wave
   int64_t rpw = rows / ((int64_t)2 * cus * waves);
@@ -675,8 +718,9 @@ nm_status generic_check_cfg(const nm_launch_cfg &c, int batch, int n, int m,
   if (c.rows_per_wave < 1 || c.rows_per_wave > kWave) return NM_ERR_INVALID_ARG;
   if (c.seg_cols <= 0 || c.seg_cols % 32 != 0) return NM_ERR_INVALID_ARG;
   const int p = 32 * n / m;
-  if (fixed_lds_bytes(pad_b(batch), c.seg_cols, t / kWave, win_loads(p)) > lds_budget)
-    return NM_ERR_INVALID_ARG;
+  const size_t need = direct_p(p) ? fixedp_lds_bytes(pad_b(batch), c.seg_cols)
+                                  : fixed_lds_bytes(pad_b(batch), c.seg_cols, t / kWave, win_loads(p));
+  if (need > lds_budget) return NM_ERR_INVALID_ARG;
   return NM_OK;
 }
 
@@ -768,15 +812,16 @@ nm_status generic_launch(const void *values, const uint32_t *bits, const void *X
   const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
   if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
   const int seg = cfg.seg_cols < cols ? cfg.seg_cols : (int)cols;
-  if (direct_p(p) && seg == cols && cols > 0) {
-    // all of x in LDS (its bytes are within the checked window-kernel bytes)
+  if (direct_p(p) && cols > 0) {
+    // x in segments of seg columns (checked against the budget)
     const int ch = m <= 8 ? 4 : m == 16 ? 2 : 1;
-    const fixedp_fn fn =
-        in_dt == NM_BF16 ? pick_fixedp<true>(bp, p, ch) : pick_fixedp<false>(bp, p, ch);
+    const bool segs = seg < cols;
+    const fixedp_fn fn = in_dt == NM_BF16 ? pick_fixedp<true>(bp, p, ch, segs)
+                                          : pick_fixedp<false>(bp, p, ch, segs);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(cfg.threads_per_wg),
-                       fixedp_lds_bytes(bp, cols), (hipStream_t)stream, (const uint16_t *)values,
+                       fixedp_lds_bytes(bp, seg), (hipStream_t)stream, (const uint16_t *)values,
                        bits, (const uint16_t *)X, Y, batch, rows, (int)cols, cfg.rows_per_wave,
-                       (int)out_dt);
+                       (int)out_dt, seg);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? NM_OK : hip_fail(e);
   }

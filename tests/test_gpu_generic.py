@@ -111,18 +111,34 @@ def test_one_hot_x_picks_the_kept_weight(n, m):
         assert np.array_equal(y, want)
 
 
-@pytest.mark.parametrize("n,m", [(1, 4), (3, 4)])
+@pytest.mark.parametrize("n,m", [(1, 4), (3, 4), (3, 8), (5, 16)])
 @pytest.mark.parametrize("seg,threads,rpw", [(2048, 256, 1), (4096, 128, 3), (6144, 512, 2),
                                              (32, 64, 1), (8320, 512, 64)])
 def test_launch_shapes_and_x_segments(n, m, seg, threads, rpw):
-    """x staged in several segments (seg < cols), several rows per wave, other
-    workgroup sizes: the same sums."""
+    """x staged in several segments (seg < cols; segments that end inside a
+    load batch, a one-word segment), several rows per wave, other workgroup
+    sizes: the same sums, on the direct kernel (1:4, 3:4, 3:8) and the window
+    kernel (5:16)."""
     rows, cols, batch = 149, 8320, 2
     W, keep, X = inputs(rows, cols, n, m, "bf16", batch, seed=seg + rpw)
     values, bits = gpu_pack(W, keep, n, m, "bf16")
     want = oracle.masked_gemv(W, keep, X, True)
     cfg = native.LaunchCfg(threads, rpw, seg, native.NM_KERNEL_VALU)
     Y = native.nm_spmm_small(values, bits, t16(X, "bf16"), n, m, cfg=cfg)
+    for b in range(batch):
+        assert rel_l2(f64(Y[b]), want[b]) <= TOL
+
+
+@pytest.mark.parametrize("n,m", [(1, 4), (3, 4), (1, 8), (3, 8), (5, 16)])
+@pytest.mark.parametrize("batch", [5, 8])
+def test_default_x_segments_at_large_k(n, m, batch):
+    """K = 14336 at batch 5-8: all of x does not fit the LDS budget, so the
+    library's own launch stages it in segments."""
+    rows, cols = 67, 14336
+    W, keep, X = inputs(rows, cols, n, m, "f16", batch, seed=batch + 7 * n + m)
+    values, bits = gpu_pack(W, keep, n, m, "f16")
+    want = oracle.masked_gemv(W, keep, X, False)
+    Y = native.nm_spmm_small(values, bits, t16(X, "f16"), n, m)
     for b in range(batch):
         assert rel_l2(f64(Y[b]), want[b]) <= TOL
 
