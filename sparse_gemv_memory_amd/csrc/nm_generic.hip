@@ -176,6 +176,13 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
     const int S = K - s0 < seg ? K - s0 : seg;
     __syncthreads();  // every wave is done with the previous segment's x
     stage_x_cols<BP>(lds, x, B, K, s0, S);
+    if constexpr (UN) {  // the pad after each word's slots reads as x = 0
+      for (int w = threadIdx.x; w < (S >> 5); w += blockDim.x) {
+        uint32_t *pad = reinterpret_cast<uint32_t *>(lds + w * XCols<BP>::WS + 32 * XCols<BP>::SB);
+#pragma unroll
+        for (int q = 0; q < XCols<BP>::PB / 4; ++q) pad[q] = 0u;
+      }
+    }
     __syncthreads();
     const int sw0 = s0 >> 5, sw = S >> 5;
     const int nwin = (sw + kWinWords - 1) / kWinWords;
@@ -251,6 +258,35 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
         // byte offset of the word's x slots in the segment's image
         const int cb = (t * kWinWords + lane) * XCols<BP>::WS;
         uint32_t m = mw;
+        if constexpr (UN) {
+          // The counts differ between lanes, so the step loop runs a
+          // wave-uniform number of 8-step groups (from ballots) with no
+          // branch per step: a step past the lane's count finds no set bit
+          // and takes the word's zeroed pad slot as its x (column 32), and
+          // its value is zeroed, so it adds an exact 0.  Per-lane loop bounds
+          // and a branch per pair left the kernel bound by instruction issue.
+          const int ng = (__ballot(pl > 0) != 0) + (__ballot(pl > 8) != 0) +
+                         (__ballot(pl > 16) != 0) + (__ballot(pl > 24) != 0);
+          for (int g = 0; g < ng; ++g) {
+            const int j0 = 8 * g;
+            int c[8];
+            uint32_t v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t f = (uint32_t)ffbl_hw(m);  // 0xffffffff once m == 0
+              c[e] = cb + (int)(f < 32u ? f : 32u) * XCols<BP>::SB;
+              m &= m - 1;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * (j0 + e)));
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const int left = pl - j0 - e;
+              const uint32_t w = (left >= 1 ? v[e] : 0u) | (left >= 2 ? v[e + 1] << 16 : 0u);
+              pair_acc<BF, BP>(lds, c[e], c[e + 1], w, acc);
+            }
+          }
+        } else
         // eight scan steps at a time: the columns first (a short VALU chain),
         // then every LDS read of the group, then the products.  Steps past P
         // read slots inside the buffer (see win_loads) and are dropped.
@@ -774,15 +810,28 @@ nm_status bitmask_launch(const void *values, const uint32_t *bits, const int64_t
                          nm_dtype in_dt, nm_dtype out_dt, int cus, size_t lds_budget,
                          void *stream) {
   constexpr int kNI = 5;  // a window holds up to 64 x 32 values (+ alignment)
-  const int bp = pad_b(batch), waves = 4;
-  int64_t rpw = rows / ((int64_t)2 * cus * waves);
-  rpw = rpw < 1 ? 1 : rpw > 8 ? 8 : rpw;
-  int64_t seg = cols;
-  if (fixed_lds_bytes(bp, (int)cols, waves, kNI) > lds_budget) {
+  const int bp = pad_b(batch);
+  // x whole, or in segments of whole windows, next to the waves' buffers
+  auto seg_for = [&](int waves) -> int64_t {
+    if (fixed_lds_bytes(bp, (int)cols, waves, kNI) <= lds_budget) return cols;
     const size_t wave_area = fixed_lds_bytes(bp, 0, waves, kNI);
-    seg = (int64_t)((lds_budget - wave_area - 16) / xcols_bytes(bp, 32)) * 32 / 2048 * 2048;
-    if (seg < 2048) return NM_ERR_UNSUPPORTED;
+    if (wave_area + 16 + xcols_bytes(bp, 2048) > lds_budget) return 0;
+    return (int64_t)((lds_budget - wave_area - 16) / xcols_bytes(bp, 32)) * 32 / 2048 * 2048;
+  };
+  // 4-wave workgroups, about two per CU; where only one of them fits a CU's
+  // LDS (batch 5-8), 8-wave workgroups, one per CU, every row in one round
+  // (measured 1.2-1.4x faster there, slower at batch 1)
+  int waves = 4;
+  int64_t seg = seg_for(4), rpw;
+  if (seg > 0 && 2 * fixed_lds_bytes(bp, (int)seg, 4, kNI) > kLdsCap && seg_for(8) > 0) {
+    waves = 8;
+    seg = seg_for(8);
+    rpw = (rows + (int64_t)cus * waves - 1) / ((int64_t)cus * waves);
+  } else {
+    rpw = rows / ((int64_t)2 * cus * waves);
   }
+  if (seg <= 0) return NM_ERR_UNSUPPORTED;
+  rpw = rpw < 1 ? 1 : rpw > 8 ? 8 : rpw;
   const int64_t grid = (rows + waves * rpw - 1) / (waves * rpw);
   if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
   using un_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int, int64_t,
