@@ -141,7 +141,11 @@ int nm_spmv(const void *values, const uint32_t *bits, const void *x, void *y,
  *   X: device, batch x cols row-major, 16-byte aligned;
  *   Y: device, batch x rows row-major (overwritten).
  * Other arguments, precision and errors as nm_spmv; batch outside 1..8 gives
- * NM_ERR_INVALID_ARG. */
+ * NM_ERR_INVALID_ARG.  An x at a column that row r pruned never enters
+ * Y[b][r], so Inf or NaN there leaves the sum finite -- except on the
+ * decompressed-tile matrix-core path (N:M other than 2:4 at batch >= 5 in the
+ * default launch), which multiplies the tile's stored zeros as a dense product
+ * of the zero-filled matrix would (0 * Inf = NaN). */
 int nm_spmm_small(const void *values, const uint32_t *bits, const void *X,
                   void *Y, int batch, int64_t rows, int64_t cols, int n, int m,
                   nm_dtype in_dt, nm_dtype out_dt, void *stream);
