@@ -239,8 +239,8 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("15a5cb924c7854ea92781f9b7b6fca69e6a81fb57f3dd95cdafc57b093583c30",
-                    66276795),
+    (14336, 4096): ("1787969e25f24bdd8eac26600e1cf6572714c906eb630d8d75598fb226347ffb",
+                    66272572),
 }
 
 
