@@ -239,7 +239,7 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch); see
     # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("1787969e25f24bdd8eac26600e1cf6572714c906eb630d8d75598fb226347ffb",
+    (14336, 4096): ("342999766698669362fa3ac49fa2b5765a2a6e7e4d41617cf36fd466badb88f9",
                     66272572),
 }
 

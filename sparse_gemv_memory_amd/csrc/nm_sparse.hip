@@ -1319,11 +1319,13 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
     //    wave and one workgroup per CU, so x is staged once per CU;
     //  - few rows (<= 32 per CU) split evenly over the CUs: exactly two
     //    workgroups per CU; for the sparse product at batch 1 with
-    //    K <= 16384, 4 rows per wave while a workgroup keeps at least 2
-    //    waves, else 2 while it keeps at least 4 (a longer pipeline per wave:
-    //    70B q 8192x8192 -20%, Qwen3 q and 8B down 4-5%, 8B q/o 3%, the
-    //    fused 8B q|k|v 6144x4096 -13% with 3 waves of 4 rows instead of 6
-    //    of 2), otherwise one row per wave (better or equal at K >= 25600);
+    //    K <= 16384, 4 or else 2 rows per wave while a workgroup keeps at
+    //    least 4 waves (a longer pipeline per wave: 70B q 8192x8192 -20%,
+    //    Qwen3 q and 8B down 4-5%, 8B q/o 3%); for 2:4, 4 rows already while
+    //    it keeps 2 waves (the fused 8B q|k|v 6144x4096 -13% with 3 waves of
+    //    4 rows instead of 6 of 2; the scan of the other 50% patterns ran
+    //    20-48% slower so on 4096-row shapes), otherwise one row per wave
+    //    (better or equal at K >= 25600);
     //  - otherwise, rows split evenly: 256 threads and the same number of
     //    rows rpw (<= 8) for every wave, at least two workgroups per CU, so
     //    x is staged rarely and no CU finishes early;
@@ -1342,7 +1344,8 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
       // wave: 8 waves per workgroup measured 3% faster for K = 14336)
       if (!dense && bp == 1 && cols <= 16384 && !(m == 4 && rows_batch_chunks(cols, bp) == 2))
         for (int r = 4; r >= 2; r -= 2)
-          if (rows % (r * two_per_cu) == 0 && rows / (r * two_per_cu) >= (r == 4 ? 2 : 4)) {
+          if (rows % (r * two_per_cu) == 0 &&
+              rows / (r * two_per_cu) >= (r == 4 && m == 4 ? 2 : 4)) {
             rpw = r;
             break;
           }
