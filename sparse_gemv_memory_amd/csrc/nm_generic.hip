@@ -534,14 +534,17 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixedp_kernel(
 using fixedp_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *, void *, int,
                            int64_t, int, int, int, int);
 
-// The densities with a direct kernel, and its words per lane per load batch.
+// The densities with a direct kernel, and its words per lane per load batch:
+// two for every P (a batch of 128 words is one row of K = 4096; four words
+// per lane left half of each batch idle there and measured 2-8% slower for
+// P = 4 and 8 on the 8B gate and down shapes, eight 6-19% slower).
 __host__ __device__ constexpr bool direct_p(int p) { return p == 4 || p == 8 || p == 12 || p == 24; }
 
 template <bool BF, int BP, int CH, bool SEGS>
 fixedp_fn pick_fixedp_p(int p) {
   switch (p) {
-    case 4: return nm_spmv_fixedp_kernel<BF, BP, 4, 4, CH, SEGS>;
-    case 8: return nm_spmv_fixedp_kernel<BF, BP, 8, 4, CH, SEGS>;
+    case 4: return nm_spmv_fixedp_kernel<BF, BP, 4, 2, CH, SEGS>;
+    case 8: return nm_spmv_fixedp_kernel<BF, BP, 8, 2, CH, SEGS>;
     case 12: return nm_spmv_fixedp_kernel<BF, BP, 12, 2, CH, SEGS>;
     default: return nm_spmv_fixedp_kernel<BF, BP, 24, 2, CH, SEGS>;
   }
