@@ -821,15 +821,20 @@ nm_status bitmask_launch(const void *values, const uint32_t *bits, const int64_t
     if (wave_area + 16 + xcols_bytes(bp, 2048) > lds_budget) return 0;
     return (int64_t)((lds_budget - wave_area - 16) / xcols_bytes(bp, 32)) * 32 / 2048 * 2048;
   };
-  // 4-wave workgroups, about two per CU; where only one of them fits a CU's
-  // LDS (batch 5-8), 8-wave workgroups, one per CU, every row in one round
-  // (measured 1.2-1.4x faster there, slower at batch 1)
+  // 4-wave workgroups: about three per CU where three fit its LDS (batch 1:
+  // gate 14336x4096 31.4 -> 29.1 us), else about two (a three-per-CU grid
+  // then runs in one and a half rounds: 1.2x slower at batch 2-4); where only
+  // one of them fits (batch 4-8 here), 8-wave workgroups, one per CU, every
+  // row in one round (measured 1.2-1.4x faster there, slower at batch 1)
   int waves = 4;
   int64_t seg = seg_for(4), rpw;
-  if (seg > 0 && 2 * fixed_lds_bytes(bp, (int)seg, 4, kNI) > kLdsCap && seg_for(8) > 0) {
+  const size_t wg4 = seg > 0 ? fixed_lds_bytes(bp, (int)seg, 4, kNI) : 0;
+  if (seg > 0 && 2 * wg4 > kLdsCap && seg_for(8) > 0) {
     waves = 8;
     seg = seg_for(8);
     rpw = (rows + (int64_t)cus * waves - 1) / ((int64_t)cus * waves);
+  } else if (seg > 0 && 3 * wg4 <= kLdsCap) {
+    rpw = (rows + (int64_t)3 * cus * waves - 1) / ((int64_t)3 * cus * waves);
   } else {
     rpw = rows / ((int64_t)2 * cus * waves);
   }
