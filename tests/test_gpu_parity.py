@@ -453,6 +453,26 @@ def test_default_launch_picks_matrix_cores_for_small_batch():
     assert native.nm_default_launch(14336, 4096, 8, dense=True).kernel == VALU
 
 
+def test_default_launch_shapes_follow_the_measured_rules():
+    """Launch shapes the library picks on the 8B shapes (256 CUs), each the
+    measured best of its sweep: 2:4 q|k|v 6144x4096 as 3 waves of 4 rows; the
+    scan of 4:8 keeps 2 rows per wave and 4-wave workgroups; at other
+    densities, x of K = 14336 at batch 8 in two equal segments staged by
+    16-wave workgroups, and K = 4096 whole with 4-wave workgroups."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the rules are pinned for 256 CUs")
+
+    def shape(*a):
+        c = native.nm_default_launch(*a)
+        return c.threads_per_wg, c.rows_per_wave, c.seg_cols
+
+    assert shape(6144, 4096, 1, 2, 4) == (192, 4, 4096)
+    assert shape(4096, 4096, 1, 4, 8) == (256, 2, 4096)
+    assert shape(4096, 14336, 1, 4, 8) == (256, 2, 14336)
+    assert shape(4096, 14336, 8, 1, 4) == (1024, 1, 7168)
+    assert shape(14336, 4096, 8, 1, 4) == (256, 7, 4096)
+
+
 def test_zero_columns_give_zero_output_batch():
     for batch in (1, 2, 8):
         values = torch.empty((7, 0), dtype=torch.float16, device=DEV)
