@@ -68,7 +68,7 @@ def test_pack_bitmask_exact(rows, cols, kind, dtype):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("kind", ["half", "random", "edges"])
 @pytest.mark.parametrize("rows,cols", SHAPES)
-@pytest.mark.parametrize("batch", [1, 3, 8])
+@pytest.mark.parametrize("batch", [1, 2, 3, 5, 8])
 def test_bitmask_product_matches_oracle(rows, cols, kind, dtype, batch):
     W = synth.weights(rows, cols, seed=rows * 3 + cols, dtype=dtype)
     keep = masks(kind, rows, cols, W, seed=rows)
@@ -118,8 +118,10 @@ def test_bitmask_all_zero_and_empty():
 
 
 @pytest.mark.parametrize("rows,cols", [(14336, 4096), (4096, 14336)])
-@pytest.mark.parametrize("batch", [1, 8])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
 def test_bitmask_full_size_sampled_rows(rows, cols, batch):
+    # the library's launches: three 4-wave workgroups per CU (batch 1), two
+    # (batch 2), 8-wave workgroups with x whole or in segments (batch 4-8)
     W = synth.weights(rows, cols, seed=rows)
     keep = synth.topk_row_mask(W, 0.5)
     X = synth.activations(batch, cols, seed=rows)
