@@ -535,9 +535,11 @@ using fixedp_fn = void (*)(const uint16_t *, const uint32_t *, const uint16_t *,
                            int64_t, int, int, int, int);
 
 // The densities with a direct kernel, and its words per lane per load batch:
-// two for every P (a batch of 128 words is one row of K = 4096; four words
-// per lane left half of each batch idle there and measured 2-8% slower for
-// P = 4 and 8 on the 8B gate and down shapes, eight 6-19% slower).
+// two for P = 4, 8, 12 (a batch of 128 words is one row of K = 4096; four
+// words per lane left half of each batch idle there and measured 2-8% slower
+// for P = 4 and 8 on the 8B gate and down shapes, eight 6-19% slower, one
+// 3-36% slower), one for P = 24, whose word already carries 48 value bytes
+// (up to 8% faster than two, equal on gate at batch 1).
 __host__ __device__ constexpr bool direct_p(int p) { return p == 4 || p == 8 || p == 12 || p == 24; }
 
 template <bool BF, int BP, int CH, bool SEGS>
@@ -546,7 +548,7 @@ fixedp_fn pick_fixedp_p(int p) {
     case 4: return nm_spmv_fixedp_kernel<BF, BP, 4, 2, CH, SEGS>;
     case 8: return nm_spmv_fixedp_kernel<BF, BP, 8, 2, CH, SEGS>;
     case 12: return nm_spmv_fixedp_kernel<BF, BP, 12, 2, CH, SEGS>;
-    default: return nm_spmv_fixedp_kernel<BF, BP, 24, 2, CH, SEGS>;
+    default: return nm_spmv_fixedp_kernel<BF, BP, 24, 1, CH, SEGS>;
   }
 }
 
