@@ -179,9 +179,12 @@ def chain_graphs(projs, call, b, nsteps, copies_attr, parallel=True):
     return graphs
 
 
-def per_kernel_us(p, call, b, ncopies, reps):
-    """Average duration of one launch: a graph of back-to-back launches over
-    the projection's rotation, HIP events around each replay."""
+def per_kernel_stats(p, call, b, ncopies, reps):
+    """Duration of one launch: a graph of back-to-back launches over the
+    projection's rotation, HIP events around each replay, divided by the
+    launch count.  Returns the median over the replays and their 10th and
+    90th percentiles (µs per launch); per-dispatch percentiles come from the
+    profiler's kernel trace (--summarize-trace)."""
     g = capture(lambda: [call(p, b, c) for c in range(ncopies)])
     g.replay()
     torch.cuda.synchronize()
@@ -192,39 +195,54 @@ def per_kernel_us(p, call, b, ncopies, reps):
         g.replay()
         z.record()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(z) for a, z in evs]
-    return 1e3 * float(np.median(ms)) / ncopies
+    us = 1e3 * np.array([a.elapsed_time(z) for a, z in evs]) / ncopies
+    return {"us": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+            "p90": float(np.percentile(us, 90))}
+
+
+def per_kernel_us(p, call, b, ncopies, reps):
+    """Median duration of one launch (see per_kernel_stats)."""
+    return per_kernel_stats(p, call, b, ncopies, reps)["us"]
 
 
 def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
-    """The oracle on the whole layer at batch 1, on the host cores."""
+    """The oracle on the whole layer at batch 1, on the host cores; projs are
+    (name, W, keep, X, sbytes) of the layer's projections."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     threads = max(1, min(threads, os.cpu_count() or 1))
-    total_bytes = sum(p.sbytes[1] for p in projs)
+    total_bytes = sum(sb[1] for _, _, _, _, sb in projs)
     reps, wall = 0, 0.0
     errs = {}
     while True:
         t0 = time.perf_counter()
-        for p in projs:
-            y = oracle.masked_gemv(p.W, p.keep, p.X[1], False, threads=threads)
+        for name, W, keep, X, _ in projs:
+            y = oracle.masked_gemv(W, keep, X[1], False, threads=threads)
             if reps == 0:
-                got = gpu_y[p.name].astype(np.float64)
-                errs[p.name] = float(np.linalg.norm(got - y[0]) / np.linalg.norm(y[0]))
+                got = gpu_y[name].astype(np.float64)
+                errs[name] = float(np.linalg.norm(got - y[0]) / np.linalg.norm(y[0]))
         wall += time.perf_counter() - t0
         reps += 1
         if wall * threads >= min_cpu_seconds or reps >= 20:
             break
     sec_per_layer = wall / reps
+    # one core: the same layer pass once more with a single thread (the
+    # per-row summation order is the same, so the result is identical)
+    t0 = time.perf_counter()
+    for _, W, keep, X, _ in projs:
+        oracle.masked_gemv(W, keep, X[1], False, threads=1)
+    sec_1 = time.perf_counter() - t0
     return {
         "value": total_bytes / sec_per_layer / 1e9,
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": (f"the whole workload: all 7 projections of the layer at batch 1, {reps} passes "
-                   f"(fp64 dense-masked product, C + OpenMP over rows); "
-                   f"{1e6 * sec_per_layer:.0f} us per layer pass"),
+                   f"on {threads} threads and 1 pass on one thread (fp64 dense-masked product, "
+                   f"C + OpenMP over rows); {1e6 * sec_per_layer:.0f} us per layer pass"),
         "us_per_step": 1e6 * sec_per_layer,
+        "single_core": {"value": total_bytes / sec_1 / 1e9, "unit": "GB/s", "cores": 1,
+                        "us_per_step": 1e6 * sec_1},
         "gpu_vs_oracle_rel_l2": errs,
         "host": platform.processor() or platform.machine(),
         "host_cpus": os.cpu_count(),
@@ -409,6 +427,63 @@ def gpu_layer(rows, cols, n, m, seed, want_dense):
     W = (torch.randn((rows, cols), device=DEV, generator=g) * 0.02).half()
     values, bits = pack_gpu(W, n, m)
     return values, bits, (W if want_dense else None)
+
+
+# The 2:4 layers of 14336x4096 weights and more besides the 8B layer's own:
+# the Llama-3.3-70B and Qwen3-32B projections of workload 4 with at least
+# 58.7 M weights, timed at batch 1 in the default run.
+LARGE_LAYERS = ("70b.q", "70b.gate", "70b.down", "qwen32b.gate", "qwen32b.down")
+
+
+class GpuProj(Proj):
+    """A 2:4 fp16 projection drawn and packed on the GPU (gpu_layer; the
+    kernels' time does not depend on the values), x drawn as in Proj, with
+    Proj's rotation of packed and dense copies and its launch calls."""
+
+    def __init__(self, mt, want_dense):
+        self.mt, self.name = mt, mt.name
+        t0 = time.time()
+        values, bits, W = gpu_layer(mt.rows, mt.cols, mt.n, mt.m, mt.seed, want_dense)
+        packed = values.numel() * 2 + bits.numel() * 4
+        self.nc = pow2_copies(packed)
+        self.vals = [values] + [native.clone_packed(values) for _ in range(self.nc - 1)]
+        self.bits = [bits] + [bits.clone() for _ in range(self.nc - 1)]
+        self.ndc = pow2_copies(W.numel() * 2) if want_dense else 0
+        self.dense = ([W] + [W.clone() for _ in range(self.ndc - 1)]) if want_dense else []
+        self.X = {1: synth.activations(1, mt.cols, seed=mt.seed, dtype=mt.dtype, outliers=True)}
+        self.Xd = {1: t16(self.X[1], mt.dtype)}
+        self.Y = {1: torch.empty((1, mt.rows), dtype=torch.float32, device=DEV)}
+        self.sbytes = {1: workloads.sparse_bytes(mt.rows, mt.cols, mt.n, mt.m, 1, 4)}
+        log(f"  {self.name:12s} {mt.rows}x{mt.cols}: {self.nc} packed copies "
+            f"({self.nc * packed / 2**30:.2f} GiB), {self.ndc} dense copies, {time.time() - t0:.1f}s")
+
+
+def large_layers_run(args, want_dense):
+    """Batch-1 µs/call (median, p10, p90 over replays), GB/s and fraction of
+    the 8 TB/s peak of the LARGE_LAYERS shapes, cache-cold, beside the dense
+    GEMV and torch linear; one shape resident at a time."""
+    out = {}
+    for mt, _ in workloads.config_matrices(4):
+        if mt.name not in LARGE_LAYERS:
+            continue
+        p = GpuProj(mt, want_dense)
+        st = per_kernel_stats(p, Proj.sparse_call, 1, p.nc, args.reps)
+        gbs = p.sbytes[1] / st["us"] / 1e3
+        d = {"us": round(st["us"], 3), "us_p10": round(st["p10"], 3), "us_p90": round(st["p90"], 3),
+             "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4),
+             "bytes_per_launch": p.sbytes[1]}
+        if want_dense:
+            dus = per_kernel_us(p, Proj.dense_call, 1, p.ndc, args.reps)
+            tus = per_kernel_us(p, Proj.torch_call, 1, p.ndc, args.reps)
+            d.update({"dense_us": round(dus, 3), "torch_linear_us": round(tus, 3),
+                      "speedup_vs_best_dense": round(min(dus, tus) / st["us"], 3)})
+        out[f"{mt.name} {mt.rows}x{mt.cols}"] = d
+        log(f"  {mt.name:12s} {mt.rows:5d}x{mt.cols:5d}: {st['us']:7.2f} us  {gbs:7.1f} GB/s "
+            f"({100 * gbs / PEAK_GBS:.1f}% of 8 TB/s)"
+            + (f"  dense {d['dense_us']:.2f} us, torch {d['torch_linear_us']:.2f} us" if want_dense else ""))
+        del p
+        torch.cuda.empty_cache()
+    return out
 
 
 def fused_layer_run(args):
@@ -738,6 +813,28 @@ def decode_run(args):
     return out
 
 
+def summarize_trace(path):
+    """Per-kernel dispatch statistics of a rocprofv3 kernel-trace CSV: one row
+    per (kernel, grid, workgroup) with the dispatch count and the mean, p10,
+    p50, p90, min and max of End - Start in µs, in order of first dispatch."""
+    import csv
+    groups = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | grid threads | WG | dispatches | mean us | p10 | p50 | p90 | min | max |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for (name, grid, wg), us in groups.items():
+        a = np.array(us)
+        # drop the return type, namespace and parameter list; keep template arguments
+        short = name.replace("void (anonymous namespace)::", "").split("(")[0] or name
+        short = short if len(short) <= 90 else short[:87] + "..."
+        print(f"| `{short}` | {grid} | {wg} | {len(a)} | {a.mean():.3f} | {np.percentile(a, 10):.3f} | "
+              f"{np.percentile(a, 50):.3f} | {np.percentile(a, 90):.3f} | {a.min():.3f} | {a.max():.3f} |")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -747,6 +844,11 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch4", action="store_true")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the 70B / Qwen3-32B layers of >= 58.7 M weights at batch 1")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print per-kernel dispatch statistics (count, mean, p10, p50, p90) of a "
+                         "rocprofv3 kernel-trace CSV and exit (no GPU needed)")
     ap.add_argument("--workload", default="llama8b-layer",
                     choices=["llama8b-layer", "single", "patterns", "70b-qwen", "decode-32-layers",
                              "llama8b-layer-fused", "calibration-hessian", "prefill-contrast",
@@ -769,6 +871,9 @@ def main():
                          "reference for FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the N:M SpMV path is built and timed on a single "
@@ -855,8 +960,10 @@ def main():
     # per-kernel durations (batch 1) and the roofline of the dominant kernel
     per = {}
     for p in projs:
-        us = per_kernel_us(p, Proj.sparse_call, 1, p.nc, args.reps)
-        d = {"us": round(us, 3), "GB/s": round(p.sbytes[1] / us / 1e3, 1),
+        st = per_kernel_stats(p, Proj.sparse_call, 1, p.nc, args.reps)
+        us = st["us"]
+        d = {"us": round(us, 3), "us_p10": round(st["p10"], 3), "us_p90": round(st["p90"], 3),
+             "GB/s": round(p.sbytes[1] / us / 1e3, 1),
              "frac_of_peak": round(p.sbytes[1] / us / 1e3 / PEAK_GBS, 4)}
         if want_dense:
             dus = per_kernel_us(p, Proj.dense_call, 1, p.ndc, args.reps)
@@ -885,6 +992,23 @@ def main():
                 "bytes_per_launch": dbytes, "us_per_launch": round(dus, 3),
                 "launches_per_step": len(dps)}
 
+    # the larger 2:4 layers of workload 4 at batch 1 (the 8B layer's
+    # projections are freed first)
+    gpu_y = {}
+    if not args.no_cpu_baseline:
+        for p in projs:
+            p.sparse_call(1, 0)
+        torch.cuda.synchronize()
+        for p in projs:
+            gpu_y[p.name] = p.Y[1][0].cpu().numpy()
+    host = [(p.name, p.W, p.keep, p.X, p.sbytes) for p in projs]
+    del projs, shape_time, dps, p
+    torch.cuda.empty_cache()
+    large = {} if args.no_large else large_layers_run(args, want_dense)
+    # which of the named 2:4 layers of >= 58.7 M weights reach 70% of peak at batch 1
+    target = {k: v["frac_of_peak"] for k, v in list(per.items()) + list(large.items())
+              if int(k.split()[-1].split("x")[0]) * int(k.split("x")[-1]) >= 14336 * 4096}
+
     ms = timings[("sparse", 1, False)]
     res = {
         "metric": METRIC,
@@ -903,11 +1027,15 @@ def main():
                                "(q,o 4096x4096; k,v 1024x4096; gate,up 14336x4096; down 4096x14336), "
                                "2:4 fp16, x N(0,1) + 0.1% outlier channels x20",
                    "batch": 1, "pattern": "2:4", "bytes_per_step": layer_bytes[1],
-                   "launches_per_step": len(projs), "timing": "one HIP graph per step, the 7 "
+                   "launches_per_step": len(host), "timing": "one HIP graph per step, the 7 "
                    "launches in series, >=1 GiB rotation per projection (cache-cold)"},
         "frac_of_peak": round(layer_bytes[1] / (ms * 1e-3) / 1e9 / PEAK_GBS, 4),
         "us_per_call": per,
         "roofline": roofline,
+        "large_layers_batch1": large,
+        "layers_at_or_above_70pct": {"frac_of_peak": target,
+                                     "met": sum(1 for v in target.values() if v >= 0.70),
+                                     "of": len(target)},
     }
     res["ms_per_step_parallel_branches"] = round(timings[("sparse", 1, True)], 5)
 
@@ -927,14 +1055,8 @@ def main():
             b4["speedup_vs_best_dense"] = round(best_dense(4) / ms4, 3)
         res["batch4"] = b4
     if not args.no_cpu_baseline:
-        gpu_y = {}
-        for p in projs:
-            p.sparse_call(1, 0)
-        torch.cuda.synchronize()
-        for p in projs:
-            gpu_y[p.name] = p.Y[1][0].cpu().numpy()
         log("cpu baseline: timing the oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(projs, gpu_y)
+        res["cpu_baseline"] = cpu_baseline(host, gpu_y)
     print(json.dumps(res), flush=True)
 
 

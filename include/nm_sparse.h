@@ -13,12 +13,14 @@
  * Accurate and Efficient LLM Inference" (paper text):
  *   - Method, kernel subsection, opening paragraph: decoding is dominated by
  *     N:M SpMV at batch one and small batch;
- *   - same subsection, item (1) "Bitmask indexing": one bit per column, kept
- *     weights stored in increasing column order so the set bits line up with
- *     the stored values; 2 bits of metadata per kept weight at 50%;
- *   - same subsection, item (2) "Fixed-step bitmask traversal": at 50% N:M
- *     density with M <= 32 every aligned 32-bit word holds exactly 16 set
- *     bits, and the least significant set bit gives the next kept column;
+ *   - same subsection, item (1) "Bitmask indexing": a row's mask has one
+ *     bit per column and its kept weights are stored in column order, so the
+ *     k-th set bit of the row names the column of its k-th stored value; at
+ *     50% that costs 2 bits of metadata per kept weight;
+ *   - same subsection, item (2) "Fixed-step bitmask traversal": under a 50%
+ *     N:M pattern with M <= 32, a 32-bit mask word covers whole groups, so
+ *     its count of set bits is always 16 and a per-word loop has a fixed
+ *     trip count; each step takes the lowest set bit as the next kept column;
  *   - Appendix C (kernel implementation): one compiled kernel per N:M pattern,
  *     N and M fixed at compile time.
  *
@@ -85,8 +87,14 @@ int nm_last_hip_error(void);
  * aligned 32-bit mask word then holds exactly P = 32N/M set bits, so word w's
  * values start at w*P of the row and each word is walked in P fixed steps
  * (the fixed-count argument of Method item (2), which the pages make at 50%).
- * Those densities run on a generic kernel (values staged per 64-word window
- * in LDS); the other entry points reject them with NM_ERR_UNSUPPORTED. */
+ * Those densities run on two generic kernels.  P = 4, 8, 12 and 24 (1:8, 1:4,
+ * 3:8, 3:4, and 2:16, 6:16, 8:32, 24:32) take the direct kernel: each lane
+ * loads whole mask words and their 2P value bytes straight into registers
+ * with 8- or 16-byte loads.  Every other P takes the window kernel, which
+ * copies the values of 64 mask words at a time into LDS with 16-byte loads.
+ * Both read whole 16-byte chunks of values, so the last one may reach into
+ * the padding that nm_packed_bytes adds (values_bytes rounded up to 16).
+ * The other entry points reject these densities with NM_ERR_UNSUPPORTED. */
 
 /* Sizes in bytes of the packed buffers of an R x K matrix under pattern N:M
  * with 16-bit elements of type dt (Method item (1): K*N/M values and K/32
@@ -142,10 +150,10 @@ int nm_spmv(const void *values, const uint32_t *bits, const void *x, void *y,
  *   Y: device, batch x rows row-major (overwritten).
  * Other arguments, precision and errors as nm_spmv; batch outside 1..8 gives
  * NM_ERR_INVALID_ARG.  An x at a column that row r pruned never enters
- * Y[b][r], so Inf or NaN there leaves the sum finite -- except on the
- * decompressed-tile matrix-core path (N:M other than 2:4 at batch >= 5 in the
- * default launch), which multiplies the tile's stored zeros as a dense product
- * of the zero-filled matrix would (0 * Inf = NaN). */
+ * Y[b][r], so Inf or NaN there leaves the sum finite, on every kernel.  (The
+ * decompressed-tile matrix-core path, N:M other than 2:4 at batch >= 5 by
+ * default, multiplies a zero-filled dense tile; where that gives NaN for a
+ * 256-column block, the block is summed again over its kept columns only.) */
 int nm_spmm_small(const void *values, const uint32_t *bits, const void *X,
                   void *Y, int batch, int64_t rows, int64_t cols, int n, int m,
                   nm_dtype in_dt, nm_dtype out_dt, void *stream);
@@ -266,6 +274,16 @@ typedef struct {
  * product's argument checks. */
 int nm_default_launch(int64_t rows, int64_t cols, int batch, int n, int m,
                       int dense, nm_launch_cfg *cfg);
+
+/* The launch shape nm_spmm_small_cfg (n:m) or nm_dense_gemv_cfg (dense != 0)
+ * would use with the overrides in `user` (NULL or all fields 0 = the
+ * default): the fields `user` leaves at 0 are the library's choice for the
+ * kernel `user` names, with that kernel's launch rules for the pattern.
+ * Host only apart from one query of the current device's properties on first
+ * use.  Errors as the _cfg call's (an invalid or unsupported override gives
+ * the same status that call would return). */
+int nm_resolve_launch(int64_t rows, int64_t cols, int batch, int n, int m, int dense,
+                      const nm_launch_cfg *user, nm_launch_cfg *cfg);
 
 /* nm_spmm_small / nm_dense_gemv with an explicit launch shape (cfg may be
  * NULL for the default).  Invalid shapes give NM_ERR_INVALID_ARG; asking for

@@ -9,13 +9,14 @@
  * 2610.12327):
  *   - N:M semi-structured sparsity: N kept weights in every group of M
  *     consecutive weights of a row ("Related work", N:M sparsity paragraph).
- *   - Bitmask indexing: one bit per column of a row, set when the weight is
- *     retained; kept weights are stored in increasing column order so the set
- *     bits line up with the stored values ("Method", kernel subsection, item
- *     (1) "Bitmask indexing"; the learnaivisually explainer, "Why the pruned
- *     model was not faster").
- *   - Aligned 32-bit words: at 50% density with M <= 32 each aligned word has
- *     exactly 16 set bits ("Method", item (2) "Fixed-step bitmask traversal").
+ *   - Bitmask indexing: a row's mask has one bit per column, set for a kept
+ *     weight, and the kept weights are stored in column order, so the k-th
+ *     set bit of a row gives the column of its k-th stored value ("Method",
+ *     kernel subsection, item (1) "Bitmask indexing"; the learnaivisually
+ *     explainer, "Why the pruned model was not faster").
+ *   - Aligned 32-bit words: a 50% pattern with M <= 32 keeps half of every
+ *     group and a word covers whole groups, so each word's set-bit count is
+ *     16 ("Method", item (2) "Fixed-step bitmask traversal").
  *   - The product itself: the method reaches exactly the dense product of the
  *     masked weight matrix with x, so the oracle computes that definition in
  *     fp64 from the dense masked form, never from the packed form.

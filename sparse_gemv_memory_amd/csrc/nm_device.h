@@ -62,6 +62,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// A 16-bit pattern (bfloat16 if BF, else binary16) widened exactly to fp32.
+template <bool BF>
+__device__ __forceinline__ float half_to_f32(uint16_t h) {
+  if constexpr (BF)
+    return __uint_as_float((uint32_t)h << 16);
+  else
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
 // out_kind: the output nm_dtype in bits 0..7 and the epilogue above them.
 constexpr int kEpiShift = 8;
 constexpr int kEpiNone = 0;

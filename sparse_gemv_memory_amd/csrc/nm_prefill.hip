@@ -256,6 +256,8 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
   if (n != 2 || m != 4) return NM_ERR_UNSUPPORTED;  // the sparse instruction is 2:4
   if (cols % 64 != 0) return NM_ERR_SHAPE;
   if (batch == 0 || rows == 0) return NM_OK;
+  // each size alone first, so the products below cannot overflow int64
+  if (batch > INT32_MAX || rows > INT32_MAX || cols > INT32_MAX) return NM_ERR_INVALID_ARG;
   if (rows * cols > INT32_MAX || batch * cols * 2 > INT32_MAX) return NM_ERR_INVALID_ARG;
   if (!Y || (cols > 0 && (!values || !bits || !X))) return NM_ERR_INVALID_ARG;
   if (!aligned(values, 16) || !aligned(bits, 4) || !aligned(X, 16) ||

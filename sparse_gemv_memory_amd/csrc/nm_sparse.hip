@@ -801,16 +801,20 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     return ld<uint32_t>((lds_ptr)(size_t)(sl + kMValBytes + n * 32 +
                                           4 * ((2 * s + (j >> 1)) ^ ((n >> 2) & 7))));
   };
-  auto scatter = [&](uint32_t tile, u32x4_t v, uint32_t w) {
-    uint32_t m;
+  // the set bits of mask word w that belong to the lane's chunk: its lowest
+  // 8 kept columns for an even chunk, the next 8 for an odd one
+  auto chunk_bits = [&](uint32_t w) -> uint32_t {
     if constexpr (KIND == kMfmaDenseHalf) {
-      m = w & ((j & 1) ? 0xffff0000u : 0x0000ffffu);
+      return w & ((j & 1) ? 0xffff0000u : 0x0000ffffu);
     } else {
       uint32_t hi = w;
 #pragma unroll
       for (int k = 0; k < 8; ++k) hi &= hi - 1;
-      m = (j & 1) ? hi : w;
+      return (j & 1) ? hi : w;
     }
+  };
+  auto scatter = [&](uint32_t tile, u32x4_t v, uint32_t w) {
+    uint32_t m = chunk_bits(w);
     const uint32_t row = tile + (uint32_t)(n * kMTileRow);
     lds_st<u32x4_t>(row + 32 * j, (u32x4_t){0u, 0u, 0u, 0u});
     lds_st<u32x4_t>(row + 32 * j + 16, (u32x4_t){0u, 0u, 0u, 0u});
@@ -834,11 +838,64 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t) acc = dmfma<BF>(tile_a(tile, t), x_of(sl, s, t), acc);
   };
+  // Kept-column product of the block in slot sl, the decompressing kinds'
+  // fallback.  The tile product multiplies the zeros stored at pruned
+  // entries with x, so Inf or NaN in x at a column that some row of the tile
+  // pruned makes the block's sums NaN, while the product sums kept weights
+  // only (Method, item (1)).  Here lane (j, n) walks the 8 kept values of
+  // chunk 4 s + j of row n (the columns scatter would write) against every
+  // token's x in the block, in fp32 (16-bit products are exact); the four
+  // lanes of a row are added, and the row sums reach the output layout
+  // (rows 4 j .. 4 j + 3, token n) through the wave's tile.
+  auto exact_block = [&](uint32_t sl, int ns) -> f4v_t {
+    float p[BP];
+#pragma unroll
+    for (int t = 0; t < BP; ++t) p[t] = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const u32x4_t v = chunk_of(sl, s);
+      uint32_t m = chunk_bits(word_of(sl, s));
+      const int cb = 64 * s + 32 * (j >> 1);  // block column of the word's bit 0
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = cb + (ffbl_hw(m) & 31);  // an exhausted (malformed) word repeats column 31
+        m &= m - 1;
+        const float w = half_to_f32<BF>((uint16_t)(v[k >> 1] >> (16 * (k & 1))));
+#pragma unroll
+        for (int t = 0; t < BP; ++t) {
+          const uint32_t xa = sl + kMValBytes + kMMaskBytes + t * kMXTok +
+                              16 * ((c >> 3) ^ (t & 7)) + 2 * (c & 7);
+          p[t] = fmaf(w, half_to_f32<BF>(ld<uint16_t>((lds_ptr)(size_t)xa)), p[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < BP; ++t) {
+      p[t] += __shfl_xor(p[t], 16);
+      p[t] += __shfl_xor(p[t], 32);
+    }
+    // the tile's last reads (the block's products) precede these writes:
+    // one wave's LDS operations complete in order
+    if (j == 0) {
+#pragma unroll
+      for (int t = 0; t < BP; ++t) lds_st<float>(tile + 4 * (n * BP + t), p[t]);
+    }
+    f4v_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = ld<float>((lds_ptr)(size_t)(tile + 4 * ((4 * j + i) * BP + tn)));
+    return r;
+  };
   auto compute = [&](int b) {
     const uint32_t sl = ring + (uint32_t)((b % NB) * SLOT);
     const int ns = min(4, mysteps - 4 * b);
     if constexpr (KIND != kMfmaSparse24) {
+      // the block's tile product from zero; a NaN in it means Inf or NaN in
+      // the block's x, and the block is summed again over kept columns only
+      const f4v_t prev = acc;
+      acc = (f4v_t){0.f, 0.f, 0.f, 0.f};
       for (int s = 0; s < ns; ++s) dense_step(sl, s);
+      const bool nan = acc[0] != acc[0] || acc[1] != acc[1] || acc[2] != acc[2] || acc[3] != acc[3];
+      if (__builtin_amdgcn_ballot_w64(nan) != 0) acc = exact_block(sl, ns);
+      acc += prev;
     } else if (ns == 4) {  // whole block: every LDS read is issued before the first product
       MfmaOps o[4];
 #pragma unroll
@@ -1296,13 +1353,16 @@ constexpr int kDenseMfmaMinBatch = 5;  // measured: the VALU kernel wins at batc
 int rows_batch_chunks(int64_t cols, int bp);
 
 // pair: the rows come in (gate, up) pairs for the SwiGLU epilogue, so a
-// wave of the row kernel must own an even number of rows.
+// wave of the row kernel must own an even number of rows.  allow_mfma =
+// false gives the VALU kernels' shape for the pattern (a caller that forces
+// NM_KERNEL_VALU), with the same pattern-specific launch rules as the
+// automatic choice.
 nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool dense,
-                      nm_launch_cfg *cfg, bool pair = false) {
+                      nm_launch_cfg *cfg, bool pair = false, bool allow_mfma = true) {
   DevInfo di;
   nm_status st = device_info(&di);
   if (st != NM_OK) return st;
-  if (!dense && mfma_ok(rows, cols, n, m) &&
+  if (allow_mfma && !dense && mfma_ok(rows, cols, n, m) &&
       batch >= (mfma_kind(n, m) == kMfmaSparse24 ? kMfmaMinBatch : kDenseMfmaMinBatch)) {
     mfma_default(rows, cols, batch, mfma_kind(n, m), di, cfg);
     return NM_OK;
@@ -1408,7 +1468,7 @@ nm_status resolve_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
   if (user && user->kernel == NM_KERNEL_MFMA && !dense && mfma_ok(rows, cols, n, m))
     mfma_default(rows, cols, batch, mfma_kind(n, m), di, out);
   else if (user && user->kernel == NM_KERNEL_VALU)
-    st = default_cfg(rows, cols, batch, 0, 0, dense, out, pair);  // no pattern: never picks MFMA
+    st = default_cfg(rows, cols, batch, n, m, dense, out, pair, false);
   else
     st = default_cfg(rows, cols, batch, n, m, dense, out, pair);
   if (st != NM_OK) return st;
@@ -1597,6 +1657,26 @@ mfma_fn pick_mfma(bool bf, int kind, int bp, int nb) {
   return bf ? pick_mfma_kind<true>(kind, bp, nb) : pick_mfma_kind<false>(kind, bp, nb);
 }
 
+// The launch shape of a sparse product with the caller's overrides (user may
+// be NULL), checked: the 50% patterns through resolve_cfg, the other
+// densities through the generic kernels' rules.
+nm_status resolve_sparse(int64_t rows, int64_t cols, int batch, int n, int m,
+                         const nm_launch_cfg *user, nm_launch_cfg *cfg, bool pair) {
+  if (pattern_ok(n, m)) return resolve_cfg(rows, cols, batch, n, m, false, user, cfg, pair);
+  DevInfo di;
+  nm_status st = device_info(&di);
+  if (st != NM_OK) return st;
+  st = generic_default_cfg(rows, cols, batch, n, m, di.cus, lds_budget(di), cfg);
+  if (st != NM_OK) return st;
+  if (user) {
+    if (user->kernel) cfg->kernel = user->kernel;
+    if (user->threads_per_wg) cfg->threads_per_wg = user->threads_per_wg;
+    if (user->rows_per_wave) cfg->rows_per_wave = user->rows_per_wave;
+    if (user->seg_cols) cfg->seg_cols = user->seg_cols;
+  }
+  return generic_check_cfg(*cfg, batch, n, m, lds_budget(di));
+}
+
 // epi: kEpiNone, or kEpiSwiglu (rows are (gate, up) pairs, Y has rows / 2
 // columns per token).
 int sparse_product(const void *values, const uint32_t *bits, const void *X,
@@ -1616,25 +1696,11 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     return NM_ERR_ALIGN;
   if (rows == 0) return NM_OK;
   nm_launch_cfg cfg;
-  if (!pattern_ok(n, m)) {  // densities other than 50%: the generic kernel
-    DevInfo di;
-    st = device_info(&di);
-    if (st != NM_OK) return st;
-    st = generic_default_cfg(rows, cols, batch, n, m, di.cus, lds_budget(di), &cfg);
-    if (st != NM_OK) return st;
-    if (user) {
-      if (user->kernel) cfg.kernel = user->kernel;
-      if (user->threads_per_wg) cfg.threads_per_wg = user->threads_per_wg;
-      if (user->rows_per_wave) cfg.rows_per_wave = user->rows_per_wave;
-      if (user->seg_cols) cfg.seg_cols = user->seg_cols;
-    }
-    st = generic_check_cfg(cfg, batch, n, m, lds_budget(di));
-    if (st != NM_OK) return st;
-    return generic_launch(values, bits, X, Y, batch, rows, cols, n, m, in_dt, out_dt, cfg, stream);
-  }
   const bool pair = epi == kEpiSwiglu;
-  st = resolve_cfg(rows, cols, batch, n, m, false, user, &cfg, pair);
+  st = resolve_sparse(rows, cols, batch, n, m, user, &cfg, pair);
   if (st != NM_OK) return st;
+  if (!pattern_ok(n, m))  // densities other than 50%: the generic kernels
+    return generic_launch(values, bits, X, Y, batch, rows, cols, n, m, in_dt, out_dt, cfg, stream);
   if (pair && cfg.kernel != NM_KERNEL_MFMA) {
     // the epilogue lives in the row kernel: each wave an even number of rows
     if (!rows_kernel(false, cols, cfg.seg_cols)) return NM_ERR_UNSUPPORTED;
@@ -1806,6 +1872,16 @@ int nm_default_launch(int64_t rows, int64_t cols, int batch, int n, int m, int d
     return generic_default_cfg(rows, cols, batch, n, m, di.cus, lds_budget(di), cfg);
   }
   return default_cfg(rows, cols, batch, n, m, dense != 0, cfg);
+}
+
+int nm_resolve_launch(int64_t rows, int64_t cols, int batch, int n, int m, int dense,
+                      const nm_launch_cfg *user, nm_launch_cfg *cfg) {
+  if (!cfg) return NM_ERR_INVALID_ARG;
+  nm_status st = check_dims(rows, cols, batch);
+  if (st != NM_OK) return st;
+  if (dense) return resolve_cfg(rows, cols, batch, 0, 0, true, user, cfg);
+  if (!pattern_any_ok(n, m)) return NM_ERR_UNSUPPORTED;
+  return resolve_sparse(rows, cols, batch, n, m, user, cfg, false);
 }
 
 int nm_dense_gemv_cfg(const void *W, const void *X, void *Y, int batch,

@@ -106,6 +106,9 @@ def lib():
     L.nm_dense_gemv_cfg.restype = ci
     L.nm_default_launch.argtypes = [i64, i64, ci, ci, ci, ci, ctypes.POINTER(LaunchCfg)]
     L.nm_default_launch.restype = ci
+    L.nm_resolve_launch.argtypes = [i64, i64, ci, ci, ci, ci, ctypes.POINTER(LaunchCfg),
+                                    ctypes.POINTER(LaunchCfg)]
+    L.nm_resolve_launch.restype = ci
     L.nm_bitmask_offsets.argtypes = [p, i64, i64, p, ctypes.POINTER(i64), p]
     L.nm_bitmask_offsets.restype = ci
     L.nm_pack_bitmask.argtypes = [p, p, i64, i64, ci, p, p, p, p]
@@ -368,6 +371,15 @@ def nm_default_launch(rows: int, cols: int, batch: int, n: int = 2, m: int = 4,
     c = LaunchCfg()
     _check(lib().nm_default_launch(rows, cols, batch, n, m, int(bool(dense)), ctypes.byref(c)),
            "nm_default_launch")
+    return c
+
+
+def nm_resolve_launch(rows: int, cols: int, batch: int, n: int = 2, m: int = 4,
+                      dense: bool = False, cfg: Optional[LaunchCfg] = None) -> LaunchCfg:
+    """The launch shape a _cfg call with overrides cfg would use."""
+    c = LaunchCfg()
+    _check(lib().nm_resolve_launch(rows, cols, batch, n, m, int(bool(dense)), _cfg_ptr(cfg),
+                                   ctypes.byref(c)), "nm_resolve_launch")
     return c
 
 

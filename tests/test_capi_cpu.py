@@ -183,6 +183,10 @@ def test_prefill_rejects_bad_arguments(L):
     assert pf(cols=96) == SHAPE
     assert pf(rows=1 << 20, cols=1 << 12) == INV  # rows * cols > INT32_MAX
     assert pf(batch=1 << 20, cols=1 << 11) == INV  # batch * cols * 2 > INT32_MAX
+    # sizes whose products wrap int64 are rejected before any multiplication
+    assert pf(rows=(1 << 35) + 3, cols=1 << 29) == INV
+    assert pf(batch=(1 << 40) + 1, cols=1 << 24) == INV
+    assert pf(batch=1, rows=1, cols=(1 << 40)) == INV
     assert pf(y=None) == INV
     assert pf(v=None) == INV
     assert pf(x=P + 8) == ALIGN

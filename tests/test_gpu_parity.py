@@ -473,6 +473,30 @@ def test_default_launch_shapes_follow_the_measured_rules():
     assert shape(14336, 4096, 8, 1, 4) == (256, 7, 4096)
 
 
+def test_forced_valu_shape_equals_the_automatic_valu_shape():
+    """Forcing NM_KERNEL_VALU keeps the pattern's own launch rules: where the
+    library's choice is already the VALU kernel (batch 1) the forced shape is
+    the same, e.g. 2:4 at K = 14336 keeps one row per wave; at batch 2..8 a
+    forced VALU launch gets the VALU shape of that pattern and batch."""
+    V = native.LaunchCfg(0, 0, 0, VALU)
+    for rows, cols in [(14336, 4096), (4096, 14336), (4096, 4096), (1024, 4096), (6144, 4096),
+                       (8192, 8192), (28672, 8192), (5120, 25600), (96, 2112)]:
+        for n, m in PATTERNS + [(1, 4), (3, 4), (3, 8)]:
+            auto = native.nm_default_launch(rows, cols, 1, n, m)
+            forced = native.nm_resolve_launch(rows, cols, 1, n, m, cfg=V)
+            assert auto.kernel == VALU
+            assert (forced.kernel, forced.threads_per_wg, forced.rows_per_wave, forced.seg_cols) == \
+                (auto.kernel, auto.threads_per_wg, auto.rows_per_wave, auto.seg_cols), (rows, cols, n, m)
+        for batch in (2, 4, 8):
+            forced = native.nm_resolve_launch(rows, cols, batch, 2, 4, cfg=V)
+            assert forced.kernel == VALU
+    # no override: the resolved shape is the default one
+    for b in (1, 2, 5, 8):
+        a, r = native.nm_default_launch(4096, 4096, b, 4, 8), native.nm_resolve_launch(4096, 4096, b, 4, 8)
+        assert (a.kernel, a.threads_per_wg, a.rows_per_wave, a.seg_cols) == \
+            (r.kernel, r.threads_per_wg, r.rows_per_wave, r.seg_cols)
+
+
 def test_zero_columns_give_zero_output_batch():
     for batch in (1, 2, 8):
         values = torch.empty((7, 0), dtype=torch.float16, device=DEV)
