@@ -125,6 +125,21 @@ int nm_pack(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
             int n, int m, nm_dtype dt, void *values, uint32_t *bits,
             void *stream);
 
+/* nm_pack for callers that cannot allocate device memory (code under HIP
+ * graph capture elsewhere in the process, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, checks, output and status as
+ * nm_pack, but the invalid-group counter lives in a 256-byte device array of
+ * the library (one per GPU, looked up on the first call on that device and
+ * held until the process ends) instead of a per-call hipMalloc / hipFree.
+ * The counter does not grow with the matrix, so any size nm_pack accepts is
+ * accepted (rows or cols above INT32_MAX give NM_ERR_INVALID_ARG, as there).
+ * Calls on one GPU share that counter: the library serialises them within
+ * the process (the call is synchronous, like nm_pack), and the counter is
+ * cleared by a kernel on `stream` at the start of every call. */
+int nm_pack_noalloc(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
+                    int n, int m, nm_dtype dt, void *values, uint32_t *bits,
+                    void *stream);
+
 /* Batch-1 sparse matrix-vector product (Method, kernel subsection; the
  * decoding-specialised N:M SpMV):
  *   y[r] = sum over kept columns c of row r of W[r][c] * x[c],  r < rows.

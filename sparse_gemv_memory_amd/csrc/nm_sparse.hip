@@ -39,6 +39,13 @@
 #include "nm_device.h"
 #include "nm_host.h"
 
+// Scratch of the allocation-free pack (nm_pack_noalloc): element 0 counts
+// the invalid groups of the running call.  256 bytes per device, held until
+// the process ends.  Host code must use the per-device address from
+// hipGetSymbolAddress, never this name.
+constexpr int kPackScratchInts = 64;
+static __device__ __align__(256) int scratch[kPackScratchInts];
+
 namespace nm_host {
 
 thread_local int g_last_hip = 0;
@@ -1216,6 +1223,12 @@ __global__ __launch_bounds__(1024) void nm_stream_read_kernel(const char *__rest
   if (lane == 0) out[wave] = (uint32_t)sv;
 }
 
+// Zero n ints of p (one workgroup): the scratch counter is cleared by a
+// kernel on the call's stream rather than a memset node.
+__global__ __launch_bounds__(64) void nm_zero_ints_kernel(int *__restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 // ---------------------------------------------------------------------------
 // host side
 
@@ -1749,6 +1762,70 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
   return e == hipSuccess ? NM_OK : hip_fail(e);
 }
 
+// Argument checks of the pack entry points (nothing here touches HIP);
+// *empty: there is nothing to pack.
+nm_status pack_check(const void *W, const uint8_t *keep, int64_t rows, int64_t cols, int n, int m,
+                     nm_dtype dt, const void *values, const uint32_t *bits, bool *empty) {
+  if (rows < 0 || cols < 0) return NM_ERR_INVALID_ARG;
+  if (rows > INT32_MAX || cols > INT32_MAX) return NM_ERR_INVALID_ARG;
+  if (!pattern_any_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
+  if (cols % 32 != 0) return NM_ERR_SHAPE;
+  *empty = rows == 0 || cols == 0;
+  if (!*empty && (!W || !keep || !values || !bits)) return NM_ERR_INVALID_ARG;
+  if (!aligned(W, 2) || !aligned(values, 16) || !aligned(bits, 4)) return NM_ERR_ALIGN;
+  return NM_OK;
+}
+
+// The pack kernel for pattern n:m on stream s; invalid groups are counted
+// into *dbad (device), which the caller has cleared.
+hipError_t pack_launch(const void *W, const uint8_t *keep, int64_t rows, int64_t cols, int n, int m,
+                       void *values, uint32_t *bits, int *dbad, hipStream_t s) {
+  const int threads = 256, wpg = threads / kWave;
+  int64_t grid = (rows + wpg - 1) / wpg;
+  if (grid > (1 << 20)) grid = 1 << 20;
+  const int K = (int)cols;
+  const uint16_t *w16 = (const uint16_t *)W;
+  uint16_t *v16 = (uint16_t *)values;
+  switch (m) {
+    case 4: hipLaunchKernelGGL(nm_pack_kernel<4>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
+    case 8: hipLaunchKernelGGL(nm_pack_kernel<8>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
+    case 16: hipLaunchKernelGGL(nm_pack_kernel<16>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
+    default: hipLaunchKernelGGL(nm_pack_kernel<32>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
+  }
+  return hipGetLastError();
+}
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU holds its own copy of the array
+// at its own address; the array's name in host code is only a stand-in), and
+// the lock that serialises the allocation-free calls on that device.
+struct ScratchDev {
+  bool init = false;
+  int *ptr = nullptr;
+  std::mutex mu;
+};
+ScratchDev g_scratch[kMaxDev];
+std::mutex g_scratch_mu;
+
+nm_status scratch_of_device(int **ptr, std::mutex **mu) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDev) return NM_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  ScratchDev &d = g_scratch[dev];
+  if (!d.init) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    d.ptr = static_cast<int *>(p);
+    d.init = true;
+  }
+  *ptr = d.ptr;
+  *mu = &d.mu;
+  return NM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1785,40 +1862,47 @@ int nm_packed_bytes(int64_t rows, int64_t cols, int n, int m, nm_dtype dt,
 int nm_pack(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
             int n, int m, nm_dtype dt, void *values, uint32_t *bits,
             void *stream) {
-  if (rows < 0 || cols < 0) return NM_ERR_INVALID_ARG;
-  if (rows > INT32_MAX || cols > INT32_MAX) return NM_ERR_INVALID_ARG;
-  if (!pattern_any_ok(n, m) || !is16(dt)) return NM_ERR_UNSUPPORTED;
-  if (cols % 32 != 0) return NM_ERR_SHAPE;
-  const bool empty = rows == 0 || cols == 0;
-  if (!empty && (!W || !keep || !values || !bits)) return NM_ERR_INVALID_ARG;
-  if (!aligned(W, 2) || !aligned(values, 16) || !aligned(bits, 4)) return NM_ERR_ALIGN;
-  if (empty) return NM_OK;
+  bool empty = false;
+  nm_status st = pack_check(W, keep, rows, cols, n, m, dt, values, bits, &empty);
+  if (st != NM_OK || empty) return st;
   hipStream_t s = (hipStream_t)stream;
   int *dbad = nullptr;
   hipError_t e = hipMalloc((void **)&dbad, sizeof(int));
   if (e != hipSuccess) return hip_fail(e);
   int hbad = 0;
   e = hipMemsetAsync(dbad, 0, sizeof(int), s);
-  if (e == hipSuccess) {
-    const int threads = 256, wpg = threads / kWave;
-    int64_t grid = (rows + wpg - 1) / wpg;
-    if (grid > (1 << 20)) grid = 1 << 20;
-    const int K = (int)cols;
-    const uint16_t *w16 = (const uint16_t *)W;
-    uint16_t *v16 = (uint16_t *)values;
-    switch (m) {
-      case 4: hipLaunchKernelGGL(nm_pack_kernel<4>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
-      case 8: hipLaunchKernelGGL(nm_pack_kernel<8>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
-      case 16: hipLaunchKernelGGL(nm_pack_kernel<16>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
-      default: hipLaunchKernelGGL(nm_pack_kernel<32>, dim3((unsigned)grid), dim3(threads), 0, s, w16, keep, rows, K, n, v16, bits, dbad); break;
-    }
-    e = hipGetLastError();
-  }
+  if (e == hipSuccess) e = pack_launch(W, keep, rows, cols, n, m, values, bits, dbad, s);
   if (e == hipSuccess) e = hipMemcpyAsync(&hbad, dbad, sizeof(int), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   hipError_t ef = hipFree(dbad);
   if (e != hipSuccess) return hip_fail(e);
   if (ef != hipSuccess) return hip_fail(ef);
+  return hbad ? NM_ERR_MASK : NM_OK;
+}
+
+int nm_pack_noalloc(const void *W, const uint8_t *keep, int64_t rows, int64_t cols,
+                    int n, int m, nm_dtype dt, void *values, uint32_t *bits,
+                    void *stream) {
+  bool empty = false;
+  nm_status st = pack_check(W, keep, rows, cols, n, m, dt, values, bits, &empty);
+  if (st != NM_OK || empty) return st;
+  int *dbad = nullptr;
+  std::mutex *mu = nullptr;
+  st = scratch_of_device(&dbad, &mu);
+  if (st != NM_OK) return st;
+  // one call at a time per device in this process: the calls share the
+  // device's counter, and the call is synchronous
+  std::lock_guard<std::mutex> g(*mu);
+  hipStream_t s = (hipStream_t)stream;
+  int hbad = 0;
+  // the counter keeps the previous call's count: cleared by a one-thread
+  // kernel on the call's stream, ordered before the pack
+  hipLaunchKernelGGL(nm_zero_ints_kernel, dim3(1), dim3(kWave), 0, s, dbad, kPackScratchInts);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = pack_launch(W, keep, rows, cols, n, m, values, bits, dbad, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&hbad, dbad, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
   return hbad ? NM_ERR_MASK : NM_OK;
 }
 

@@ -82,6 +82,8 @@ def lib():
     L.nm_packed_bytes.restype = ci
     L.nm_pack.argtypes = [p, p, i64, i64, ci, ci, ci, p, p, p]
     L.nm_pack.restype = ci
+    L.nm_pack_noalloc.argtypes = [p, p, i64, i64, ci, ci, ci, p, p, p]
+    L.nm_pack_noalloc.restype = ci
     L.nm_spmv.argtypes = [p, p, p, p, i64, i64, ci, ci, ci, ci, p]
     L.nm_spmv.restype = ci
     L.nm_spmm_small.argtypes = [p, p, p, p, ci, i64, i64, ci, ci, ci, ci, p]
@@ -182,6 +184,27 @@ def nm_pack(W: torch.Tensor, keep: torch.Tensor, n: int, m: int):
         st = lib().nm_pack(_dev(W, "W"), _dev(keep, "keep"), rows, cols, n, m, dt,
                            _dev(values, "values"), _dev(bits, "bits"), _stream(W.device))
     _check(st, "nm_pack")
+    return values, bits
+
+
+def nm_pack_noalloc(W: torch.Tensor, keep: torch.Tensor, n: int, m: int, values: torch.Tensor,
+                    bits: torch.Tensor):
+    """nm_pack into caller-provided values and bits (as nm_pack returns
+    them), with the library's static device counter instead of a per-call
+    allocation."""
+    if W.dim() != 2 or keep.shape != W.shape:
+        raise ValueError("W must be 2-D and keep must have its shape")
+    if keep.dtype not in (torch.uint8, torch.bool, torch.int8):
+        raise TypeError("keep must be uint8, int8 or bool")
+    rows, cols = W.shape
+    if values.dtype != W.dtype or bits.dtype != torch.int32 or \
+            values.numel() * 2 < _padded_elems(rows, cols, n, m, W.dtype) * 2 or \
+            bits.numel() * 32 < rows * cols:
+        raise ValueError("values / bits too small or of the wrong dtype")
+    with torch.cuda.device(W.device):
+        st = lib().nm_pack_noalloc(_dev(W, "W"), _dev(keep, "keep"), rows, cols, n, m, _in_dt(W),
+                                   _dev(values, "values"), _dev(bits, "bits"), _stream(W.device))
+    _check(st, "nm_pack_noalloc")
     return values, bits
 
 
