@@ -275,12 +275,23 @@ typedef enum { NM_KERNEL_AUTO = 0, NM_KERNEL_VALU = 1, NM_KERNEL_MFMA = 2 } nm_k
  *                   columns (waves x (depth x block bytes + tile bytes)
  *                   must fit the LDS, else NM_ERR_INVALID_ARG);
  *   seg_cols:       ignored.
- * kernel: an nm_kernel (0 = the library's choice). */
+ * kernel: an nm_kernel (0 = the library's choice).
+ * k_split: 0 = the library's choice, 1 = each row reduced by one wavefront,
+ *   2 or 4 = the split reduction (Appendix C splits a row's reduction over
+ *   several programs for shapes with few rows): k_split consecutive waves of
+ *   a workgroup share each group of rows_per_wave rows, wave s taking the
+ *   row's load batches s, s + k_split, ...; their partial row sums are added
+ *   in a fixed order (wave 0, 1, ...) through LDS, so results are
+ *   deterministic.  Only for the VALU kernel at batch 1 with 2:4, all of x in
+ *   LDS (seg_cols >= cols), cols % (1024 * k_split) == 0, threads_per_wg / 64
+ *   a multiple of k_split and no SwiGLU epilogue; elsewhere k_split > 1 gives
+ *   NM_ERR_UNSUPPORTED, and values other than 0, 1, 2, 4 NM_ERR_INVALID_ARG. */
 typedef struct {
   int threads_per_wg;
   int rows_per_wave;
   int seg_cols;
   int kernel;
+  int k_split;
 } nm_launch_cfg;
 
 /* The launch shape nm_spmm_small (pattern n:m) or nm_dense_gemv (dense != 0;

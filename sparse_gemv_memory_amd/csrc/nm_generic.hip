@@ -716,6 +716,7 @@ nm_status generic_default_cfg(int64_t rows, int64_t cols, int batch, int n, int 
                               size_t lds_budget, nm_launch_cfg *cfg) {
   const int p = 32 * n / m, ni = win_loads(p), bp = pad_b(batch);
   cfg->kernel = NM_KERNEL_VALU;
+  cfg->k_split = 1;
   if (direct_p(p)) {
     // x in as few equal segments as fit the budget.  Workgroups of 4 waves,
     // about two per CU, unless only one x image fits a CU's LDS or there are

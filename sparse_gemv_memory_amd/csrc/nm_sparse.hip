@@ -91,6 +91,12 @@ struct XLay {
   }
 };
 
+// Byte offset of the split reduction's partial sums in the batch-1 row
+// kernel's LDS: after the x image, 16-byte aligned.
+__host__ __device__ constexpr size_t split_lds_offset(int K) {
+  return (XLay<1>::bytes(K) + 15) / 16 * 16;
+}
+
 // Staging of x into the XLay<BP> layout, one 8-column group at a time: the
 // group's 16-byte chunk of each batch row is loaded, and for BP > 1 the
 // chunks are transposed in registers into 8 column slots of BP values.
@@ -477,7 +483,7 @@ __device__ __forceinline__ void collect_row(float (&acc)[BP], float (&res)[BP], 
 // in flight while item k is consumed.  U is chosen per shape so that it
 // divides the row's chunks per lane (no idle load slots in the last batch).  The first item's loads are issued
 // before x is committed to LDS, so the x and weight latencies overlap.
-template <bool BF, int BP, int PK, int U, int XS>
+template <bool BF, int BP, int PK, int U, int XS, int KS = 1>
 __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
     const uint4 *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int rpw,
@@ -485,6 +491,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   // XS: x groups per thread held in registers before the weight loads (the
   // host picks enough for all of x where it can: a group left to the staging
   // loop below waits for every outstanding load, the weights' included)
+  // KS: waves per row group (the split reduction; 1 = one wave per row)
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wpg = blockDim.x / kWave;
@@ -493,11 +500,17 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   // wave index as a wave-uniform (scalar) value: the item loop below is then
   // scalar control flow and the wait counts of the pipeline stay exact
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t r0 = ((int64_t)blockIdx.x * wpg + wid) * rpw;
+  // row group of the wave and its place in the group: with KS > 1 the KS
+  // waves of a group share its rows, wave `sub` taking the load batches
+  // sub, sub + KS, ... of each row (KS divides nb; exact kinds only)
+  const int grp = wid / KS, sub = wid - grp * KS;
+  const int nbs = nb / KS;                               // this wave's batches per row
+  const int64_t r0 = ((int64_t)blockIdx.x * (wpg / KS) + grp) * rpw;
   const int64_t left = R - r0;
   const int nrows = left <= 0 ? 0 : (left < rpw ? (int)left : rpw);
-  const int nitems = nrows * nb;
+  const int nitems = nrows * nbs;
   const int64_t cpr = nch, wpr = K >> 5;
+  static_assert(KS == 1 || PK == kPat24xE, "the split reduction is built for the exact 2:4 kind");
 
   float acc[BP];
 #pragma unroll
@@ -528,7 +541,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   // an item past the wave's last is a dummy load (no memory traffic)
   auto item_load = [&](Batch<U> &bt, int k) {
     const bool real = k < nitems;
-    const int ii = real ? k / nb : 0, tt = real ? k - ii * nb : 0;
+    const int ii = real ? k / nbs : 0, tt = real ? sub + KS * (k - ii * nbs) : 0;
     const int64_t r = real ? r0 + ii : 0;
     load_batch<U, plain_x(PK)>(bt, values + r * cpr, bits + r * wpr, real ? nch : 0, tt, lane);
   };
@@ -556,15 +569,30 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   for (int b = 0; b < BP; ++b) res[b] = 0.f;
   // two-buffer pipeline: while one batch is consumed the other is in flight
   for (int k = 0; k < nitems; k += 2) {
-    const int i = k / nb, t = k - i * nb;
+    const int i = k / nbs, j = k - i * nbs, t = sub + KS * j;
     run_batch<BF, BP, PK, U>(lds, A, t * kWave * U + lane, nch, acc, t * kWave * U);
-    if (t == nb - 1) collect_row<BP>(acc, res, i, lane);
+    if (j == nbs - 1) collect_row<BP>(acc, res, i, lane);
     item_load(A, k + 2);
     if (k + 1 >= nitems) break;
-    const int i1 = (k + 1) / nb, t1 = (k + 1) - i1 * nb;
+    const int i1 = (k + 1) / nbs, j1 = (k + 1) - i1 * nbs, t1 = sub + KS * j1;
     run_batch<BF, BP, PK, U>(lds, Bt, t1 * kWave * U + lane, nch, acc, t1 * kWave * U);
-    if (t1 == nb - 1) collect_row<BP>(acc, res, i1, lane);
+    if (j1 == nbs - 1) collect_row<BP>(acc, res, i1, lane);
     item_load(Bt, k + 3);
+  }
+  if constexpr (KS > 1) {
+    // the split reduction: each wave's partial row sums (lane i: row i of the
+    // group) meet in LDS after the x image; the group's first wave adds them
+    // in wave order and stores the rows
+    float *part = reinterpret_cast<float *>(lds + split_lds_offset(K));
+    if (lane < rpw) part[wid * rpw + lane] = res[0];
+    __syncthreads();
+    if (sub == 0 && lane < nrows) {
+      float sum = part[grp * KS * rpw + lane];
+#pragma unroll
+      for (int w = 1; w < KS; ++w) sum += part[(grp * KS + w) * rpw + lane];
+      store_out(y, r0 + lane, sum, out_kind);
+    }
+    return;
   }
   if (swiglu) {
     // the wave's rows come in (gate, up) pairs at even offsets: lane 2p
@@ -1303,6 +1331,18 @@ size_t lds_budget(const DevInfo &di) {
   return di.lds_per_wg < kLdsCap ? di.lds_per_wg : kLdsCap;
 }
 
+// Chunks per lane per load batch of a split launch: the largest of 4, 5, 2, 1
+// that divides a wave's share of the row's chunks per lane (K / 1024 / ks).
+int split_batch_chunks(int64_t cols, int ks) {
+  const int64_t c = cols / 1024 / ks;
+  return c % 4 == 0 ? 4 : c % 5 == 0 ? 5 : c % 2 == 0 ? 2 : 1;
+}
+
+// LDS of a split launch: the x image and one partial sum per row per wave.
+size_t split_lds_bytes(int64_t cols, int waves, int rpw) {
+  return split_lds_offset((int)cols) + (size_t)waves * rpw * 4;
+}
+
 // Is this a launch of the single-segment row kernel (all of x in LDS)?
 bool rows_kernel(bool dense, int64_t cols, int seg) {
   (void)dense;
@@ -1353,6 +1393,7 @@ void mfma_default(int64_t rows, int64_t cols, int batch, int kind, const DevInfo
   const int nb = (kind == kMfmaSparse24 && 2 * mfma_lds_bytes(w, 3, bp, kind) <= kLdsCap) ? 3 : 2;
   while (w > 1 && mfma_lds_bytes(w, nb, bp, kind) > budget) --w;
   cfg->kernel = NM_KERNEL_MFMA;
+  cfg->k_split = 1;
   cfg->threads_per_wg = w * kWave;
   cfg->rows_per_wave = nb;
   cfg->seg_cols = cols > 0 ? (int)cols : 64;
@@ -1381,6 +1422,7 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
     return NM_OK;
   }
   cfg->kernel = NM_KERNEL_VALU;
+  cfg->k_split = 1;
   const int bp = pad_batch(batch);
   const size_t budget = lds_budget(di);
   const int smax = max_seg(dense, bp, budget);
@@ -1450,9 +1492,22 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
 }
 
 nm_status check_cfg(const nm_launch_cfg &c, int64_t rows, int64_t cols, int n, int m,
-                    bool dense, int bp, const DevInfo &di) {
+                    bool dense, int bp, const DevInfo &di, bool pair = false) {
   const int t = c.threads_per_wg;
   if (t < kWave || t > 1024 || t % kWave != 0) return NM_ERR_INVALID_ARG;
+  if (!(c.k_split == 0 || c.k_split == 1 || c.k_split == 2 || c.k_split == 4))
+    return NM_ERR_INVALID_ARG;
+  if (c.k_split > 1) {
+    // the split reduction: 2:4 at batch 1 on the VALU row kernel, x whole in
+    // LDS, whole load batches per wave, no epilogue
+    if (dense || c.kernel != NM_KERNEL_VALU || bp != 1 || !(n == 2 && m == 4) || pair ||
+        !rows_kernel(false, cols, c.seg_cols) || cols % (1024LL * c.k_split) != 0 ||
+        (t / kWave) % c.k_split != 0)
+      return NM_ERR_UNSUPPORTED;
+    if (c.rows_per_wave < 1 || c.rows_per_wave > 64) return NM_ERR_INVALID_ARG;
+    if (split_lds_bytes(cols, t / kWave, c.rows_per_wave) > lds_budget(di)) return NM_ERR_INVALID_ARG;
+    return NM_OK;
+  }
   if (c.kernel == NM_KERNEL_MFMA) {
     if (dense || !mfma_ok(rows, cols, n, m)) return NM_ERR_UNSUPPORTED;
     if (c.rows_per_wave < 2 || c.rows_per_wave > 4) return NM_ERR_INVALID_ARG;
@@ -1490,8 +1545,9 @@ nm_status resolve_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
     if (user->threads_per_wg) out->threads_per_wg = user->threads_per_wg;
     if (user->rows_per_wave) out->rows_per_wave = user->rows_per_wave;
     if (user->seg_cols) out->seg_cols = user->seg_cols;
+    if (user->k_split) out->k_split = user->k_split;
   }
-  return check_cfg(*out, rows, cols, n, m, dense, pad_batch(batch), di);
+  return check_cfg(*out, rows, cols, n, m, dense, pad_batch(batch), di, pair);
 }
 
 typedef void (*seg_fn)(const uint4 *, const uint32_t *, const uint16_t *, void *, int,
@@ -1580,6 +1636,29 @@ rows_fn pick_rows_pk(int pk, int bp, int u, int xs, bool exact) {
 rows_fn pick_rows(bool bf, int pk, int bp, int u, int xs, bool exact) {
   return bf ? pick_rows_pk<true>(pk, bp, u, xs, exact) : pick_rows_pk<false>(pk, bp, u, xs, exact);
 }
+
+// The split-reduction kernels (2:4, batch 1, exact kind): KS waves per row
+// group, U chunks per lane per load batch.
+template <bool BF, int KS, int XS>
+rows_fn pick_split_u(int u) {
+  switch (u) {
+    case 1: return nm_spmv_rows_kernel<BF, 1, kPat24xE, 1, XS, KS>;
+    case 2: return nm_spmv_rows_kernel<BF, 1, kPat24xE, 2, XS, KS>;
+    case 5: return nm_spmv_rows_kernel<BF, 1, kPat24xE, 5, XS, KS>;
+    default: return nm_spmv_rows_kernel<BF, 1, kPat24xE, 4, XS, KS>;
+  }
+}
+
+template <bool BF>
+rows_fn pick_split_bf(int ks, int u, int xs) {
+  if (ks == 2) return xs > 4 ? pick_split_u<BF, 2, 8>(u) : pick_split_u<BF, 2, 4>(u);
+  return xs > 4 ? pick_split_u<BF, 4, 8>(u) : pick_split_u<BF, 4, 4>(u);
+}
+
+rows_fn pick_split(bool bf, int ks, int u, int xs) {
+  return bf ? pick_split_bf<true>(ks, u, xs) : pick_split_bf<false>(ks, u, xs);
+}
+
 
 // Chunks per lane per load batch of the batch-1 row kernel: 4, or 5 when
 // that divides the row's chunks per lane (K / 1024) and 4 does not, or 2 when
@@ -1682,6 +1761,9 @@ nm_status resolve_sparse(int64_t rows, int64_t cols, int batch, int n, int m,
   st = generic_default_cfg(rows, cols, batch, n, m, di.cus, lds_budget(di), cfg);
   if (st != NM_OK) return st;
   if (user) {
+    if (!(user->k_split == 0 || user->k_split == 1 || user->k_split == 2 || user->k_split == 4))
+      return NM_ERR_INVALID_ARG;
+    if (user->k_split > 1) return NM_ERR_UNSUPPORTED;  // the split reduction is 2:4 only
     if (user->kernel) cfg->kernel = user->kernel;
     if (user->threads_per_wg) cfg->threads_per_wg = user->threads_per_wg;
     if (user->rows_per_wave) cfg->rows_per_wave = user->rows_per_wave;
@@ -1708,7 +1790,7 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
   if (!aligned(values, 16) || !aligned(bits, 4) || !aligned(X, 16) || !aligned(Y, ysz))
     return NM_ERR_ALIGN;
   if (rows == 0) return NM_OK;
-  nm_launch_cfg cfg;
+  nm_launch_cfg cfg = {};
   const bool pair = epi == kEpiSwiglu;
   st = resolve_sparse(rows, cols, batch, n, m, user, &cfg, pair);
   if (st != NM_OK) return st;
@@ -1737,6 +1819,19 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
   }
   const int pk = pattern_kind(m);
   const int wpg = cfg.threads_per_wg / kWave;
+  if (cfg.k_split > 1) {  // the split reduction (checked by resolve_cfg)
+    const int ks = cfg.k_split;
+    const int64_t rows_per_wg = (int64_t)(wpg / ks) * cfg.rows_per_wave;
+    const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
+    if (grid > INT32_MAX) return NM_ERR_INVALID_ARG;
+    const int xs = (int)((cols / 8 + cfg.threads_per_wg - 1) / cfg.threads_per_wg);
+    hipLaunchKernelGGL(pick_split(bf, ks, split_batch_chunks(cols, ks), xs), dim3((unsigned)grid),
+                       dim3(cfg.threads_per_wg), split_lds_bytes(cols, wpg, cfg.rows_per_wave),
+                       (hipStream_t)stream, (const uint4 *)values, bits, (const uint16_t *)X, Y,
+                       batch, rows, (int)cols, cfg.rows_per_wave, out_kind);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? NM_OK : hip_fail(e);
+  }
   if (rows_kernel(false, cols, cfg.seg_cols)) {
     const int64_t rows_per_wg = (int64_t)wpg * cfg.rows_per_wave;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;
@@ -1980,7 +2075,7 @@ int nm_dense_gemv_cfg(const void *W, const void *X, void *Y, int batch,
   const uintptr_t ysz = out_dt == NM_F32 ? 4 : 2;
   if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, ysz)) return NM_ERR_ALIGN;
   if (rows == 0) return NM_OK;
-  nm_launch_cfg cfg;
+  nm_launch_cfg cfg = {};
   st = resolve_cfg(rows, cols, batch, 0, 0, true, user, &cfg);
   if (st != NM_OK) return st;
   const int bp = pad_batch(batch);

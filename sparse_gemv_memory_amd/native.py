@@ -53,12 +53,12 @@ NM_KERNEL_AUTO, NM_KERNEL_VALU, NM_KERNEL_MFMA = 0, 1, 2
 
 
 class LaunchCfg(ctypes.Structure):
-    """nm_launch_cfg: (threads_per_wg, rows_per_wave, seg_cols, kernel); 0 = library's choice."""
+    """nm_launch_cfg: (threads_per_wg, rows_per_wave, seg_cols, kernel, k_split); 0 = library's choice."""
     _fields_ = [("threads_per_wg", ctypes.c_int), ("rows_per_wave", ctypes.c_int),
-                ("seg_cols", ctypes.c_int), ("kernel", ctypes.c_int)]
+                ("seg_cols", ctypes.c_int), ("kernel", ctypes.c_int), ("k_split", ctypes.c_int)]
 
     def as_tuple(self):
-        return (self.threads_per_wg, self.rows_per_wave, self.seg_cols, self.kernel)
+        return (self.threads_per_wg, self.rows_per_wave, self.seg_cols, self.kernel, self.k_split)
 
 
 _lib = None

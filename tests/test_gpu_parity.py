@@ -891,3 +891,89 @@ def test_prefill_rejects_what_it_cannot_run():
     v, b = gpu_pack(W, keep, 2, 4, "f16")
     with pytest.raises(native.NMError):
         native.nm_spmm_prefill(v, b, t16(X, "f16"))
+
+
+# ---- the split reduction (k_split waves per row group) ----------------------
+
+# K = 1024 c: a wave of a k_split group takes c / k_split chunks per lane per
+# row, in load batches of 1 (2048, 14336), 2 (4096 at 4), 4 (8192 at 2) or
+# 5 (10240 at 2) chunks per lane
+SPLIT_SHAPES = [(96, 2048), (37, 4096), (130, 8192), (1, 4096), (64, 10240), (203, 14336),
+                (50, 20480), (300, 4096)]
+
+
+def _split_cfgs(cols):
+    out = []
+    for ks in (2, 4):
+        if cols % (1024 * ks):
+            continue
+        for waves, rpw in ((ks, 1), (ks, 3), (2 * ks, 2), (4 * ks, 1), (16 // ks * ks, 4)):
+            out.append(native.LaunchCfg(64 * waves, rpw, 0, VALU, ks))
+    return out
+
+
+@pytest.mark.parametrize("rows,cols", SPLIT_SHAPES)
+def test_split_reduction_integer_exact(rows, cols):
+    """2:4 at batch 1 with each row's load batches shared by 2 or 4 waves and
+    their partial sums added through LDS: exact on integer inputs for every
+    split, wave count and rows per wave, ragged row counts included."""
+    W = synth.integer_weights(rows, cols, seed=81)
+    keep = synth.random_mask(rows, cols, 2, 4, seed=82)
+    xi = np.random.default_rng(83).integers(-4, 5, size=(1, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    want = oracle.masked_gemv(W, keep, X, False)
+    cfgs = _split_cfgs(cols)
+    assert cfgs
+    for cfg in cfgs:
+        got = native.nm_resolve_launch(rows, cols, 1, 2, 4, cfg=cfg)
+        assert got.k_split == cfg.k_split
+        y = native.nm_spmv(values, bits, t16(X[0], "f16"), 2, 4, cfg=cfg)
+        assert np.array_equal(f64(y), want[0]), cfg.as_tuple()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("rows,cols", [(203, 14336), (130, 8192), (300, 4096)])
+def test_split_reduction_random(rows, cols, dtype):
+    """Random weights and outlier activations: within rel-L2 1e-3 of the
+    oracle, and the 16-bit output is the split launch's fp32 sum rounded."""
+    W, keep, X = inputs(rows, cols, 2, 4, dtype, 1, seed=91)
+    values, bits = gpu_pack(W, keep, 2, 4, dtype)
+    want = oracle.masked_gemv(W, keep, X, dtype == "bf16")
+    for cfg in _split_cfgs(cols):
+        y = native.nm_spmv(values, bits, t16(X[0], dtype), 2, 4, cfg=cfg)
+        assert rel_l2(f64(y), want[0]) <= TOL, cfg.as_tuple()
+        y16 = native.nm_spmv(values, bits, t16(X[0], dtype), 2, 4, out_dtype=TDT[dtype], cfg=cfg)
+        assert np.array_equal(u16(y16), round16_f64(f64(y), dtype)), cfg.as_tuple()
+
+
+def test_split_reduction_argument_rules():
+    """k_split 2 or 4 only for 2:4 at batch 1 on the VALU row kernel with x
+    whole in LDS, whole load batches per wave and a wave count it divides."""
+    L = native.lib()
+    c = native.LaunchCfg()
+
+    def res(rows, cols, batch, n, m, cfg, dense=0):
+        return L.nm_resolve_launch(rows, cols, batch, n, m, dense, ctypes.byref(cfg), ctypes.byref(c))
+
+    ok = native.LaunchCfg(256, 2, 0, VALU, 2)
+    assert res(512, 4096, 1, 2, 4, ok) == native.NM_OK and c.k_split == 2
+    assert res(512, 4096, 1, 2, 4, native.LaunchCfg(256, 2, 0, VALU, 4)) == native.NM_OK
+    assert res(512, 4096, 1, 2, 4, native.LaunchCfg(256, 2, 0, VALU, 3)) == native.NM_ERR_INVALID_ARG
+    assert res(512, 4096, 1, 2, 4, native.LaunchCfg(256, 2, 0, VALU, -1)) == native.NM_ERR_INVALID_ARG
+    assert res(512, 4096, 4, 2, 4, ok) == native.NM_ERR_UNSUPPORTED  # batch 4
+    assert res(512, 4096, 1, 4, 8, ok) == native.NM_ERR_UNSUPPORTED  # 4:8
+    assert res(512, 4096, 1, 1, 4, ok) == native.NM_ERR_UNSUPPORTED  # 1:4
+    assert res(512, 3072, 1, 2, 4, native.LaunchCfg(256, 2, 0, VALU, 4)) == native.NM_ERR_UNSUPPORTED
+    assert res(512, 4096, 1, 2, 4, native.LaunchCfg(192, 2, 0, VALU, 2)) == native.NM_ERR_UNSUPPORTED
+    assert res(512, 4096, 1, 2, 4, native.LaunchCfg(256, 2, 1024, VALU, 2)) == native.NM_ERR_UNSUPPORTED
+    assert res(512, 4096, 1, 2, 4, native.LaunchCfg(256, 2, 0, MFMA, 2)) == native.NM_ERR_UNSUPPORTED
+    assert res(512, 4096, 1, 0, 0, ok, dense=1) == native.NM_ERR_UNSUPPORTED
+    # the SwiGLU epilogue has no split form
+    W = synth.weights(64, 2048, seed=3)
+    keep = synth.topn_mask(W, 2, 4)
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    X = t16(synth.activations(1, 2048, seed=3), "f16")
+    with pytest.raises(native.NMError) as e:
+        native.nm_spmm_swiglu(values, bits, X, 2, 4, cfg=native.LaunchCfg(128, 2, 0, VALU, 2))
+    assert e.value.status == native.NM_ERR_UNSUPPORTED
