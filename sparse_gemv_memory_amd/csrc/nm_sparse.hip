@@ -314,6 +314,33 @@ __device__ __forceinline__ void chunk24x_ops(int q, uint32_t mw, const uint4 v, 
   }
 }
 
+// chunk24x_ops for BP tokens whose x rows are stored plainly one after
+// another in LDS (token b's columns at b * xrow): the nibble selectors are
+// computed once and cut every token's pair operand out of its own 32 bytes.
+template <bool BF, int BP>
+__device__ __forceinline__ void chunk24x_multi(const char *lds, int xrow, int q, uint32_t mw,
+                                               const uint4 v, float (&acc)[BP]) {
+  const uint32_t m = (mw >> ((q & 1) << 4)) & 0xffffu;
+  const uint32_t t = m >> 1;
+  const uint32_t S = (t & 0x0707u) | (((t >> 4) & 0x0707u) << 16);
+  const uint32_t P0 = __builtin_amdgcn_perm(kPos0Hi, kPos0Lo, S);
+  const uint32_t P1 = __builtin_amdgcn_perm(kPos1Hi, kPos1Lo, S);
+  const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  constexpr uint32_t kPick[4] = {0x04040000u, 0x06060202u, 0x05050101u, 0x07070303u};
+  uint32_t sel[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sel[j] = __builtin_amdgcn_perm(P1, P0, kPick[j]) | 0x01000100u;
+#pragma unroll
+  for (int b = 0; b < BP; ++b) {
+    const lds_ptr xb = (lds_ptr)lds + b * xrow + 32 * q;
+    const u32x4_t xa = ld<u32x4_t>(xb), xc = ld<u32x4_t>(xb + 16);
+    const uint32_t X[8] = {xa[0], xa[1], xa[2], xa[3], xc[0], xc[1], xc[2], xc[3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[b] = dot2<BF>(vv[j], __builtin_amdgcn_perm(X[2 * j + 1], X[2 * j], sel[j]), acc[b]);
+  }
+}
+
 template <bool BF>
 __device__ __forceinline__ void chunk24x(const char *lds, int q, uint32_t mw, const uint4 v,
                                          float &acc) {
@@ -325,9 +352,8 @@ template <bool BF, int BP, int PK>
 __device__ __forceinline__ void chunk(const char *lds, int q, uint32_t mw, const uint4 v,
                                       float (&acc)[BP]) {
   using L = XLay<BP>;
-  if constexpr (plain_x(PK)) {
-    static_assert(BP == 1, "the plain x layout is for batch 1");
-    chunk24x<BF>(lds, q, mw, v, acc[0]);
+  if constexpr (plain_x(PK)) {  // (run_batch handles the plain kinds itself)
+    if constexpr (BP == 1) chunk24x<BF>(lds, q, mw, v, acc[0]);
     return;
   }
   const uint32_t h = q & 1;
@@ -412,7 +438,25 @@ __device__ __forceinline__ void load_batch(Batch<U> &bt, const uint4 *vrow,
 template <bool BF, int BP, int PK, int U>
 __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, int q0, int nch,
                                           float (&acc)[BP], int qb = 0) {
-  if constexpr (plain_x(PK)) {
+  if constexpr (plain_x(PK) && BP > 1) {
+    // 2:4 at batch 2..8 with x stored plainly (token b's row at b * 32 nch)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (PK == kPat24xE) {
+        chunk24x_multi<BF, BP>(lds, 32 * nch, q0 + kWave * u, bt.m[u], bt.v[u], acc);
+        continue;
+      }
+      if (qb + kWave * u >= nch) break;  // uniform: the rest of the batch is past the row end
+      const int q = q0 + kWave * u;
+      float part[BP];
+#pragma unroll
+      for (int b = 0; b < BP; ++b) part[b] = 0.f;
+      chunk24x_multi<BF, BP>(lds, 32 * nch, min(q, nch - 1), bt.m[u], bt.v[u], part);
+#pragma unroll
+      for (int b = 0; b < BP; ++b) acc[b] += q < nch ? part[b] : 0.f;
+    }
+    return;
+  } else if constexpr (plain_x(PK)) {
     if (PK == kPat24xE || qb + kWave * U <= nch) {
       // the x operands of every chunk first: their LDS addresses do not
       // depend on the loaded data, so the reads overlap the wait for the batch
@@ -549,13 +593,18 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   item_load(A, 0);
   item_load(Bt, 1);
   // clamped groups rewrite group ngx-1 with the same data it already holds
-  if constexpr (plain_x(PK)) {  // plain layout: group g at byte 16 g
+  if constexpr (plain_x(PK)) {  // plain layout: token b's group g at byte b * 2K + 16 g
 #pragma unroll
     for (int s = 0; s < XS; ++s)
-      reinterpret_cast<uint4 *>(lds)[min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1)] =
-          xg[s].r[0];
+#pragma unroll
+      for (int b = 0; b < BP; ++b)
+        reinterpret_cast<uint4 *>(lds)[b * ngx + min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1)] =
+            xg[s].r[b];
     for (int g = threadIdx.x + XS * blockDim.x; g < ngx; g += blockDim.x)
-      reinterpret_cast<uint4 *>(lds)[g] = reinterpret_cast<const uint4 *>(x)[g];
+#pragma unroll
+      for (int b = 0; b < BP; ++b)
+        reinterpret_cast<uint4 *>(lds)[b * ngx + g] =
+            b < B ? reinterpret_cast<const uint4 *>(x + (int64_t)b * K)[g] : make_uint4(0, 0, 0, 0);
   } else {
 #pragma unroll
     for (int s = 0; s < XS; ++s)
@@ -1404,6 +1453,18 @@ void mfma_default(int64_t rows, int64_t cols, int batch, int kind, const DevInfo
 constexpr int kMfmaMinBatch = 2;
 constexpr int kDenseMfmaMinBatch = 5;  // measured: the VALU kernel wins at batch <= 4
 
+// 2:4 shapes where the VALU row kernel with x stored plainly per token beats
+// the sparse matrix cores although batch >= kMfmaMinBatch.  Measured (us,
+// cache-cold): batch 2 with K <= 5120 (14336x4096 13.7 vs 15.2, 4096x4096 5.8
+// vs 6.3, 1024x4096 3.85 vs 4.96, 25600x5120 27.3 vs 30.6; at K = 8192 and
+// 14336 the matrix cores win), and the smallest layers at batch <= 4
+// (1024x4096 at batch 4: 4.75 vs 5.21).  From batch 8 the matrix cores win
+// everywhere.
+bool valu_beats_mfma_24(int64_t rows, int64_t cols, int batch) {
+  if (batch == 2 && cols <= 5120) return true;
+  return batch <= 4 && rows * cols <= 1024LL * 4096;
+}
+
 int rows_batch_chunks(int64_t cols, int bp);
 
 // pair: the rows come in (gate, up) pairs for the SwiGLU epilogue, so a
@@ -1416,8 +1477,11 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
   DevInfo di;
   nm_status st = device_info(&di);
   if (st != NM_OK) return st;
+  const bool sp24 = mfma_kind(n, m) == kMfmaSparse24;
   if (allow_mfma && !dense && mfma_ok(rows, cols, n, m) &&
-      batch >= (mfma_kind(n, m) == kMfmaSparse24 ? kMfmaMinBatch : kDenseMfmaMinBatch)) {
+      batch >= (sp24 ? kMfmaMinBatch : kDenseMfmaMinBatch) &&
+      !(sp24 && valu_beats_mfma_24(rows, cols, batch) &&
+        sparse_lds_bytes(pad_batch(batch), (int)cols) <= lds_budget(di))) {
     mfma_default(rows, cols, batch, mfma_kind(n, m), di, cfg);
     return NM_OK;
   }
@@ -1621,10 +1685,22 @@ rows_fn pick_rows_24x(int u, int xs, bool exact) {
   return exact ? pick_rows_24x_xs<BF, kPat24xE>(u, xs) : pick_rows_24x_xs<BF, kPat24x>(u, xs);
 }
 
+// 2:4 at batch 2..8 (padded to 2, 4, 8): x stored plainly per token.
+template <bool BF, int PK>
+rows_fn pick_rows_24xm_bp(int bp) {
+  switch (bp) {
+    case 2: return nm_spmv_rows_kernel<BF, 2, PK, 4, 1>;
+    case 4: return nm_spmv_rows_kernel<BF, 4, PK, 4, 1>;
+    default: return nm_spmv_rows_kernel<BF, 8, PK, 4, 1>;
+  }
+}
+
 template <bool BF>
 rows_fn pick_rows_pk(int pk, int bp, int u, int xs, bool exact) {
   switch (pk) {
-    case kPat24: return bp == 1 ? pick_rows_24x<BF>(u, xs, exact) : pick_rows_bp<BF, kPat24>(bp, u, xs);
+    case kPat24:
+      if (bp == 1) return pick_rows_24x<BF>(u, xs, exact);
+      return exact ? pick_rows_24xm_bp<BF, kPat24xE>(bp) : pick_rows_24xm_bp<BF, kPat24x>(bp);
     case kPatHalf: return pick_rows_bp<BF, kPatHalf>(bp, u, xs);
     default: return pick_rows_bp<BF, kPat1632>(bp, u, xs);
   }

@@ -453,6 +453,40 @@ def test_default_launch_picks_matrix_cores_for_small_batch():
     assert native.nm_default_launch(14336, 4096, 8, dense=True).kernel == VALU
 
 
+def test_default_launch_2of4_small_batch_rule():
+    """2:4 at batch 2 takes the VALU kernel (x plain per token) for K <= 5120
+    and the matrix cores above; at batch 4 only the smallest layers stay on
+    the VALU kernel; batch 8 always takes the matrix cores."""
+    d = native.nm_default_launch
+    for rows, cols in [(14336, 4096), (4096, 4096), (1024, 4096), (25600, 5120), (8192, 5120)]:
+        assert d(rows, cols, 2, 2, 4).kernel == VALU, (rows, cols)
+    for rows, cols in [(4096, 14336), (8192, 8192), (28672, 8192), (5120, 25600)]:
+        assert d(rows, cols, 2, 2, 4).kernel == MFMA, (rows, cols)
+    assert d(1024, 4096, 4, 2, 4).kernel == VALU
+    assert d(1024, 4096, 3, 2, 4).kernel == VALU
+    for rows, cols in [(4096, 4096), (14336, 4096), (1024, 8192)]:
+        assert d(rows, cols, 4, 2, 4).kernel == MFMA, (rows, cols)
+    for rows, cols in [(1024, 4096), (4096, 4096), (14336, 4096)]:
+        assert d(rows, cols, 8, 2, 4).kernel == MFMA, (rows, cols)
+
+
+@pytest.mark.parametrize("batch", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("rows,cols", [(203, 4096), (130, 8192), (257, 2080), (64, 14336)])
+def test_plain_x_batch_integer_exact(rows, cols, batch):
+    """The VALU 2:4 kernel at batch 2..8 with x stored plainly per token (the
+    chunk's pair selectors applied to every token's x): exact on integer
+    inputs, for whole and ragged last load batches and several launch shapes."""
+    W = synth.integer_weights(rows, cols, seed=101)
+    keep = synth.random_mask(rows, cols, 2, 4, seed=102)
+    xi = np.random.default_rng(103).integers(-4, 5, size=(batch, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    want = oracle.masked_gemv(W, keep, X, False)
+    for cfg in (native.LaunchCfg(0, 0, 0, VALU), (64, 1, 0, VALU), (256, 4, 0, VALU), (512, 2, 0, VALU)):
+        Y = native.nm_spmm_small(values, bits, t16(X, "f16"), 2, 4, cfg=cfg)
+        assert np.array_equal(f64(Y), want), cfg
+
+
 def test_default_launch_shapes_follow_the_measured_rules():
     """Launch shapes the library picks on the 8B shapes (256 CUs), each the
     measured best of its sweep: 2:4 q|k|v 6144x4096 as 3 waves of 4 rows; the

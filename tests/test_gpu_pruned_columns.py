@@ -28,7 +28,8 @@ pytestmark = pytest.mark.gpu
 INF, NINF, NAN = 0x7C00, 0xFC00, 0x7E00  # binary16 patterns
 
 # (n, m, batch) on every kernel the default launch picks: 2:4 chunk path
-# (batch 1) and sparse matrix cores (4, 8); the scan (4:8, 8:16 at batch 1);
+# (batch 1), its form with x plain per token (batch 4 on this small shape) and
+# the sparse matrix cores (batch 8); the scan (4:8, 8:16 at batch 1);
 # the decompressed tile (4:8 at 5 and 8, 8:16 and 16:32 at 8); other densities
 CASES = [(2, 4, 1), (2, 4, 4), (2, 4, 8), (4, 8, 1), (8, 16, 1), (4, 8, 5), (4, 8, 8),
          (8, 16, 8), (16, 32, 8), (1, 4, 1), (3, 4, 8), (3, 8, 3), (5, 16, 2), (7, 8, 1)]
@@ -75,11 +76,13 @@ def test_nonfinite_x_at_pruned_columns(n, m, batch):
 
 
 def test_cases_cover_every_kernel():
-    """The decompressed-tile kinds are among the cases: 4:8 at batch 5 and
-    8:16 / 16:32 at batch 8 take the matrix cores by default."""
-    for n, m, batch in [(4, 8, 5), (4, 8, 8), (8, 16, 8), (16, 32, 8), (2, 4, 4)]:
+    """The decompressed-tile kinds are among the cases (4:8 at batch 5, and
+    8:16 / 16:32 at batch 8 take the matrix cores by default), and so are the
+    sparse matrix cores (2:4 at batch 8) and the VALU 2:4 kernel with x stored
+    plainly per token (2:4 at batch 4 on this small shape)."""
+    for n, m, batch in [(4, 8, 5), (4, 8, 8), (8, 16, 8), (16, 32, 8), (2, 4, 8)]:
         assert default_kernel(96, 2112, batch, n, m) == native.NM_KERNEL_MFMA
-    for n, m, batch in [(2, 4, 1), (4, 8, 1), (8, 16, 1)]:
+    for n, m, batch in [(2, 4, 1), (2, 4, 4), (4, 8, 1), (8, 16, 1)]:
         assert default_kernel(96, 2112, batch, n, m) == native.NM_KERNEL_VALU
 
 
