@@ -418,13 +418,15 @@ def pack_gpu(W, n, m):
     return native.nm_pack(W, keep.view(rows, cols), n, m)
 
 
-def gpu_layer(rows, cols, n, m, seed, want_dense):
+def gpu_layer(rows, cols, n, m, seed, want_dense, dtype="f16"):
     """A seeded synthetic matrix drawn on the GPU (timing only: the kernels'
-    time does not depend on the values): W = fp16(0.02 z), the n largest |w|
-    of every m kept (ties to the lower column), packed by nm_pack."""
+    time does not depend on the values): W = fp16 or bf16 of 0.02 z, the n
+    largest |w| of every m kept (ties to the lower column), packed by
+    nm_pack."""
     g = torch.Generator(device=DEV)
     g.manual_seed(seed)
-    W = (torch.randn((rows, cols), device=DEV, generator=g) * 0.02).half()
+    W = (torch.randn((rows, cols), device=DEV, generator=g) * 0.02).to(
+        torch.bfloat16 if dtype == "bf16" else torch.float16)
     values, bits = pack_gpu(W, n, m)
     return values, bits, (W if want_dense else None)
 
@@ -443,7 +445,7 @@ class GpuProj(Proj):
     def __init__(self, mt, want_dense):
         self.mt, self.name = mt, mt.name
         t0 = time.time()
-        values, bits, W = gpu_layer(mt.rows, mt.cols, mt.n, mt.m, mt.seed, want_dense)
+        values, bits, W = gpu_layer(mt.rows, mt.cols, mt.n, mt.m, mt.seed, want_dense, mt.dtype)
         packed = values.numel() * 2 + bits.numel() * 4
         self.nc = pow2_copies(packed)
         self.vals = [values] + [native.clone_packed(values) for _ in range(self.nc - 1)]

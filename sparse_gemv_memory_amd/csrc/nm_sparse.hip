@@ -264,9 +264,14 @@ __device__ __forceinline__ void chunk8_nibbles(const char *lds, uint32_t base, u
 // batch 1 in the row kernel, with x stored plainly (see chunk24x); kPat24xE
 // is the same where the load batches divide the row exactly (no chunk of a
 // batch lies past the row end, so the guards of run_batch are left out).
-enum { kPat24 = 0, kPatHalf = 1, kPat1632 = 2, kPat24x = 3, kPat24xE = 4 };
+enum { kPat24 = 0, kPatHalf = 1, kPat1632 = 2, kPat24x = 3, kPat24xE = 4, kPat48x = 5, kPat48xE = 6 };
 
-__host__ __device__ constexpr bool plain_x(int pk) { return pk == kPat24x || pk == kPat24xE; }
+// x stored plainly in LDS (column c at byte 2c): 2:4 at any batch, 4:8 at batch 1
+__host__ __device__ constexpr bool plain_x(int pk) {
+  return pk == kPat24x || pk == kPat24xE || pk == kPat48x || pk == kPat48xE;
+}
+__host__ __device__ constexpr bool is48(int pk) { return pk == kPat48x || pk == kPat48xE; }
+__host__ __device__ constexpr bool exact_kind(int pk) { return pk == kPat24xE || pk == kPat48xE; }
 
 __host__ __device__ constexpr int pattern_kind(int m) {
   return m == 4 ? kPat24 : m == 32 ? kPat1632 : kPatHalf;
@@ -346,6 +351,64 @@ __device__ __forceinline__ void chunk24x(const char *lds, int q, uint32_t mw, co
                                          float &acc) {
   const lds_ptr xb = (lds_ptr)lds + 32 * q;
   chunk24x_ops<BF>(q, mw, v, ld<u32x4_t>(xb), ld<u32x4_t>(xb + 16), acc);
+}
+
+// 4:8 at batch 1 with x stored plainly.  Every byte of a valid 4:8 mask word
+// keeps exactly 4 of its 8 columns, i.e. the chunk's two bytes hold the kept
+// pairs (p0, p1), (p2, p3) of their own 8 columns (four x registers).  The
+// pair's x operand is cut out of the two 4-column windows with two v_perm and
+// joined with an or: a selector byte of 12 yields zero, so each window
+// contributes only the columns that lie in it.  The four selectors of a mask
+// byte (pair 0: window 0, window 1; pair 1: window 0, window 1) come from a
+// 256-entry table in LDS (pair48_table); a malformed byte selects some
+// columns of its own 8, so only its row's sum is undefined.
+constexpr int kPair48TableBytes = 256 * 16;
+
+__device__ __forceinline__ uint32_t pair48_sel(int a, int c, int w) {
+  const uint32_t sa = (a >> 2) == w ? (uint32_t)(2 * (a & 3)) : 12u;
+  const uint32_t sc = (c >> 2) == w ? (uint32_t)(2 * (c & 3)) : 12u;
+  const uint32_t sa1 = sa == 12u ? 12u : sa + 1, sc1 = sc == 12u ? 12u : sc + 1;
+  return sa | (sa1 << 8) | (sc << 16) | (sc1 << 24);
+}
+
+// Table entry of mask byte b: the selectors of its two kept pairs.
+__device__ __forceinline__ u32x4_t pair48_entry(uint32_t b) {
+  int p[4];
+  uint32_t t = b;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    p[k] = ffbl_hw(t) & 7;  // an exhausted (malformed) byte repeats a column
+    t &= t - 1;
+  }
+  return (u32x4_t){pair48_sel(p[0], p[1], 0), pair48_sel(p[0], p[1], 1), pair48_sel(p[2], p[3], 0),
+                   pair48_sel(p[2], p[3], 1)};
+}
+
+template <bool BF>
+__device__ __forceinline__ void chunk48x_ops(const char *table, int q, uint32_t mw, const uint4 v,
+                                             const u32x4_t xa, const u32x4_t xc, float &acc) {
+  const uint32_t m = (mw >> ((q & 1) << 4)) & 0xffffu;
+  const u32x4_t e0 = ld<u32x4_t>((lds_ptr)table + 16 * (m & 0xffu));
+  const u32x4_t e1 = ld<u32x4_t>((lds_ptr)table + 16 * (m >> 8));
+  const uint32_t x0 = __builtin_amdgcn_perm(xa[1], xa[0], e0[0]) | __builtin_amdgcn_perm(xa[3], xa[2], e0[1]);
+  const uint32_t x1 = __builtin_amdgcn_perm(xa[1], xa[0], e0[2]) | __builtin_amdgcn_perm(xa[3], xa[2], e0[3]);
+  const uint32_t x2 = __builtin_amdgcn_perm(xc[1], xc[0], e1[0]) | __builtin_amdgcn_perm(xc[3], xc[2], e1[1]);
+  const uint32_t x3 = __builtin_amdgcn_perm(xc[1], xc[0], e1[2]) | __builtin_amdgcn_perm(xc[3], xc[2], e1[3]);
+  acc = dot2<BF>(v.x, x0, acc);
+  acc = dot2<BF>(v.y, x1, acc);
+  acc = dot2<BF>(v.z, x2, acc);
+  acc = dot2<BF>(v.w, x3, acc);
+}
+
+// The plain-x chunk of a batch-1 kind: x operands already read from LDS.
+template <bool BF, int PK>
+__device__ __forceinline__ void chunk_plain_ops(const char *lds, int nch, int q, uint32_t mw,
+                                                const uint4 v, const u32x4_t xa, const u32x4_t xc,
+                                                float &acc) {
+  if constexpr (is48(PK))
+    chunk48x_ops<BF>(lds + 32 * nch, q, mw, v, xa, xc, acc);  // the table follows x
+  else
+    chunk24x_ops<BF>(q, mw, v, xa, xc, acc);
 }
 
 template <bool BF, int BP, int PK>
@@ -440,6 +503,7 @@ __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, i
                                           float (&acc)[BP], int qb = 0) {
   if constexpr (plain_x(PK) && BP > 1) {
     // 2:4 at batch 2..8 with x stored plainly (token b's row at b * 32 nch)
+    static_assert(!is48(PK), "the plain 4:8 kind is for batch 1");
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (PK == kPat24xE) {
@@ -457,7 +521,7 @@ __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, i
     }
     return;
   } else if constexpr (plain_x(PK)) {
-    if (PK == kPat24xE || qb + kWave * U <= nch) {
+    if (exact_kind(PK) || qb + kWave * U <= nch) {
       // the x operands of every chunk first: their LDS addresses do not
       // depend on the loaded data, so the reads overlap the wait for the batch
       u32x4_t xa[U], xc[U];
@@ -470,15 +534,18 @@ __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, i
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        chunk24x_ops<BF>(q0 + kWave * u, bt.m[u], bt.v[u], xa[u], xc[u], acc[0]);
+        chunk_plain_ops<BF, PK>(lds, nch, q0 + kWave * u, bt.m[u], bt.v[u], xa[u], xc[u], acc[0]);
       return;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (qb + kWave * u >= nch) break;
       const int q = q0 + kWave * u;
+      const int qc = min(q, nch - 1);
       float part = 0.f;
-      chunk24x<BF>(lds, min(q, nch - 1), bt.m[u], bt.v[u], part);
+      const lds_ptr xb = (lds_ptr)lds + 32 * qc;
+      chunk_plain_ops<BF, PK>(lds, nch, qc, bt.m[u], bt.v[u], ld<u32x4_t>(xb), ld<u32x4_t>(xb + 16),
+                              part);
       acc[0] += q < nch ? part : 0.f;
     }
     return;
@@ -593,6 +660,10 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   item_load(A, 0);
   item_load(Bt, 1);
   // clamped groups rewrite group ngx-1 with the same data it already holds
+  if constexpr (is48(PK)) {  // the 4:8 pair selectors, after x
+    u32x4_t *table = reinterpret_cast<u32x4_t *>(lds + 2 * (size_t)K);
+    for (int b = threadIdx.x; b < 256; b += blockDim.x) table[b] = pair48_entry((uint32_t)b);
+  }
   if constexpr (plain_x(PK)) {  // plain layout: token b's group g at byte b * 2K + 16 g
 #pragma unroll
     for (int s = 0; s < XS; ++s)
@@ -1387,6 +1458,13 @@ int split_batch_chunks(int64_t cols, int ks) {
   return c % 4 == 0 ? 4 : c % 5 == 0 ? 5 : c % 2 == 0 ? 2 : 1;
 }
 
+// Does 4:8 at this batch take the plain-x kind with the pair table?  Batch 1,
+// K > 0, and x plus the table within the LDS a workgroup may use.
+bool plain48_ok(int64_t cols, int bp, int n, int m) {
+  return bp == 1 && n == 4 && m == 8 && cols > 0 &&
+         (size_t)cols * 2 + 256 * 16 <= kLdsCap;
+}
+
 // LDS of a split launch: the x image and one partial sum per row per wave.
 size_t split_lds_bytes(int64_t cols, int waves, int rpw) {
   return split_lds_offset((int)cols) + (size_t)waves * rpw * 4;
@@ -1520,11 +1598,13 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
     if (full <= budget / 2 && rows % (rmin * two_per_cu) == 0 && rows / two_per_cu <= 16) {
       int rpw = rmin;
       // (2:4 rows whose load batches hold 2 chunks per lane keep one row per
-      // wave: 8 waves per workgroup measured 3% faster for K = 14336)
-      if (!dense && bp == 1 && cols <= 16384 && !(m == 4 && rows_batch_chunks(cols, bp) == 2))
+      // wave: 8 waves per workgroup measured 3% faster for K = 14336; 4:8 in
+      // its plain-x kind follows the 2:4 rules, measured equal or better)
+      const bool plain_rules = m == 4 || plain48_ok(cols, bp, n, m);
+      if (!dense && bp == 1 && cols <= 16384 && !(plain_rules && rows_batch_chunks(cols, bp) == 2))
         for (int r = 4; r >= 2; r -= 2)
           if (rows % (r * two_per_cu) == 0 &&
-              rows / (r * two_per_cu) >= (r == 4 && m == 4 ? 2 : 4)) {
+              rows / (r * two_per_cu) >= (r == 4 && plain_rules ? 2 : 4)) {
             rpw = r;
             break;
           }
@@ -1584,6 +1664,8 @@ nm_status check_cfg(const nm_launch_cfg &c, int64_t rows, int64_t cols, int n, i
   if (rows_kernel(dense, cols, c.seg_cols)) {
     if (c.rows_per_wave < 1 || c.rows_per_wave > 64) return NM_ERR_INVALID_ARG;
     if (lds_bytes(dense, bp, cols > 0 ? (int)cols : 32) > lds_budget(di)) return NM_ERR_INVALID_ARG;
+    if (!dense && plain48_ok(cols, bp, n, m) && (size_t)cols * 2 + 256 * 16 > lds_budget(di))
+      return NM_ERR_INVALID_ARG;
     return NM_OK;
   }
   if (!(c.rows_per_wave == 1 || c.rows_per_wave == 2 || c.rows_per_wave == 4))
@@ -1711,6 +1793,22 @@ rows_fn pick_rows_pk(int pk, int bp, int u, int xs, bool exact) {
 // 2:4 batch-1 kernel has a separate kind for it)
 rows_fn pick_rows(bool bf, int pk, int bp, int u, int xs, bool exact) {
   return bf ? pick_rows_pk<true>(pk, bp, u, xs, exact) : pick_rows_pk<false>(pk, bp, u, xs, exact);
+}
+
+// 4:8 at batch 1 with x stored plainly and the pair-selector table.
+template <bool BF, int PK>
+rows_fn pick_rows_48x_xs(int u, int xs) {
+  return xs > 4 ? pick_rows_24x_u<BF, PK, 8>(u) : pick_rows_24x_u<BF, PK, 4>(u);
+}
+
+rows_fn pick_rows48(bool bf, int u, int xs, bool exact) {
+  if (bf) return exact ? pick_rows_48x_xs<true, kPat48xE>(u, xs) : pick_rows_48x_xs<true, kPat48x>(u, xs);
+  return exact ? pick_rows_48x_xs<false, kPat48xE>(u, xs) : pick_rows_48x_xs<false, kPat48x>(u, xs);
+}
+
+// LDS of the 4:8 plain kind: x (2 bytes per column) and the 4 KiB table.
+size_t plain48_lds_bytes(int64_t cols) {
+  return (size_t)cols * 2 + kPair48TableBytes;
 }
 
 // The split-reduction kernels (2:4, batch 1, exact kind): KS waves per row
@@ -1915,11 +2013,18 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     const int xs = (int)((cols / 8 + cfg.threads_per_wg - 1) / cfg.threads_per_wg);
     const int ub = rows_batch_chunks(cols, bp);
     const bool exact = cols % (1024LL * ub) == 0;  // 16 columns per chunk, 64 lanes
-    hipLaunchKernelGGL(pick_rows(bf, pk, bp, ub, xs, exact), dim3((unsigned)grid),
-                       dim3(cfg.threads_per_wg),
-                       sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32), (hipStream_t)stream,
-                       (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
-                       (int)cols, cfg.rows_per_wave, out_kind);
+    if (plain48_ok(cols, bp, n, m)) {
+      hipLaunchKernelGGL(pick_rows48(bf, ub, xs, exact), dim3((unsigned)grid),
+                         dim3(cfg.threads_per_wg), plain48_lds_bytes(cols), (hipStream_t)stream,
+                         (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
+                         (int)cols, cfg.rows_per_wave, out_kind);
+    } else {
+      hipLaunchKernelGGL(pick_rows(bf, pk, bp, ub, xs, exact), dim3((unsigned)grid),
+                         dim3(cfg.threads_per_wg),
+                         sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32), (hipStream_t)stream,
+                         (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
+                         (int)cols, cfg.rows_per_wave, out_kind);
+    }
   } else {
     const int64_t rows_per_wg = (int64_t)wpg * cfg.rows_per_wave;
     const int64_t grid = (rows + rows_per_wg - 1) / rows_per_wg;

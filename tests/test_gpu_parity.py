@@ -202,7 +202,7 @@ CFGS = [(64, 1, 32, VALU), (64, 4, 96, VALU), (128, 2, 1024, VALU), (256, 1, 0, 
 
 @pytest.mark.parametrize("cfg", CFGS)
 @pytest.mark.parametrize("batch", [1, 3, 8])
-@pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (16, 32)])
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32)])
 def test_launch_shapes_integer_exact(cfg, batch, n, m):
     """Every launch shape (threads, rows per wave, LDS segment) gives the exact
     result on integer inputs, including segments that split K raggedly."""
@@ -489,10 +489,11 @@ def test_plain_x_batch_integer_exact(rows, cols, batch):
 
 def test_default_launch_shapes_follow_the_measured_rules():
     """Launch shapes the library picks on the 8B shapes (256 CUs), each the
-    measured best of its sweep: 2:4 q|k|v 6144x4096 as 3 waves of 4 rows; the
-    scan of 4:8 keeps 2 rows per wave and 4-wave workgroups; at other
-    densities, x of K = 14336 at batch 8 in two equal segments staged by
-    16-wave workgroups, and K = 4096 whole with 4-wave workgroups."""
+    measured best of its sweep: 2:4 q|k|v 6144x4096 as 3 waves of 4 rows;
+    4:8 (x plain, pair table) takes the 2:4 shapes; the scan of 8:16 keeps 2
+    rows per wave and 4-wave workgroups; at other densities, x of K = 14336 at
+    batch 8 in two equal segments staged by 16-wave workgroups, and K = 4096
+    whole with 4-wave workgroups."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the rules are pinned for 256 CUs")
 
@@ -501,8 +502,10 @@ def test_default_launch_shapes_follow_the_measured_rules():
         return c.threads_per_wg, c.rows_per_wave, c.seg_cols
 
     assert shape(6144, 4096, 1, 2, 4) == (192, 4, 4096)
-    assert shape(4096, 4096, 1, 4, 8) == (256, 2, 4096)
-    assert shape(4096, 14336, 1, 4, 8) == (256, 2, 14336)
+    assert shape(4096, 4096, 1, 4, 8) == shape(4096, 4096, 1, 2, 4)
+    assert shape(4096, 14336, 1, 4, 8) == shape(4096, 14336, 1, 2, 4)
+    assert shape(4096, 4096, 1, 8, 16) == (256, 2, 4096)
+    assert shape(4096, 14336, 1, 8, 16) == (256, 2, 14336)
     assert shape(4096, 14336, 8, 1, 4) == (1024, 1, 7168)
     assert shape(14336, 4096, 8, 1, 4) == (256, 7, 4096)
 
@@ -1011,3 +1014,28 @@ def test_split_reduction_argument_rules():
     with pytest.raises(native.NMError) as e:
         native.nm_spmm_swiglu(values, bits, X, 2, 4, cfg=native.LaunchCfg(128, 2, 0, VALU, 2))
     assert e.value.status == native.NM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("cols", [1024, 2080, 4096, 5120, 14336])
+def test_4of8_plain_x_integer_exact_and_one_hot(cols, dtype):
+    """4:8 at batch 1 takes x plainly in LDS with the per-byte pair selectors:
+    exact on integer inputs (whole and ragged load batches), and a one-hot x
+    picks out exactly the kept weight of that column in every row (the
+    selector of each kept position, both 4-column windows of each byte)."""
+    rows = 70
+    W = synth.integer_weights(rows, cols, seed=111, dtype=dtype)
+    keep = synth.random_mask(rows, cols, 4, 8, seed=112)
+    xi = np.random.default_rng(113).integers(-4, 5, size=(1, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, dtype)
+    values, bits = gpu_pack(W, keep, 4, 8, dtype)
+    want = oracle.masked_gemv(W, keep, X, dtype == "bf16")
+    for cfg in (None, (64, 1, 0, VALU), (256, 3, 0, VALU), (512, 2, 0, VALU)):
+        y = native.nm_spmv(values, bits, t16(X[0], dtype), 4, 8, cfg=cfg)
+        assert np.array_equal(f64(y), want[0]), cfg
+    one = 0x3F80 if dtype == "bf16" else 0x3C00
+    for j in (0, 3, 4, 7, 8, 13, cols - 1):
+        xo = np.zeros((1, cols), dtype=np.uint16)
+        xo[0, j] = one
+        y = native.nm_spmv(values, bits, t16(xo[0], dtype), 4, 8)
+        assert np.array_equal(f64(y), oracle.masked_gemv(W, keep, xo, dtype == "bf16")[0]), j
