@@ -255,10 +255,12 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 # source they were taken on.  Any change to the source makes the figure stale,
 # and it is then reported as null.
 MEASURED_TRAFFIC = {
-    # (rows, cols): (kernel_digest() when measured, bytes per launch); see
-    # profiles/nm_spmv_14336x4096_hbm_counters.md
-    (14336, 4096): ("342999766698669362fa3ac49fa2b5765a2a6e7e4d41617cf36fd466badb88f9",
-                    66272572),
+    # (rows, cols): (kernel_digest() when measured, bytes per launch) at batch
+    # 1; see profiles/nm_spmv_2of4_hbm_counters.md
+    (14336, 4096): ("34ad2456382a467fdbf2885cccba63821a431f55153e03a9a04184d5c56c79b5",
+                    66271549),
+    (8192, 8192): ("34ad2456382a467fdbf2885cccba63821a431f55153e03a9a04184d5c56c79b5",
+                   75739191),
 }
 
 
@@ -290,7 +292,9 @@ def measured_traffic(rows, cols):
 
 
 def counters_run():
-    """Eager launches with known byte counts, for hardware-counter passes."""
+    """Eager launches with known byte counts, for hardware-counter passes:
+    the 14336x4096 layer at batch 1 (VALU row kernel) and 8 (matrix cores),
+    the 8192x8192 layer at batch 1, then plain copies of known size."""
     mt = [m for m, _ in workloads.config_matrices(2) if m.name == "gate"][0]
     p = Proj(mt, (1, 8), False)
     torch.cuda.synchronize()
@@ -298,6 +302,12 @@ def counters_run():
         for c in range(5):
             p.sparse_call(b, c)
         torch.cuda.synchronize()
+    mq = [m for m, _ in workloads.config_matrices(4) if m.name == "70b.q"][0]
+    q = GpuProj(mq, False)
+    torch.cuda.synchronize()
+    for c in range(5):
+        q.sparse_call(1, c)
+    torch.cuda.synchronize()
     n = 64 << 20
     src = torch.empty(n, dtype=torch.uint8, device=DEV).fill_(1)
     dst = torch.empty(n, dtype=torch.uint8, device=DEV)
@@ -305,7 +315,9 @@ def counters_run():
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"sparse_kernel_bytes_per_launch": p.sbytes[1],
+    print(json.dumps({"q8192_bytes_per_launch": q.sbytes[1],
+                      "q8192_write_bytes": mq.rows * 4,
+                      "sparse_kernel_bytes_per_launch": p.sbytes[1],
                       "sparse_kernel_read_bytes": p.sbytes[1] - mt.rows * 4,
                       "sparse_kernel_write_bytes": mt.rows * 4,
                       "batch8_bytes_per_launch": p.sbytes[8],
@@ -473,7 +485,7 @@ def large_layers_run(args, want_dense):
         gbs = p.sbytes[1] / st["us"] / 1e3
         d = {"us": round(st["us"], 3), "us_p10": round(st["p10"], 3), "us_p90": round(st["p90"], 3),
              "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4),
-             "bytes_per_launch": p.sbytes[1]}
+             "bytes_per_launch": p.sbytes[1], "traffic": measured_traffic(mt.rows, mt.cols)}
         if want_dense:
             dus = per_kernel_us(p, Proj.dense_call, 1, p.ndc, args.reps)
             tus = per_kernel_us(p, Proj.torch_call, 1, p.ndc, args.reps)
@@ -815,25 +827,36 @@ def decode_run(args):
     return out
 
 
-def summarize_trace(path):
-    """Per-kernel dispatch statistics of a rocprofv3 kernel-trace CSV: one row
-    per (kernel, grid, workgroup) with the dispatch count and the mean, p10,
-    p50, p90, min and max of End - Start in µs, in order of first dispatch."""
+def summarize_trace(path, min_run=16):
+    """Per-dispatch statistics of a rocprofv3 kernel-trace CSV, by contiguous
+    run: consecutive dispatches of one kernel, grid and workgroup size form a
+    run (each per-kernel timing of this benchmark is one run: back-to-back
+    replays of one projection's rotation), and runs of at least min_run
+    dispatches are listed in dispatch order with the count and the mean,
+    p10, p50, p90, min and max of End - Start in µs."""
     import csv
-    groups = {}
     with open(path, newline="") as f:
-        for r in csv.DictReader(f):
-            name = r["Kernel_Name"]
-            key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
-            groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    print("| kernel | grid threads | WG | dispatches | mean us | p10 | p50 | p90 | min | max |")
-    print("|---|---|---|---|---|---|---|---|---|---|")
-    for (name, grid, wg), us in groups.items():
+        recs = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    runs = []
+    for r in recs:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if runs and runs[-1][0] == key:
+            runs[-1][1].append(us)
+        else:
+            runs.append((key, [us]))
+    print("| run | kernel | grid threads | WG | dispatches | mean us | p10 | p50 | p90 | min | max |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    i = 0
+    for (name, grid, wg), us in runs:
+        if len(us) < min_run:
+            continue
+        i += 1
         a = np.array(us)
         # drop the return type, namespace and parameter list; keep template arguments
         short = name.replace("void (anonymous namespace)::", "").split("(")[0] or name
         short = short if len(short) <= 90 else short[:87] + "..."
-        print(f"| `{short}` | {grid} | {wg} | {len(a)} | {a.mean():.3f} | {np.percentile(a, 10):.3f} | "
+        print(f"| {i} | `{short}` | {grid} | {wg} | {len(a)} | {a.mean():.3f} | {np.percentile(a, 10):.3f} | "
               f"{np.percentile(a, 50):.3f} | {np.percentile(a, 90):.3f} | {a.min():.3f} | {a.max():.3f} |")
 
 
