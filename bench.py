@@ -10,14 +10,17 @@ A step is one pass of the hot path over the layer: the seven nm_spmv calls.
 Measurement:
 * every projection has its own rotation of packed copies totalling >= 1 GiB,
   so no call finds its weights in the 256 MiB Infinity Cache or in L2;
-* each step's seven launches are captured once in a HIP graph and replayed
-  (the kernels are a few microseconds long, shorter than a Python launch);
-  the graph follows the layer's data flow: q, k, v (same input) run as
-  parallel branches, then o, then gate and up in parallel, then down; the
-  strictly serial chain of the seven launches is timed beside it;
+* the steps' launches are captured in HIP graphs of several consecutive
+  steps each (the kernels are a few microseconds long, shorter than a Python
+  launch, and a graph replay costs about 10 us of its own), as a decode loop
+  captures a token's layers; the value is the strictly serial chain of the
+  seven launches; a graph that follows the layer's data flow (q, k, v as
+  parallel branches, then o, then gate and up in parallel, then down) and
+  the serial chain at one graph per step are timed beside it;
 * the K timed steps are bracketed by torch.cuda.synchronize() and HIP events;
-* per-kernel duration: a graph of back-to-back launches of one projection
-  over its rotation, HIP events around each replay, divided by the launches;
+* per-kernel duration: a graph of at least 128 back-to-back launches of one
+  projection cycling over its rotation, HIP events around each replay,
+  divided by the launches;
 * value = algorithmic bytes of the layer (packed values + mask words + x + y,
   each moved once) / step time.
 The dense comparison runs the same protocol with nm_dense_gemv and with
@@ -128,20 +131,29 @@ def capture(fn):
     return g
 
 
-def time_steps(graphs, steps, warmup):
-    """Replay graphs[i % len] for warmup + steps; return ms per timed step."""
+def time_steps(graphs, steps, warmup, per_graph=1):
+    """Replay graphs (each holding per_graph consecutive steps) in turn for
+    warmup + steps steps; return ms per timed step."""
     n = len(graphs)
-    for i in range(warmup):
+    nw, nt = warmup // per_graph, steps // per_graph
+    for i in range(nw):
         graphs[i % n].replay()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        graphs[(warmup + i) % n].replay()
+    for i in range(nt):
+        graphs[(nw + i) % n].replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return e0.elapsed_time(e1) / (nt * per_graph)
+
+
+def steps_per_graph(steps, warmup, cap=16):
+    """The largest count <= cap that divides both the timed and the warm-up
+    step counts, so both are whole graphs."""
+    g = math.gcd(steps, warmup)
+    return max(d for d in range(1, cap + 1) if g % d == 0)
 
 
 # The layer's data flow: q, k, v read the same x and are independent; o
@@ -150,42 +162,52 @@ LAYER_STAGES = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 _side = []
 
 
-def chain_graphs(projs, call, b, nsteps, copies_attr, parallel=True):
-    """One graph per step.  parallel: the independent projections of a stage
-    run on side streams (default priority) as parallel graph branches;
-    otherwise the seven launches form one serial chain."""
+def chain_graphs(projs, call, b, nsteps, copies_attr, parallel=True, per_graph=1):
+    """Graphs of per_graph consecutive steps each (step s on rotation copy s).
+    parallel: the independent projections of a stage run on side streams
+    (default priority) as parallel graph branches; otherwise the seven
+    launches of a step form one serial chain."""
     by_name = {p.name: p for p in projs}
     while len(_side) < 2:
         _side.append(torch.cuda.Stream())
+
+    def one_step(s):
+        if not parallel:
+            for p in projs:
+                call(p, b, s % getattr(p, copies_attr))
+            return
+        main = torch.cuda.current_stream()
+        for stage in LAYER_STAGES:
+            side = _side[:len(stage) - 1]
+            for st in side:
+                st.wait_stream(main)
+            call(by_name[stage[0]], b, s % getattr(by_name[stage[0]], copies_attr))
+            for name, st in zip(stage[1:], side):
+                with torch.cuda.stream(st):
+                    call(by_name[name], b, s % getattr(by_name[name], copies_attr))
+            for st in side:
+                main.wait_stream(st)
+
     graphs = []
-    for s in range(nsteps):
-        def step(s=s):
-            if not parallel:
-                for p in projs:
-                    call(p, b, s % getattr(p, copies_attr))
-                return
-            main = torch.cuda.current_stream()
-            for stage in LAYER_STAGES:
-                side = _side[:len(stage) - 1]
-                for st in side:
-                    st.wait_stream(main)
-                call(by_name[stage[0]], b, s % getattr(by_name[stage[0]], copies_attr))
-                for name, st in zip(stage[1:], side):
-                    with torch.cuda.stream(st):
-                        call(by_name[name], b, s % getattr(by_name[name], copies_attr))
-                for st in side:
-                    main.wait_stream(st)
-        graphs.append(capture(step))
+    for g0 in range(0, nsteps, per_graph):
+        graphs.append(capture(lambda g0=g0: [one_step(s) for s in range(g0, g0 + per_graph)]))
     return graphs
 
 
+# A replay of a graph costs about 10 us beyond its kernels (launch and the
+# end-of-graph release); 128 back-to-back launches make that < 0.1 us each.
+MIN_LAUNCHES_PER_REPLAY = 128
+
+
 def per_kernel_stats(p, call, b, ncopies, reps):
-    """Duration of one launch: a graph of back-to-back launches over the
-    projection's rotation, HIP events around each replay, divided by the
-    launch count.  Returns the median over the replays and their 10th and
+    """Duration of one launch: a graph of back-to-back launches cycling over
+    the projection's rotation (at least MIN_LAUNCHES_PER_REPLAY launches, so
+    the graph's own launch cost spreads thin), HIP events around each replay,
+    divided by the launch count.  Returns the median over the replays and their 10th and
     90th percentiles (µs per launch); per-dispatch percentiles come from the
     profiler's kernel trace (--summarize-trace)."""
-    g = capture(lambda: [call(p, b, c) for c in range(ncopies)])
+    launches = ncopies * max(1, -(-MIN_LAUNCHES_PER_REPLAY // ncopies))
+    g = capture(lambda: [call(p, b, c % ncopies) for c in range(launches)])
     g.replay()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -195,7 +217,7 @@ def per_kernel_stats(p, call, b, ncopies, reps):
         g.replay()
         z.record()
     torch.cuda.synchronize()
-    us = 1e3 * np.array([a.elapsed_time(z) for a, z in evs]) / ncopies
+    us = 1e3 * np.array([a.elapsed_time(z) for a, z in evs]) / launches
     return {"us": float(np.median(us)), "p10": float(np.percentile(us, 10)),
             "p90": float(np.percentile(us, 90))}
 
@@ -965,6 +987,7 @@ def main():
     projs = [Proj(mt, batches, want_dense) for mt, _ in workloads.config_matrices(2)]
     layer_bytes = {b: sum(p.sbytes[b] for p in projs) for b in batches}
     nsteps = min(args.steps + args.warmup, 256)
+    spg = steps_per_graph(args.steps, args.warmup)
 
     timings = {}
     kinds = [("sparse", Proj.sparse_call, "nc")]
@@ -973,13 +996,19 @@ def main():
     for b in batches:
         for kind, call, attr in kinds:
             for par in (True, False):
-                g = chain_graphs(projs, call, b, nsteps, attr, parallel=par)
+                g = chain_graphs(projs, call, b, nsteps, attr, parallel=par, per_graph=spg)
                 torch.cuda.synchronize()
-                timings[(kind, b, par)] = time_steps(g, args.steps, args.warmup)
+                timings[(kind, b, par)] = time_steps(g, args.steps, args.warmup, spg)
                 del g
+        # the same serial chain with one graph per step (each step pays the
+        # graph's own launch cost)
+        g = chain_graphs(projs, Proj.sparse_call, b, nsteps, "nc", parallel=False)
+        torch.cuda.synchronize()
+        timings[("sparse-1", b, False)] = time_steps(g, args.steps, args.warmup)
+        del g
         for k, v in timings.items():
             if k[1] == b:
-                log(f"  {k[0]:6s} b={b} {'layer graph' if k[2] else 'serial chain'}: "
+                log(f"  {k[0]:8s} b={b} {'layer graph' if k[2] else 'serial chain'}: "
                     f"{1e3 * v:8.1f} us/step")
 
     # per-kernel durations (batch 1) and the roofline of the dominant kernel
@@ -1052,8 +1081,11 @@ def main():
                                "(q,o 4096x4096; k,v 1024x4096; gate,up 14336x4096; down 4096x14336), "
                                "2:4 fp16, x N(0,1) + 0.1% outlier channels x20",
                    "batch": 1, "pattern": "2:4", "bytes_per_step": layer_bytes[1],
-                   "launches_per_step": len(host), "timing": "one HIP graph per step, the 7 "
-                   "launches in series, >=1 GiB rotation per projection (cache-cold)"},
+                   "launches_per_step": len(host),
+                   "timing": f"the 7 launches of a step in series, {spg} consecutive steps per HIP "
+                             "graph (each step on its own rotation copy), >=1 GiB rotation per "
+                             "projection (cache-cold); per-call figures from graphs of >= "
+                             f"{MIN_LAUNCHES_PER_REPLAY} back-to-back launches"},
         "frac_of_peak": round(layer_bytes[1] / (ms * 1e-3) / 1e9 / PEAK_GBS, 4),
         "us_per_call": per,
         "roofline": roofline,
@@ -1063,6 +1095,7 @@ def main():
                                      "of": len(target)},
     }
     res["ms_per_step_parallel_branches"] = round(timings[("sparse", 1, True)], 5)
+    res["ms_per_step_one_graph_per_step"] = round(timings[("sparse-1", 1, False)], 5)
 
     def best_dense(b):
         return min(timings[(k, b, par)] for k in ("dense", "torch") for par in (False, True))
@@ -1075,7 +1108,9 @@ def main():
     if 4 in batches:
         ms4 = timings[("sparse", 4, False)]
         b4 = {"ms_per_step": round(ms4, 5), "GB/s": round(layer_bytes[4] / (ms4 * 1e-3) / 1e9, 1),
-              "ms_per_step_parallel_branches": round(timings[("sparse", 4, True)], 5)}
+              "frac_of_peak": round(layer_bytes[4] / (ms4 * 1e-3) / 1e9 / PEAK_GBS, 4),
+              "ms_per_step_parallel_branches": round(timings[("sparse", 4, True)], 5),
+              "ms_per_step_one_graph_per_step": round(timings[("sparse-1", 4, False)], 5)}
         if want_dense:
             b4["speedup_vs_best_dense"] = round(best_dense(4) / ms4, 3)
         res["batch4"] = b4

@@ -49,6 +49,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nm_oracle.c")
 _LIB = os.path.join(_HERE, "libnm_oracle.so")
+# A build of nm_oracle.c to load instead (the sanitizer test runs the pins
+# against an AddressSanitizer / UBSan build this way); unset: _LIB.
+_LIB_OVERRIDE = os.environ.get("NM_ORACLE_LIB")
 
 OK = 0
 ERR_UNSUPPORTED = -2
@@ -72,9 +75,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
     p = ctypes.c_void_p
     i64 = ctypes.c_int64
     ci = ctypes.c_int

@@ -72,7 +72,13 @@ def lib():
     if not os.path.exists(LIB):
         raise RuntimeError(f"{LIB} is not built; run `python -m sparse_gemv_memory_amd.build` "
                            "or __graft_entry__.build() first")
-    L = ctypes.CDLL(LIB)
+    _lib = declare(ctypes.CDLL(LIB))
+    return _lib
+
+
+def declare(L):
+    """Set the argument and result types of every entry point of a loaded
+    libnm_sparse.so; returns L."""
     p, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.nm_status_string.argtypes = [ci]
     L.nm_status_string.restype = ctypes.c_char_p
@@ -119,7 +125,6 @@ def lib():
     L.nm_spmm_bitmask.restype = ci
     L.nm_stream_read.argtypes = [p, sz, p, ci, ci, p]
     L.nm_stream_read.restype = ci
-    _lib = L
     return L
 
 

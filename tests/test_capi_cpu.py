@@ -25,9 +25,14 @@ P = 0x7F0000000000  # a 256-byte aligned fake address, never dereferenced
 
 @pytest.fixture(scope="session")
 def L():
+    from sparse_gemv_memory_amd import native
+    # NM_CAPI_LIB: another build of the same sources to check instead (the
+    # sanitizer test points it at a host-side AddressSanitizer / UBSan build)
+    other = os.environ.get("NM_CAPI_LIB")
+    if other:
+        return native.declare(ctypes.CDLL(other))
     if not os.path.exists(nbuild.LIB):
         nbuild.build()
-    from sparse_gemv_memory_amd import native
     return native.lib()
 
 
