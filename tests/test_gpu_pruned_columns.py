@@ -5,7 +5,8 @@ The product sums kept weights only (y[r] = sum over kept c of W[r][c] x[c],
 columns), and the oracle skips every pruned entry.  So x may hold Inf or NaN
 at a column that every row pruned, and the result is still the finite sum of
 the kept terms.  This pins every traversal under its default launch: the 2:4
-chunk path and the sparse matrix cores, the fixed-step scan, the
+chunk path and the sparse matrix cores, the 4:8 pair table (whose zero
+selectors never read a pruned column's x), the fixed-step scan, the
 decompressed-tile matrix-core kinds (4:8, 8:16, 16:32 at batch >= 5, whose
 tile product falls back to a kept-column sum for a block whose x is not
 finite), the direct and window kernels at other densities, and the
@@ -29,10 +30,12 @@ INF, NINF, NAN = 0x7C00, 0xFC00, 0x7E00  # binary16 patterns
 
 # (n, m, batch) on every kernel the default launch picks: 2:4 chunk path
 # (batch 1), its form with x plain per token (batch 4 on this small shape) and
-# the sparse matrix cores (batch 8); the scan (4:8, 8:16 at batch 1);
-# the decompressed tile (4:8 at 5 and 8, 8:16 and 16:32 at 8); other densities
-CASES = [(2, 4, 1), (2, 4, 4), (2, 4, 8), (4, 8, 1), (8, 16, 1), (4, 8, 5), (4, 8, 8),
-         (8, 16, 8), (16, 32, 8), (1, 4, 1), (3, 4, 8), (3, 8, 3), (5, 16, 2), (7, 8, 1)]
+# the sparse matrix cores (batch 8); the 4:8 pair table (batch 1) and the
+# scan (8:16, 16:32 at batch 1, 8:16 at batch 2); the decompressed
+# tile (4:8 at 5 and 8, 8:16 and 16:32 at 8); other densities
+CASES = [(2, 4, 1), (2, 4, 4), (2, 4, 8), (4, 8, 1), (8, 16, 1), (16, 32, 1), (8, 16, 2),
+         (4, 8, 5), (4, 8, 8), (8, 16, 8), (16, 32, 8), (1, 4, 1), (3, 4, 8), (3, 8, 3),
+         (5, 16, 2), (7, 8, 1)]
 
 
 def prune_columns(keep, cols_j, m):
@@ -82,7 +85,7 @@ def test_cases_cover_every_kernel():
     plainly per token (2:4 at batch 4 on this small shape)."""
     for n, m, batch in [(4, 8, 5), (4, 8, 8), (8, 16, 8), (16, 32, 8), (2, 4, 8)]:
         assert default_kernel(96, 2112, batch, n, m) == native.NM_KERNEL_MFMA
-    for n, m, batch in [(2, 4, 1), (2, 4, 4), (4, 8, 1), (8, 16, 1)]:
+    for n, m, batch in [(2, 4, 1), (2, 4, 4), (4, 8, 1), (8, 16, 1), (16, 32, 1), (8, 16, 2)]:
         assert default_kernel(96, 2112, batch, n, m) == native.NM_KERNEL_VALU
 
 
