@@ -346,6 +346,44 @@ __device__ __forceinline__ void chunk24x_multi(const char *lds, int xrow, int q,
   }
 }
 
+// chunk24x_multi with every token's 32 bytes of x already read from LDS
+// (xa[b]: columns 0..7 of token b, xc[b]: columns 8..15).
+template <bool BF, int BP>
+__device__ __forceinline__ void chunk24x_multi_ops(int q, uint32_t mw, const uint4 v,
+                                                   const u32x4_t (&xa)[BP],
+                                                   const u32x4_t (&xc)[BP], float (&acc)[BP]) {
+  const uint32_t m = (mw >> ((q & 1) << 4)) & 0xffffu;
+  const uint32_t t = m >> 1;
+  const uint32_t S = (t & 0x0707u) | (((t >> 4) & 0x0707u) << 16);
+  const uint32_t P0 = __builtin_amdgcn_perm(kPos0Hi, kPos0Lo, S);
+  const uint32_t P1 = __builtin_amdgcn_perm(kPos1Hi, kPos1Lo, S);
+  const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  constexpr uint32_t kPick[4] = {0x04040000u, 0x06060202u, 0x05050101u, 0x07070303u};
+  uint32_t sel[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sel[j] = __builtin_amdgcn_perm(P1, P0, kPick[j]) | 0x01000100u;
+#pragma unroll
+  for (int b = 0; b < BP; ++b) {
+    const uint32_t X[8] = {xa[b][0], xa[b][1], xa[b][2], xa[b][3],
+                           xc[b][0], xc[b][1], xc[b][2], xc[b][3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[b] = dot2<BF>(vv[j], __builtin_amdgcn_perm(X[2 * j + 1], X[2 * j], sel[j]), acc[b]);
+  }
+}
+
+// Read chunk q's 32 bytes of x of every token (token b's row at b * xrow).
+template <int BP>
+__device__ __forceinline__ void x_multi(const char *lds, int xrow, int q, u32x4_t (&xa)[BP],
+                                        u32x4_t (&xc)[BP]) {
+#pragma unroll
+  for (int b = 0; b < BP; ++b) {
+    const lds_ptr xb = (lds_ptr)lds + b * xrow + 32 * q;
+    xa[b] = ld<u32x4_t>(xb);
+    xc[b] = ld<u32x4_t>(xb + 16);
+  }
+}
+
 template <bool BF>
 __device__ __forceinline__ void chunk24x(const char *lds, int q, uint32_t mw, const uint4 v,
                                          float &acc) {
@@ -504,12 +542,45 @@ __device__ __forceinline__ void run_batch(const char *lds, const Batch<U> &bt, i
   if constexpr (plain_x(PK) && BP > 1) {
     // 2:4 at batch 2..8 with x stored plainly (token b's row at b * 32 nch)
     static_assert(!is48(PK), "the plain 4:8 kind is for batch 1");
+    if (exact_kind(PK) || qb + kWave * U <= nch) {
+      // the x operands of a chunk are read for up to 4 tokens at once, ahead
+      // of their use (their LDS addresses do not depend on the loaded data,
+      // so the first reads overlap the wait for the batch), within 32..64
+      // registers of x (the row kernel's launch bound leaves 128 VGPRs): every
+      // chunk's at batch 2 in the exact kind (the other kind also holds the
+      // ragged batch's code), else a chunk's at a time, at batch 8 in two
+      // halves of 4 tokens
+      if constexpr (U * BP <= 8 && exact_kind(PK)) {
+        u32x4_t xa[U][BP], xc[U][BP];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x_multi<BP>(lds, 32 * nch, q0 + kWave * u, xa[u], xc[u]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          chunk24x_multi_ops<BF, BP>(q0 + kWave * u, bt.m[u], bt.v[u], xa[u], xc[u], acc);
+      } else {
+        constexpr int G = BP < 4 ? BP : 4;  // tokens per group of reads
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int g = 0; g < BP; g += G) {
+            u32x4_t xa[G], xc[G];
+            x_multi<G>(lds + g * 32 * nch, 32 * nch, q0 + kWave * u, xa, xc);
+            __builtin_amdgcn_sched_barrier(0);
+            float part[G];
+#pragma unroll
+            for (int b = 0; b < G; ++b) part[b] = acc[g + b];
+            chunk24x_multi_ops<BF, G>(q0 + kWave * u, bt.m[u], bt.v[u], xa, xc, part);
+#pragma unroll
+            for (int b = 0; b < G; ++b) acc[g + b] = part[b];
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (PK == kPat24xE) {
-        chunk24x_multi<BF, BP>(lds, 32 * nch, q0 + kWave * u, bt.m[u], bt.v[u], acc);
-        continue;
-      }
       if (qb + kWave * u >= nch) break;  // uniform: the rest of the batch is past the row end
       const int q = q0 + kWave * u;
       float part[BP];
