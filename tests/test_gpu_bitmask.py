@@ -95,6 +95,48 @@ def test_bitmask_integer_inputs_bit_exact(dtype):
     assert np.array_equal(f64(Y), oracle.masked_gemv(W, keep, X, dtype == "bf16"))
 
 
+def clustered_mask(rows, cols, seed):
+    """Rows whose kept columns come in a few short runs separated by long
+    empty stretches (a group's 8 values then span many words), with a dense
+    row, an empty row and rows of one kept column among them."""
+    rng = np.random.default_rng(seed)
+    keep = np.zeros((rows, cols), np.uint8)
+    for r in range(rows):
+        for _ in range(int(rng.integers(0, 6))):
+            c0 = int(rng.integers(0, cols))
+            keep[r, c0:c0 + int(rng.integers(1, 12))] = 1
+    keep[0] = 1
+    if rows > 1:
+        keep[1] = 0
+    if rows > 2:
+        keep[2] = 0
+        keep[2, int(rng.integers(0, cols))] = 1
+    return keep
+
+
+@pytest.mark.parametrize("kind", ["half", "random", "clustered", "dense"])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (7, 64), (37, 2080), (300, 4096), (64, 14336),
+                                       (5, 32768)])
+def test_bitmask_batch1_integer_exact(rows, cols, kind):
+    """Batch 1 (the value-major traversal: groups of 8 values aligned in the
+    value array, their columns from the row's group table): exact on integer
+    inputs for per-row halves, row densities from 0 to 1, short runs of kept
+    columns between long empty stretches (groups spanning many words), nearly
+    full rows, empty rows and single kept columns, K from 32 to 32768."""
+    rng = np.random.default_rng(rows + cols)
+    W = synth.f32_to_16_bits(rng.integers(-3, 4, size=(rows, cols)).astype(np.float32), "f16")
+    x = synth.f32_to_16_bits(rng.integers(-3, 4, size=(1, cols)).astype(np.float32), "f16")
+    if kind == "clustered":
+        keep = clustered_mask(rows, cols, seed=cols)
+    elif kind == "dense":
+        keep = (rng.random((rows, cols)) < 0.97).astype(np.uint8)
+    else:
+        keep = masks(kind, rows, cols, W, seed=rows)
+    values, bits, offs = native.nm_pack_bitmask(t16(W, "f16"), torch.from_numpy(keep).to(DEV))
+    Y = native.nm_spmm_bitmask(values, bits, offs, t16(x, "f16"))
+    assert np.array_equal(f64(Y), oracle.masked_gemv(W, keep, x, False))
+
+
 def test_bitmask_one_hot_x():
     rows, cols = 48, 4160
     W = synth.weights(rows, cols, seed=11)
