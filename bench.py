@@ -279,10 +279,10 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch) at batch
     # 1; see profiles/nm_spmv_2of4_hbm_counters.md
-    (14336, 4096): ("34ad2456382a467fdbf2885cccba63821a431f55153e03a9a04184d5c56c79b5",
-                    66271549),
-    (8192, 8192): ("34ad2456382a467fdbf2885cccba63821a431f55153e03a9a04184d5c56c79b5",
-                   75739191),
+    (14336, 4096): ("852ae973c5ada7949c897c182674873ad43b357cb4c8c2d17ad3ab4c6f2bc47f",
+                    66260289),
+    (8192, 8192): ("852ae973c5ada7949c897c182674873ad43b357cb4c8c2d17ad3ab4c6f2bc47f",
+                   75727931),
 }
 
 

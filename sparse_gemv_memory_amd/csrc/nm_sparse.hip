@@ -1603,15 +1603,23 @@ constexpr int kMfmaMinBatch = 2;
 constexpr int kDenseMfmaMinBatch = 5;  // measured: the VALU kernel wins at batch <= 4
 
 // 2:4 shapes where the VALU row kernel with x stored plainly per token beats
-// the sparse matrix cores although batch >= kMfmaMinBatch.  Measured (us,
-// cache-cold): batch 2 with K <= 5120 (14336x4096 13.7 vs 15.2, 4096x4096 5.8
-// vs 6.3, 1024x4096 3.85 vs 4.96, 25600x5120 27.3 vs 30.6; at K = 8192 and
-// 14336 the matrix cores win), and the smallest layers at batch <= 4
-// (1024x4096 at batch 4: 4.75 vs 5.21).  From batch 8 the matrix cores win
-// everywhere.
+// the sparse matrix cores although batch >= kMfmaMinBatch.  Measured on the
+// 8B, 70B and Qwen3-32B shapes (us, cache-cold, one box, VALU / matrix cores):
+//  - at most 1024 rows, batch 2..4: 1024x4096 3.79 / 4.99 (batch 2), 4.50 /
+//    5.26 (batch 4); 1024x8192 5.56 / 6.88, 6.77 / 7.45;
+//  - batch 2: 14336 rows or more (14336x4096 13.25 / 15.02, 25600x5120 25.08
+//    / 29.42, 28672x8192 42.46 / 43.34), K >= 25600 (8192x28672 43.01 /
+//    46.88, 5120x25600 33.67 / 36.50), up to 4096 x 4096 weights (5.81 /
+//    5.98); the matrix cores win between (8192x5120 13.15 / 10.96, 8192x8192
+//    17.45 / 15.13, 5120x8192, 4096x14336, 6144x4096);
+//  - batch 3, 4: 14336 rows or more with K <= 4096 (14336x4096 15.02 / 15.81
+//    at batch 4); the matrix cores win elsewhere (4096x4096 6.66 / 6.23).
+// From batch 5 the matrix cores win everywhere.
 bool valu_beats_mfma_24(int64_t rows, int64_t cols, int batch) {
-  if (batch == 2 && cols <= 5120) return true;
-  return batch <= 4 && rows * cols <= 1024LL * 4096;
+  if (batch > 4) return false;
+  if (rows <= 1024) return true;
+  if (batch == 2) return rows >= 14336 || cols >= 25600 || rows * cols <= 4096LL * 4096;
+  return rows >= 14336 && cols <= 4096;
 }
 
 int rows_batch_chunks(int64_t cols, int bp);
