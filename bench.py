@@ -702,7 +702,8 @@ def prefill_run(args):
     entry point nm_spmm_small (batch <= 8), nm_dense_gemv (batch <= 8) and
     torch linear (hipBLASLt) on the dense weights; four resident copies of
     each (cache-cold at small batch), us per call and dense-equivalent
-    TFLOP/s (2 R K B / time)."""
+    TFLOP/s (2 R K B / time).  The prefill product and torch linear both
+    write fp16 output; the decode entry points write fp32."""
     out = {}
     L = native.lib()
     for name, R, K in (("gate", 14336, 4096), ("down", 4096, 14336)):
@@ -719,8 +720,8 @@ def prefill_run(args):
                 return ms * 1e3
             def pre(i):
                 v, b, _ = mats[i % 4]
-                st = L.nm_spmm_prefill(v.data_ptr(), b.data_ptr(), X.data_ptr(), Y.data_ptr(), B, R,
-                                       K, 2, 4, native.NM_F16, native.NM_F32,
+                st = L.nm_spmm_prefill(v.data_ptr(), b.data_ptr(), X.data_ptr(), Yh.data_ptr(), B, R,
+                                       K, 2, 4, native.NM_F16, native.NM_F16,
                                        torch.cuda.current_stream().cuda_stream)
                 assert st == 0, st
             def dense(i):

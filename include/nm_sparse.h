@@ -372,18 +372,22 @@ int nm_spmm_bitmask(const void *values, const uint32_t *bits, const int64_t *off
  * any number of tokens.  The pages contrast the structured-sparsity matrix
  * path with the dense GEMM: it gains in prefill and loses in decode
  * ("Introduction" and Figure 1(b)); this entry point is that path here, fed
- * from the same stored format.  A GEMM tiling (256 rows x 128 tokens per
- * workgroup, v_smfmac_f32_16x16x64) reuses each weight byte for up to 128
- * tokens, where the decode entry points stream the weights once per call for
- * at most 8 tokens.
+ * from the same stored format.  A GEMM tiling (224 or 256 rows x 64, 128 or
+ * 256 tokens per workgroup of 8 waves, v_smfmac_f32_16x16x64, chosen per
+ * shape so that the workgroups fill the compute units) reuses each weight
+ * byte for up to 256 tokens, where the decode entry points stream the
+ * weights once per call for at most 8 tokens.  A workgroup takes up to
+ * 160 KiB of LDS.
  *   values, bits: nm_pack output for 2:4 (rows x cols/2 and rows x cols/32),
  *                 device; values and X 16-byte aligned, bits 4-byte aligned;
  *   X:            device, batch x cols, in_dt, row-major (token-major);
  *   Y:            device, batch x rows, out_dt (NM_F32 or in_dt), row-major;
  *   cols % 64 == 0; rows * cols and batch * cols * 2 at most INT32_MAX.
  * batch == 0 or rows == 0 does nothing; cols == 0 writes zeros.
- * Errors: NM_ERR_INVALID_ARG, NM_ERR_UNSUPPORTED (not 2:4, dtypes),
- * NM_ERR_SHAPE (cols % 64), NM_ERR_ALIGN, NM_ERR_HIP.  Asynchronous on stream. */
+ * Errors: NM_ERR_INVALID_ARG, NM_ERR_UNSUPPORTED (not 2:4, dtypes, or a
+ * device whose workgroups get less LDS than the smallest tile's 88 KiB),
+ * NM_ERR_SHAPE (cols % 64), NM_ERR_ALIGN, NM_ERR_HIP.  Asynchronous on
+ * stream. */
 int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, void *Y,
                     int64_t batch, int64_t rows, int64_t cols, int n, int m,
                     nm_dtype in_dt, nm_dtype out_dt, void *stream);

@@ -7,30 +7,42 @@
 // path gains in prefill and loses in decode).  The decode kernels of
 // nm_sparse.hip stream the weights once per call for at most 8 tokens; here
 // the weights and the tokens are both tiled, so each weight byte read from
-// memory serves up to 128 tokens and each token serves 256 rows.
+// memory serves 256 tokens and each token serves up to 256 rows.
 //
 // Tiling (gfx950, v_smfmac_f32_16x16x64_{f16,bf16}):
-//   - a workgroup of 4 waves owns 256 rows x 128 tokens of Y; wave w owns rows
-//     128 (w & 1) .. +128 and tokens 64 (w >> 1) .. +64, i.e. 8 x 4 output
-//     tiles of 16 x 16 (32 accumulators of 4 floats per lane);
-//   - K is walked in steps of 64 columns.  Each step's operands are staged in
-//     LDS by direct-to-LDS buffer loads, double-buffered with one barrier per
-//     step: the 256 rows' 32 kept values (64 bytes) and 2 mask words each,
-//     and the 128 tokens' 64 x values (128 bytes) each;
+//   - a workgroup of 8 waves (two per SIMD) owns 32 RT rows x 256 tokens of Y
+//     (RT = 8 or 7 row tiles of 16 per wave, chosen per shape so that the
+//     tiles fill the compute units in whole rounds); wave w owns rows
+//     16 RT (w & 1) .. + 16 RT and tokens 64 (w >> 1) .. + 64, i.e. RT x 4
+//     output tiles of 16 x 16;
+//   - K is walked in steps of 64 columns.  A step's operands are staged in
+//     LDS by direct-to-LDS buffer loads in a ring of 3 stages (48 KiB each:
+//     the rows' 32 kept values (64 bytes) and the tokens' 64 x values (128
+//     bytes)); the mask words come 4 steps at a time (32 bytes per row) into
+//     a ring of 2 slots, since a load of 8 bytes per row costs as much
+//     issue as one of 64.  The loads of step s + 2 are issued among the
+//     products of step s, and one barrier per step both publishes step s + 1
+//     and frees the slot of step s;
 //   - operand layouts are those of the instruction: lane l = 16 j + n holds
 //     A row n, columns 16 j .. 16 j + 15 (its 8 kept values, and the 2-bit
 //     in-group positions derived from the mask nibbles); B token n, columns
 //     8 j .. 8 j + 7 and 32 + 8 j .. 32 + 8 j + 7; D rows 4 j .. 4 j + 3 of
-//     token n;
+//     token n.  Two row tiles share one index register: the lane's 16 mask
+//     bits of each are packed with v_perm, converted at once, and each
+//     product takes its half (the instruction's ABID field);
 //   - LDS rows are XOR-swizzled by 16-byte chunk (values: chunk c of row r
-//     at c ^ ((r >> 2) & 3); x: chunk c of token t at c ^ ((t >> 1) & 7)),
-//     so the 16 rows or tokens a quarter-wave reads fall on distinct banks.
+//     at c ^ ((r >> 2) & 3); x: chunk c of token t at c ^ ((t >> 1) & 7);
+//     mask words: the two 16-byte halves of row r swapped when bit 3 of r is
+//     set), so the reads in MFMA layout spread over the banks; every lane's
+//     read address is a per-lane base plus per-tile immediates.
 // Ragged edges: rows past R load row R - 1 and are not stored; tokens past
 // the batch read zeros (buffer range check); K must be a multiple of 64.
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <stdint.h>
+#include <type_traits>
 
 #include "nm_device.h"
 #include "nm_host.h"
@@ -40,43 +52,62 @@ namespace {
 
 using namespace nm_host;
 
-constexpr int kPRows = 256;                 // rows per workgroup
-constexpr int kPToks = 128;                 // tokens per workgroup
-constexpr int kPValRow = 64;                // LDS bytes of a row's values per step
-constexpr int kPValBytes = kPRows * kPValRow;       // 16 KiB
-constexpr int kPMaskBytes = kPRows * 8;             // 2 KiB: 2 words per row
-constexpr int kPXRow = 128;                 // LDS bytes of a token's x per step
-constexpr int kPXBytes = kPToks * kPXRow;           // 16 KiB
-constexpr int kPStage = kPValBytes + kPMaskBytes + kPXBytes;
-constexpr int kPDma = 4 + 2 + 4;  // direct-to-LDS loads per wave per step
+constexpr int kPWaves = 8;                           // waves per workgroup
+constexpr int kPValBytes = 256 * 64;                 // values of up to 256 rows per step
+constexpr int kPNS = 3;                              // stages in the ring
+constexpr int kPMaskSlot = 256 * 32;                 // mask words of 4 steps, 256 rows
 
-__host__ __device__ constexpr int prefill_lds(int ns) { return ns * kPStage; }
+// LDS of a workgroup with TT token tiles of 16 per wave (64 TT tokens): the
+// ring of stages (values, then x of 64 TT tokens, 128 bytes each), then the
+// two mask slots; 160 KiB at TT = 4.
+__host__ __device__ constexpr int prefill_stage(int tt) { return kPValBytes + 8192 * tt; }
+__host__ __device__ constexpr int prefill_mask_base(int tt) { return kPNS * prefill_stage(tt); }
+__host__ __device__ constexpr int prefill_lds(int tt) {
+  return prefill_mask_base(tt) + 2 * kPMaskSlot;
+}
 
-#ifndef NM_PREFILL_STAGES
-#define NM_PREFILL_STAGES 4
-#endif
-constexpr int kPrefillStages = NM_PREFILL_STAGES;  // ring depth (LDS: 34 KiB per step)
-
-// An LDS read the compiler may not repeat or drop: the fragments of the next
-// step are read once, into registers, while the current step's products run.
+// An LDS read the compiler may not repeat or drop.
 template <typename T>
 __device__ __forceinline__ T vld(uint32_t addr) {
   return *(volatile __attribute__((address_space(3))) T *)(size_t)addr;
 }
 
-// Direct-to-LDS load of 4 bytes per lane with the default cache policy: the
-// weights are reused by every token tile of their row tile, so they must stay
-// in L2 (the streaming policy of the decode kernels measured 20% slower here).
-__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(size_t)lds, 4, voff, soff, 0, 0);
+// In-group position codes of 8 nibbles at once (two 16-bit mask halves, each
+// nibble holding exactly 2 set bits p0 < p1 -> p0 | p1 << 2), by the rule of
+// nib_codes.
+__device__ __forceinline__ int nib_codes2(uint32_t m) {
+  const uint32_t s1 = m >> 1, s2 = m >> 2, s3 = m >> 3;
+  const uint32_t c0 = ~m & s1 & 0x11111111u;
+  const uint32_t c1 = ~m & ~s1 & 0x11111111u;
+  const uint32_t c2 = (s3 | ~s2) & 0x11111111u;
+  const uint32_t c3 = (s3 | s2) & 0x11111111u;
+  return (int)(c0 | (c1 << 1) | (c2 << 2) | (c3 << 3));
 }
 
-template <bool BF, int NS>
-__global__ __launch_bounds__(256) void nm_spmm_prefill_kernel(
+// The 16x16x64 sparse product with its index set in half AB of idx.
+template <bool BF, int AB>
+__device__ __forceinline__ f4v_t smfmac_half(u32x4_t a, u32x4_t b0, u32x4_t b1, int idx, f4v_t c) {
+  const u32x8_t b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+  if constexpr (BF)
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(b8v_t, a),
+                                                    __builtin_bit_cast(b16v_t, b), c, idx, 0, AB);
+  else
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8v_t, a),
+                                                   __builtin_bit_cast(h16v_t, b), c, idx, 0, AB);
+}
+
+template <bool BF, int RT, int TT>
+__global__ __launch_bounds__(512) void nm_spmm_prefill_kernel(
     const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int R, int K, int nrt, int ntt,
-    int out_kind) {
-  static_assert(NS >= 3 && (NS - 2) * kPDma < 64, "ring depth");
+    int out_kind, int vec) {
+  static_assert(RT == 7 || RT == 8, "row tiles per wave");
+  static_assert(TT == 1 || TT == 2 || TT == 4, "token tiles per wave");
+  constexpr int kRows = 32 * RT;    // rows per workgroup
+  constexpr int kToks = 64 * TT;    // tokens per workgroup
+  constexpr int kStage = prefill_stage(TT);
+  constexpr int kMaskBase = prefill_mask_base(TT);
+  constexpr int kDma = 2 + TT;      // stage loads per wave per step
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -94,7 +125,7 @@ __global__ __launch_bounds__(256) void nm_spmm_prefill_kernel(
   const int first_r = 4 * group, gr = min(nrt - first_r, 4);
   const int in = tile - group * 4 * ntt;
   const int rt = first_r + in % gr, tt = in / gr;
-  const int row0 = rt * kPRows, tok0 = tt * kPToks;
+  const int row0 = rt * kRows, tok0 = tt * kToks;
   const int nk = K >> 6;
   const uint32_t base = (uint32_t)(size_t)(lds_ptr)lds;
 
@@ -107,141 +138,204 @@ __global__ __launch_bounds__(256) void nm_spmm_prefill_kernel(
   const __amdgpu_buffer_rsrc_t r0 = __builtin_amdgcn_make_buffer_rsrc((void *)values, 0, 0,
                                                                       kRsrcWord3);
 
-  // Per-lane source offsets of step 0 (bytes); a step adds 64 (values),
-  // 8 (masks) or 128 (x) through the scalar offset.
-  // values: instruction q of wave w fills LDS bytes 1024 (4 q + w) .. + 1024,
-  // i.e. rows 16 (4 q + w) .. + 16, lane i -> row (i >> 2), position i & 3
-  int voff[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 16 * (4 * q + w) + (lane >> 2);
-    const int p = lane & 3;
-    const int c = p ^ ((r >> 2) & 3);
-    const int gr = min(row0 + r, R - 1);
-    voff[q] = gr * K + 16 * c;
-  }
-  // masks: instruction q of wave w fills LDS bytes 256 (4 q + w) .. + 256,
-  // i.e. rows 32 (4 q + w) .. + 32, lane i -> row (i >> 1), word i & 1
-  int moff[2];
+  // Per-lane source offsets of step 0 (bytes); a step adds 64 (values) or
+  // 128 (x) through the scalar offset, a group of 4 steps adds 32 (masks).
+  // values: instruction q of wave w fills LDS bytes 1024 (8 q + w) .. + 1024,
+  // i.e. rows 16 (8 q + w) .. + 16, lane i -> row (i >> 2), chunk slot i & 3;
+  // the instructions past the workgroup's rows load from the empty resource
+  const bool vreal[2] = {w < 2 * RT, 8 + w < 2 * RT};
+  int voff[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int r = 32 * (4 * q + w) + (lane >> 1);
-    const int gr = min(row0 + r, R - 1);
-    moff[q] = gr * (K / 8) + 4 * (lane & 1);
+    const int r = 16 * (8 * q + w) + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    voff[q] = min(row0 + r, R - 1) * K + 16 * c;
   }
-  // x: instruction q of wave w fills LDS bytes 1024 (4 q + w) .. + 1024,
-  // i.e. tokens 8 (4 q + w) .. + 8, lane i -> token (i >> 3), position i & 7
-  int xoff[4];
+  // masks: wave w fills LDS bytes 1024 w .. + 1024 of a mask slot, i.e. rows
+  // 32 w .. + 32, lane i -> row (i >> 1), 16-byte half (i & 1) ^ (row >> 3 & 1)
+  const bool mreal = w < RT;
+  int moff;
+  {
+    const int r = 32 * w + (lane >> 1);
+    moff = min(row0 + r, R - 1) * (K / 8) + 16 * ((lane & 1) ^ ((r >> 3) & 1));
+  }
+  // x: instruction q of wave w fills LDS bytes 1024 (8 q + w) .. + 1024 of
+  // the stage's x, i.e. tokens 8 (8 q + w) .. + 8, lane i -> token (i >> 3),
+  // chunk slot i & 7; a token past the batch points at the end of x, where
+  // the range check reads zeros
+  int xoff[TT];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int t = 8 * (4 * q + w) + (lane >> 3);
-    const int p = lane & 7;
-    const int c = p ^ ((t >> 1) & 7);
-    // a token past the batch points at the end of x: the range check reads zeros
+  for (int q = 0; q < TT; ++q) {
+    const int t = 8 * (8 * q + w) + (lane >> 3);
+    const int c = (lane & 7) ^ ((t >> 1) & 7);
     xoff[q] = (int)min((int64_t)(tok0 + t) * K * 2, (int64_t)B * K * 2) + 16 * c;
   }
-
-  // step s into ring slot s % NS; a step past the last loads from
-  // zero-size resources (no memory traffic, same instruction count), so the
-  // wait counts below are the same at every step
+  // step s into stage slot s % 3; a step past the last loads from the empty
+  // resource (no memory traffic, same instruction count), so the wait counts
+  // below are the same at every step
   auto issue = [&](int s) {
     const bool real = s < nk;
-    const __amdgpu_buffer_rsrc_t V = real ? rv : r0, M = real ? rb : r0, X = real ? rx : r0;
-    const uint32_t st = base + (uint32_t)((s % NS) * kPStage);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lds_load16(V, st + 1024 * (4 * q + w), voff[q], 64 * s);
+    const uint32_t st = base + (uint32_t)((s % kPNS) * kStage);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
-      lds_load4(M, st + kPValBytes + 256 * (4 * q + w), moff[q], 8 * s);
+      lds_load16(real && vreal[q] ? rv : r0, st + 1024 * (8 * q + w), voff[q], 64 * s);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      lds_load16(X, st + kPValBytes + kPMaskBytes + 1024 * (4 * q + w), xoff[q], 128 * s);
+    for (int q = 0; q < TT; ++q)
+      lds_load16(real ? rx : r0, st + kPValBytes + 1024 * (8 * q + w), xoff[q], 128 * s);
   };
-
-  f4v_t acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = (f4v_t){0.f, 0.f, 0.f, 0.f};
+  // mask words of steps 4 S .. 4 S + 3 into mask slot S % 2; the group offset
+  // goes into the vector offset, which the range check covers
+  const int ngroups = (nk + 3) >> 2;
+  auto issue_masks = [&](int S) {
+    lds_load16(S < ngroups && mreal ? rb : r0, base + kMaskBase + (S & 1) * kPMaskSlot + 1024 * w,
+               moff + 32 * S, 0);
+  };
 
   const int wr = w & 1, wc = w >> 1;
-  // operands of one step: A fragments and raw mask words of the 8 row tiles,
-  // B fragments of the 4 token tiles
-  struct Frag {
-    u32x4_t a[8];
-    uint32_t mw[8];
-    u32x4_t b[4][2];
-  };
-  auto read_frags = [&](Frag &f, int s) {
-    const uint32_t st = base + (uint32_t)((s % NS) * kPStage);
+  f4v_t acc[RT][TT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 128 * wr + 16 * i + n;
-      f.a[i] = vld<u32x4_t>(st + r * kPValRow + 16 * (j ^ ((r >> 2) & 3)));
-      f.mw[i] = vld<uint32_t>(st + kPValBytes + r * 8 + 4 * (j >> 1));
-    }
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tk = 64 * wc + 16 * t + n;
-      const uint32_t xr = st + kPValBytes + kPMaskBytes + tk * kPXRow;
-      const int sw = (tk >> 1) & 7;
-      f.b[t][0] = vld<u32x4_t>(xr + 16 * (j ^ sw));
-      f.b[t][1] = vld<u32x4_t>(xr + 16 * ((4 + j) ^ sw));
-    }
-  };
-  // Software pipeline: the products of step s run while the fragments of
-  // step s + 1 are read from LDS.  Steps s + 2 .. s + NS - 1 are in flight.
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s);
-  wait_vmcnt<(NS - 2) * kPDma>();  // step 0 has landed
+    for (int t = 0; t < TT; ++t) acc[i][t] = (f4v_t){0.f, 0.f, 0.f, 0.f};
+
+  // per-lane LDS offsets: row tile i adds 1024 i (values) or 512 i (masks),
+  // token tile t adds 2048 t
+  const int r_lane = 16 * RT * wr + n;  // the lane's row within row tile 0
+  const uint32_t a_off = (uint32_t)(r_lane * 64 + 16 * (j ^ ((n >> 2) & 3)));
+  const uint32_t b_off0 =
+      (uint32_t)(kPValBytes + (16 * TT * wc + n) * 128 + 16 * (j ^ ((n >> 1) & 7)));
+  const uint32_t b_off1 =
+      (uint32_t)(kPValBytes + (16 * TT * wc + n) * 128 + 16 * ((4 + j) ^ ((n >> 1) & 7)));
+  // mask word 2 (s % 4) + (j >> 1) of the lane's row: its 16-byte half is
+  // (s >> 1) & 1, swapped for rows with bit 3 set, and its word within the
+  // half 2 (s & 1) + (j >> 1)
+  const int hn = (n >> 3) & 1;
+  const uint32_t m_lane = (uint32_t)(kMaskBase + r_lane * 32 + 4 * (j >> 1));
+  const uint32_t m_off0 = m_lane + 16 * hn, m_off1 = m_lane + 16 * (hn ^ 1);
+  // v_perm selector: the lane's 16-bit half of two mask words -> the low and
+  // the high half of one register
+  const uint32_t psel = (j & 1) ? 0x07060302u : 0x05040100u;
+
+  issue_masks(0);
+  issue(0);
+  issue(1);
+  wait_vmcnt<kDma>();  // the masks of steps 0..3 and step 0 have landed
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  Frag cur;
-  read_frags(cur, 0);
+  int slot3 = 0;
   for (int s = 0; s < nk; ++s) {
-    // step s + 1 has landed (NS - 3 younger steps stay in flight); the
-    // fragments of step s are in registers, so after the barrier every
-    // wave is done with slot (s - 1) % NS, which is refilled next
-    wait_vmcnt<(NS - 3) * kPDma>();
+    // the masks of the next 4 steps, before the stage 2 steps ahead: the
+    // wait at the end of the iteration then leaves only that stage in flight
+    if ((s & 3) == 0) issue_masks((s >> 2) + 1);
+    const uint32_t st = base + (uint32_t)(slot3 * kStage);
+    const uint32_t ms = base + ((s >> 2) & 1) * kPMaskSlot + 8 * (s & 1);
+    const uint32_t mo = ((s >> 1) & 1) ? m_off1 : m_off0;
+    u32x4_t a[RT];
+    uint32_t mw[RT + 1];
+    u32x4_t b[TT][2];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      a[i] = vld<u32x4_t>(st + a_off + 1024 * i);
+      mw[i] = vld<uint32_t>(ms + mo + 512 * i);
+    }
+    mw[RT] = 0;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      b[t][0] = vld<u32x4_t>(st + b_off0 + 2048 * t);
+      b[t][1] = vld<u32x4_t>(st + b_off1 + 2048 * t);
+    }
+    issue(s + 2);
+#pragma unroll
+    for (int i = 0; i < RT; i += 2) {
+      const int idx = nib_codes2(__builtin_amdgcn_perm(mw[i + 1], mw[i], psel));
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        acc[i][t] = smfmac_half<BF, 0>(a[i], b[t][0], b[t][1], idx, acc[i][t]);
+      if (i + 1 < RT) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+          acc[i + 1][t] = smfmac_half<BF, 1>(a[i + 1], b[t][0], b[t][1], idx, acc[i + 1][t]);
+      }
+    }
+    // issue order: the LDS reads, then the products with the loads of step
+    // s + 2 spread among them
+    constexpr int kPer = RT * TT / kDma;  // products before each load
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RT + 2 * TT, 0);
+#pragma unroll
+    for (int k = 0; k < kDma; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, RT * TT - kPer * kDma, 0);
+    // every LDS read of this step has returned and step s + 1 has landed
+    // (step s + 2 may be in flight): after the barrier, step s + 1 is
+    // visible to all waves and slot s % 3 is free for step s + 3
     wait_lgkmcnt0();
+    wait_vmcnt<kDma>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(s + NS - 1);
-    Frag nxt;
-    read_frags(nxt, s + 1);
-    int idx[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) idx[i] = nib_codes(cur.mw[i] >> ((j & 1) * 16));
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        acc[i][t] = smfmac<BF>(cur.a[i], cur.b[t][0], cur.b[t][1], idx[i], acc[i][t]);
-    // issue order: one product, one LDS read of the next step, 24 times,
-    // then the last 8 products
-#pragma unroll
-    for (int k = 0; k < 24; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    cur = nxt;
+    slot3 = slot3 == kPNS - 1 ? 0 : slot3 + 1;
   }
-  wait_vmcnt<0>();  // the trailing dummy loads still write LDS
+  wait_vmcnt<0>();  // the trailing loads from the empty resource still write LDS
 
-  // lane (j, n) of tile (i, t): rows 4 j .. 4 j + 3 of row tile i, token n
+  // lane (j, n) of tile (i, t): rows 4 j .. 4 j + 3 of row tile i, token n;
+  // one 16-byte (fp32) or 8-byte store per tile where vec (R % 4 == 0 and y
+  // aligned to that size) and the 4 rows exist
+  const int kind = out_kind & 0xff;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int tok = tok0 + 64 * wc + 16 * t + n;
+  for (int t = 0; t < TT; ++t) {
+    const int tok = tok0 + 16 * TT * wc + 16 * t + n;
     if (tok >= B) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = row0 + 128 * wr + 16 * i + 4 * j;
+    for (int i = 0; i < RT; ++i) {
+      const int r = row0 + 16 * RT * wr + 16 * i + 4 * j;
+      const int64_t o = (int64_t)tok * R + r;
+      if (vec && r + 3 < R) {
+        if (kind == NM_F32) {
+          *reinterpret_cast<f4v_t *>(static_cast<float *>(y) + o) = acc[i][t];
+        } else {
+          uint16_t h[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (r + e < R) store_out(y, (int64_t)tok * R + r + e, acc[i][t][e], out_kind);
+          for (int e = 0; e < 4; ++e)
+            h[e] = kind == NM_F16 ? __builtin_bit_cast(uint16_t, (_Float16)acc[i][t][e])
+                                  : f32_to_bf16_rne(acc[i][t][e]);
+          const uint2 v = {h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16};
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + o) = v;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (r + e < R) store_out(y, o + e, acc[i][t][e], out_kind);
+      }
     }
   }
+}
+
+// Compute units and the LDS one workgroup may use, per device (queried once).
+struct PrefillDev {
+  int cus = 0;
+  size_t lds = 0;
+};
+PrefillDev g_prefill_dev[64];
+std::mutex g_prefill_mu;
+
+nm_status prefill_device(PrefillDev *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return NM_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_prefill_mu);
+  PrefillDev &d = g_prefill_dev[dev];
+  if (d.cus == 0) {
+    int cus = 0, lds = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    d.lds = (size_t)lds;
+    d.cus = cus;
+  }
+  *out = d;
+  return NM_OK;
 }
 
 }  // namespace
@@ -263,18 +357,51 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
   if (!aligned(values, 16) || !aligned(bits, 4) || !aligned(X, 16) ||
       !aligned(Y, out_dt == NM_F32 ? 4 : 2))
     return NM_ERR_ALIGN;
-  const int64_t nrt = (rows + kPRows - 1) / kPRows, ntt = (batch + kPToks - 1) / kPToks;
+  const int vec = rows % 4 == 0 && aligned(Y, out_dt == NM_F32 ? 16 : 8);
+  PrefillDev dev;
+  const nm_status ds = prefill_device(&dev);
+  if (ds != NM_OK) return ds;
+  // Tile shape: 7 or 8 row tiles and 1, 2 or 4 token tiles per wave.  The
+  // time of a shape is taken as the rounds of workgroups over the compute
+  // units times the bytes a workgroup stages per step (values and mask words
+  // of 32 RT rows, x of 64 TT tokens): small batches take narrower token
+  // tiles so that more workgroups run, large ones the widest tile that
+  // fills whole rounds.  Ties go to the larger tile.
+  int best_rt = 0, best_tt = 0;
+  int64_t best = INT64_MAX;
+  for (int tt : {4, 2, 1}) {
+    if ((size_t)prefill_lds(tt) > dev.lds) continue;
+    for (int rt : {8, 7}) {
+      const int64_t tiles = (rows + 32 * rt - 1) / (32 * rt) * ((batch + 64 * tt - 1) / (64 * tt));
+      const int64_t c = (tiles + dev.cus - 1) / dev.cus * (2304 * rt + 8192 * tt);
+      if (c < best) best = c, best_rt = rt, best_tt = tt;
+    }
+  }
+  if (best_rt == 0) return NM_ERR_UNSUPPORTED;
+  const int64_t nrt = (rows + 32 * best_rt - 1) / (32 * best_rt);
+  const int64_t ntt = (batch + 64 * best_tt - 1) / (64 * best_tt);
   if (nrt * ntt > INT32_MAX) return NM_ERR_INVALID_ARG;
-  constexpr int NS = kPrefillStages;
-  auto go = [&](auto fn) {
-    hipLaunchKernelGGL(fn, dim3((unsigned)(nrt * ntt)), dim3(256), prefill_lds(NS), (hipStream_t)stream,
-                       (const uint16_t *)values, bits, (const uint16_t *)X, Y, (int)batch,
-                       (int)rows, (int)cols, (int)nrt, (int)ntt, (int)out_dt);
+  auto go = [&](auto fn, int tt) {
+    hipLaunchKernelGGL(fn, dim3((unsigned)(nrt * ntt)), dim3(kPWaves * kWave), prefill_lds(tt),
+                       (hipStream_t)stream, (const uint16_t *)values, bits, (const uint16_t *)X, Y,
+                       (int)batch, (int)rows, (int)cols, (int)nrt, (int)ntt, (int)out_dt, vec);
+  };
+  auto pick = [&](auto bf) {
+    constexpr bool BF = decltype(bf)::value;
+    const int key = best_rt * 10 + best_tt;
+    switch (key) {
+      case 84: go(nm_spmm_prefill_kernel<BF, 8, 4>, 4); break;
+      case 82: go(nm_spmm_prefill_kernel<BF, 8, 2>, 2); break;
+      case 81: go(nm_spmm_prefill_kernel<BF, 8, 1>, 1); break;
+      case 74: go(nm_spmm_prefill_kernel<BF, 7, 4>, 4); break;
+      case 72: go(nm_spmm_prefill_kernel<BF, 7, 2>, 2); break;
+      default: go(nm_spmm_prefill_kernel<BF, 7, 1>, 1); break;
+    }
   };
   if (in_dt == NM_BF16)
-    go(nm_spmm_prefill_kernel<true, NS>);
+    pick(std::true_type{});
   else
-    go(nm_spmm_prefill_kernel<false, NS>);
+    pick(std::false_type{});
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? NM_OK : hip_fail(e);
 }

@@ -844,8 +844,13 @@ def test_select_zero_sized_and_rejections():
 
 # ---- prefill-side product (2:4 on the sparse matrix cores, any batch) ----------------
 
+# Tile shapes the launch picks on 256 compute units (row tiles, token tiles
+# per wave): (7, 1) for the small shapes, (7, 2) for 7201 x 600, (8, 1),
+# (8, 2) and (8, 4) for 4096 rows at 1024, 2048 and 4096 tokens, (7, 4) for
+# 14336 rows at 1024 tokens
 PREFILL_SHAPES = [(1, 64, 1), (16, 128, 16), (300, 320, 17), (257, 1024, 130), (512, 4096, 128),
-                  (100, 64, 300), (640, 2112, 257)]
+                  (100, 64, 300), (640, 2112, 257), (7201, 128, 600), (4096, 64, 1024),
+                  (4096, 64, 2048), (4096, 64, 4096), (14336, 64, 1024)]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -875,9 +880,10 @@ def test_prefill_matches_oracle(dtype):
         assert rel_l2(Y[b], want[b]) <= TOL
 
 
+@pytest.mark.parametrize("rows", [300, 257])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_prefill_16bit_output_is_rounded_fp32(dtype):
-    rows, cols, batch = 300, 512, 40
+def test_prefill_16bit_output_is_rounded_fp32(dtype, rows):
+    cols, batch = 512, 40
     W, keep, X = inputs(rows, cols, 2, 4, dtype, batch, seed=32)
     values, bits = gpu_pack(W, keep, 2, 4, dtype)
     Xt = t16(X, dtype)
