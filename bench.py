@@ -279,10 +279,10 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch) at batch
     # 1; see profiles/nm_spmv_2of4_hbm_counters.md
-    (14336, 4096): ("852ae973c5ada7949c897c182674873ad43b357cb4c8c2d17ad3ab4c6f2bc47f",
-                    66260289),
-    (8192, 8192): ("852ae973c5ada7949c897c182674873ad43b357cb4c8c2d17ad3ab4c6f2bc47f",
-                   75727931),
+    (14336, 4096): ("6fb401fd75d9001f1f07edf1e817f9b2869f676bd80e374025ec4f0f67f26cda",
+                    66264639),
+    (8192, 8192): ("6fb401fd75d9001f1f07edf1e817f9b2869f676bd80e374025ec4f0f67f26cda",
+                   75727675),
 }
 
 

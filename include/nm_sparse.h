@@ -260,9 +260,8 @@ int nm_dense_gemv(const void *W, const void *X, void *Y, int batch,
  * batch >= 2 and for the other patterns at batch >= 5 where they can run,
  * the VALU kernels otherwise; except that 2:4 at batch 2..4 stays on the
  * VALU kernel (x stored plainly per token in LDS) where that measured
- * faster: at most 1024 rows; at batch 2 also rows >= 14336, cols >= 25600
- * or rows * cols <= 4096 * 4096; at batch 3 and 4 also rows >= 14336 with
- * cols <= 4096. */
+ * faster: at most 1024 rows, and at batch 2 also rows >= 14336, cols >=
+ * 25600 or rows * cols <= 4096 * 4096. */
 typedef enum { NM_KERNEL_AUTO = 0, NM_KERNEL_VALU = 1, NM_KERNEL_MFMA = 2 } nm_kernel;
 
 /* Launch shape of the sparse and dense kernels, for tuning sweeps.  Fields

@@ -899,10 +899,14 @@ constexpr int kMValBytes = 16 * kMBlkCols;      // 16 rows x 128 values x 2 B
 constexpr int kMMaskBytes = 16 * kMBlkCols / 8;  // 16 rows x 8 words x 4 B
 constexpr int kMXTok = 2 * kMBlkCols;           // x bytes per token per block
 
-// LDS bytes of one ring slot for a padded batch BP (x for BP tokens).
-__host__ __device__ constexpr int mfma_slot_bytes(int bp) {
-  return kMValBytes + kMMaskBytes + kMXTok * bp;
+// LDS bytes of one ring slot for a padded batch BP (x for BP tokens); the
+// 2:4 kind keeps its mask words in a ring of its own (two blocks per slot).
+__host__ __device__ constexpr int mfma_slot_bytes(int bp, int kind) {
+  return kMValBytes + (kind == 0 ? 0 : kMMaskBytes) + kMXTok * bp;
 }
+// Mask ring of the 2:4 kind: slots of two blocks' mask words (16 rows x 64
+// bytes), enough that a slot is refilled only after both blocks are done.
+__host__ __device__ constexpr int mfma_mask_slots(int nb) { return (nb + 2) / 2; }
 
 // Dense 16 x 64 tile of the decompressing kinds: rows padded to 144 bytes
 // (64 x 2 + 16), so the 16 rows of a 16-lane read start on distinct banks.
@@ -911,7 +915,8 @@ constexpr int kMTileBytes = 16 * kMTileRow;
 
 // LDS of one wave: its ring, and the dense tile of the decompressing kinds.
 __host__ __device__ constexpr int mfma_wave_bytes(int bp, int nb, int kind) {
-  return nb * mfma_slot_bytes(bp) + (kind == kMfmaSparse24 ? 0 : kMTileBytes);
+  return nb * mfma_slot_bytes(bp, kind) +
+         (kind == kMfmaSparse24 ? 1024 * mfma_mask_slots(nb) : kMTileBytes);
 }
 
 // Operands of one 64-column step of the matrix-core kernel.
@@ -926,8 +931,11 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K,
     int out_kind) {
   constexpr int XQ = BP / 2;          // x instructions per block (2 tokens each)
-  constexpr int ND = 4 + 2 + XQ;      // direct-to-LDS instructions per block
-  constexpr int SLOT = mfma_slot_bytes(BP);
+  constexpr int ND = 4 + 2 + XQ;      // direct-to-LDS instructions per block (not 2:4)
+  constexpr int SLOT = mfma_slot_bytes(BP, KIND);
+  constexpr bool M2 = KIND == kMfmaSparse24;     // masks by pairs of blocks
+  constexpr int MS = mfma_mask_slots(NB);
+  constexpr int XB = M2 ? kMValBytes : kMValBytes + kMMaskBytes;  // x within a slot
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -965,6 +973,13 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     const int64_t r = min(row0 + rr, R - 1);
     boff[q] = (int)(r * (K / 8)) + 8 * sbeg + 4 * ((lane & 7) ^ ((rr >> 2) & 7));
   }
+  // 2:4: the mask words of blocks 2p, 2p + 1 (64 bytes per row) in one load,
+  // lane i -> row i >> 2, 16-byte piece (i & 3) ^ (row >> 2 & 3)
+  const int mrow = lane >> 2;
+  const int moff2 = (int)(min(row0 + mrow, R - 1) * (K / 8)) + 8 * sbeg +
+                    16 * ((lane & 3) ^ ((mrow >> 2) & 3));
+  const int npairs = (nblk + 1) >> 1;
+  const uint32_t mring = ring + (uint32_t)(NB * SLOT);
 #pragma unroll
   for (int q = 0; q < XQ; ++q) {
     const int t = 2 * q + (lane >> 5);
@@ -980,15 +995,22 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     // the block offset goes into the vector offset, which the range check
     // covers (the scalar offset is not checked): a wave's last block may
     // reach past its K range, and on the last rows past the arrays
+    if constexpr (M2) {
+      if ((b & 1) == 0)
+        lds_load16_nt((b >> 1) < npairs ? rb : r0, mring + (uint32_t)(((b >> 1) % MS) * 1024),
+                      moff2 + 64 * (b >> 1), 0);
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       lds_load16_nt(V, sl + 1024 * q, voff[q] + kMValBytes / 16 * b, 0);
+    if constexpr (!M2) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      lds_load4_nt(M, sl + kMValBytes + 256 * q, boff[q] + kMMaskBytes / 16 * b, 0);
+      for (int q = 0; q < 2; ++q)
+        lds_load4_nt(M, sl + kMValBytes + 256 * q, boff[q] + kMMaskBytes / 16 * b, 0);
+    }
 #pragma unroll
     for (int q = 0; q < XQ; ++q)
-      lds_load16(X, sl + kMValBytes + kMMaskBytes + 1024 * q, xoff[q] + kMXTok * b, 0);
+      lds_load16(X, sl + XB + 1024 * q, xoff[q] + kMXTok * b, 0);
   };
 
   // reader addresses within a slot, step 0 (steps add constant offsets only
@@ -996,12 +1018,17 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
   const int tn = min(n, B - 1);
   f4v_t acc = {0.f, 0.f, 0.f, 0.f};
   // operands of step s of the block in slot sl
-  auto fetch = [&](uint32_t sl, int s) {
+  auto fetch = [&](uint32_t sl, int s, int b) {
     MfmaOps o;
     o.a = ld<u32x4_t>((lds_ptr)(size_t)(sl + n * 256 + 16 * ((4 * s + j) ^ n)));
-    o.w = ld<uint32_t>((lds_ptr)(size_t)(sl + kMValBytes + n * 32 +
-                                         4 * ((2 * s + (j >> 1)) ^ ((n >> 2) & 7))));
-    const uint32_t xb = sl + kMValBytes + kMMaskBytes + tn * kMXTok;
+    if constexpr (M2)
+      o.w = ld<uint32_t>((lds_ptr)(size_t)(mring + ((b >> 1) % MS) * 1024 + n * 64 +
+                                           16 * ((2 * (b & 1) + (s >> 1)) ^ ((n >> 2) & 3)) +
+                                           4 * (2 * (s & 1) + (j >> 1))));
+    else
+      o.w = ld<uint32_t>((lds_ptr)(size_t)(sl + kMValBytes + n * 32 +
+                                           4 * ((2 * s + (j >> 1)) ^ ((n >> 2) & 7))));
+    const uint32_t xb = sl + XB + tn * kMXTok;
     o.x0 = ld<u32x4_t>((lds_ptr)(size_t)(xb + 16 * ((8 * s + j) ^ (tn & 7))));
     o.x1 = ld<u32x4_t>((lds_ptr)(size_t)(xb + 16 * ((8 * s + 4 + j) ^ (tn & 7))));
     return o;
@@ -1056,7 +1083,7 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     return ld<u32x4_t>((lds_ptr)(size_t)(tile + n * kMTileRow + 64 * t + 16 * j));
   };
   auto x_of = [&](uint32_t sl, int s, int t) {
-    const uint32_t xb = sl + kMValBytes + kMMaskBytes + tn * kMXTok;
+    const uint32_t xb = sl + XB + tn * kMXTok;
     return ld<u32x4_t>((lds_ptr)(size_t)(xb + 16 * ((8 * s + 4 * t + j) ^ (tn & 7))));
   };
   auto dense_step = [&](uint32_t sl, int s) {
@@ -1088,7 +1115,7 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
         const float w = half_to_f32<BF>((uint16_t)(v[k >> 1] >> (16 * (k & 1))));
 #pragma unroll
         for (int t = 0; t < BP; ++t) {
-          const uint32_t xa = sl + kMValBytes + kMMaskBytes + t * kMXTok +
+          const uint32_t xa = sl + XB + t * kMXTok +
                               16 * ((c >> 3) ^ (t & 7)) + 2 * (c & 7);
           p[t] = fmaf(w, half_to_f32<BF>(ld<uint16_t>((lds_ptr)(size_t)xa)), p[t]);
         }
@@ -1125,11 +1152,11 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     } else if (ns == 4) {  // whole block: every LDS read is issued before the first product
       MfmaOps o[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) o[s] = fetch(sl, s);
+      for (int s = 0; s < 4; ++s) o[s] = fetch(sl, s, b);
 #pragma unroll
       for (int s = 0; s < 4; ++s) mac(o[s]);
     } else {  // the wave's ragged last block
-      for (int s = 0; s < ns; ++s) mac(fetch(sl, s));
+      for (int s = 0; s < ns; ++s) mac(fetch(sl, s, b));
     }
   };
 
@@ -1141,7 +1168,17 @@ __global__ __launch_bounds__(1024) void nm_spmm_mfma_kernel(
     wait_lgkmcnt0();
     __builtin_amdgcn_sched_barrier(0);
     issue(b + NB - 1);
-    wait_vmcnt<(NB - 1) * ND>();  // block b has landed; NB - 1 blocks stay in flight
+    // block b has landed; NB - 1 blocks stay in flight (with the 2:4 kind,
+    // each even block among them also carries a mask load)
+    if constexpr (M2) {
+      constexpr int D = 4 + XQ;
+      if (b & 1)
+        wait_vmcnt<(NB - 1) * D + NB / 2>();  // evens among b+1..b+NB-1, b odd
+      else
+        wait_vmcnt<(NB - 1) * D + (NB - 1) / 2>();
+    } else {
+      wait_vmcnt<(NB - 1) * ND>();
+    }
     __builtin_amdgcn_sched_barrier(0);
     compute(b);
   }
@@ -1570,12 +1607,16 @@ size_t mfma_lds_bytes(int waves, int nb, int bp, int kind) {
 
 // Launch shape of the matrix-core kernel: threads_per_wg / 64 waves split K
 // for one 16-row tile; rows_per_wave is each wave's ring depth (blocks).
-// Measured on the 8B, 70B and Qwen3-32B shapes at batch 2..8: four waves
-// per workgroup is best or within 5% everywhere; a ring of three blocks is
-// best while two such workgroups fit a CU's LDS (batch <= 4), else two.
-// For the decompressing kinds (measured on the 8B shapes at batch 2..8) the
-// ring of two blocks is best, with about 8 waves per CU in total, at most 8
-// per workgroup.
+// Measured on the 8B, 70B and Qwen3-32B shapes at batch 2..8 (2:4): four
+// waves per workgroup, halved while a wave would walk fewer than 32 steps of
+// 64 columns and the grid keeps at least 1024 waves (14336x4096 at batch 8:
+// 14.9 us with two waves against 16.2 with four; 8192x5120 11.5 against
+// 12.5; 4096x4096, 256 tiles, keeps four: 6.4 against 7.4); a ring of three
+// blocks while at least 8 waves of such workgroups fit a CU's LDS, else two
+// (two waves of three blocks at batch 8 leave 6 waves per CU: 17.5 us on
+// 14336x4096).  For the decompressing kinds (measured on the 8B shapes at
+// batch 2..8) the ring of two blocks is best, with about 8 waves per CU in
+// total, at most 8 per workgroup.
 void mfma_default(int64_t rows, int64_t cols, int batch, int kind, const DevInfo &di,
                   nm_launch_cfg *cfg) {
   const int bp = pad_batch(batch) < 2 ? 2 : pad_batch(batch);
@@ -1588,7 +1629,10 @@ void mfma_default(int64_t rows, int64_t cols, int batch, int kind, const DevInfo
     w = t < 1 ? 1 : t > 8 ? 8 : (int)t;
   }
   while (w > 1 && nsteps / w < 8) --w;  // at least two blocks of K per wave
-  const int nb = (kind == kMfmaSparse24 && 2 * mfma_lds_bytes(w, 3, bp, kind) <= kLdsCap) ? 3 : 2;
+  if (kind == kMfmaSparse24)
+    while (w > 1 && nsteps / w < 32 && tiles * (w / 2) >= 1024) w /= 2;
+  const int nb =
+      (kind == kMfmaSparse24 && (int64_t)(kLdsCap / mfma_lds_bytes(w, 3, bp, kind)) * w >= 8) ? 3 : 2;
   while (w > 1 && mfma_lds_bytes(w, nb, bp, kind) > budget) --w;
   cfg->kernel = NM_KERNEL_MFMA;
   cfg->k_split = 1;
@@ -1605,21 +1649,19 @@ constexpr int kDenseMfmaMinBatch = 5;  // measured: the VALU kernel wins at batc
 // 2:4 shapes where the VALU row kernel with x stored plainly per token beats
 // the sparse matrix cores although batch >= kMfmaMinBatch.  Measured on the
 // 8B, 70B and Qwen3-32B shapes (us, cache-cold, one box, VALU / matrix cores):
-//  - at most 1024 rows, batch 2..4: 1024x4096 3.79 / 4.99 (batch 2), 4.50 /
-//    5.26 (batch 4); 1024x8192 5.56 / 6.88, 6.77 / 7.45;
-//  - batch 2: 14336 rows or more (14336x4096 13.25 / 15.02, 25600x5120 25.08
-//    / 29.42, 28672x8192 42.46 / 43.34), K >= 25600 (8192x28672 43.01 /
-//    46.88, 5120x25600 33.67 / 36.50), up to 4096 x 4096 weights (5.81 /
-//    5.98); the matrix cores win between (8192x5120 13.15 / 10.96, 8192x8192
-//    17.45 / 15.13, 5120x8192, 4096x14336, 6144x4096);
-//  - batch 3, 4: 14336 rows or more with K <= 4096 (14336x4096 15.02 / 15.81
-//    at batch 4); the matrix cores win elsewhere (4096x4096 6.66 / 6.23).
-// From batch 5 the matrix cores win everywhere.
+//  - at most 1024 rows, batch 2..4: 1024x4096 3.78 / 4.82 (batch 2), 4.49 /
+//    5.08 (batch 4); 1024x8192 5.51 / 6.60, 6.75 / 7.00;
+//  - batch 2: 14336 rows or more (14336x4096 13.28 / 13.90, 25600x5120 25.28
+//    / 29.67, 28672x8192 42.40 / 42.21), K >= 25600 (5120x25600 33.52 /
+//    34.94, 8192x28672 43.47 / 43.43), up to 4096 x 4096 weights (5.77 /
+//    5.90); the matrix cores win between (8192x5120 13.39 / 10.83, 8192x8192
+//    17.81 / 14.21, 5120x8192, 4096x14336, 6144x4096).
+// From batch 3 the matrix cores win on every shape above 1024 rows
+// (14336x4096 at batch 4: 15.73 / 14.13).
 bool valu_beats_mfma_24(int64_t rows, int64_t cols, int batch) {
   if (batch > 4) return false;
   if (rows <= 1024) return true;
-  if (batch == 2) return rows >= 14336 || cols >= 25600 || rows * cols <= 4096LL * 4096;
-  return rows >= 14336 && cols <= 4096;
+  return batch == 2 && (rows >= 14336 || cols >= 25600 || rows * cols <= 4096LL * 4096);
 }
 
 int rows_batch_chunks(int64_t cols, int bp);

@@ -446,10 +446,10 @@ def test_default_launch_picks_matrix_cores_for_small_batch():
     for n, m in PATTERNS:
         assert native.nm_default_launch(14336, 4096, 8, n, m).kernel == MFMA, (n, m)
         assert native.nm_default_launch(14336, 4096, 1, n, m).kernel == VALU, (n, m)
-        # the decompressing kinds start at batch 5; 2:4 at 14336 x 4096 keeps the
-        # VALU kernel to batch 4 (measured faster there)
-        assert native.nm_default_launch(14336, 4096, 4, n, m).kernel == VALU, (n, m)
+        # the decompressing kinds start at batch 5, 2:4 on the sparse
+        # instruction at batch 3 on these shapes
         want4 = MFMA if (n, m) == (2, 4) else VALU
+        assert native.nm_default_launch(14336, 4096, 4, n, m).kernel == want4, (n, m)
         assert native.nm_default_launch(8192, 8192, 4, n, m).kernel == want4, (n, m)
     assert native.nm_default_launch(14336, 4080 + 16, 8, 2, 4).kernel == MFMA
     assert native.nm_default_launch(14336, 4064, 8, 2, 4).kernel == VALU  # K % 64 != 0
@@ -458,24 +458,40 @@ def test_default_launch_picks_matrix_cores_for_small_batch():
 
 def test_default_launch_2of4_small_batch_rule():
     """2:4 at batch 2..4 takes the VALU kernel (x plain per token) where it
-    measured faster than the matrix cores: at most 1024 rows (batch 2..4); at
-    batch 2 also 14336 rows or more, K >= 25600, or up to 4096 x 4096 weights;
-    at batch 3 and 4 also 14336 rows or more with K <= 4096.  Batch 5..8
-    always takes the matrix cores."""
+    measured faster than the matrix cores: at most 1024 rows (batch 2..4), and
+    at batch 2 also 14336 rows or more, K >= 25600, or up to 4096 x 4096
+    weights.  Every other shape at batch 3 and 4, and every shape at batch
+    5..8, takes the matrix cores."""
     d = native.nm_default_launch
     for b in (2, 3, 4):
-        for rows, cols in [(1024, 4096), (1024, 8192), (14336, 4096)]:
+        for rows, cols in [(1024, 4096), (1024, 8192)]:
             assert d(rows, cols, b, 2, 4).kernel == VALU, (rows, cols, b)
-    for rows, cols in [(4096, 4096), (25600, 5120), (28672, 8192), (8192, 28672), (5120, 25600)]:
+    for rows, cols in [(4096, 4096), (14336, 4096), (25600, 5120), (28672, 8192), (8192, 28672),
+                       (5120, 25600)]:
         assert d(rows, cols, 2, 2, 4).kernel == VALU, (rows, cols)
     for rows, cols in [(4096, 14336), (8192, 8192), (8192, 5120), (5120, 8192), (6144, 4096)]:
         assert d(rows, cols, 2, 2, 4).kernel == MFMA, (rows, cols)
     for b in (3, 4):
-        for rows, cols in [(4096, 4096), (4096, 14336), (25600, 5120), (28672, 8192), (8192, 28672)]:
+        for rows, cols in [(4096, 4096), (14336, 4096), (4096, 14336), (25600, 5120), (28672, 8192),
+                           (8192, 28672)]:
             assert d(rows, cols, b, 2, 4).kernel == MFMA, (rows, cols, b)
     for b in (5, 8):
         for rows, cols in [(1024, 4096), (4096, 4096), (14336, 4096)]:
             assert d(rows, cols, b, 2, 4).kernel == MFMA, (rows, cols, b)
+
+
+def test_default_launch_matrix_core_shape():
+    """Waves per workgroup and ring depth of the 2:4 matrix-core kernel (256
+    CUs, 160 KiB of LDS): four waves, halved while a wave would walk fewer
+    than 32 steps of 64 columns and at least 1024 waves remain; three blocks
+    in the ring while 8 waves of such workgroups fit a CU, else two."""
+    d = native.nm_default_launch
+    want = {(14336, 4096, 4): (128, 3), (14336, 4096, 8): (128, 2), (4096, 4096, 8): (256, 2),
+            (4096, 4096, 4): (256, 3), (8192, 5120, 8): (128, 2), (8192, 8192, 8): (256, 2),
+            (4096, 14336, 4): (256, 3), (28672, 8192, 8): (256, 2), (6144, 4096, 8): (256, 2)}
+    for (rows, cols, b), (threads, nb) in want.items():
+        c = d(rows, cols, b, 2, 4)
+        assert c.kernel == MFMA and (c.threads_per_wg, c.rows_per_wave) == (threads, nb), (rows, cols, b)
 
 
 @pytest.mark.parametrize("batch", [2, 3, 4, 5, 8])
