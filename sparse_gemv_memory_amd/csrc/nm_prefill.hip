@@ -100,7 +100,7 @@ template <bool BF, int RT, int TT>
 __global__ __launch_bounds__(512) void nm_spmm_prefill_kernel(
     const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int R, int K, int nrt, int ntt,
-    int out_kind, int vec) {
+    int out_kind, int vec, int ks, int kper, float *__restrict__ part) {
   static_assert(RT == 7 || RT == 8, "row tiles per wave");
   static_assert(TT == 1 || TT == 2 || TT == 4, "token tiles per wave");
   constexpr int kRows = 32 * RT;    // rows per workgroup
@@ -113,20 +113,24 @@ __global__ __launch_bounds__(512) void nm_spmm_prefill_kernel(
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15, j = lane >> 4;
-  // Tile of this workgroup.  Workgroups go to the 8 XCDs round-robin
-  // (block b on XCD b % 8), and each XCD has its own L2: XCD x takes a
-  // contiguous range of tiles, ordered by groups of 4 row tiles x all token
-  // tiles, so the workgroups running together on one XCD share their
-  // weights and activations through its L2.
-  const int T = nrt * ntt;
+  // Tile and part of K of this workgroup.  Workgroups go to the 8 XCDs
+  // round-robin (block b on XCD b % 8), and each XCD has its own L2: XCD x
+  // takes a contiguous range of (tile, part) pairs, the tiles ordered by
+  // groups of 4 row tiles x all token tiles, so the workgroups running
+  // together on one XCD share their weights and activations through its L2.
+  const int T = nrt * ntt, TV = T * ks;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  const int tile = xcd * (T / 8) + min(xcd, T % 8) + slot;
+  const int vt = xcd * (TV / 8) + min(xcd, TV % 8) + slot;
+  const int tile = vt / ks, kpart = vt - tile * ks;
   const int group = tile / (4 * ntt);
   const int first_r = 4 * group, gr = min(nrt - first_r, 4);
   const int in = tile - group * 4 * ntt;
   const int rt = first_r + in % gr, tt = in / gr;
   const int row0 = rt * kRows, tok0 = tt * kToks;
-  const int nk = K >> 6;
+  // steps of 64 columns of this part of K: sbeg .. sbeg + nk - 1 (kper is a
+  // multiple of 4, so the parts start on a group of mask words)
+  const int sbeg = min(K >> 6, kpart * kper);
+  const int nk = min(K >> 6, sbeg + kper) - sbeg;
   const uint32_t base = (uint32_t)(size_t)(lds_ptr)lds;
 
   const __amdgpu_buffer_rsrc_t rv =
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(512) void nm_spmm_prefill_kernel(
   for (int q = 0; q < 2; ++q) {
     const int r = 16 * (8 * q + w) + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
-    voff[q] = min(row0 + r, R - 1) * K + 16 * c;
+    voff[q] = min(row0 + r, R - 1) * K + 16 * c + 64 * sbeg;
   }
   // masks: wave w fills LDS bytes 1024 w .. + 1024 of a mask slot, i.e. rows
   // 32 w .. + 32, lane i -> row (i >> 1), 16-byte half (i & 1) ^ (row >> 3 & 1)
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(512) void nm_spmm_prefill_kernel(
   int moff;
   {
     const int r = 32 * w + (lane >> 1);
-    moff = min(row0 + r, R - 1) * (K / 8) + 16 * ((lane & 1) ^ ((r >> 3) & 1));
+    moff = min(row0 + r, R - 1) * (K / 8) + 16 * ((lane & 1) ^ ((r >> 3) & 1)) + 8 * sbeg;
   }
   // x: instruction q of wave w fills LDS bytes 1024 (8 q + w) .. + 1024 of
   // the stage's x, i.e. tokens 8 (8 q + w) .. + 8, lane i -> token (i >> 3),
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(512) void nm_spmm_prefill_kernel(
   for (int q = 0; q < TT; ++q) {
     const int t = 8 * (8 * q + w) + (lane >> 3);
     const int c = (lane & 7) ^ ((t >> 1) & 7);
-    xoff[q] = (int)min((int64_t)(tok0 + t) * K * 2, (int64_t)B * K * 2) + 16 * c;
+    xoff[q] = (int)min((int64_t)(tok0 + t) * K * 2, (int64_t)B * K * 2) + 16 * c + 128 * sbeg;
   }
   // step s into stage slot s % 3; a step past the last loads from the empty
   // resource (no memory traffic, same instruction count), so the wait counts
@@ -280,8 +284,13 @@ __global__ __launch_bounds__(512) void nm_spmm_prefill_kernel(
 
   // lane (j, n) of tile (i, t): rows 4 j .. 4 j + 3 of row tile i, token n;
   // one 16-byte (fp32) or 8-byte store per tile where vec (R % 4 == 0 and y
-  // aligned to that size) and the 4 rows exist
-  const int kind = out_kind & 0xff;
+  // aligned to that size) and the 4 rows exist.  With K in several parts the
+  // fp32 sums go to this part's slice of part (B x R each) instead.
+  const int kind = part ? NM_F32 : out_kind & 0xff;
+  if (part) {
+    y = part + (int64_t)kpart * B * R;
+    vec = (R & 3) == 0;
+  }
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     const int tok = tok0 + 16 * TT * wc + 16 * t + n;
@@ -305,8 +314,39 @@ __global__ __launch_bounds__(512) void nm_spmm_prefill_kernel(
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (r + e < R) store_out(y, o + e, acc[i][t][e], out_kind);
+          if (r + e < R) store_out(y, o + e, acc[i][t][e], kind);
       }
+    }
+  }
+}
+
+// Sum of the ks fp32 partial products of a split K (each n = B x R values,
+// laid out as Y), in part order, into Y in out_kind; 4 values per thread
+// where vec (n % 4 == 0 and Y aligned to 4 values).
+__global__ __launch_bounds__(256) void nm_prefill_reduce_kernel(const float *__restrict__ part,
+                                                               int ks, int64_t n, void *y,
+                                                               int out_kind, int vec) {
+  const int64_t i0 = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (i0 >= n) return;
+  if (vec) {
+    f4v_t s = *reinterpret_cast<const f4v_t *>(part + i0);
+    for (int k = 1; k < ks; ++k) s += *reinterpret_cast<const f4v_t *>(part + k * n + i0);
+    const int kind = out_kind & 0xff;
+    if (kind == NM_F32) {
+      *reinterpret_cast<f4v_t *>(static_cast<float *>(y) + i0) = s;
+    } else {
+      uint16_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        h[e] = kind == NM_F16 ? __builtin_bit_cast(uint16_t, (_Float16)s[e]) : f32_to_bf16_rne(s[e]);
+      const uint2 v = {h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16};
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + i0) = v;
+    }
+  } else {
+    for (int64_t i = i0; i < i0 + 4 && i < n; ++i) {
+      float s = part[i];
+      for (int k = 1; k < ks; ++k) s += part[k * n + i];
+      store_out(y, i, s, out_kind);
     }
   }
 }
@@ -361,30 +401,49 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
   PrefillDev dev;
   const nm_status ds = prefill_device(&dev);
   if (ds != NM_OK) return ds;
-  // Tile shape: 7 or 8 row tiles and 1, 2 or 4 token tiles per wave.  The
-  // time of a shape is taken as the rounds of workgroups over the compute
-  // units times the bytes a workgroup stages per step (values and mask words
-  // of 32 RT rows, x of 64 TT tokens): small batches take narrower token
-  // tiles so that more workgroups run, large ones the widest tile that
-  // fills whole rounds.  Ties go to the larger tile.
-  int best_rt = 0, best_tt = 0;
-  int64_t best = INT64_MAX;
-  for (int tt : {4, 2, 1}) {
-    if ((size_t)prefill_lds(tt) > dev.lds) continue;
-    for (int rt : {8, 7}) {
-      const int64_t tiles = (rows + 32 * rt - 1) / (32 * rt) * ((batch + 64 * tt - 1) / (64 * tt));
-      const int64_t c = (tiles + dev.cus - 1) / dev.cus * (2304 * rt + 8192 * tt);
-      if (c < best) best = c, best_rt = rt, best_tt = tt;
+  // Tile shape: 7 or 8 row tiles and 1, 2 or 4 token tiles per wave, and K in
+  // 1, 2 or 4 parts.  The time of a shape is taken as the rounds of
+  // workgroups over the compute units times the bytes a workgroup stages
+  // (values and mask words of 32 RT rows, x of 64 TT tokens, per step, over
+  // its part of K), plus, for a split K, twice the bytes of the fp32 partial
+  // products written and summed (HBM traffic, about half the rate of the
+  // staging).  Small batches take narrow token tiles, and a split K where the
+  // tiles alone leave compute units idle; ties go to the earlier choice.
+  const int64_t nk = cols / 64;
+  int best_rt = 0, best_tt = 0, best_ks = 1;
+  int64_t best = INT64_MAX, best_kper = nk;
+  for (int ks : {1, 2, 4}) {
+    const int64_t kper = ((nk + ks - 1) / ks + 3) / 4 * 4;
+    if (ks > 1 && (nk < 8 * ks || kper * (ks - 1) >= nk)) continue;
+    for (int tt : {4, 2, 1}) {
+      if ((size_t)prefill_lds(tt) > dev.lds) continue;
+      for (int rt : {8, 7}) {
+        const int64_t tiles =
+            (rows + 32 * rt - 1) / (32 * rt) * ((batch + 64 * tt - 1) / (64 * tt)) * ks;
+        int64_t c = (tiles + dev.cus - 1) / dev.cus * kper * (2304 * rt + 8192 * tt);
+        if (ks > 1) c += 4 * (ks + 1) * batch * rows * 4 / dev.cus;
+        if (c < best) best = c, best_rt = rt, best_tt = tt, best_ks = ks, best_kper = kper;
+      }
     }
   }
   if (best_rt == 0) return NM_ERR_UNSUPPORTED;
   const int64_t nrt = (rows + 32 * best_rt - 1) / (32 * best_rt);
   const int64_t ntt = (batch + 64 * best_tt - 1) / (64 * best_tt);
-  if (nrt * ntt > INT32_MAX) return NM_ERR_INVALID_ARG;
+  if (nrt * ntt * best_ks > INT32_MAX) return NM_ERR_INVALID_ARG;
+  float *part = nullptr;
+  const hipStream_t hs = (hipStream_t)stream;
+  if (best_ks > 1) {
+    // the partial products, freed in stream order after the sum (a split K
+    // is chosen only where the tiles leave compute units idle, so small)
+    if ((batch * rows + 1023) / 1024 > INT32_MAX) return NM_ERR_INVALID_ARG;
+    hipError_t e = hipMallocAsync((void **)&part, (size_t)best_ks * batch * rows * 4, hs);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   auto go = [&](auto fn, int tt) {
-    hipLaunchKernelGGL(fn, dim3((unsigned)(nrt * ntt)), dim3(kPWaves * kWave), prefill_lds(tt),
-                       (hipStream_t)stream, (const uint16_t *)values, bits, (const uint16_t *)X, Y,
-                       (int)batch, (int)rows, (int)cols, (int)nrt, (int)ntt, (int)out_dt, vec);
+    hipLaunchKernelGGL(fn, dim3((unsigned)(nrt * ntt * best_ks)), dim3(kPWaves * kWave),
+                       prefill_lds(tt), hs, (const uint16_t *)values, bits, (const uint16_t *)X, Y,
+                       (int)batch, (int)rows, (int)cols, (int)nrt, (int)ntt, (int)out_dt, vec,
+                       best_ks, (int)best_kper, part);
   };
   auto pick = [&](auto bf) {
     constexpr bool BF = decltype(bf)::value;
@@ -402,6 +461,17 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
     pick(std::true_type{});
   else
     pick(std::false_type{});
+  if (best_ks > 1) {
+    const int64_t n = batch * rows;
+    const int rvec = n % 4 == 0 && aligned(Y, out_dt == NM_F32 ? 16 : 8);
+    const int64_t groups = (n + 3) / 4;
+    hipLaunchKernelGGL(nm_prefill_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                       hs, part, best_ks, n, Y, (int)out_dt, rvec);
+    hipError_t e = hipGetLastError();
+    const hipError_t f = hipFreeAsync(part, hs);
+    if (e == hipSuccess) e = f;
+    return e == hipSuccess ? NM_OK : hip_fail(e);
+  }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? NM_OK : hip_fail(e);
 }

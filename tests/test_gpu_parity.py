@@ -861,12 +861,16 @@ def test_select_zero_sized_and_rejections():
 # ---- prefill-side product (2:4 on the sparse matrix cores, any batch) ----------------
 
 # Tile shapes the launch picks on 256 compute units (row tiles, token tiles
-# per wave): (7, 1) for the small shapes, (7, 2) for 7201 x 600, (8, 1),
-# (8, 2) and (8, 4) for 4096 rows at 1024, 2048 and 4096 tokens, (7, 4) for
-# 14336 rows at 1024 tokens
+# per wave, parts of K): (7, 1, 1) for the smallest shapes, (7, 1, 2) for
+# 257 x 1024 x 130 and 640 x 2112 x 257, (7, 1, 4) for 512 x 4096 x 128,
+# (7, 2, 1) for 7201 x 600, (8, 1, 1), (8, 2, 1) and (8, 4, 1) for 4096 rows
+# at 1024, 2048 and 4096 tokens, (7, 4, 1) for 14336 rows at 1024 tokens,
+# (8, 1, 4) for 1000 x 2048 x 1024, (7, 2, 4) for 4100 x 4096 x 256, (8, 2, 4)
+# for 1000 x 4096 x 2048
 PREFILL_SHAPES = [(1, 64, 1), (16, 128, 16), (300, 320, 17), (257, 1024, 130), (512, 4096, 128),
                   (100, 64, 300), (640, 2112, 257), (7201, 128, 600), (4096, 64, 1024),
-                  (4096, 64, 2048), (4096, 64, 4096), (14336, 64, 1024)]
+                  (4096, 64, 2048), (4096, 64, 4096), (14336, 64, 1024), (1000, 2048, 1024),
+                  (4100, 4096, 256), (1000, 4096, 2048)]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -935,6 +939,24 @@ def test_prefill_full_size_sampled_rows():
     got = Y[:, idx]
     for b in range(batch):
         assert rel_l2(got[b], want[b]) <= TOL
+
+
+@pytest.mark.parametrize("rows,cols,batch", [(4096, 14336, 1024), (4100, 8192, 512)])
+def test_prefill_split_k_sampled_rows_integer_exact(rows, cols, batch):
+    """K in 4 parts with the widest token tile ((8, 4, 4) for the 4096 x 14336
+    down shape at 1024 tokens, (7, 4, 4) for 4100 x 8192 at 512): integer
+    inputs, 384 sampled rows against the oracle exactly (the fp32 partial
+    sums of the parts and their total are exact integers)."""
+    W = synth.integer_weights(rows, cols, seed=rows + 3, dtype="f16")
+    keep = synth.random_mask(rows, cols, 2, 4, seed=batch + 1)
+    xi = np.random.default_rng(rows).integers(-4, 5, size=(batch, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    Y = f64(native.nm_spmm_prefill(values, bits, t16(X, "f16")))
+    idx = np.sort(np.random.default_rng(44).choice(rows, SAMPLE_ROWS, replace=False))
+    idx[0], idx[-1] = 0, rows - 1
+    want = oracle.masked_gemv(W, keep, X, False, rows_idx=idx, threads=8)
+    assert np.array_equal(Y[:, idx], want)
 
 
 def test_prefill_zero_columns_and_empty_batch():
