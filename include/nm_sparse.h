@@ -376,7 +376,12 @@ int nm_spmm_bitmask(const void *values, const uint32_t *bits, const int64_t *off
  * shape so that the workgroups fill the compute units) reuses each weight
  * byte for up to 256 tokens, where the decode entry points stream the
  * weights once per call for at most 8 tokens.  A workgroup takes up to
- * 160 KiB of LDS.
+ * 160 KiB of LDS.  Where the tiles alone would leave compute units idle, K
+ * is cut into 2 or 4 parts: the fp32 partial products go to a workspace
+ * (parts x batch x rows x 4 bytes) taken with hipMallocAsync on `stream` and
+ * freed with hipFreeAsync after a second kernel adds them in part order, so
+ * the result is deterministic and the call stays asynchronous (and
+ * capturable in a HIP graph).
  *   values, bits: nm_pack output for 2:4 (rows x cols/2 and rows x cols/32),
  *                 device; values and X 16-byte aligned, bits 4-byte aligned;
  *   X:            device, batch x cols, in_dt, row-major (token-major);
