@@ -377,7 +377,7 @@ int nm_spmm_bitmask(const void *values, const uint32_t *bits, const int64_t *off
  * byte for up to 256 tokens, where the decode entry points stream the
  * weights once per call for at most 8 tokens.  A workgroup takes up to
  * 160 KiB of LDS.  Where the tiles alone would leave compute units idle, K
- * is cut into 2 or 4 parts: the fp32 partial products go to a workspace
+ * is cut into 2, 4 or 8 parts: the fp32 partial products go to a workspace
  * (parts x batch x rows x 4 bytes) taken with hipMallocAsync on `stream` and
  * freed with hipFreeAsync after a second kernel adds them in part order, so
  * the result is deterministic and the call stays asynchronous (and

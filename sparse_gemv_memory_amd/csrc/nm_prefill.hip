@@ -402,7 +402,7 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
   const nm_status ds = prefill_device(&dev);
   if (ds != NM_OK) return ds;
   // Tile shape: 7 or 8 row tiles and 1, 2 or 4 token tiles per wave, and K in
-  // 1, 2 or 4 parts.  The time of a shape is taken as the rounds of
+  // 1, 2, 4 or 8 parts (each at least 8 steps).  The time of a shape is taken as the rounds of
   // workgroups over the compute units times the bytes a workgroup stages
   // (values and mask words of 32 RT rows, x of 64 TT tokens, per step, over
   // its part of K), plus, for a split K, twice the bytes of the fp32 partial
@@ -412,7 +412,7 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
   const int64_t nk = cols / 64;
   int best_rt = 0, best_tt = 0, best_ks = 1;
   int64_t best = INT64_MAX, best_kper = nk;
-  for (int ks : {1, 2, 4}) {
+  for (int ks : {1, 2, 4, 8}) {
     const int64_t kper = ((nk + ks - 1) / ks + 3) / 4 * 4;
     if (ks > 1 && (nk < 8 * ks || kper * (ks - 1) >= nk)) continue;
     for (int tt : {4, 2, 1}) {
