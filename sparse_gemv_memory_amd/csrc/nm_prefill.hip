@@ -405,10 +405,13 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
   // 1, 2, 4 or 8 parts (each at least 8 steps).  The time of a shape is taken as the rounds of
   // workgroups over the compute units times the bytes a workgroup stages
   // (values and mask words of 32 RT rows, x of 64 TT tokens, per step, over
-  // its part of K), plus, for a split K, twice the bytes of the fp32 partial
-  // products written and summed (HBM traffic, about half the rate of the
-  // staging).  Small batches take narrow token tiles, and a split K where the
-  // tiles alone leave compute units idle; ties go to the earlier choice.
+  // its part of K), plus, for a split K, 2.5 times the bytes of the fp32
+  // partial products written and summed (HBM traffic, at a lower rate than
+  // the staging; the weight was fitted to a sweep of every tile shape and
+  // split on the 8B gate and down shapes at 64..2048 tokens, where this
+  // choice came within 2% of the fastest).  Small batches take narrow token
+  // tiles, and a split K where the tiles alone leave compute units idle; ties
+  // go to the earlier choice.
   const int64_t nk = cols / 64;
   int best_rt = 0, best_tt = 0, best_ks = 1;
   int64_t best = INT64_MAX, best_kper = nk;
@@ -421,7 +424,7 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
         const int64_t tiles =
             (rows + 32 * rt - 1) / (32 * rt) * ((batch + 64 * tt - 1) / (64 * tt)) * ks;
         int64_t c = (tiles + dev.cus - 1) / dev.cus * kper * (2304 * rt + 8192 * tt);
-        if (ks > 1) c += 4 * (ks + 1) * batch * rows * 4 / dev.cus;
+        if (ks > 1) c += 5 * (ks + 1) * batch * rows * 4 / (2 * dev.cus);
         if (c < best) best = c, best_rt = rt, best_tt = tt, best_ks = ks, best_kper = kper;
       }
     }
