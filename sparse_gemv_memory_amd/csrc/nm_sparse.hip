@@ -665,11 +665,16 @@ __device__ __forceinline__ void collect_row(float (&acc)[BP], float (&res)[BP], 
 // in flight while item k is consumed.  U is chosen per shape so that it
 // divides the row's chunks per lane (no idle load slots in the last batch).  The first item's loads are issued
 // before x is committed to LDS, so the x and weight latencies overlap.
+// xdma (the plain-x kinds only): x's LDS image is x itself, BP rows of K
+// values, and is copied by direct-to-LDS loads issued before the weights',
+// instead of passing through registers; the host takes it where the image is
+// large beside the workgroup's weights (batch >= 2, or at most 4 rows per
+// workgroup).
 template <bool BF, int BP, int PK, int U, int XS, int KS = 1>
 __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
     const uint4 *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int rpw,
-    int out_kind) {
+    int out_kind, int xdma) {
   // XS: x groups per thread held in registers before the weight loads (the
   // host picks enough for all of x where it can: a group left to the staging
   // loop below waits for every outstanding load, the weights' included)
@@ -713,12 +718,39 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   // wave's first two items, then the groups are written to LDS.  Every load
   // here is issued unconditionally (indices clamped, dummy batches) so that
   // the waits before the LDS writes count exactly and leave the weight loads
-  // in flight.
+  // in flight.  With xdma the waves instead copy x's image in 1 KiB pieces
+  // (lane i's 16 bytes of piece p land at byte 1024 p + 16 i; rows of the
+  // image past B read as zeros through the range check), then issue the
+  // weights, and wait for the copies only.
   const int ngx = K >> 3;
+  const bool xd = plain_x(PK) && xdma != 0;
+  if (xd) {
+    const __amdgpu_buffer_rsrc_t rxs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, B * K * 2, kRsrcWord3);
+    const int nq = BP * ngx;  // 16-byte pieces of the image
+    const uint32_t lbase = (uint32_t)(size_t)(lds_ptr)lds;
+    for (int q0 = wid * kWave; q0 < nq; q0 += wpg * kWave)
+      if (q0 + lane < nq) lds_load16(rxs, lbase + 16 * q0, 16 * (q0 + lane), 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   XGroup<BP> xg[XS];
+  if constexpr (plain_x(PK)) {
+    // buffer loads (rows past B read as zeros); under xdma the resource is
+    // empty, so the same loads are issued without a branch and move no data
+    const __amdgpu_buffer_rsrc_t rxg =
+        __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, xd ? 0 : B * K * 2, kRsrcWord3);
 #pragma unroll
-  for (int s = 0; s < XS; ++s)
-    xgroup_load<BP>(xg[s], x, B, K, 0, min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1));
+    for (int s = 0; s < XS; ++s)
+#pragma unroll
+      for (int b = 0; b < BP; ++b)
+        xg[s].r[b] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rxg, b * K * 2 + 16 * min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1), 0, 0));
+  } else {
+#pragma unroll
+    for (int s = 0; s < XS; ++s)
+      xgroup_load<BP>(xg[s], x, B, K, 0, min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1));
+  }
   // the wave's items k = 0, 1 are in flight before x is committed to LDS;
   // an item past the wave's last is a dummy load (no memory traffic)
   auto item_load = [&](Batch<U> &bt, int k) {
@@ -735,7 +767,21 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
     u32x4_t *table = reinterpret_cast<u32x4_t *>(lds + 2 * (size_t)K);
     for (int b = threadIdx.x; b < 256; b += blockDim.x) table[b] = pair48_entry((uint32_t)b);
   }
-  if constexpr (plain_x(PK)) {  // plain layout: token b's group g at byte b * 2K + 16 g
+  if (xd) {
+    // the copies were issued before the two items' 4U loads, and loads
+    // complete in issue order
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<4 * U>();
+    // the empty register loads are consumed here too, so that the compiler
+    // keeps them ahead of the branch (used on one side only, it would sink
+    // them below the weight loads of the other)
+#pragma unroll
+    for (int s = 0; s < XS; ++s)
+#pragma unroll
+      for (int b = 0; b < BP; ++b)
+        asm volatile("" ::"v"(xg[s].r[b].x), "v"(xg[s].r[b].y), "v"(xg[s].r[b].z),
+                     "v"(xg[s].r[b].w));
+  } else if constexpr (plain_x(PK)) {  // plain layout: token b's group g at byte b * 2K + 16 g
 #pragma unroll
     for (int s = 0; s < XS; ++s)
 #pragma unroll
@@ -1819,8 +1865,18 @@ nm_status resolve_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
 
 typedef void (*seg_fn)(const uint4 *, const uint32_t *, const uint16_t *, void *, int,
                        int64_t, int, int, int);
+// Does the row kernel copy x to LDS by direct-to-LDS loads (its plain-x
+// kinds)?  Where x's image is large beside the workgroup's weights: batch >= 2,
+// or at most 4 rows per workgroup.  Measured (us, cache-cold, 2:4 fp16): k
+// 1024x4096 batch 1 / 2 / 4: 3.36 / 3.77 / 4.51 -> 2.99 / 3.26 / 3.94; 70B k
+// 1024x8192 batch 1 / 4: 4.41 / 6.75 -> 3.92 / 5.33; 14336x4096 batch 2:
+// 13.24 -> 12.38; but at batch 1 with 12 or more rows per workgroup the
+// register path stays ahead (14336x4096 11.57 against 11.80, 6144x4096 6.50
+// against 6.85).
+int x_by_dma(int bp, int64_t rows_per_wg) { return bp >= 2 || rows_per_wg <= 4 ? 1 : 0; }
+
 typedef void (*rows_fn)(const uint4 *, const uint32_t *, const uint16_t *, void *, int,
-                        int64_t, int, int, int);
+                        int64_t, int, int, int, int);
 typedef void (*dense_fn)(const uint4 *, const uint16_t *, void *, int, int64_t,
                          int, int, int);
 
@@ -2123,7 +2179,8 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     hipLaunchKernelGGL(pick_split(bf, ks, split_batch_chunks(cols, ks), xs), dim3((unsigned)grid),
                        dim3(cfg.threads_per_wg), split_lds_bytes(cols, wpg, cfg.rows_per_wave),
                        (hipStream_t)stream, (const uint4 *)values, bits, (const uint16_t *)X, Y,
-                       batch, rows, (int)cols, cfg.rows_per_wave, out_kind);
+                       batch, rows, (int)cols, cfg.rows_per_wave, out_kind,
+                       x_by_dma(bp, rows_per_wg));
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? NM_OK : hip_fail(e);
   }
@@ -2134,17 +2191,18 @@ int sparse_product(const void *values, const uint32_t *bits, const void *X,
     const int xs = (int)((cols / 8 + cfg.threads_per_wg - 1) / cfg.threads_per_wg);
     const int ub = rows_batch_chunks(cols, bp);
     const bool exact = cols % (1024LL * ub) == 0;  // 16 columns per chunk, 64 lanes
+    const int xdma = x_by_dma(bp, rows_per_wg);
     if (plain48_ok(cols, bp, n, m)) {
       hipLaunchKernelGGL(pick_rows48(bf, ub, xs, exact), dim3((unsigned)grid),
                          dim3(cfg.threads_per_wg), plain48_lds_bytes(cols), (hipStream_t)stream,
                          (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
-                         (int)cols, cfg.rows_per_wave, out_kind);
+                         (int)cols, cfg.rows_per_wave, out_kind, xdma);
     } else {
       hipLaunchKernelGGL(pick_rows(bf, pk, bp, ub, xs, exact), dim3((unsigned)grid),
                          dim3(cfg.threads_per_wg),
                          sparse_lds_bytes(bp, cols > 0 ? (int)cols : 32), (hipStream_t)stream,
                          (const uint4 *)values, bits, (const uint16_t *)X, Y, batch, rows,
-                         (int)cols, cfg.rows_per_wave, out_kind);
+                         (int)cols, cfg.rows_per_wave, out_kind, xdma);
     }
   } else {
     const int64_t rows_per_wg = (int64_t)wpg * cfg.rows_per_wave;
