@@ -723,7 +723,9 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
   // image past B read as zeros through the range check), then issue the
   // weights, and wait for the copies only.
   const int ngx = K >> 3;
-  const bool xd = plain_x(PK) && xdma != 0;
+  // (the host takes xdma at every batch >= 2: those kinds have no other path)
+  constexpr bool kDmaOnly = plain_x(PK) && BP >= 2;
+  const bool xd = kDmaOnly || (plain_x(PK) && xdma != 0);
   if (xd) {
     const __amdgpu_buffer_rsrc_t rxs =
         __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, B * K * 2, kRsrcWord3);
@@ -734,7 +736,9 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
   XGroup<BP> xg[XS];
-  if constexpr (plain_x(PK)) {
+  if constexpr (kDmaOnly) {
+    (void)xg;
+  } else if constexpr (plain_x(PK)) {
     // buffer loads (rows past B read as zeros); under xdma the resource is
     // empty, so the same loads are issued without a branch and move no data
     const __amdgpu_buffer_rsrc_t rxg =
@@ -775,13 +779,15 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
     // the empty register loads are consumed here too, so that the compiler
     // keeps them ahead of the branch (used on one side only, it would sink
     // them below the weight loads of the other)
+    if constexpr (!kDmaOnly) {
 #pragma unroll
-    for (int s = 0; s < XS; ++s)
+      for (int s = 0; s < XS; ++s)
 #pragma unroll
-      for (int b = 0; b < BP; ++b)
-        asm volatile("" ::"v"(xg[s].r[b].x), "v"(xg[s].r[b].y), "v"(xg[s].r[b].z),
-                     "v"(xg[s].r[b].w));
-  } else if constexpr (plain_x(PK)) {  // plain layout: token b's group g at byte b * 2K + 16 g
+        for (int b = 0; b < BP; ++b)
+          asm volatile("" ::"v"(xg[s].r[b].x), "v"(xg[s].r[b].y), "v"(xg[s].r[b].z),
+                       "v"(xg[s].r[b].w));
+    }
+  } else if constexpr (plain_x(PK) && !kDmaOnly) {  // token b's group g at byte b * 2K + 16 g
 #pragma unroll
     for (int s = 0; s < XS; ++s)
 #pragma unroll
@@ -793,7 +799,7 @@ __global__ __launch_bounds__(1024) void nm_spmv_rows_kernel(
       for (int b = 0; b < BP; ++b)
         reinterpret_cast<uint4 *>(lds)[b * ngx + g] =
             b < B ? reinterpret_cast<const uint4 *>(x + (int64_t)b * K)[g] : make_uint4(0, 0, 0, 0);
-  } else {
+  } else if constexpr (!plain_x(PK)) {
 #pragma unroll
     for (int s = 0; s < XS; ++s)
       xgroup_store<BP>(lds, xg[s], min((int)threadIdx.x + s * (int)blockDim.x, ngx - 1));
