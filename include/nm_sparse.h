@@ -257,11 +257,11 @@ int nm_dense_gemv(const void *W, const void *X, void *Y, int batch,
  *                   tile in LDS and run on v_mfma_f32_16x16x32.  Only for
  *                   cols % 64 == 0, cols <= 2^25 and rows * cols <= 2^31 - 1.
  * The library's choice (NM_KERNEL_AUTO) takes the matrix cores for 2:4 at
- * batch >= 2 and for the other patterns at batch >= 5 where they can run,
- * the VALU kernels otherwise; except that 2:4 at batch 2..4 stays on the
- * VALU kernel (x stored plainly per token in LDS) where that measured
- * faster: at most 1024 rows, and at batch 2 also rows >= 14336, cols >=
- * 25600 or rows * cols <= 4096 * 4096. */
+ * batch >= 3 and for the other patterns at batch >= 5 where they can run,
+ * the VALU kernels otherwise; except that 2:4 at batch 3 and 4 stays on the
+ * VALU kernel (x stored plainly per token in LDS) with at most 1024 rows,
+ * where that measured faster.  2:4 at batch 2 takes the VALU kernel
+ * wherever all of x fits in LDS (cols <= 39680). */
 typedef enum { NM_KERNEL_AUTO = 0, NM_KERNEL_VALU = 1, NM_KERNEL_MFMA = 2 } nm_kernel;
 
 /* Launch shape of the sparse and dense kernels, for tuning sweeps.  Fields

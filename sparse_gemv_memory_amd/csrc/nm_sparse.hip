@@ -1681,8 +1681,13 @@ void mfma_default(int64_t rows, int64_t cols, int batch, int kind, const DevInfo
     w = t < 1 ? 1 : t > 8 ? 8 : (int)t;
   }
   while (w > 1 && nsteps / w < 8) --w;  // at least two blocks of K per wave
-  if (kind == kMfmaSparse24)
+  if (kind == kMfmaSparse24) {
     while (w > 1 && nsteps / w < 32 && tiles * (w / 2) >= 1024) w /= 2;
+    // one wave per workgroup where two would walk fewer than 64 steps and the
+    // grid still holds 1024 tiles (25600x5120: 27.3 us at batch 2 against
+    // 30.3 with two waves; 14336x4096, 896 tiles, keeps two)
+    if (w == 2 && nsteps / 2 < 64 && tiles >= 1024) w = 1;
+  }
   const int nb =
       (kind == kMfmaSparse24 && (int64_t)(kLdsCap / mfma_lds_bytes(w, 3, bp, kind)) * w >= 8) ? 3 : 2;
   while (w > 1 && mfma_lds_bytes(w, nb, bp, kind) > budget) --w;
@@ -1700,20 +1705,20 @@ constexpr int kDenseMfmaMinBatch = 5;  // measured: the VALU kernel wins at batc
 
 // 2:4 shapes where the VALU row kernel with x stored plainly per token beats
 // the sparse matrix cores although batch >= kMfmaMinBatch.  Measured on the
-// 8B, 70B and Qwen3-32B shapes (us, cache-cold, one box, VALU / matrix cores):
-//  - at most 1024 rows, batch 2..4: 1024x4096 3.78 / 4.82 (batch 2), 4.49 /
-//    5.08 (batch 4); 1024x8192 5.51 / 6.60, 6.75 / 7.00;
-//  - batch 2: 14336 rows or more (14336x4096 13.28 / 13.90, 25600x5120 25.28
-//    / 29.67, 28672x8192 42.40 / 42.21), K >= 25600 (5120x25600 33.52 /
-//    34.94, 8192x28672 43.47 / 43.43), up to 4096 x 4096 weights (5.77 /
-//    5.90); the matrix cores win between (8192x5120 13.39 / 10.83, 8192x8192
-//    17.81 / 14.21, 5120x8192, 4096x14336, 6144x4096).
-// From batch 3 the matrix cores win on every shape above 1024 rows
-// (14336x4096 at batch 4: 15.73 / 14.13).
+// 13 shapes of the 8B, 70B and Qwen3-32B layers (us, cache-cold, one box,
+// each kernel at its default launch, VALU / matrix cores):
+//  - batch 2: every shape (1024x4096 3.29 / 4.84, 6144x4096 6.79 / 8.22,
+//    14336x4096 12.47 / 13.88, 4096x14336 12.93 / 13.10, 8192x8192 13.96 /
+//    14.30, 28672x8192 41.63 / 42.24, 8192x28672 41.00 / 43.60, 5120x8192
+//    9.86 / 12.45, 5120x25600 24.90 / 35.13);
+//  - batch 3 and 4: at most 1024 rows (1024x4096 3.86 / 5.02, 1024x8192
+//    5.26 / 6.88); above that the matrix cores win on every shape but
+//    5120x8192 (11.3 / 12.8), e.g. 14336x4096 14.61 / 14.10, 8192x8192
+//    15.83 / 14.58, 5120x25600 50.98 / 36.28.
 bool valu_beats_mfma_24(int64_t rows, int64_t cols, int batch) {
+  (void)cols;
   if (batch > 4) return false;
-  if (rows <= 1024) return true;
-  return batch == 2 && (rows >= 14336 || cols >= 25600 || rows * cols <= 4096LL * 4096);
+  return batch == 2 || rows <= 1024;
 }
 
 int rows_batch_chunks(int64_t cols, int bp);
@@ -1742,6 +1747,30 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
   const size_t budget = lds_budget(di);
   const int smax = max_seg(dense, bp, budget);
   const size_t full = lds_bytes(dense, bp, cols > 0 ? (int)cols : 32);
+  if (!dense && sp24 && bp >= 2 && full <= budget && cols > 0 && rows > 0) {
+    // 2:4 at batch 2..8 (x staged by direct-to-LDS copies): the CU's rows
+    // (rows / CUs) split evenly over one workgroup of 4 waves where K <= 4096
+    // or where K >= 8192 with 32 or more rows per CU, else of 8 (no more
+    // waves than rows), and over two workgroups where a wave would hold more
+    // than 8 rows; at batch 2 with K >= 8192, 32 or more rows per CU and room
+    // for two workgroups per CU, 4 rows per wave.  Measured on the 13 shapes
+    // of the 8B, 70B and Qwen3-32B layers at batch 2 (us; a sweep of 256/512
+    // threads x 1..16 rows per wave): within 4% of the best launch on each,
+    // and up to 23% faster than the row-kernel rules below (5120x25600 24.90
+    // against 32.23, 6144x4096 6.79 against 8.62, 8192x8192 13.96 against
+    // 17.82, 5120x8192 9.86 against 13.23).
+    const int64_t per_cu = (rows + di.cus - 1) / di.cus;
+    int64_t w = cols <= 4096 || (cols >= 8192 && per_cu >= 32) ? 4 : 8;
+    if (per_cu < w) w = per_cu;
+    int64_t rpw = (per_cu + w - 1) / w;
+    if (rpw > 8) rpw = (rpw + 1) / 2;
+    if (bp == 2 && cols >= 8192 && per_cu >= 32 && 2 * full <= kLdsCap) rpw = 4;
+    if (pair) rpw += rpw & 1;  // (gate, up) pairs stay within a wave
+    cfg->seg_cols = (int)cols;
+    cfg->threads_per_wg = (int)w * kWave;
+    cfg->rows_per_wave = (int)(rpw < 64 ? rpw : 64);
+    return NM_OK;
+  }
   if (full <= budget) {
     // row kernel: x staged once per workgroup.  Measured on the 8B, 70B and
     // Qwen3-32B shapes:

@@ -447,7 +447,7 @@ def test_default_launch_picks_matrix_cores_for_small_batch():
         assert native.nm_default_launch(14336, 4096, 8, n, m).kernel == MFMA, (n, m)
         assert native.nm_default_launch(14336, 4096, 1, n, m).kernel == VALU, (n, m)
         # the decompressing kinds start at batch 5, 2:4 on the sparse
-        # instruction at batch 3 on these shapes
+        # instruction at batch 3
         want4 = MFMA if (n, m) == (2, 4) else VALU
         assert native.nm_default_launch(14336, 4096, 4, n, m).kernel == want4, (n, m)
         assert native.nm_default_launch(8192, 8192, 4, n, m).kernel == want4, (n, m)
@@ -457,20 +457,20 @@ def test_default_launch_picks_matrix_cores_for_small_batch():
 
 
 def test_default_launch_2of4_small_batch_rule():
-    """2:4 at batch 2..4 takes the VALU kernel (x plain per token) where it
-    measured faster than the matrix cores: at most 1024 rows (batch 2..4), and
-    at batch 2 also 14336 rows or more, K >= 25600, or up to 4096 x 4096
-    weights.  Every other shape at batch 3 and 4, and every shape at batch
-    5..8, takes the matrix cores."""
+    """2:4 at batch 2 takes the VALU kernel (x plain per token) on every shape
+    whose x fits in LDS, and at batch 3 and 4 on shapes of at most 1024 rows,
+    where it measured faster than the matrix cores; every other shape at
+    batch 3 and 4, every shape at batch 5..8, and batch 2 with x beyond the
+    LDS take the matrix cores."""
     d = native.nm_default_launch
     for b in (2, 3, 4):
         for rows, cols in [(1024, 4096), (1024, 8192)]:
             assert d(rows, cols, b, 2, 4).kernel == VALU, (rows, cols, b)
     for rows, cols in [(4096, 4096), (14336, 4096), (25600, 5120), (28672, 8192), (8192, 28672),
-                       (5120, 25600)]:
+                       (5120, 25600), (4096, 14336), (8192, 8192), (8192, 5120), (5120, 8192),
+                       (6144, 4096)]:
         assert d(rows, cols, 2, 2, 4).kernel == VALU, (rows, cols)
-    for rows, cols in [(4096, 14336), (8192, 8192), (8192, 5120), (5120, 8192), (6144, 4096)]:
-        assert d(rows, cols, 2, 2, 4).kernel == MFMA, (rows, cols)
+    assert d(4096, 65536, 2, 2, 4).kernel == MFMA  # 2 x 128 KiB of x
     for b in (3, 4):
         for rows, cols in [(4096, 4096), (14336, 4096), (4096, 14336), (25600, 5120), (28672, 8192),
                            (8192, 28672)]:
@@ -483,12 +483,14 @@ def test_default_launch_2of4_small_batch_rule():
 def test_default_launch_matrix_core_shape():
     """Waves per workgroup and ring depth of the 2:4 matrix-core kernel (256
     CUs, 160 KiB of LDS): four waves, halved while a wave would walk fewer
-    than 32 steps of 64 columns and at least 1024 waves remain; three blocks
-    in the ring while 8 waves of such workgroups fit a CU, else two."""
+    than 32 steps of 64 columns and at least 1024 waves remain, and one wave
+    where two would walk fewer than 64 steps on at least 1024 tiles; three
+    blocks in the ring while 8 waves of such workgroups fit a CU, else two."""
     d = native.nm_default_launch
     want = {(14336, 4096, 4): (128, 3), (14336, 4096, 8): (128, 2), (4096, 4096, 8): (256, 2),
             (4096, 4096, 4): (256, 3), (8192, 5120, 8): (128, 2), (8192, 8192, 8): (256, 2),
-            (4096, 14336, 4): (256, 3), (28672, 8192, 8): (256, 2), (6144, 4096, 8): (256, 2)}
+            (4096, 14336, 4): (256, 3), (28672, 8192, 8): (256, 2), (6144, 4096, 8): (256, 2),
+            (25600, 5120, 4): (64, 3), (25600, 5120, 8): (64, 2)}
     for (rows, cols, b), (threads, nb) in want.items():
         c = d(rows, cols, b, 2, 4)
         assert c.kernel == MFMA and (c.threads_per_wg, c.rows_per_wave) == (threads, nb), (rows, cols, b)
@@ -532,6 +534,18 @@ def test_default_launch_shapes_follow_the_measured_rules():
     assert shape(4096, 14336, 1, 8, 16) == (256, 2, 14336)
     assert shape(4096, 14336, 8, 1, 4) == (1024, 1, 7168)
     assert shape(14336, 4096, 8, 1, 4) == (256, 7, 4096)
+    # 2:4 at batch 2: the CU's rows over one workgroup of 4 (K <= 4096) or 8
+    # waves, two workgroups past 8 rows a wave, 4 rows a wave for the long-K
+    # tall shapes
+    assert shape(1024, 4096, 2, 2, 4) == (256, 1, 4096)
+    assert shape(4096, 4096, 2, 2, 4) == (256, 4, 4096)
+    assert shape(6144, 4096, 2, 2, 4) == (256, 6, 4096)
+    assert shape(14336, 4096, 2, 2, 4) == (256, 7, 4096)
+    assert shape(4096, 14336, 2, 2, 4) == (512, 2, 14336)
+    assert shape(5120, 8192, 2, 2, 4) == (512, 3, 8192)
+    assert shape(8192, 8192, 2, 2, 4) == (256, 4, 8192)
+    assert shape(8192, 28672, 2, 2, 4) == (256, 8, 28672)
+    assert shape(25600, 5120, 2, 2, 4) == (512, 7, 5120)
 
 
 def test_forced_valu_shape_equals_the_automatic_valu_shape():
