@@ -279,10 +279,10 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch) at batch
     # 1; see profiles/nm_spmv_2of4_hbm_counters.md
-    (14336, 4096): ("6fb401fd75d9001f1f07edf1e817f9b2869f676bd80e374025ec4f0f67f26cda",
-                    66264639),
-    (8192, 8192): ("6fb401fd75d9001f1f07edf1e817f9b2869f676bd80e374025ec4f0f67f26cda",
-                   75727675),
+    (14336, 4096): ("ea8a3d88622c2074dcd50b20039a5b598f965b6db12f2f0e33456d7cc5de41d6",
+                    66275643),
+    (8192, 8192): ("ea8a3d88622c2074dcd50b20039a5b598f965b6db12f2f0e33456d7cc5de41d6",
+                   75742876),
 }
 
 
