@@ -1029,29 +1029,31 @@ def main():
         log(f"  {p.name:5s} {p.mt.rows:5d}x{p.mt.cols:5d}: {us:7.2f} us  "
             f"{d['GB/s']:7.1f} GB/s ({100 * d['frac_of_peak']:.1f}% of 8 TB/s)"
             + (f"  dense {d['dense_us']:.2f} us, torch {d['torch_linear_us']:.2f} us" if want_dense else ""))
-    # batch 8 on the 8B layer's three shapes (the sparse matrix cores), beside
-    # torch linear on the dense weights
-    batch8 = {}
+    # batch 2 (the VALU row kernel) and batch 8 (the sparse matrix cores) on
+    # the 8B layer's shapes, beside torch linear on the dense weights
+    small = {2: {}, 8: {}}
     if not args.no_batch4:
-        for p in projs:
-            if p.name not in ("q", "gate", "down"):
-                continue
-            mt = p.mt
-            p.X[8] = synth.activations(8, mt.cols, seed=mt.seed, dtype=mt.dtype, outliers=mt.outliers)
-            p.Xd[8] = t16(p.X[8], mt.dtype)
-            p.Y[8] = torch.empty((8, mt.rows), dtype=torch.float32, device=DEV)
-            p.sbytes[8] = workloads.sparse_bytes(mt.rows, mt.cols, mt.n, mt.m, 8, 4)
-            st = per_kernel_stats(p, Proj.sparse_call, 8, p.nc, args.reps)
-            d = {"us": round(st["us"], 3), "us_p10": round(st["p10"], 3), "us_p90": round(st["p90"], 3),
-                 "GB/s": round(p.sbytes[8] / st["us"] / 1e3, 1),
-                 "frac_of_peak": round(p.sbytes[8] / st["us"] / 1e3 / PEAK_GBS, 4)}
-            if want_dense:
-                d["torch_linear_us"] = round(per_kernel_us(p, Proj.torch_call, 8, p.ndc, args.reps), 3)
-            batch8[f"{p.name} {mt.rows}x{mt.cols}"] = d
-            log(f"  {p.name:5s} {mt.rows:5d}x{mt.cols:5d} batch 8: {d['us']:7.2f} us  "
-                f"{d['GB/s']:7.1f} GB/s ({100 * d['frac_of_peak']:.1f}% of 8 TB/s)"
-                + (f"  torch {d['torch_linear_us']:.2f} us" if want_dense else ""))
-            del p.X[8], p.Xd[8], p.Y[8]
+        for b, names in ((2, ("q", "k", "gate", "down")), (8, ("q", "gate", "down"))):
+            for p in projs:
+                if p.name not in names:
+                    continue
+                mt = p.mt
+                p.X[b] = synth.activations(b, mt.cols, seed=mt.seed, dtype=mt.dtype, outliers=mt.outliers)
+                p.Xd[b] = t16(p.X[b], mt.dtype)
+                p.Y[b] = torch.empty((b, mt.rows), dtype=torch.float32, device=DEV)
+                p.sbytes[b] = workloads.sparse_bytes(mt.rows, mt.cols, mt.n, mt.m, b, 4)
+                st = per_kernel_stats(p, Proj.sparse_call, b, p.nc, args.reps)
+                d = {"us": round(st["us"], 3), "us_p10": round(st["p10"], 3), "us_p90": round(st["p90"], 3),
+                     "GB/s": round(p.sbytes[b] / st["us"] / 1e3, 1),
+                     "frac_of_peak": round(p.sbytes[b] / st["us"] / 1e3 / PEAK_GBS, 4)}
+                if want_dense:
+                    d["torch_linear_us"] = round(per_kernel_us(p, Proj.torch_call, b, p.ndc, args.reps), 3)
+                small[b][f"{p.name} {mt.rows}x{mt.cols}"] = d
+                log(f"  {p.name:5s} {mt.rows:5d}x{mt.cols:5d} batch {b}: {d['us']:7.2f} us  "
+                    f"{d['GB/s']:7.1f} GB/s ({100 * d['frac_of_peak']:.1f}% of 8 TB/s)"
+                    + (f"  torch {d['torch_linear_us']:.2f} us" if want_dense else ""))
+                del p.X[b], p.Xd[b], p.Y[b]
+    batch8 = small[8]
     # the dominant kernel: the launch shape with the most time per step (the
     # 14336x4096 shape runs twice per layer, as gate and up)
     shape_time = {}
@@ -1138,6 +1140,8 @@ def main():
         if want_dense:
             b4["speedup_vs_best_dense"] = round(best_dense(4) / ms4, 3)
         res["batch4"] = b4
+    if small[2]:
+        res["batch2_per_call"] = small[2]
     if batch8:
         res["batch8_per_call"] = batch8
     if not args.no_cpu_baseline:

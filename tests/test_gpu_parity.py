@@ -513,6 +513,28 @@ def test_plain_x_batch_integer_exact(rows, cols, batch):
         assert np.array_equal(f64(Y), want), cfg
 
 
+@pytest.mark.parametrize("rows,cols", [(1024, 4096), (300, 2080), (77, 8192)])
+def test_batch1_x_staging_paths_integer_exact(rows, cols):
+    """The batch-1 2:4 row kernel copies x into LDS with direct-to-LDS loads
+    when a workgroup holds at most 4 rows, and stages it through registers
+    otherwise: both exact on integer inputs, for launch shapes on either side
+    of that line, with whole and ragged load batches and with the split
+    reduction."""
+    W = synth.integer_weights(rows, cols, seed=111)
+    keep = synth.random_mask(rows, cols, 2, 4, seed=112)
+    xi = np.random.default_rng(113).integers(-4, 5, size=(1, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    want = oracle.masked_gemv(W, keep, X, False)
+    cfgs = [(256, 1, 0, VALU), (64, 4, 0, VALU), (128, 2, 0, VALU),  # <= 4 rows: copies
+            (256, 2, 0, VALU), (512, 4, 0, VALU), (1024, 1, 0, VALU)]  # more: registers
+    if cols % 2048 == 0:
+        cfgs += [(256, 1, 0, VALU, 2), (1024, 1, 0, VALU, 2)]  # split over 2 waves: 2 / 8 rows
+    for cfg in cfgs:
+        Y = native.nm_spmm_small(values, bits, t16(X, "f16"), 2, 4, cfg=native.LaunchCfg(*cfg))
+        assert np.array_equal(f64(Y), want), cfg
+
+
 def test_default_launch_shapes_follow_the_measured_rules():
     """Launch shapes the library picks on the 8B shapes (256 CUs), each the
     measured best of its sweep: 2:4 q|k|v 6144x4096 as 3 waves of 4 rows;
