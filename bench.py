@@ -703,7 +703,12 @@ def prefill_run(args):
     torch linear (hipBLASLt) on the dense weights; four resident copies of
     each (cache-cold at small batch), us per call and dense-equivalent
     TFLOP/s (2 R K B / time).  The prefill product and torch linear both
-    write fp16 output; the decode entry points write fp32."""
+    write fp16 output; the decode entry points write fp32.  Prefill and torch
+    linear are timed as eager back-to-back launches (HIP events over 16 calls,
+    best of 5), the way a prefill runs, and also as graph replays (the
+    `_graph` keys): a split-K prefill captured in a graph allocates its
+    workspace per replay (a memory node), where eager calls keep one per
+    stream."""
     out = {}
     L = native.lib()
     for name, R, K in (("gate", 14336, 4096), ("down", 4096, 14336)):
@@ -718,6 +723,21 @@ def prefill_run(args):
                 ms = time_steps([g], max(5, args.steps // 10), 2) / 8
                 del g
                 return ms * 1e3
+
+            def eager(fn, n=16, reps=5):
+                for i in range(4):
+                    fn(i)
+                torch.cuda.synchronize()
+                best = float("inf")
+                for _ in range(reps):
+                    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    for i in range(n):
+                        fn(i)
+                    z.record()
+                    torch.cuda.synchronize()
+                    best = min(best, a.elapsed_time(z) / n * 1e3)
+                return best
             def pre(i):
                 v, b, _ = mats[i % 4]
                 st = L.nm_spmm_prefill(v.data_ptr(), b.data_ptr(), X.data_ptr(), Yh.data_ptr(), B, R,
@@ -726,7 +746,8 @@ def prefill_run(args):
                 assert st == 0, st
             def dense(i):
                 torch.nn.functional.linear(X, mats[i % 4][2], out=Yh)
-            row = {"nm_spmm_prefill": round(run(pre), 2), "torch_linear": round(run(dense), 2)}
+            row = {"nm_spmm_prefill": round(eager(pre), 2), "torch_linear": round(eager(dense), 2),
+                   "nm_spmm_prefill_graph": round(run(pre), 2), "torch_linear_graph": round(run(dense), 2)}
             if B <= 8:
                 def small(i):
                     v, b, _ = mats[i % 4]
@@ -741,7 +762,7 @@ def prefill_run(args):
                     assert st == 0, st
                 row["nm_spmm_small"] = round(run(small), 2)
                 row["nm_dense_gemv"] = round(run(dgemv), 2)
-            best_sparse = min(v for k, v in row.items() if k.startswith("nm_spmm"))
+            best_sparse = min(v for k, v in row.items() if k.startswith("nm_spmm") and not k.endswith("_graph"))
             best_dense = min(v for k, v in row.items() if k in ("torch_linear", "nm_dense_gemv"))
             row["prefill_TFLOP/s"] = round(2.0 * R * K * B / (row["nm_spmm_prefill"] * 1e-6) / 1e12, 1)
             row["dense_TFLOP/s"] = round(2.0 * R * K * B / (row["torch_linear"] * 1e-6) / 1e12, 1)

@@ -378,10 +378,16 @@ int nm_spmm_bitmask(const void *values, const uint32_t *bits, const int64_t *off
  * weights once per call for at most 8 tokens.  A workgroup takes up to
  * 160 KiB of LDS.  Where the tiles alone would leave compute units idle, K
  * is cut into 2, 4 or 8 parts: the fp32 partial products go to a workspace
- * (parts x batch x rows x 4 bytes) taken with hipMallocAsync on `stream` and
- * freed with hipFreeAsync after a second kernel adds them in part order, so
- * the result is deterministic and the call stays asynchronous (and
- * capturable in a HIP graph).
+ * of parts x batch x rows x 4 bytes and a second kernel adds them in part
+ * order, so the result is deterministic.  The library keeps that workspace
+ * between calls, one per (device, stream), grown with hipMallocAsync and
+ * hipFreeAsync on `stream` when a call needs more (it holds the largest
+ * split a stream has needed, e.g. 64 MiB for 4096 x 14336 at 512 tokens,
+ * until the process ends); calls on one stream share it, which is safe
+ * because they run in stream order.  A call made while `stream` is being
+ * captured into a HIP graph takes its own workspace with hipMallocAsync and
+ * frees it with hipFreeAsync after the sum (memory nodes of the graph), so a
+ * graph shares no memory with other work.  The call stays asynchronous.
  *   values, bits: nm_pack output for 2:4 (rows x cols/2 and rows x cols/32),
  *                 device; values and X 16-byte aligned, bits 4-byte aligned;
  *   X:            device, batch x cols, in_dt, row-major (token-major);

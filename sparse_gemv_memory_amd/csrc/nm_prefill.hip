@@ -43,6 +43,7 @@
 #include <mutex>
 #include <stdint.h>
 #include <type_traits>
+#include <vector>
 
 #include "nm_device.h"
 #include "nm_host.h"
@@ -378,6 +379,27 @@ nm_status prefill_device(PrefillDev *out) {
   return NM_OK;
 }
 
+// Split-K workspace of uncaptured calls: one per (device, stream), kept
+// between calls and grown in stream order (the old one freed after the work
+// already queued on the stream).  Calls on one stream run in order, so they
+// can share it; the lock is held from the workspace lookup until both of a
+// call's kernels are queued, so that calls made on one stream from several
+// host threads cannot interleave their products and sums.  A call made
+// while its stream is being captured takes a fresh stream-ordered
+// allocation instead (a memory node of the graph), so that no graph shares
+// memory with other work.  Measured on the 8B shapes (us per call, eager):
+// 14336x4096 at 64 / 256 tokens 29.1 / 46.8 with an allocation per call,
+// 24.8 / 42.8 with the kept workspace; 4096x14336 35.0 / 49.8 against
+// 30.9 / 44.9.
+struct PrefillWs {
+  int dev;
+  hipStream_t stream;
+  float *ptr;
+  size_t bytes;
+};
+std::vector<PrefillWs> g_prefill_ws;
+std::mutex g_prefill_ws_mu;
+
 }  // namespace
 
 extern "C" {
@@ -434,13 +456,49 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
   const int64_t ntt = (batch + 64 * best_tt - 1) / (64 * best_tt);
   if (nrt * ntt * best_ks > INT32_MAX) return NM_ERR_INVALID_ARG;
   float *part = nullptr;
+  bool part_owned = false;  // a per-call allocation, freed after the sum
   const hipStream_t hs = (hipStream_t)stream;
+  std::unique_lock<std::mutex> ws_lock(g_prefill_ws_mu, std::defer_lock);
   if (best_ks > 1) {
-    // the partial products, freed in stream order after the sum (a split K
-    // is chosen only where the tiles leave compute units idle, so small)
+    // the partial products (a split K is chosen only where the tiles leave
+    // compute units idle, so they are small beside the weights)
     if ((batch * rows + 1023) / 1024 > INT32_MAX) return NM_ERR_INVALID_ARG;
-    hipError_t e = hipMallocAsync((void **)&part, (size_t)best_ks * batch * rows * 4, hs);
+    const size_t need = (size_t)best_ks * batch * rows * 4;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(hs, &cs);
     if (e != hipSuccess) return hip_fail(e);
+    if (cs != hipStreamCaptureStatusNone) {
+      e = hipMallocAsync((void **)&part, need, hs);
+      if (e != hipSuccess) return hip_fail(e);
+      part_owned = true;
+    } else {
+      int dv = 0;
+      e = hipGetDevice(&dv);
+      if (e != hipSuccess) return hip_fail(e);
+      ws_lock.lock();
+      PrefillWs *w = nullptr;
+      for (PrefillWs &c : g_prefill_ws)
+        if (c.dev == dv && c.stream == hs) w = &c;
+      if (!w) {
+        g_prefill_ws.push_back(PrefillWs{dv, hs, nullptr, 0});
+        w = &g_prefill_ws.back();
+      }
+      if (w->bytes < need) {
+        if (w->ptr) {
+          e = hipFreeAsync(w->ptr, hs);
+          w->ptr = nullptr;
+          w->bytes = 0;
+          if (e != hipSuccess) return hip_fail(e);
+        }
+        e = hipMallocAsync((void **)&w->ptr, need, hs);
+        if (e != hipSuccess) {
+          w->ptr = nullptr;
+          return hip_fail(e);
+        }
+        w->bytes = need;
+      }
+      part = w->ptr;
+    }
   }
   auto go = [&](auto fn, int tt) {
     hipLaunchKernelGGL(fn, dim3((unsigned)(nrt * ntt * best_ks)), dim3(kPWaves * kWave),
@@ -471,8 +529,10 @@ int nm_spmm_prefill(const void *values, const uint32_t *bits, const void *X, voi
     hipLaunchKernelGGL(nm_prefill_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
                        hs, part, best_ks, n, Y, (int)out_dt, rvec);
     hipError_t e = hipGetLastError();
-    const hipError_t f = hipFreeAsync(part, hs);
-    if (e == hipSuccess) e = f;
+    if (part_owned) {
+      const hipError_t f = hipFreeAsync(part, hs);
+      if (e == hipSuccess) e = f;
+    }
     return e == hipSuccess ? NM_OK : hip_fail(e);
   }
   hipError_t e = hipGetLastError();

@@ -508,7 +508,13 @@ def test_plain_x_batch_integer_exact(rows, cols, batch):
     X = synth.f32_to_16_bits(xi, "f16")
     values, bits = gpu_pack(W, keep, 2, 4, "f16")
     want = oracle.masked_gemv(W, keep, X, False)
-    for cfg in (native.LaunchCfg(0, 0, 0, VALU), (64, 1, 0, VALU), (256, 4, 0, VALU), (512, 2, 0, VALU)):
+    cfgs = [native.LaunchCfg(0, 0, 0, VALU), (64, 1, 0, VALU), (256, 4, 0, VALU), (512, 2, 0, VALU)]
+    if native.nm_resolve_launch(rows, cols, batch, 2, 4, cfg=native.LaunchCfg(0, 0, 0, VALU)).seg_cols >= cols:
+        # all of x in LDS (the row kernel): shapes the batch >= 2 rule picks on
+        # larger layers (6, 7 or 14 rows a wave in 4-wave workgroups, 3 in
+        # 8-wave ones), each with a ragged last workgroup here
+        cfgs += [(256, 6, 0, VALU), (256, 7, 0, VALU), (256, 14, 0, VALU), (512, 3, 0, VALU)]
+    for cfg in cfgs:
         Y = native.nm_spmm_small(values, bits, t16(X, "f16"), 2, 4, cfg=cfg)
         assert np.array_equal(f64(Y), want), cfg
 
@@ -993,6 +999,63 @@ def test_prefill_split_k_sampled_rows_integer_exact(rows, cols, batch):
     idx[0], idx[-1] = 0, rows - 1
     want = oracle.masked_gemv(W, keep, X, False, rows_idx=idx, threads=8)
     assert np.array_equal(Y[:, idx], want)
+
+
+def _split_case(rows, cols, batch, seed):
+    """Integer inputs for a prefill shape that the launch splits in K, with
+    the oracle's (exact) result."""
+    W = synth.integer_weights(rows, cols, seed=seed, dtype="f16")
+    keep = synth.random_mask(rows, cols, 2, 4, seed=seed + 1)
+    xi = np.random.default_rng(seed + 2).integers(-4, 5, size=(batch, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "f16")
+    values, bits = gpu_pack(W, keep, 2, 4, "f16")
+    return values, bits, t16(X, "f16"), oracle.masked_gemv(W, keep, X, False, threads=8)
+
+
+def test_prefill_split_workspace_kept_across_calls_and_streams():
+    """Split-K calls keep one workspace per stream: a larger split grows it in
+    stream order, a smaller one after it reuses it, and calls queued back to
+    back on two streams each use their own; every result is exact.  (K in 4
+    parts for all three shapes, 16.4, 16.8 and 32.8 MB of partial sums.)"""
+    cases = [_split_case(1000, 2048, 1024, 51), _split_case(4100, 4096, 256, 52),
+             _split_case(1000, 4096, 2048, 53)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    out = []
+    for i1, i2 in ((0, 1), (2, 0), (1, 2), (0, 1)):
+        with torch.cuda.stream(s1):
+            v, b, X, _ = cases[i1]
+            out.append((i1, native.nm_spmm_prefill(v, b, X)))
+        with torch.cuda.stream(s2):
+            v, b, X, _ = cases[i2]
+            out.append((i2, native.nm_spmm_prefill(v, b, X)))
+    torch.cuda.synchronize()
+    for i, Y in out:
+        assert np.array_equal(f64(Y), cases[i][3]), i
+
+
+def test_prefill_split_in_graph_replays():
+    """A split-K call captured in a HIP graph takes its own workspace (a
+    memory node of the graph): replayed several times, with eager split-K
+    calls and other eager work on the same stream between the replays, every
+    replay and every eager call is exact."""
+    values, bits, X, want = _split_case(4100, 4096, 256, 61)
+    v2, b2, X2, want2 = _split_case(1000, 2048, 1024, 62)
+    Y = torch.empty((256, 4100), device=DEV)
+    native.nm_spmm_prefill(values, bits, X, out=Y)  # eager first: initialises everything
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        native.nm_spmm_prefill(values, bits, X, out=Y)
+    for _ in range(3):
+        Y.fill_(-1.0)
+        Z = native.nm_spmm_prefill(v2, b2, X2)
+        g.replay()
+        Z2 = native.nm_spmm_prefill(v2, b2, X2)
+        torch.cuda.synchronize()
+        assert np.array_equal(f64(Y), want)
+        assert np.array_equal(f64(Z), want2) and np.array_equal(f64(Z2), want2)
+    del g
 
 
 def test_prefill_zero_columns_and_empty_batch():
