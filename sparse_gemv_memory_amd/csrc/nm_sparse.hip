@@ -1797,6 +1797,17 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
       cfg->rows_per_wave = rmin;
       return NM_OK;
     }
+    // 2:4 at batch 1 with 12..24 rows per CU (a multiple of 4) and K <= 8192:
+    // one workgroup of 4 waves per CU, so x is staged once per CU (4096x4096
+    // 5.11 us against 5.57 with two 2-wave workgroups; 6144x4096 6.36 against
+    // 6.63; 5120x8192 9.05 against 9.34); at 32 rows per CU (8192x8192) and
+    // at K = 14336 two workgroups stay ahead
+    if (!dense && sp24 && bp == 1 && !pair && cols <= 8192 && rows % di.cus == 0 &&
+        rows / di.cus > 8 && rows / di.cus <= 24 && (rows / di.cus) % 4 == 0) {
+      cfg->threads_per_wg = 4 * kWave;
+      cfg->rows_per_wave = (int)(rows / di.cus / 4);
+      return NM_OK;
+    }
     if (full <= budget / 2 && rows % (rmin * two_per_cu) == 0 && rows / two_per_cu <= 16) {
       int rpw = rmin;
       // (2:4 rows whose load batches hold 2 chunks per lane keep one row per
