@@ -279,10 +279,10 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch) at batch
     # 1; see profiles/nm_spmv_2of4_hbm_counters.md
-    (14336, 4096): ("ea8a3d88622c2074dcd50b20039a5b598f965b6db12f2f0e33456d7cc5de41d6",
+    (14336, 4096): ("dba8d4748244f522e7ec5d08df0926fc5e25a468212a3b31f9c9616c4ac95301",
                     66275643),
-    (8192, 8192): ("ea8a3d88622c2074dcd50b20039a5b598f965b6db12f2f0e33456d7cc5de41d6",
-                   75742876),
+    (8192, 8192): ("dba8d4748244f522e7ec5d08df0926fc5e25a468212a3b31f9c9616c4ac95301",
+                   75743285),
 }
 
 
