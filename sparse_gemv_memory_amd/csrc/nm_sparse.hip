@@ -1797,15 +1797,25 @@ nm_status default_cfg(int64_t rows, int64_t cols, int batch, int n, int m, bool 
       cfg->rows_per_wave = rmin;
       return NM_OK;
     }
-    // 2:4 at batch 1 with 12..24 rows per CU (a multiple of 4) and K <= 8192:
-    // one workgroup of 4 waves per CU, so x is staged once per CU (4096x4096
-    // 5.11 us against 5.57 with two 2-wave workgroups; 6144x4096 6.36 against
-    // 6.63; 5120x8192 9.05 against 9.34); at 32 rows per CU (8192x8192) and
-    // at K = 14336 two workgroups stay ahead
-    if (!dense && sp24 && bp == 1 && !pair && cols <= 8192 && rows % di.cus == 0 &&
-        rows / di.cus > 8 && rows / di.cus <= 24 && (rows / di.cus) % 4 == 0) {
+    // 2:4, and 4:8 in its plain-x kind, at batch 1 with 12..24 rows per CU
+    // (a multiple of 4) and K <= 8192: one workgroup of 4 waves per CU, so x
+    // is staged once per CU (4096x4096 5.11 us against 5.57 with two 2-wave
+    // workgroups, 4:8 bf16 5.18 against 5.77; 6144x4096 6.36 against 6.63,
+    // 4:8 6.38 against 6.77; 5120x8192 9.05 against 9.34); at 32 rows per CU
+    // (8192x8192) and at K = 14336 two workgroups stay ahead
+    if (!dense && (sp24 || plain48_ok(cols, bp, n, m)) && bp == 1 && !pair && cols <= 8192 &&
+        rows % di.cus == 0 && rows / di.cus > 8 && rows / di.cus <= 24 && (rows / di.cus) % 4 == 0) {
       cfg->threads_per_wg = 4 * kWave;
       cfg->rows_per_wave = (int)(rows / di.cus / 4);
+      return NM_OK;
+    }
+    // 8:16 and 16:32 (the scan) at batch 1 with 24 rows per CU: two workgroups
+    // of 4 waves per CU, 3 rows a wave (6144x4096 bf16: 7.84 / 7.99 us
+    // against 8.59 / 9.03 with 6 waves of 2 rows)
+    if (!dense && (m == 16 || m == 32) && 2 * n == m && bp == 1 && !pair && cols <= 8192 &&
+        rows == 24LL * di.cus) {
+      cfg->threads_per_wg = 4 * kWave;
+      cfg->rows_per_wave = 3;
       return NM_OK;
     }
     if (full <= budget / 2 && rows % (rmin * two_per_cu) == 0 && rows / two_per_cu <= 16) {

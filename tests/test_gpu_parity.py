@@ -197,7 +197,7 @@ MFMA = native.NM_KERNEL_MFMA
 # (threads_per_wg, rows_per_wave, seg_cols, kernel)
 CFGS = [(64, 1, 32, VALU), (64, 4, 96, VALU), (128, 2, 1024, VALU), (256, 1, 0, VALU),
         (256, 4, 64, VALU), (512, 2, 2080, VALU), (1024, 1, 160, VALU), (1024, 4, 0, VALU),
-        (64, 3, 0, VALU), (256, 7, 0, VALU), (128, 64, 0, VALU)]
+        (64, 3, 0, VALU), (256, 7, 0, VALU), (128, 64, 0, VALU), (256, 3, 0, VALU), (256, 6, 0, VALU)]
 
 
 @pytest.mark.parametrize("cfg", CFGS)
@@ -544,8 +544,8 @@ def test_batch1_x_staging_paths_integer_exact(rows, cols):
 def test_default_launch_shapes_follow_the_measured_rules():
     """Launch shapes the library picks on the 8B shapes (256 CUs), each the
     measured best of its sweep: 2:4 q|k|v 6144x4096 and q 4096x4096 as one
-    4-wave workgroup per CU; 4:8 (x plain, pair table) two workgroups of 4
-    rows a wave; the scan of 8:16 keeps 2
+    4-wave workgroup per CU; 4:8 (x plain, pair table) takes the 2:4 shapes;
+    the scan of 8:16 keeps 2
     rows per wave and 4-wave workgroups; at other densities, x of K = 14336 at
     batch 8 in two equal segments staged by 16-wave workgroups, and K = 4096
     whole with 4-wave workgroups."""
@@ -556,13 +556,17 @@ def test_default_launch_shapes_follow_the_measured_rules():
         c = native.nm_default_launch(*a)
         return c.threads_per_wg, c.rows_per_wave, c.seg_cols
 
-    # 2:4 at batch 1, 12..24 rows per CU and K <= 8192: one 4-wave workgroup
-    # per CU; 4:8 keeps two workgroups of 4 rows a wave
+    # 2:4 and 4:8 at batch 1, 12..24 rows per CU and K <= 8192: one 4-wave
+    # workgroup per CU; the 8:16 / 16:32 scan at 24 rows per CU: two 4-wave
+    # workgroups of 3 rows a wave
     assert shape(6144, 4096, 1, 2, 4) == (256, 6, 4096)
     assert shape(4096, 4096, 1, 2, 4) == (256, 4, 4096)
     assert shape(5120, 8192, 1, 2, 4) == (256, 5, 8192)
     assert shape(8192, 8192, 1, 2, 4) == (256, 4, 8192)
-    assert shape(4096, 4096, 1, 4, 8) == (128, 4, 4096)
+    assert shape(4096, 4096, 1, 4, 8) == shape(4096, 4096, 1, 2, 4)
+    assert shape(6144, 4096, 1, 4, 8) == (256, 6, 4096)
+    assert shape(6144, 4096, 1, 8, 16) == (256, 3, 4096)
+    assert shape(6144, 4096, 1, 16, 32) == (256, 3, 4096)
     assert shape(4096, 14336, 1, 4, 8) == shape(4096, 14336, 1, 2, 4)
     assert shape(4096, 4096, 1, 8, 16) == (256, 2, 4096)
     assert shape(4096, 14336, 1, 8, 16) == (256, 2, 14336)
