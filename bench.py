@@ -279,10 +279,10 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch) at batch
     # 1; see profiles/nm_spmv_2of4_hbm_counters.md
-    (14336, 4096): ("dba8d4748244f522e7ec5d08df0926fc5e25a468212a3b31f9c9616c4ac95301",
+    (14336, 4096): ("0511e9068abfdd025b7d199432546b196ec49da80b2e15f4e7462f1cab83b26a",
                     66275643),
-    (8192, 8192): ("dba8d4748244f522e7ec5d08df0926fc5e25a468212a3b31f9c9616c4ac95301",
-                   75743285),
+    (8192, 8192): ("0511e9068abfdd025b7d199432546b196ec49da80b2e15f4e7462f1cab83b26a",
+                   75743157),
 }
 
 
