@@ -139,17 +139,59 @@ __device__ __forceinline__ void single_acc(const char *lds, int a0, uint32_t v,
     acc[b] = dot2<BF>(v, (uint32_t)ld<uint16_t>(x0 + 2 * b), acc[b]);
 }
 
+// The BP batch values of one x slot, as loaded from LDS.
+template <int BP> struct XSlot { using T = u32x4_t; };
+template <> struct XSlot<1> { using T = uint16_t; };
+template <> struct XSlot<2> { using T = uint32_t; };
+template <> struct XSlot<4> { using T = u32x2_t; };
+
+// Kept pair w (packed 16-bit values) against the x slots p, q of its two
+// columns, already in registers.
+template <bool BF, int BP>
+__device__ __forceinline__ void pair_fma(typename XSlot<BP>::T p, typename XSlot<BP>::T q,
+                                         uint32_t w, float (&acc)[BP]) {
+  if constexpr (BP == 1) {
+    acc[0] = dot2<BF>(w, (uint32_t)p | ((uint32_t)q << 16), acc[0]);
+  } else if constexpr (BP == 2) {
+    acc[0] = dot2<BF>(w, (p & 0xffffu) | (q << 16), acc[0]);
+    acc[1] = dot2<BF>(w, (p >> 16) | (q & 0xffff0000u), acc[1]);
+  } else {
+#pragma unroll
+    for (int d = 0; d < BP / 2; ++d) {
+      acc[2 * d] = dot2<BF>(w, (p[d] & 0xffffu) | (q[d] << 16), acc[2 * d]);
+      acc[2 * d + 1] = dot2<BF>(w, (p[d] >> 16) | (q[d] & 0xffff0000u), acc[2 * d + 1]);
+    }
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round
+// trips): row shifts by 1, 2, 4, 8 within each row of 16 lanes, then lane 15
+// of each row into the next and lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // Wave w of the grid owns rows w * rpw .. + rpw - 1.  Its work per segment of
-// x is a sequence of items (row i, window t); the copy of item k + 1 is in
-// flight while item k is consumed.  Lane i accumulates the sums of the wave's
-// row i across segments (rpw <= 64).
+// x is a sequence of items (row i, window t), copied into a ring of NB
+// buffers per wave: the copies of items k + 1 .. k + NB - 1 are in flight
+// while item k is consumed (with NB > 2 the item's mask words are copied into
+// its buffer too, else they are loaded into registers).  Lane i accumulates
+// the sums of the wave's row i across segments (rpw <= 64).
 // UN: unstructured bitmask (any keep mask).  A word's count varies, so offs
 // holds the value index of every 64-word window of every row (row r, window
 // t at offs[r * nwr + t], nwr = windows per row, offs[R * nwr] = all kept
 // values); lane l of a window finds its values at the window's start plus
 // the set bits of the window's words before it (a wave prefix sum), and
-// walks popc(word) steps.  seg is then a multiple of 64 words.
-template <bool BF, int BP, int NI, bool UN = false>
+// walks popc(word) steps.  seg is then a multiple of 64 words.  A window
+// whose values do not fit a buffer (more than NI KiB with the copy's 16-byte
+// alignment) has its values read by the lanes from global memory.
+template <bool BF, int BP, int NI, bool UN = false, int NB = 2>
 __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
     const uint16_t *__restrict__ values, const uint32_t *__restrict__ bits,
     const uint16_t *__restrict__ x, void *__restrict__ y, int B, int64_t R, int K, int P,
@@ -165,8 +207,10 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
   const int64_t vstride = (int64_t)W * P;  // values per row (N:M)
   const int nwr = (W + kWinWords - 1) / kWinWords;  // windows per row (UN)
   const uint32_t xbytes = ((uint32_t)XCols<BP>::bytes(seg) + 15u) & ~15u;
-  // LDS address of the wave's two window buffers (NI KiB each)
-  const uint32_t wbuf = (uint32_t)(size_t)(lds_ptr)lds + xbytes + (uint32_t)wid * (2 * NI * 1024);
+  // LDS address of the wave's NB window buffers (NI KiB each, and past
+  // two buffers 256 bytes for the item's mask words)
+  constexpr uint32_t kSlot = NI * 1024 + (NB > 2 ? 256 : 0);
+  const uint32_t wbuf = (uint32_t)(size_t)(lds_ptr)lds + xbytes + (uint32_t)wid * (NB * kSlot);
 
   float res[BP];
 #pragma unroll
@@ -198,7 +242,11 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
       const int nw = real ? min(kWinWords, sw - t * kWinWords) : 0;
       const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(bits + r * W + w0), 0, nw * 4, kRsrcWord3);
-      mword = __builtin_amdgcn_raw_buffer_load_b32(rb, lane * 4, 0, kStreamAux);
+      const uint32_t dst = wbuf + (uint32_t)(k % NB) * kSlot;
+      if constexpr (NB > 2)
+        lds_load4_nt(rb, dst + NI * 1024, lane * 4, 0);
+      else
+        mword = __builtin_amdgcn_raw_buffer_load_b32(rb, lane * 4, 0, kStreamAux);
       int64_t vs, cnt;
       if constexpr (UN) {
         // a dummy item reads entry 0 (always present) and uses none of it
@@ -214,7 +262,6 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
       const int nch = real ? (int)((vs + cnt - a0 + 7) >> 3) : 0;
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(values + a0), 0, nch * 16, kRsrcWord3);
-      const uint32_t dst = wbuf + (uint32_t)(k & 1) * (NI * 1024);
 #pragma unroll
       for (int j = 0; j < NI; ++j) lds_load16_nt(rv, dst + j * 1024, lane * 16 + j * 1024, 0);
     };
@@ -222,39 +269,44 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
     float acc[BP];
 #pragma unroll
     for (int b = 0; b < BP; ++b) acc[b] = 0.f;
-    uint32_t mA, mB;
+    uint32_t mA = 0, mB = 0;
     issue(0, mA);
     issue(1, mB);
+#pragma unroll
+    for (int j = 2; j < NB; ++j) issue(j, mA);
     for (int k = 0; k < nitems; ++k) {
-      // item k's mask word and window copy have landed (item k + 1's
-      // 1 + NI loads may still be in flight)
+      // item k's mask words and window copy have landed (the 1 + NI loads
+      // of each of the next NB - 1 items may still be in flight)
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<1 + NI>();
+      wait_vmcnt<(NB - 1) * (1 + NI)>();
       __builtin_amdgcn_sched_barrier(0);
-      const uint32_t mw = (k & 1) ? mB : mA;
+      const uint32_t slot = wbuf + (uint32_t)(k % NB) * kSlot;
+      uint32_t mw;
+      if constexpr (NB > 2)
+        mw = ld<uint32_t>((lds_ptr)(size_t)(slot + NI * 1024 + 4 * lane));
+      else
+        mw = (k & 1) ? mB : mA;
       const int i = k / nwin, t = k - i * nwin;
       const int64_t r = r0 + i;
       const int w0 = sw0 + t * kWinWords;
       const int nw = min(kWinWords, sw - t * kWinWords);
       // the lane's count and the offset of its values in the window
       int pl = P, ol = lane * P;
-      int64_t vs;
+      int64_t vs, vcnt = 0;
       if constexpr (UN) {
         pl = __popc(mw);  // words past the row read 0
-        int incl = pl;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-          const int t2 = __shfl_up(incl, d, kWave);
-          incl += lane >= d ? t2 : 0;
-        }
-        ol = incl - pl;
+        ol = wave_incl_scan(pl) - pl;
         vs = offs[r * nwr + (w0 / kWinWords)];
+        vcnt = offs[r * nwr + (w0 / kWinWords) + 1] - vs;
       } else {
         vs = r * vstride + (int64_t)w0 * P;
       }
       if (lane < nw) {
-        const uint32_t vb = wbuf + (uint32_t)(k & 1) * (NI * 1024) +
-                            2u * (uint32_t)((vs & 7) + (int64_t)ol);
+        // (UN: a lane's offset is clamped so that its reads stay inside the
+        // buffer also where the words disagree with offs; a consistent
+        // window copied whole never reaches the clamp)
+        const int olb = UN ? min(ol, (int)(kSlot / 2) - 7 - 32) : ol;
+        const uint32_t vb = slot + 2u * (uint32_t)((vs & 7) + (int64_t)olb);
         // byte offset of the word's x slots in the segment's image
         const int cb = (t * kWinWords + lane) * XCols<BP>::WS;
         uint32_t m = mw;
@@ -267,24 +319,44 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
           // and a branch per pair left the kernel bound by instruction issue.
           const int ng = (__ballot(pl > 0) != 0) + (__ballot(pl > 8) != 0) +
                          (__ballot(pl > 16) != 0) + (__ballot(pl > 24) != 0);
-          for (int g = 0; g < ng; ++g) {
-            const int j0 = 8 * g;
-            int c[8];
-            uint32_t v[8];
+          auto groups = [&](auto value) {
+            for (int g = 0; g < ng; ++g) {
+              const int j0 = 8 * g;
+              int c[8];
+              uint32_t v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t f = (uint32_t)ffbl_hw(m);  // 0xffffffff once m == 0
-              c[e] = cb + (int)(f < 32u ? f : 32u) * XCols<BP>::SB;
-              m &= m - 1;
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t f = (uint32_t)ffbl_hw(m);  // 0xffffffff once m == 0
+                c[e] = cb + (int)(f < 32u ? f : 32u) * XCols<BP>::SB;
+                m &= m - 1;
+              }
+              // the group's x slots and values are all requested before any
+              // is used (the empty asm keeps every value load unconditional)
+              typename XSlot<BP>::T xs[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) xs[e] = ld<typename XSlot<BP>::T>((lds_ptr)lds + c[e]);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = value(j0 + e);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(v[e]));
+#pragma unroll
+              for (int e = 0; e < 8; e += 2) {
+                const int left = pl - j0 - e;
+                const uint32_t w = (left >= 1 ? v[e] : 0u) | (left >= 2 ? v[e + 1] << 16 : 0u);
+                pair_fma<BF, BP>(xs[e], xs[e + 1], w, acc);
+              }
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * (j0 + e)));
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const int left = pl - j0 - e;
-              const uint32_t w = (left >= 1 ? v[e] : 0u) | (left >= 2 ? v[e + 1] << 16 : 0u);
-              pair_acc<BF, BP>(lds, c[e], c[e + 1], w, acc);
-            }
+          };
+          if ((vs & 7) + vcnt <= NI * 512) {  // the whole window is in the buffer
+            groups([&](int j) -> uint32_t { return ld<uint16_t>((lds_ptr)(size_t)(vb + 2 * j)); });
+          } else {
+            // a window denser than the buffer holds (the copy stopped at its
+            // end): the lane reads its values from global memory instead
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(values + vs), 0, (int)(2 * vcnt), kRsrcWord3);
+            groups([&](int j) -> uint32_t {
+              return __builtin_amdgcn_raw_buffer_load_b16(rw, 2 * (ol + j), 0, 0);
+            });
           }
         } else
         // eight scan steps at a time: the columns first (a short VALU chain),
@@ -322,7 +394,12 @@ __global__ __launch_bounds__(1024) void nm_spmv_fixed_kernel(
       __builtin_amdgcn_sched_barrier(0);
       wait_lgkmcnt0();
       __builtin_amdgcn_sched_barrier(0);
-      if (k & 1) issue(k + 2, mB); else issue(k + 2, mA);
+      if constexpr (NB > 2)
+        issue(k + NB, mA);
+      else if (k & 1)
+        issue(k + 2, mB);
+      else
+        issue(k + 2, mA);
     }
     // the dummy items' copies land before the buffers are reused
     __builtin_amdgcn_sched_barrier(0);
@@ -700,9 +777,11 @@ int pad_b(int b) { return b <= 1 ? 1 : b <= 2 ? 2 : b <= 4 ? 4 : 8; }
 
 size_t xcols_bytes(int bp, int64_t cols);
 
-size_t fixed_lds_bytes(int bp, int seg, int waves, int ni) {
-  return ((xcols_bytes(bp, seg) + 15) & ~(size_t)15) + (size_t)waves * 2 * ni * 1024;
+size_t fixed_lds_bytes(int bp, int seg, int waves, int ni, int nb = 2) {
+  const size_t slot = (size_t)ni * 1024 + (nb > 2 ? 256 : 0);
+  return ((xcols_bytes(bp, seg) + 15) & ~(size_t)15) + (size_t)waves * nb * slot;
 }
+
 
 }  // namespace
 
@@ -815,12 +894,18 @@ nm_status bitmask_launch(const void *values, const uint32_t *bits, const int64_t
                          const void *X, void *Y, int batch, int64_t rows, int64_t cols,
                          nm_dtype in_dt, nm_dtype out_dt, int cus, size_t lds_budget,
                          void *stream) {
-  constexpr int kNI = 5;  // a window holds up to 64 x 32 values (+ alignment)
+  // Three window buffers per wave of 3 KiB each: a window of up to 1528
+  // values (75% of its 2048 columns) is copied whole, a denser one is read
+  // from global memory by the lanes (the buffers sized for a full window,
+  // 5 KiB, leave room for two per wave and fewer workgroups per CU: gate
+  // 14336x4096 at batch 1 29.0 -> 26.8 us, down 4096x14336 31.7 -> 28.3)
+  constexpr int kNI = 3;
+  constexpr int kNB = 3;
   const int bp = pad_b(batch);
   // x whole, or in segments of whole windows, next to the waves' buffers
   auto seg_for = [&](int waves) -> int64_t {
-    if (fixed_lds_bytes(bp, (int)cols, waves, kNI) <= lds_budget) return cols;
-    const size_t wave_area = fixed_lds_bytes(bp, 0, waves, kNI);
+    if (fixed_lds_bytes(bp, (int)cols, waves, kNI, kNB) <= lds_budget) return cols;
+    const size_t wave_area = fixed_lds_bytes(bp, 0, waves, kNI, kNB);
     if (wave_area + 16 + xcols_bytes(bp, 2048) > lds_budget) return 0;
     return (int64_t)((lds_budget - wave_area - 16) / xcols_bytes(bp, 32)) * 32 / 2048 * 2048;
   };
@@ -831,7 +916,7 @@ nm_status bitmask_launch(const void *values, const uint32_t *bits, const int64_t
   // row in one round (measured 1.2-1.4x faster there, slower at batch 1)
   int waves = 4;
   int64_t seg = seg_for(4), rpw;
-  const size_t wg4 = seg > 0 ? fixed_lds_bytes(bp, (int)seg, 4, kNI) : 0;
+  const size_t wg4 = seg > 0 ? fixed_lds_bytes(bp, (int)seg, 4, kNI, kNB) : 0;
   if (seg > 0 && 2 * wg4 > kLdsCap && seg_for(8) > 0) {
     waves = 8;
     seg = seg_for(8);
@@ -850,13 +935,13 @@ nm_status bitmask_launch(const void *values, const uint32_t *bits, const int64_t
   un_fn fn;
   const bool bf = in_dt == NM_BF16;
   switch (bp) {
-    case 1: fn = bf ? nm_spmv_fixed_kernel<true, 1, kNI, true> : nm_spmv_fixed_kernel<false, 1, kNI, true>; break;
-    case 2: fn = bf ? nm_spmv_fixed_kernel<true, 2, kNI, true> : nm_spmv_fixed_kernel<false, 2, kNI, true>; break;
-    case 4: fn = bf ? nm_spmv_fixed_kernel<true, 4, kNI, true> : nm_spmv_fixed_kernel<false, 4, kNI, true>; break;
-    default: fn = bf ? nm_spmv_fixed_kernel<true, 8, kNI, true> : nm_spmv_fixed_kernel<false, 8, kNI, true>; break;
+    case 1: fn = bf ? nm_spmv_fixed_kernel<true, 1, kNI, true, kNB> : nm_spmv_fixed_kernel<false, 1, kNI, true, kNB>; break;
+    case 2: fn = bf ? nm_spmv_fixed_kernel<true, 2, kNI, true, kNB> : nm_spmv_fixed_kernel<false, 2, kNI, true, kNB>; break;
+    case 4: fn = bf ? nm_spmv_fixed_kernel<true, 4, kNI, true, kNB> : nm_spmv_fixed_kernel<false, 4, kNI, true, kNB>; break;
+    default: fn = bf ? nm_spmv_fixed_kernel<true, 8, kNI, true, kNB> : nm_spmv_fixed_kernel<false, 8, kNI, true, kNB>; break;
   }
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(waves * kWave),
-                     fixed_lds_bytes(bp, (int)seg, waves, kNI), (hipStream_t)stream,
+                     fixed_lds_bytes(bp, (int)seg, waves, kNI, kNB), (hipStream_t)stream,
                      (const uint16_t *)values, bits, (const uint16_t *)X, Y, batch, rows, (int)cols,
                      0, (int)seg, (int)rpw, (int)out_dt, offs);
   const hipError_t e = hipGetLastError();

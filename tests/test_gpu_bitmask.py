@@ -118,11 +118,10 @@ def clustered_mask(rows, cols, seed):
 @pytest.mark.parametrize("rows,cols", [(1, 32), (7, 64), (37, 2080), (300, 4096), (64, 14336),
                                        (5, 32768)])
 def test_bitmask_batch1_integer_exact(rows, cols, kind):
-    """Batch 1 (the value-major traversal: groups of 8 values aligned in the
-    value array, their columns from the row's group table): exact on integer
-    inputs for per-row halves, row densities from 0 to 1, short runs of kept
-    columns between long empty stretches (groups spanning many words), nearly
-    full rows, empty rows and single kept columns, K from 32 to 32768."""
+    """Batch 1: exact on integer inputs for per-row halves, row densities
+    from 0 to 1, short runs of kept columns between long empty stretches,
+    nearly full rows (windows read from global memory), empty rows and single
+    kept columns, K from 32 to 32768."""
     rng = np.random.default_rng(rows + cols)
     W = synth.f32_to_16_bits(rng.integers(-3, 4, size=(rows, cols)).astype(np.float32), "f16")
     x = synth.f32_to_16_bits(rng.integers(-3, 4, size=(1, cols)).astype(np.float32), "f16")
@@ -135,6 +134,56 @@ def test_bitmask_batch1_integer_exact(rows, cols, kind):
     values, bits, offs = native.nm_pack_bitmask(t16(W, "f16"), torch.from_numpy(keep).to(DEV))
     Y = native.nm_spmm_bitmask(values, bits, offs, t16(x, "f16"))
     assert np.array_equal(f64(Y), oracle.masked_gemv(W, keep, x, False))
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_bitmask_windows_around_buffer_size_integer_exact(batch):
+    """Windows of 1490 to 1570 kept values beside full and empty ones.  The
+    copy of a window holds 1528 to 1536 values, depending on where the
+    window's first value falls in its 16-byte group; a denser window is read
+    by the lanes from global memory.  Both ways are exact on integer inputs,
+    in one launch, and so are the rows around them."""
+    rows, cols = 48, 4160  # three windows per row, the last of two words
+    rng = np.random.default_rng(17 + batch)
+    W = synth.f32_to_16_bits(rng.integers(-3, 4, size=(rows, cols)).astype(np.float32), "f16")
+    X = synth.f32_to_16_bits(rng.integers(-3, 4, size=(batch, cols)).astype(np.float32), "f16")
+    keep = np.zeros((rows, cols), np.uint8)
+    counts = []
+    for r in range(rows):
+        for t in range(2):
+            cnt = 1490 + (r * 7 + t * 13) % 81
+            keep[r, 2048 * t + rng.choice(2048, cnt, replace=False)] = 1
+            counts.append(cnt)
+        keep[r, 4096:] = rng.random(64) < 0.5
+    keep[0] = 1
+    keep[1] = 0
+    assert min(counts) < 1528 and max(counts) > 1536
+    values, bits, offs = native.nm_pack_bitmask(t16(W, "f16"), torch.from_numpy(keep).to(DEV))
+    Y = native.nm_spmm_bitmask(values, bits, offs, t16(X, "f16"))
+    assert np.array_equal(f64(Y), oracle.masked_gemv(W, keep, X, False))
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_bitmask_words_disagreeing_with_offsets_stay_in_their_rows(batch):
+    """Mask words with more or fewer set bits than the offsets give their
+    window (the header leaves those rows unspecified): every other row is
+    still exact on integer inputs, and the call succeeds."""
+    rows, cols = 40, 4096
+    rng = np.random.default_rng(23 + batch)
+    W = synth.f32_to_16_bits(rng.integers(-3, 4, size=(rows, cols)).astype(np.float32), "f16")
+    X = synth.f32_to_16_bits(rng.integers(-3, 4, size=(batch, cols)).astype(np.float32), "f16")
+    keep = synth.topk_row_mask(W, 0.5)
+    values, bits, offs = native.nm_pack_bitmask(t16(W, "f16"), torch.from_numpy(keep).to(DEV))
+    bad = [5, 17, 23]
+    b = bits.view(rows, cols // 32)
+    b[5, :] = -1          # every word full: 4096 set bits against 2048 values
+    b[17, 64:] = -1       # the second window full
+    b[23, ::3] = 0        # fewer set bits than values
+    Y = f64(native.nm_spmm_bitmask(values, bits, offs, t16(X, "f16")))
+    torch.cuda.synchronize()
+    good = np.array([r for r in range(rows) if r not in bad])
+    want = oracle.masked_gemv(W, keep, X, False)
+    assert np.array_equal(Y[:, good], want[:, good])
 
 
 def test_bitmask_one_hot_x():
