@@ -203,22 +203,67 @@ __device__ __forceinline__ void accum_pair(P p0, P p1, uint32_t w, float (&acc)[
   }
 }
 
+// The BP batch values of one x slot, as loaded from LDS.
+template <int BP> struct SlotT { using T = u32x4_t; };
+template <> struct SlotT<1> { using T = uint16_t; };
+template <> struct SlotT<2> { using T = uint32_t; };
+template <> struct SlotT<4> { using T = u32x2_t; };
+
+// accum_pair on x slots already in registers.
+template <bool BF, int BP>
+__device__ __forceinline__ void accum_slots(typename SlotT<BP>::T a, typename SlotT<BP>::T b,
+                                            uint32_t w, float (&acc)[BP]) {
+  if constexpr (BP == 1) {
+    acc[0] = dot2<BF>(w, (uint32_t)a | ((uint32_t)b << 16), acc[0]);
+  } else if constexpr (BP == 2) {
+    acc[0] = dot2<BF>(w, (a & 0xffffu) | (b << 16), acc[0]);
+    acc[1] = dot2<BF>(w, (a >> 16) | (b & 0xffff0000u), acc[1]);
+  } else {
+#pragma unroll
+    for (int d = 0; d < BP / 2; ++d) {
+      acc[2 * d] = dot2<BF>(w, (a[d] & 0xffffu) | (b[d] << 16), acc[2 * d]);
+      acc[2 * d + 1] = dot2<BF>(w, (a[d] >> 16) | (b[d] & 0xffff0000u), acc[2 * d + 1]);
+    }
+  }
+}
+
 // Generic fixed-step traversal (item (2)): the chunk's 8 kept weights are
 // the 8 lowest set bits of m; each step takes the lowest set bit as the next
-// kept column and clears it, and two steps feed one pair.
-template <bool BF, int BP>
+// kept column and clears it, and two steps feed one pair.  TOGETHER: the 8
+// columns are found first and their x slots read together, one LDS round trip
+// per chunk (8:16: gate 14336x4096 13.64 -> 13.26 us, k 1024x4096 3.70 ->
+// 3.40 at batch 1); else each pair's reads follow its two steps, which
+// overlaps the reads with the longer chain of 16:32 (whose odd lanes first
+// clear 8 bits; 1-3% faster that way).
+template <bool BF, int BP, bool TOGETHER = true>
 __device__ __forceinline__ void chunk8_scan(const char *wb, uint32_t m, const uint4 v,
                                             float (&acc)[BP]) {
+  using T = typename SlotT<BP>::T;
   const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (!TOGETHER) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // m is never zero here (see the callers), so v_ffbl_b32 is well defined
-    const int c0 = __builtin_ctz(m);
-    m &= m - 1;
-    const int c1 = __builtin_ctz(m);
-    m &= m - 1;
-    accum_pair<BF, BP>(wb + c0 * XLay<BP>::SB, wb + c1 * XLay<BP>::SB, vv[j], acc);
+    for (int j = 0; j < 4; ++j) {
+      // m is never zero here (see the callers), so v_ffbl_b32 is well defined
+      const int c0 = __builtin_ctz(m);
+      m &= m - 1;
+      const int c1 = __builtin_ctz(m);
+      m &= m - 1;
+      accum_pair<BF, BP>(wb + c0 * XLay<BP>::SB, wb + c1 * XLay<BP>::SB, vv[j], acc);
+    }
+    return;
   }
+  int c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    // m is never zero here (see the callers), so v_ffbl_b32 is well defined
+    c[e] = __builtin_ctz(m) * XLay<BP>::SB;
+    m &= m - 1;
+  }
+  T xs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) xs[e] = ld<T>(wb + c[e]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) accum_slots<BF, BP>(xs[2 * j], xs[2 * j + 1], vv[j], acc);
 }
 
 // 2:4: nibble j of the lane's 16 columns holds exactly the pair j of kept
@@ -478,7 +523,7 @@ __device__ __forceinline__ void chunk(const char *lds, int q, uint32_t mw, const
 #pragma unroll
       for (int k = 0; k < 8; ++k) m &= m - 1;
     }
-    chunk8_scan<BF, BP>(lds + base, m, v, acc);
+    chunk8_scan<BF, BP, false>(lds + base, m, v, acc);
   }
 }
 
