@@ -266,6 +266,37 @@ __device__ __forceinline__ void chunk8_scan(const char *wb, uint32_t m, const ui
   for (int j = 0; j < 4; ++j) accum_slots<BF, BP>(xs[2 * j], xs[2 * j + 1], vv[j], acc);
 }
 
+// 16:32: a word keeps 16 columns, lane h of the pair takes kept values
+// 8h .. 8h + 7.  Lane 0 takes the word's 8 lowest set bits.  Lane 1 takes
+// its 8 highest: it scans the bit-reversed word from the bottom, so both
+// lanes walk 8 steps (rather than lane 1 first clearing 8 bits), finds the
+// columns in descending order (column 31 - f), and so meets its values in
+// reverse: the pair of steps 2j, 2j + 1 holds values 15 - 2j and 14 - 2j,
+// which are the halves of the lane's value word 3 - j swapped.
+template <bool BF, int BP>
+__device__ __forceinline__ void chunk16_scan(const char *wb, uint32_t m, uint32_t h,
+                                             const uint4 v, float (&acc)[BP]) {
+  using T = typename SlotT<BP>::T;
+  const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t flip = h ? 31u : 0u;
+  m = h ? __builtin_bitreverse32(m) : m;
+  int c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    // 16 set bits, so m is never zero here
+    c[e] = (int)(((uint32_t)__builtin_ctz(m) ^ flip) * XLay<BP>::SB);
+    m &= m - 1;
+  }
+  T xs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) xs[e] = ld<T>(wb + c[e]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = h ? __builtin_amdgcn_alignbit(vv[3 - j], vv[3 - j], 16) : vv[j];
+    accum_slots<BF, BP>(xs[2 * j], xs[2 * j + 1], w, acc);
+  }
+}
+
 // 2:4: nibble j of the lane's 16 columns holds exactly the pair j of kept
 // weights, so its lowest and highest set bits are their columns: one ffbl and
 // one ffbh per pair replace the serial scan.  A malformed nibble (no set bit)
@@ -519,11 +550,17 @@ __device__ __forceinline__ void chunk(const char *lds, int q, uint32_t mw, const
     // a word without exactly 16 set bits is replaced by one that keeps the
     // scan in range (its row's result is then undefined)
     if (__popc(m) != 16) m = 0xffffu;
-    if (h) {
+    if constexpr (BP == 1) {
+      // (one token: lane 1 clears its 8 lower set bits first; the reversed
+      // scan measured 1-8% slower here, 15% faster on 6144x4096 at batch 2-4)
+      if (h) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) m &= m - 1;
+        for (int k = 0; k < 8; ++k) m &= m - 1;
+      }
+      chunk8_scan<BF, BP, false>(lds + base, m, v, acc);
+    } else {
+      chunk16_scan<BF, BP>(lds + base, m, h, v, acc);
     }
-    chunk8_scan<BF, BP, false>(lds + base, m, v, acc);
   }
 }
 
