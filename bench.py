@@ -279,10 +279,10 @@ def cpu_baseline(projs, gpu_y, min_cpu_seconds=10.0):
 MEASURED_TRAFFIC = {
     # (rows, cols): (kernel_digest() when measured, bytes per launch) at batch
     # 1; see profiles/nm_spmv_2of4_hbm_counters.md
-    (14336, 4096): ("0511e9068abfdd025b7d199432546b196ec49da80b2e15f4e7462f1cab83b26a",
-                    66275643),
-    (8192, 8192): ("0511e9068abfdd025b7d199432546b196ec49da80b2e15f4e7462f1cab83b26a",
-                   75743157),
+    (14336, 4096): ("5ddfbc6d4d2838a4f4a6857beb7bb3b319bd12e7a16d221176aa3ddb675658c0",
+                    66268478),
+    (8192, 8192): ("5ddfbc6d4d2838a4f4a6857beb7bb3b319bd12e7a16d221176aa3ddb675658c0",
+                   75736120),
 }
 
 
