@@ -5,10 +5,10 @@
 // LLM Inference" (paper text):
 //   - Method, kernel subsection, item (1) "Bitmask indexing": per row one bit
 //     per column, kept weights stored in increasing column order;
-//   - item (2) "Fixed-step bitmask traversal": at 50% N:M density each
-//     aligned 32-bit word has exactly 16 set bits, so the per-word loop has a
-//     fixed trip count; each step takes the least significant set bit as the
-//     next kept column and clears it;
+//   - item (2) "Fixed-step bitmask traversal": a 50% N:M pattern with M
+//     dividing 32 keeps half of the 32 columns of every word, so the loop
+//     over a word runs a known number of steps; each step takes the least
+//     significant set bit as the next kept column and clears it;
 //   - Appendix C: one kernel per pattern with N and M fixed at compile time.
 // The Triton/A100 kernel described there is prior art only; the design here
 // is for CDNA4.  Batch 1 (and every pattern at batch <= 4) runs on the
