@@ -295,6 +295,28 @@ def test_24_batch1_malformed_mask_words_stay_in_their_row(dtype):
     assert np.array_equal(y[good], want[good])
 
 
+@pytest.mark.parametrize("batch", [1, 2, 4])
+@pytest.mark.parametrize("n,m", [(4, 8), (8, 16), (16, 32)])
+def test_scan_patterns_malformed_mask_words_stay_in_their_row(n, m, batch):
+    """Mask words that break the pattern (no set bit, all set, too few or
+    too many in a group) only make their own row's sum undefined under the
+    default launch: every other row stays exact on integer inputs."""
+    rows, cols = 300, 4096
+    W = synth.integer_weights(rows, cols, seed=31, dtype="bf16")
+    keep = synth.random_mask(rows, cols, n, m, seed=32)
+    xi = np.random.default_rng(33).integers(-4, 5, size=(batch, cols)).astype(np.float32)
+    X = synth.f32_to_16_bits(xi, "bf16")
+    values, bits = gpu_pack(W, keep, n, m, "bf16")
+    bad = [0, 7, 150, 299]
+    b = bits.clone()
+    for i, r in enumerate(bad):
+        b[r, (37 * i) % b.shape[1]] = [0, -1, 0x77777777, 0x1][i]
+    Y = f64(native.nm_spmm_small(values, b, t16(X, "bf16"), n, m))
+    want = oracle.masked_gemv(W, keep, X, True)
+    good = np.setdiff1d(np.arange(rows), bad)
+    assert np.array_equal(Y[:, good], want[:, good])
+
+
 @pytest.mark.parametrize("n,m", PATTERNS)
 def test_one_hot_x_selects_a_column(n, m):
     """x = e_j gives y[r] = W[r, j] * keep[r, j] exactly: pins the bit ->
