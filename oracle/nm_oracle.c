@@ -21,7 +21,7 @@
  *     masked weight matrix with x, so the oracle computes that definition in
  *     fp64 from the dense masked form, never from the packed form.
  *
- * Readings of points the pages leave open (listed again in the design doc):
+ * Readings of points the pages leave open:
  *   - bit b (LSB = 0) of word w of a row <-> column 32*w + b, so an LSB-first
  *     scan visits kept columns in increasing order;
  *   - values are row-major, row stride cols*N/M elements; bits row-major, row
